@@ -1,0 +1,234 @@
+"""CPU oracle for the JSSA sparse decode step: plain, slow, fp64.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check of the entry
+module and the CPU-baseline leg of the benchmark may import this module. The
+HIP library never calls it and shares no code with it; the only thing both
+sides share is the seeded input generator (token_level_sparse_amd.synth),
+which holds none of the method's arithmetic.
+
+Each function computes one step of the method directly from its definition,
+in float64, with numpy primitives (matmul, exp, sort) as the only building
+blocks. Sources (page title, section):
+
+* [JSSA-A]  "Joint Subspace Sparse Attention for Efficient Long-Context
+            Decoding" (weekinpapers, arXiv 2610.19026v1), Abstract.
+* [JSSA-S]  ai4snews digest "JSSA makes token-level sparse decoding
+            gather-free ...", Synopsis.
+* [JSSA-I]  same digest, Interpretation (scoring space, gather-free reads).
+* [JSSA-P]  same digest, Perspective (GQA / hybrid / MLA coverage).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+R1 group aggregation: a KV head's score is the raw sum over its GQA group of
+   the query heads' subspace scores (by linearity: the projected group-summed
+   query dotted with the projected key).
+R2 the projected key cache stores bf16(K_j P_j), rounded to nearest-even
+   from the exact (fp64) product.
+R3 selection: the first min(k, T_b) tokens of the total order (score
+   descending, token index ascending), returned ascending by index and padded
+   with -1. The decision is taken on scores rounded to fp32, the precision of
+   the GPU path's score buffer; -0.0 ranks equal to +0.0.
+R4 attention over a selected set: softmax(scale * q K_S^T) V_S per query
+   head, base e, with log-sum-exp lse = m + ln(sum exp(l - m)); an empty set
+   gives o = 0, lse = -inf.
+R5 split partials merge by weights exp(lse_s) (log-sum-exp combine).
+R6 query head h reads KV head floor(h / G).
+R7 paged layout: token t of sequence b lives in page table[b][t // 16], slot
+   t % 16, of a pool laid out [pages, Hkv, 16, width].
+R8 MLA: keys are [W_uk[h] c[:512]; c[512:]], values c[:512], output
+   W_uv[h] (sum_t p_t c_t[:512]); the selection score projects the summed
+   absorbed query [W_uk[h]^T q_nope; q_rope] and the latent row through one
+   rank-r basis; one selected set per sequence.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 16
+
+
+# ---------------------------------------------------------------------------
+# bf16 helpers (storage type of q, K, V, Kp)
+# ---------------------------------------------------------------------------
+def bf16_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns exactly: a bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to bf16 (8 significant bits), nearest-even, and
+    return the bit patterns. Written from the definition: scale the value so
+    its quantum becomes 1, round to the nearest integer (ties to even), scale
+    back. The quantum of a bf16 normal in [2^(e-1), 2^e) is 2^(e-8); bf16
+    subnormals share the fixed quantum 2^-133."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    quantum_exp = np.maximum(e - 8, -133)
+    rounded = np.ldexp(np.rint(np.ldexp(x, -quantum_exp)), quantum_exp)
+    with np.errstate(over="ignore"):          # beyond the bf16 range -> inf
+        r32 = rounded.astype(np.float32)
+    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Step 1 (append / build): the projected key cache  [JSSA-S], [JSSA-A]
+# Scoring happens in a low-dimensional subspace shared by queries and keys;
+# keys are kept projected so that scoring reads r values per token (R2).
+# ---------------------------------------------------------------------------
+def project_keys(K_bits, P) -> np.ndarray:
+    """Kp = bf16(K P) for rows K [n,d] (bf16 bits) and basis P [d,r]."""
+    return round_to_bf16(bf16_to_f64(K_bits) @ np.asarray(P, np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Step 2: subspace scores per KV head  [JSSA-S], [JSSA-I], [JSSA-A]
+# ---------------------------------------------------------------------------
+def group_heads(j: int, G: int) -> range:
+    """Query heads served by KV head j (R6)."""
+    return range(j * G, (j + 1) * G)
+
+
+def project_query(q_group_bits, P_j) -> np.ndarray:
+    """qp = P_j^T sum_h q_h over the group's query heads (R1)."""
+    qbar = bf16_to_f64(q_group_bits).sum(axis=0)
+    return np.asarray(P_j, np.float64).T @ qbar
+
+
+def subspace_scores(q_group_bits, P_j, Kp_bits) -> np.ndarray:
+    """s_t = qp . Kp_t for every row of Kp [n,r]; fp64."""
+    return bf16_to_f64(Kp_bits) @ project_query(q_group_bits, P_j)
+
+
+# ---------------------------------------------------------------------------
+# Step 3: distinct top-k token set per KV head  [JSSA-S], [JSSA-A]
+# ---------------------------------------------------------------------------
+def select_topk(scores, k: int) -> np.ndarray:
+    """Indices of the first min(k, n) tokens in the order (score desc, index
+    asc), sorted ascending and padded with -1 to length k (R3)."""
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s32.shape[0]
+    order = np.lexsort((np.arange(n), -s32))
+    keep = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, np.int64)
+    out[:keep.shape[0]] = keep
+    return out
+
+
+def kth_score(scores, k: int) -> float:
+    """The score of the last token the selection keeps (fp64)."""
+    s = np.asarray(scores, np.float64)
+    s32 = s.astype(np.float32).astype(np.float64)
+    order = np.lexsort((np.arange(s.shape[0]), -s32))
+    return float(s[order[min(k, s.shape[0]) - 1]])
+
+
+# ---------------------------------------------------------------------------
+# Step 4: attention over the selected rows  [JSSA-I], [JSSA-A]
+# Selected rows are used where they lie in the cache; the arithmetic is that
+# of ordinary softmax attention restricted to the selected set (R4).
+# ---------------------------------------------------------------------------
+def attend(q_bits, K_rows_bits, V_rows_bits, scale: float):
+    """o [G,d], lse [G] for query rows q [G,d] over key/value rows [n,d]."""
+    q = bf16_to_f64(q_bits)
+    G = q.shape[0]
+    V_rows_bits = np.asarray(V_rows_bits)
+    n = V_rows_bits.shape[0]
+    if n == 0:
+        return np.zeros((G, V_rows_bits.shape[1])), np.full(G, -np.inf)
+    Kr = bf16_to_f64(K_rows_bits)
+    Vr = bf16_to_f64(V_rows_bits)
+    logits = scale * (q @ Kr.T)
+    m = logits.max(axis=1)
+    w = np.exp(logits - m[:, None])
+    l = w.sum(axis=1)
+    return (w @ Vr) / l[:, None], m + np.log(l)
+
+
+def combine(part_o, part_lse):
+    """Merge split partials o_s [S,d], lse_s [S] into (o [d], lse) (R5)."""
+    part_o = np.asarray(part_o, np.float64)
+    part_lse = np.asarray(part_lse, np.float64)
+    m = part_lse.max()
+    if m == -np.inf:
+        return np.zeros(part_o.shape[-1]), -np.inf
+    w = np.exp(part_lse - m)
+    return (w[:, None] * part_o).sum(axis=0) / w.sum(), m + np.log(w.sum())
+
+
+# ---------------------------------------------------------------------------
+# Paged addressing (R7)
+# ---------------------------------------------------------------------------
+def paged_rows(pool, table_row, j: int, t) -> np.ndarray:
+    """Rows of KV head j at logical positions t from a pool [pages,Hkv,16,w]."""
+    t = np.asarray(t, np.int64)
+    return np.asarray(pool)[np.asarray(table_row)[t // PAGE], j, t % PAGE]
+
+
+def logical_rows(cache, b: int, j: int, t, page_table=None) -> np.ndarray:
+    if page_table is None:
+        return np.asarray(cache)[b, j, np.asarray(t, np.int64)]
+    return paged_rows(cache, page_table[b], j, t)
+
+
+# ---------------------------------------------------------------------------
+# Whole step on one (sequence, KV head) unit
+# ---------------------------------------------------------------------------
+def sparse_unit(q_group_bits, P_j, Kp_bits, K_bits, V_bits, k: int, scale: float):
+    """Score -> select -> attend for one (b, j) whose cache rows are given
+    logically ([T_b, .]). Returns (scores fp64, idx, o [G,d], lse [G])."""
+    s = subspace_scores(q_group_bits, P_j, Kp_bits)
+    idx = select_topk(s, k)
+    sel = idx[idx >= 0]
+    o, lse = attend(q_group_bits, np.asarray(K_bits)[sel], np.asarray(V_bits)[sel], scale)
+    return s, idx, o, lse
+
+
+def dense_unit(q_group_bits, K_bits, V_bits, scale: float):
+    """Full-KV attention for one (b, j): every cached row t < T_b."""
+    return attend(q_group_bits, K_bits, V_bits, scale)
+
+
+# ---------------------------------------------------------------------------
+# MLA shared latent cache  [JSSA-P] (R8)
+# ---------------------------------------------------------------------------
+def mla_absorbed_query(q_nope_bits, q_rope_bits, W_uk_bits) -> np.ndarray:
+    """qa_h = [W_uk[h]^T q_nope_h ; q_rope_h] for every head: [H, d_c]."""
+    qn = bf16_to_f64(q_nope_bits)            # [H, d_nope]
+    W = bf16_to_f64(W_uk_bits)               # [H, d_nope, d_latent]
+    q_lat = np.einsum("hi,hic->hc", qn, W)
+    return np.concatenate([q_lat, bf16_to_f64(q_rope_bits)], axis=1)
+
+
+def mla_scores(q_nope_bits, q_rope_bits, W_uk_bits, P, Kp_lat_bits) -> np.ndarray:
+    """s_t = (P^T sum_h qa_h) . Kp_lat_t; one score per latent row."""
+    qbar = mla_absorbed_query(q_nope_bits, q_rope_bits, W_uk_bits).sum(axis=0)
+    return bf16_to_f64(Kp_lat_bits) @ (np.asarray(P, np.float64).T @ qbar)
+
+
+def mla_attend_explicit(q_nope_bits, q_rope_bits, W_uk_bits, W_uv_bits, C_rows_bits, scale: float):
+    """Explicit (non-absorbed) MLA attention over latent rows C [n, d_c]:
+    per head, keys k_t = [W_uk[h] c_t[:L]; c_t[L:]], values v_t = c_t[:L],
+    output W_uv[h] (sum_t p_t v_t). Returns (o [H, d_v], o_lat [H, L], lse [H])."""
+    qn = bf16_to_f64(q_nope_bits)
+    qr = bf16_to_f64(q_rope_bits)
+    Wk = bf16_to_f64(W_uk_bits)
+    Wv = bf16_to_f64(W_uv_bits)
+    C = bf16_to_f64(C_rows_bits)
+    H, L = Wk.shape[0], Wk.shape[2]
+    n = C.shape[0]
+    o = np.zeros((H, Wv.shape[1]))
+    o_lat = np.zeros((H, L))
+    lse = np.full(H, -np.inf)
+    if n == 0:
+        return o, o_lat, lse
+    c_lat, c_rope = C[:, :L], C[:, L:]
+    for h in range(H):
+        k_nope = c_lat @ Wk[h].T                       # [n, d_nope]
+        logits = scale * (k_nope @ qn[h] + c_rope @ qr[h])
+        m = logits.max()
+        w = np.exp(logits - m)
+        o_lat[h] = (w @ c_lat) / w.sum()
+        o[h] = Wv[h] @ o_lat[h]
+        lse[h] = m + np.log(w.sum())
+    return o, o_lat, lse

@@ -1,0 +1,96 @@
+"""Each plausible mistake planted in the oracle (on the CPU) must make at
+least one pin fail: this shows the pins constrain every step."""
+import numpy as np
+import pytest
+
+from oracle import jssa_oracle as O
+import tests.test_oracle_pins as pins
+
+
+def _truncate_bf16(x):
+    x = np.asarray(x, np.float64).astype(np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _mean_query(q_group_bits, P_j):
+    return np.asarray(P_j, np.float64).T @ O.bf16_to_f64(q_group_bits).mean(axis=0)
+
+
+def _first_head_query(q_group_bits, P_j):
+    return np.asarray(P_j, np.float64).T @ O.bf16_to_f64(q_group_bits)[0]
+
+
+def _topk_highest_index_ties(scores, k):
+    s = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s.shape[0]
+    order = np.lexsort((-np.arange(n), -s))
+    out = np.full(k, -1, np.int64)
+    keep = np.sort(order[:min(k, n)])
+    out[:keep.shape[0]] = keep
+    return out
+
+
+def _topk_score_order(scores, k):
+    s = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    order = np.lexsort((np.arange(s.shape[0]), -s))[:min(k, s.shape[0])]
+    out = np.full(k, -1, np.int64)
+    out[:order.shape[0]] = order
+    return out
+
+
+def _attend_unscaled(q_bits, K_rows_bits, V_rows_bits, scale):
+    return _orig_attend(q_bits, K_rows_bits, V_rows_bits, 1.0)
+
+
+def _attend_no_max(q_bits, K_rows_bits, V_rows_bits, scale):
+    o, lse = _orig_attend(q_bits, K_rows_bits, V_rows_bits, scale)
+    return o, lse - np.log(np.asarray(K_rows_bits).shape[0])
+
+
+def _combine_wrong_sign(part_o, part_lse):
+    part_lse = np.asarray(part_lse, np.float64)
+    w = np.exp(-(part_lse - part_lse.max()))
+    return (w[:, None] * np.asarray(part_o)).sum(0) / w.sum(), part_lse.max() + np.log(w.sum())
+
+
+def _group_strided(j, G):
+    return range(j, j + 2 * G, 2)
+
+
+def _paged_swapped(pool, table_row, j, t):
+    t = np.asarray(t, np.int64)
+    return np.asarray(pool)[np.asarray(table_row)[t % 16], j, t // 16 % 16]
+
+
+def _mla_no_rope(qn, qr, Wk, Wv, C, scale):
+    return _orig_mla(qn, np.zeros_like(qr), Wk, Wv, C, scale)
+
+
+_orig_attend = O.attend
+_orig_mla = O.mla_attend_explicit
+
+MUTATIONS = [
+    ("round_to_bf16", _truncate_bf16, [pins.test_bf16_golden_values]),
+    ("project_query", _mean_query, [pins.test_score_golden_group_sum]),
+    ("project_query", _first_head_query, [pins.test_score_golden_group_sum]),
+    ("select_topk", _topk_highest_index_ties, [pins.test_topk_golden_ties]),
+    ("select_topk", _topk_score_order, [pins.test_topk_golden_ties]),
+    ("attend", _attend_unscaled, [pins.test_dense_matches_torch_sdpa]),
+    ("attend", _attend_no_max, [pins.test_attention_golden]),
+    ("combine", _combine_wrong_sign, [lambda: pins.test_combine_split_invariance(3)]),
+    ("group_heads", _group_strided, [pins.test_dense_matches_torch_sdpa]),
+    ("paged_rows", _paged_swapped, [pins.test_paged_matches_contiguous]),
+    ("mla_attend_explicit", _mla_no_rope, [pins.test_mla_brute_force_loops]),
+]
+
+
+@pytest.mark.parametrize("name,fn,checks", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, checks):
+    monkeypatch.setattr(O, name, fn)
+    caught = 0
+    for check in checks:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"mutation {name}/{fn.__name__} passed every pin"
