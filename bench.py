@@ -1,0 +1,264 @@
+"""Decode-attention benchmark of the JSSA sparse path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole sparse hot path over one batch: subspace
+scores -> per-KV-head top-k -> gather-free indexed split-K attention ->
+log-sum-exp combine, for all B sequences of one layer, inputs resident in HBM.
+The same run times the in-library dense full-KV step and the gather ablation
+on the same inputs, and the fp64 CPU oracle on a bounded sample of the same
+workload. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_128k_b16",
+                    choices=["gqa_128k_b16", "gqa_128k_b4", "llama3.1-8b_layer_32k", "qwen3-14b_paged_ragged",
+                             "deepseek-v3_mla_128k"])
+    ap.add_argument("--k", type=int, default=0, help="override the budget (paged workload sweep)")
+    ap.add_argument("--splits", type=int, default=8)
+    ap.add_argument("--dense-splits", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
+    return ap.parse_args()
+
+
+def workload(name: str):
+    from dataclasses import replace
+    from token_level_sparse_amd import synth
+    if name == "gqa_128k_b16":
+        return synth.BATCHED_128K
+    if name == "gqa_128k_b4":
+        return replace(synth.BATCHED_128K, B=4, name="gqa_128k_b4")
+    if name == "llama3.1-8b_layer_32k":
+        return synth.LLAMA8B_32K
+    if name == "qwen3-14b_paged_ragged":
+        return synth.PAGED_QWEN14B
+    return synth.MLA_DSV3
+
+
+def time_loop(fns, steps, warmup, torch, stream):
+    """Run `fns` (a list of stage callables) warmup + steps times; returns
+    (total seconds of the timed steps, per-stage mean microseconds measured
+    with events on the launch stream)."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    stage_us = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]) * 1e3)
+                for i in range(len(fns))]
+    return total, stage_us
+
+
+def cpu_oracle_gqa(inp, k, units):
+    """fp64 oracle sparse step on a sample of (b, j) units; returns seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import jssa_oracle as O
+    cfg = inp.cfg
+    prepared = []
+    for b, j in units:
+        n = int(inp.seq_lens[b])
+        K, V = inp.K[b, j, :n], inp.V[b, j, :n]
+        prepared.append((b, j, K, V, O.project_keys(K, inp.P[j])))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        res = []
+        for b, j, K, V, Kp in prepared:
+            hs = list(O.group_heads(j, cfg.G))
+            res.append(O.sparse_unit(inp.q[b, hs], inp.P[j], Kp, K, V, k, 1 / math.sqrt(cfg.d)))
+        dt = time.perf_counter() - t0
+    return dt, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-(sequence, KV-head) work would shard over batch or KV heads with no "
+              "communication; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from token_level_sparse_amd import jssa, pipeline, synth  # noqa: F401  (loads libjssa.so)
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    cfg = workload(args.workload)
+    t_gen = time.perf_counter()
+    if args.workload == "deepseek-v3_mla_128k":
+        return bench_mla(args, cfg, torch, pipeline, synth, stream)
+    if args.k:
+        from dataclasses import replace
+        cfg = replace(cfg, k=args.k)
+    inp = synth.make_gqa(cfg)
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] generated {cfg.name} in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    c = pipeline.GqaCache(inp)
+    c.project()
+    torch.cuda.synchronize()
+    print("[bench] projected keys on GPU", file=sys.stderr, flush=True)
+    k, S = cfg.k, args.splits
+    sp = pipeline.SparseStep(c, k=k, S=S)
+    total, st_us = time_loop([sp.score, sp.topk, sp.attend, sp.combine], args.steps, args.warmup, torch, stream)
+    ms = total / args.steps * 1e3
+    steps_s = args.steps / total
+    print(f"[bench] sparse {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    B, Hkv, Hq, d, r, T = cfg.B, cfg.Hkv, cfg.Hq, cfg.d, cfg.r, cfg.T
+    tot_tok = int(np.sum(inp.seq_lens)) * Hkv            # (token, KV head) pairs scanned
+    score_bytes = tot_tok * 2 * r + B * Hq * d * 2 + Hkv * d * r * 4 + B * Hkv * T * 4
+    topk_bytes = B * Hkv * T * 4 + B * Hkv * k * 4
+    nsel = int(np.sum(np.minimum(k, inp.seq_lens))) * Hkv
+    idx_bytes = nsel * 4 * d + B * Hkv * k * 4 + B * Hq * d * 2 + B * Hq * S * (d + 1) * 4
+    comb_bytes = B * Hq * S * (d + 1) * 4 + B * Hq * (d + 1) * 4
+    stage_names = ["score", "topk", "indexed", "combine"]
+    stage_bytes = [score_bytes, topk_bytes, idx_bytes, comb_bytes]
+    stages = {n: {"us": round(u, 2), "bytes": int(bb), "GB_s": round(bb / (u * 1e-6) / 1e9, 1),
+                  "frac_hbm": round(bb / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
+              for n, u, bb in zip(stage_names, st_us, stage_bytes)}
+    achieved = score_bytes / (st_us[0] * 1e-6) / 1e9
+
+    result = {
+        "metric": "sparse decode-attn steps/s at 128K,B=16 (Hkv=8,d=128,k=256); HBM GB/s vs peak",
+        "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "T": T, "r": r, "k": k,
+                   "S": S, "paged": bool(cfg.paged)},
+        "tokens_per_s": round(B * steps_s, 1),
+        "context_tokens_scanned_per_s": round(tot_tok * steps_s, 1),
+        "roofline": {"bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "stages": stages,
+    }
+
+    if not args.no_compare:
+        dn = pipeline.DenseStep(c, S=args.dense_splits)
+        dsteps = max(3, args.steps // 5)
+        dtotal, dst_us = time_loop([dn.attend, dn.combine], dsteps, 2, torch, stream)
+        dense_bytes = tot_tok * 4 * d + B * Hq * d * 2
+        result["dense"] = {"ms_per_step": round(dtotal / dsteps * 1e3, 4), "steps_per_s": round(dsteps / dtotal, 2),
+                           "attend_us": round(dst_us[0], 2), "combine_us": round(dst_us[1], 2),
+                           "GB_s": round(dense_bytes / (dst_us[0] * 1e-6) / 1e9, 1),
+                           "frac_hbm": round(dense_bytes / (dst_us[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
+        result["speedup_vs_dense"] = round((dtotal / dsteps) / (total / args.steps), 3)
+        ga = pipeline.GatherStep(sp, S=S)
+        gtotal, gst_us = time_loop([sp.score, sp.topk, ga.gather, ga.attend, ga.combine], max(3, args.steps // 5),
+                                   2, torch, stream)
+        gsteps = max(3, args.steps // 5)
+        sparse_attn_us = st_us[2] + st_us[3]
+        gather_attn_us = gst_us[2] + gst_us[3] + gst_us[4]
+        dense_attn_us = dst_us[0] + dst_us[1]
+        result["gather_ablation"] = {
+            "ms_per_step": round(gtotal / gsteps * 1e3, 4), "gather_us": round(gst_us[2], 2),
+            "dense_on_gathered_us": round(gst_us[3], 2),
+            "attention_stage_us": {"gather_free": round(sparse_attn_us, 2), "gather": round(gather_attn_us, 2),
+                                   "dense_full_kv": round(dense_attn_us, 2)},
+            "attention_stage_speedup_vs_dense": {"gather_free": round(dense_attn_us / sparse_attn_us, 2),
+                                                 "gather": round(dense_attn_us / gather_attn_us, 2)}}
+        print("[bench] dense and gather comparisons done", file=sys.stderr, flush=True)
+
+    if not args.no_cpu:
+        units = [(b, j) for b in range(min(2, B)) for j in range(Hkv)]
+        dt, res = cpu_oracle_gqa(inp, k, units)
+        per_step = dt * (B * Hkv) / len(units)
+        result["cpu_baseline"] = {"value": round(1.0 / per_step, 5), "unit": "steps/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{len(units)} of {B * Hkv} (sequence, KV-head) units of one step "
+                                            f"({dt:.2f}s), scaled to a whole step",
+                                  "cpu": _cpu_model()}
+        idx = sp.idx.cpu().numpy()
+        swaps = 0
+        from oracle import jssa_oracle as O
+        for (b, j), (s, oidx, o, lse) in zip(units, res):
+            n = min(k, int(inp.seq_lens[b]))
+            g = idx[b, j, :n]
+            diff = np.setxor1d(g, oidx[:n])
+            if diff.size:
+                sk = O.kth_score(s, k)
+                assert np.all(np.abs(s[diff] - sk) <= 1e-4 * abs(sk)), "index parity failed in bench"
+            swaps += diff.size // 2
+        result["oracle_check"] = {"units": len(units), "index_parity": "ok", "tie_swaps": int(swaps)}
+        print("[bench] cpu oracle leg done", file=sys.stderr, flush=True)
+    print(json.dumps(result), flush=True)
+
+
+def bench_mla(args, cfg, torch, pipeline, synth, stream):
+    inp = synth.make_mla(cfg)
+    st = pipeline.MlaStep(inp, S=args.splits)
+    st.project()
+    torch.cuda.synchronize()
+    from token_level_sparse_amd import jssa
+    c = cfg
+
+    def absorb():
+        jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.q_abs, stream)
+
+    def score():
+        jssa.jssa_mla_score(st.desc, st.q_abs, st.P, st.Kp, st.scores, stream)
+
+    def topk():
+        jssa.jssa_topk(c.B, 1, c.T, st.seq_lens, st.scores, st.k, st.idx, st.ws, None, stream)
+
+    def attend():
+        jssa.jssa_mla_indexed_decode(st.desc, st.q_abs, st.latent, st.idx, st.k, st.S, st.scale, st.part_o,
+                                     st.part_lse, stream)
+
+    def combine():
+        jssa.jssa_combine(c.B, c.H, st.S, c.d_latent, st.part_o, st.part_lse, st.o_lat, 0, st.lse, stream)
+
+    def up():
+        jssa.jssa_mla_up_v(st.desc, st.o_lat, st.W_uv, st.out, stream)
+
+    total, us = time_loop([absorb, score, topk, attend, combine, up], args.steps, args.warmup, torch, stream)
+    names = ["absorb", "score", "topk", "indexed_mfma", "combine", "up_v"]
+    steps_s = args.steps / total
+    core_flops = 2 * c.B * c.H * c.k * (2 * c.d_c + c.d_latent)       # QK^T (hi+lo) + PV
+    res = {"metric": "MLA sparse decode steps/s (DeepSeek-V3-shaped, 128K, k=2048)", "value": round(steps_s, 2),
+           "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(total / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16-mfma/f32", "data": "synthetic",
+           "config": {"workload": c.name, "B": c.B, "H": c.H, "T": c.T, "r": c.r, "k": c.k, "S": args.splits},
+           "stages_us": {n: round(u, 2) for n, u in zip(names, us)},
+           "indexed_mfma_TFLOP_s": round(core_flops / (us[3] * 1e-6) / 1e12, 2)}
+    print(json.dumps(res), flush=True)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,262 @@
+/*
+ * jssa.h -- C ABI of the MI355X (gfx950) JSSA sparse decode library.
+ *
+ * Joint Subspace Sparse Attention decodes one token per sequence by
+ *   (1) scoring every cached token in a low-dimensional subspace shared by
+ *       queries and keys,
+ *   (2) keeping a distinct top-k token set for each KV head, and
+ *   (3) running attention over those tokens read in place from the
+ *       standard GQA cache through their indices, with no staging copy.
+ * Sources: the JSSA abstract ("Joint Subspace Sparse Attention for Efficient
+ * Long-Context Decoding", weekinpapers page of arXiv 2610.19026v1, section
+ * Abstract) and the ai4snews digest of the same paper (sections Synopsis,
+ * Interpretation, Perspective).
+ *
+ * Conventions for every entry point
+ *  - Pointers named "device" point to GPU memory owned by the caller; the
+ *    library never allocates, frees or retains them. Descriptors are read on
+ *    the host during the call only.
+ *  - bf16 tensors are arrays of uint16 bit patterns; P and scores are fp32;
+ *    indices int32. All device pointers must be 16-byte aligned.
+ *  - Every call validates its arguments on the host before any HIP call. On
+ *    failure it returns a nonzero status, launches nothing and leaves the
+ *    outputs untouched; jssa_last_error() then describes the problem
+ *    (thread-local). Launch failures return JSSA_ERR_HIP.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream). Faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Device-side values (seq_lens, page tables, indices) are not read on the
+ *    host. Kernels clamp seq_lens to [0, max_seq] and treat a page-table
+ *    entry outside [0, num_pages) or an index outside [0, T_b) as an absent
+ *    token: it is never read, never scored above -inf and never attended.
+ *  - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ *  - No entry point keeps state between calls; calls on different streams
+ *    may run concurrently as long as they do not write the same memory.
+ */
+#ifndef JSSA_H
+#define JSSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JSSA_API __attribute__((visibility("default")))
+
+typedef int32_t jssa_status;
+enum {
+  JSSA_OK = 0,
+  JSSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  JSSA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  JSSA_ERR_UNSUPPORTED = 3, /* a size outside the supported set below */
+  JSSA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  JSSA_ERR_WORKSPACE = 5,   /* workspace smaller than jssa_topk_workspace_size */
+  JSSA_ERR_HIP = 6          /* the HIP runtime reported an error */
+};
+
+/*
+ * One layer's GQA cache (JSSA abstract: the indexed-attention kernel works
+ * under the standard grouped-query-attention KV-cache layout).
+ *
+ *  B          sequences in the batch (>= 1)
+ *  Hq, Hkv    query and KV heads; Hq % Hkv == 0; G = Hq / Hkv <= 16.
+ *             Query head h reads KV head h / G.
+ *  d          head width; must be 128
+ *  r          rank of the scoring subspace; one of 16, 32, 48, 64, 128
+ *  max_seq    cache capacity per sequence (tokens), 1 .. 2^24
+ *  page_size  0: contiguous caches K,V [B,Hkv,max_seq,d], Kp [B,Hkv,max_seq,r]
+ *             16: paged pools K,V [num_pages,Hkv,16,d], Kp [num_pages,Hkv,16,r];
+ *                 token t of sequence b lives in page
+ *                 page_table[b*max_pages_per_seq + t/16], slot t%16
+ *  num_pages, max_pages_per_seq, page_table (device int32) -- paged only;
+ *             max_pages_per_seq >= ceil(max_seq/16)
+ *  seq_lens   device int32 [B]: tokens held by each sequence (T_b), or NULL
+ *             meaning T_b = max_seq for every b
+ */
+typedef struct jssa_gqa_desc {
+  int32_t B, Hq, Hkv, d, r, max_seq;
+  int32_t page_size, num_pages, max_pages_per_seq;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+} jssa_gqa_desc;
+
+/*
+ * Append n_new tokens per sequence to the cache (decode-step write).
+ * Source: digest Synopsis (scoring in the shared subspace) -- the projected
+ * key row is written next to the key so that scoring reads r values/token.
+ *
+ *  k_new, v_new  device bf16 [B,Hkv,n_new,d]
+ *  P             device fp32 [Hkv,d,r]: per-KV-head basis (calibrated
+ *                offline, outside the decode path)
+ *  pos           device int32 [B]: first slot written for sequence b
+ *  K, V, Kp      device caches (layout per desc) -- written at slots
+ *                pos[b] .. pos[b]+n_new-1 that lie in [0, max_seq) and,
+ *                when paged, map to a valid page; other slots are skipped.
+ *  Kp[b,j,t,c] = bf16_rne(sum_i k[i] * P[j,i,c]), the sum accumulated in
+ *  fp64 so that the stored value is the correctly rounded exact product.
+ *  1 <= n_new <= max_seq.
+ */
+JSSA_API jssa_status jssa_append_kv(const jssa_gqa_desc* desc, void* K, void* V, void* Kp,
+                           const void* k_new, const void* v_new, const float* P,
+                           const int32_t* pos, int32_t n_new, void* stream);
+
+/*
+ * Build the projected key cache for tokens [0, T_b) of an existing cache
+ * (set-up, or after a basis change). Same arithmetic as jssa_append_kv.
+ *  K   device bf16 cache (read); P device fp32 [Hkv,d,r]; Kp device bf16 (written)
+ */
+JSSA_API jssa_status jssa_project_keys(const jssa_gqa_desc* desc, const void* K, const float* P,
+                              void* Kp, void* stream);
+
+/*
+ * Subspace scores (digest Synopsis and Interpretation: candidates are ranked
+ * in a low-dimensional space that holds queries and keys together).
+ *  q       device bf16 [B,Hq,d]
+ *  P       device fp32 [Hkv,d,r]
+ *  Kp      device bf16 projected key cache (layout per desc)
+ *  scores  device fp32 [B,Hkv,max_seq] (written):
+ *          scores[b,j,t] = qp . Kp[b,j,t,:] for t < T_b, -inf for t >= T_b,
+ *          where qp = P_j^T (sum of q[b,h] over the G query heads of KV
+ *          head j), accumulated in fp32.
+ */
+JSSA_API jssa_status jssa_score(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                       float* scores, void* stream);
+
+/*
+ * Workspace bytes needed by jssa_topk for `rows` = B*H score rows of length
+ * max_seq and budget k (host-only; no HIP call).
+ */
+JSSA_API jssa_status jssa_topk_workspace_size(int32_t B, int32_t H, int32_t max_seq, int32_t k, size_t* bytes);
+
+/*
+ * Distinct top-k token set per (sequence, head) (JSSA abstract: distinct
+ * per-KV-head selections; digest Synopsis).
+ *  scores   device fp32 [B,H,max_seq]
+ *  seq_lens device int32 [B] or NULL (= max_seq)
+ *  idx      device int32 [B,H,k] (written): the first min(k,T_b) tokens of
+ *           the order (score descending, index ascending; -0.0 == +0.0),
+ *           listed ascending by token index, then -1 padding.
+ *  ws       device workspace of at least jssa_topk_workspace_size bytes
+ *  1 <= k <= 4096, k <= max_seq. Deterministic: identical inputs give
+ *  identical outputs whatever the scheduling.
+ */
+JSSA_API jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int32_t* seq_lens,
+                      const float* scores, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Gather-free indexed attention, split-K partials (digest Interpretation:
+ * selected tokens are read where they lie through scattered indices rather
+ * than copied into a contiguous buffer; JSSA abstract).
+ *  q        device bf16 [B,Hq,d]
+ *  K, V     device bf16 caches (layout per desc), read in place
+ *  idx      device int32 [B,Hkv,k] (as written by jssa_topk; -1 = none)
+ *  S        splits, 1 <= S <= 64: split s covers idx slots
+ *           [s*ceil(k/S), (s+1)*ceil(k/S))
+ *  scale    logit scale (1/sqrt(d) for standard attention)
+ *  part_o   device fp32 [B,Hq,S,d]  (written) softmax-weighted V of split s
+ *  part_lse device fp32 [B,Hq,S]    (written) log-sum-exp of split s's
+ *           logits; -inf (and part_o = 0) for a split with no valid token
+ */
+JSSA_API jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* q, const void* K,
+                                const void* V, const int32_t* idx, int32_t k, int32_t S,
+                                float scale, float* part_o, float* part_lse, void* stream);
+
+/*
+ * Log-sum-exp merge of split partials.
+ *  part_o [B,H,S,dv] fp32, part_lse [B,H,S] fp32 (device)
+ *  out    device [B,H,dv] fp32 (out_bf16 = 0) or bf16 bits (out_bf16 = 1)
+ *  lse    device fp32 [B,H] or NULL
+ *  1 <= S <= 64; dv a multiple of 4, <= 1024. Rows whose splits are all
+ *  empty give out = 0, lse = -inf.
+ */
+JSSA_API jssa_status jssa_combine(int32_t B, int32_t H, int32_t S, int32_t dv, const float* part_o,
+                         const float* part_lse, void* out, int32_t out_bf16, float* lse,
+                         void* stream);
+
+/*
+ * Dense full-KV decode (the baseline the method is compared with; JSSA
+ * abstract reports decode throughput relative to full-KV attention).
+ * Attention of every query head over all tokens t < T_b; split s covers
+ * tokens [s*ceil(T_b/S), (s+1)*ceil(T_b/S)). Outputs as jssa_indexed_decode.
+ *  1 <= S <= 256.
+ */
+JSSA_API jssa_status jssa_dense_decode(const jssa_gqa_desc* desc, const void* q, const void* K,
+                              const void* V, int32_t S, float scale, float* part_o,
+                              float* part_lse, void* stream);
+
+/*
+ * Gather ablation (digest Interpretation: the common implementation copies
+ * the selected entries into a contiguous buffer before a dense kernel).
+ *  Kg, Vg    device bf16 [B,Hkv,k,d] (written): row i = cache row idx[b,j,i];
+ *            rows for -1 entries are zero
+ *  lens_out  device int32 [B] (written): min(k, T_b), the valid rows per
+ *            sequence, for use as seq_lens of a contiguous desc with
+ *            max_seq = k
+ */
+JSSA_API jssa_status jssa_gather_kv(const jssa_gqa_desc* desc, const void* K, const void* V,
+                           const int32_t* idx, int32_t k, void* Kg, void* Vg, int32_t* lens_out,
+                           void* stream);
+
+/*
+ * MLA shared latent cache (digest Perspective: for MLA models the selection
+ * runs over the shared latent cache).
+ *  B, H (query heads), d_latent (512), d_rope (64), d_nope (128), d_v (128),
+ *  r (scoring rank, 64), max_seq, seq_lens (device int32 [B] or NULL).
+ *  The latent cache is [B,max_seq,d_latent+d_rope] bf16, its projected copy
+ *  Kp_lat [B,max_seq,r] bf16.
+ */
+typedef struct jssa_mla_desc {
+  int32_t B, H, d_latent, d_rope, d_nope, d_v, r, max_seq;
+  const int32_t* seq_lens;
+} jssa_mla_desc;
+
+/* Kp_lat = bf16_rne(latent . P) for tokens [0, T_b); P device fp32 [d_c, r]. */
+JSSA_API jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const void* latent, const float* P,
+                                    void* Kp_lat, void* stream);
+
+/*
+ * Absorbed query: q_abs[b,h] = [W_uk[h]^T q_nope[b,h] ; q_rope[b,h]] (fp32).
+ *  q_nope device bf16 [B,H,d_nope], q_rope device bf16 [B,H,d_rope],
+ *  W_uk device bf16 [H,d_nope,d_latent], q_abs device fp32 [B,H,d_c] (written)
+ */
+JSSA_API jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
+                              const void* W_uk, float* q_abs, void* stream);
+
+/*
+ * MLA selection scores: scores[b,t] = (P^T sum_h q_abs[b,h]) . Kp_lat[b,t]
+ * for t < T_b, -inf beyond. scores device fp32 [B,max_seq].
+ */
+JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_abs, const float* P,
+                           const void* Kp_lat, float* scores, void* stream);
+
+/*
+ * MLA attention over the selected latent rows, read in place (bf16 MFMA):
+ * logits = scale * q_abs[b,h] . latent[b,t] (all d_c dims), values are
+ * latent[b,t,:d_latent]. idx device int32 [B,k] (jssa_topk with H = 1).
+ *  part_o   device fp32 [B,H,S,d_latent], part_lse device fp32 [B,H,S]
+ *  H must be a multiple of 16; 1 <= S <= 64.
+ */
+JSSA_API jssa_status jssa_mla_indexed_decode(const jssa_mla_desc* desc, const float* q_abs,
+                                    const void* latent, const int32_t* idx, int32_t k, int32_t S,
+                                    float scale, float* part_o, float* part_lse, void* stream);
+
+/*
+ * Value up-projection: out[b,h] = W_uv[h] . o_lat[b,h].
+ *  o_lat device fp32 [B,H,d_latent], W_uv device bf16 [H,d_v,d_latent],
+ *  out device fp32 [B,H,d_v] (written)
+ */
+JSSA_API jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const void* W_uv,
+                          float* out, void* stream);
+
+/* Diagnostics (host only). */
+JSSA_API const char* jssa_status_string(jssa_status s);
+JSSA_API const char* jssa_last_error(void);
+JSSA_API int32_t jssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JSSA_H */

@@ -1,0 +1,82 @@
+"""Helpers of the GPU parity tests: oracle per (sequence, KV head) unit and
+the comparison rules.
+
+Parity rules (spec tolerances of the decode path):
+* indices: per unit the GPU list holds min(k, T_b) distinct tokens in
+  [0, T_b), strictly ascending, then -1 padding; every token in the symmetric
+  difference with the oracle's set has an oracle score within 1e-4 (relative)
+  of the oracle's k-th score;
+* attention outputs (fp32) and lse: |gpu - oracle| <= 2e-3 * max(1, |oracle|)
+  element by element, the oracle run on the GPU's own index set.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import jssa_oracle as O
+from token_level_sparse_amd import synth
+
+IDX_REL = 1e-4
+OUT_TOL = 2e-3
+
+
+def unit_rows(inp: synth.GqaInputs, b: int, j: int):
+    """Logical K and V rows [T_b, d] of one unit, read out of the host arrays."""
+    n = int(inp.seq_lens[b])
+    t = np.arange(n)
+    if inp.page_table is None:
+        return inp.K[b, j, :n], inp.V[b, j, :n]
+    return (O.paged_rows(inp.K, inp.page_table[b], j, t), O.paged_rows(inp.V, inp.page_table[b], j, t))
+
+
+def oracle_unit(inp: synth.GqaInputs, b: int, j: int, rows=None):
+    cfg = inp.cfg
+    K, V = unit_rows(inp, b, j) if rows is None else rows
+    hs = list(O.group_heads(j, cfg.G))
+    Kp = O.project_keys(K, inp.P[j])
+    s = O.subspace_scores(inp.q[b, hs], inp.P[j], Kp)
+    return K, V, Kp, s, hs
+
+
+def check_indices(gpu_idx: np.ndarray, s: np.ndarray, k: int) -> int:
+    """Returns the number of tolerated swaps; asserts the rule."""
+    Tb = s.shape[0]
+    n = min(k, Tb)
+    g = gpu_idx[:n].astype(np.int64)
+    assert np.all(gpu_idx[n:] == -1), "padding past min(k, T_b) must be -1"
+    if n == 0:
+        return 0
+    assert np.all(g >= 0) and np.all(g < Tb), "indices outside [0, T_b)"
+    assert np.all(np.diff(g) > 0), "indices must be strictly ascending"
+    o = O.select_topk(s, k)[:n]
+    diff = np.setxor1d(g, o)
+    if diff.size:
+        sk = O.kth_score(s, k)
+        bad = diff[np.abs(s[diff] - sk) > IDX_REL * abs(sk)]
+        assert bad.size == 0, f"swapped tokens {bad[:8]} outside the tie band (s_k={sk})"
+    return int(diff.size // 2)
+
+
+def check_close(got, ref, tol=OUT_TOL, what="output"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    both_inf = np.isneginf(got) & np.isneginf(ref)
+    g, r = np.where(both_inf, 0, got), np.where(both_inf, 0, ref)
+    err = np.abs(g - r)
+    lim = tol * np.maximum(1.0, np.abs(r))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    assert np.all(err <= lim), f"{what}: max abs err {err.max():.3g} (limit {tol} rel/abs)"
+    return float(err.max()) if err.size else 0.0
+
+
+def check_attention(inp, b, j, hs, K, V, sel, out, lse, scale):
+    o_ref, lse_ref = O.attend(inp.q[b, hs], K[sel], V[sel], scale)
+    e1 = check_close(out[b, hs], o_ref, what=f"out b={b} j={j}")
+    e2 = check_close(lse[b, hs], lse_ref, what=f"lse b={b} j={j}")
+    return max(e1, e2)
+
+
+def scale_of(cfg) -> float:
+    return 1.0 / math.sqrt(cfg.d)

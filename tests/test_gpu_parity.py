@@ -1,0 +1,380 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle on the
+same seeded inputs, called through the C ABI."""
+from __future__ import annotations
+
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import jssa_oracle as O
+from token_level_sparse_amd import synth
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def J():
+    from token_level_sparse_amd import jssa  # fails loudly when the library is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return jssa
+
+
+@pytest.fixture(scope="module")
+def PL():
+    from token_level_sparse_amd import pipeline
+    return pipeline
+
+
+def _np(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+# Ragged shapes: T not a multiple of any tile, lengths that leave part-filled
+# chunks, an empty sequence, a sequence shorter than k.
+RAGGED = replace(synth.LLAMA8B_32K, name="ragged", B=4, T=5000, len_lo=1, len_hi=5000, seed=77)
+
+
+def ragged_inputs(cfg=RAGGED, lens=(5000, 0, 131, 3333)):
+    inp = synth.make_gqa(replace(cfg, len_lo=0))
+    lens = np.array(lens, np.int32)
+    inp.seq_lens = lens
+    return inp
+
+
+# ---------------------------------------------------------------------------
+# projected keys (append / project)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r", [16, 32, 48, 64, 128])
+def test_project_keys_bit_exact(J, PL, r):
+    cfg = replace(synth.TINY, r=r, T=1000, B=2, seed=10 + r)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    torch.cuda.synchronize()
+    Kp = _np(c.Kp)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            np.testing.assert_array_equal(Kp[b, j], O.project_keys(inp.K[b, j], inp.P[j]))
+
+
+def test_project_keys_paged_and_ragged(J, PL):
+    cfg = replace(synth.PAGED_QWEN14B, B=3, T=3000, len_lo=1000, len_hi=3000, seed=21)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    torch.cuda.synchronize()
+    Kp = _np(c.Kp)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            K, _ = U.unit_rows(inp, b, j)
+            got = O.paged_rows(Kp, inp.page_table[b], j, np.arange(K.shape[0]))
+            np.testing.assert_array_equal(got, O.project_keys(K, inp.P[j]))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_append_kv(J, PL, paged):
+    cfg = replace(synth.PAGED_QWEN14B if paged else synth.TINY, B=2, T=512, len_lo=0, r=32, seed=31)
+    if paged:
+        cfg = replace(cfg, len_lo=512, len_hi=512)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    n_new = 5
+    rng = np.random.default_rng(3)
+    k_new = synth.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.Hkv, n_new, cfg.d)))
+    v_new = synth.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.Hkv, n_new, cfg.d)))
+    pos = np.array([100, 509], np.int32)          # second sequence runs past max_seq: 3 slots skipped
+    J.jssa_append_kv(c.desc, c.K, c.V, c.Kp, PL.to_device(k_new), PL.to_device(v_new), c.P,
+                     PL.to_device(pos), n_new)
+    torch.cuda.synchronize()
+    K, V, Kp = _np(c.K), _np(c.V), _np(c.Kp)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            for i in range(n_new):
+                t = int(pos[b]) + i
+                if t >= cfg.T:
+                    continue
+                if paged:
+                    pg = inp.page_table[b, t // 16]
+                    kr, vr, kpr = K[pg, j, t % 16], V[pg, j, t % 16], Kp[pg, j, t % 16]
+                else:
+                    kr, vr, kpr = K[b, j, t], V[b, j, t], Kp[b, j, t]
+                np.testing.assert_array_equal(kr, k_new[b, j, i])
+                np.testing.assert_array_equal(vr, v_new[b, j, i])
+                np.testing.assert_array_equal(kpr, O.project_keys(k_new[b, j, i][None], inp.P[j])[0])
+    # untouched rows stay untouched
+    if not paged:
+        np.testing.assert_array_equal(K[0, :, :100], inp.K[0, :, :100])
+
+
+# ---------------------------------------------------------------------------
+# scores
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r", [16, 32, 48, 64, 128])
+def test_score_parity(J, PL, r):
+    inp = ragged_inputs(replace(RAGGED, r=r, seed=40 + r))
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=64)
+    st.score()
+    torch.cuda.synchronize()
+    S = _np(st.scores)
+    for b in range(inp.cfg.B):
+        Tb = int(inp.seq_lens[b])
+        for j in range(inp.cfg.Hkv):
+            K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+            qp = O.project_query(inp.q[b, hs], inp.P[j])
+            bound = 1e-5 * (np.abs(O.bf16_to_f64(Kp) * qp).sum(1) + 1e-30)
+            assert np.all(np.abs(S[b, j, :Tb] - s) <= bound), (b, j)
+            assert np.all(np.isneginf(S[b, j, Tb:]))
+
+
+# ---------------------------------------------------------------------------
+# top-k on host-made scores (identical fp32 input on both sides: bit-exact)
+# ---------------------------------------------------------------------------
+def _topk_case(J, B, H, T, k, lens, scores):
+    dev = "cuda"
+    sc = torch.from_numpy(scores).to(dev)
+    sl = torch.from_numpy(np.asarray(lens, np.int32)).to(dev)
+    n = J.jssa_topk_workspace_size(B, H, T, k)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, H, k), dtype=torch.int32, device=dev)
+    J.jssa_topk(B, H, T, sl, sc, k, idx, ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            Tb = int(lens[b])
+            np.testing.assert_array_equal(got[b, h], O.select_topk(scores[b, h, :Tb].astype(np.float64), k),
+                                          err_msg=f"b={b} h={h} T_b={Tb} k={k}")
+    return got
+
+
+@pytest.mark.parametrize("T,k", [(4096, 256), (32768, 256), (50000, 1), (20000, 1024), (70000, 2048),
+                                 (40000, 4096), (3000, 3000), (1500, 700), (100, 7)])
+def test_topk_bit_exact(J, T, k):
+    rng = np.random.default_rng(T + k)
+    B, H = 3, 2
+    s = rng.standard_normal((B, H, T)).astype(np.float32)
+    s[0, 1] = np.round(s[0, 1] * 4) / 4                   # heavy exact ties
+    s[1, 0, : T // 2] = 1.0                               # a long plateau at the top
+    s[1, 0, T // 2:] = rng.standard_normal(T - T // 2).astype(np.float32) * 0.1
+    s[2, 1, ::3] = -0.0
+    s[2, 1, 1::3] = 0.0
+    lens = [T, max(1, T // 3), min(T, max(1, k // 2))]
+    _topk_case(J, B, H, T, k, lens, s)
+
+
+def test_topk_long_row_multi_round(J):
+    """A row long enough that the chunk lists need more than one merge."""
+    rng = np.random.default_rng(5)
+    T, k = 600000, 4096
+    s = rng.standard_normal((1, 1, T)).astype(np.float32)
+    _topk_case(J, 1, 1, T, k, [T], s)
+
+
+def test_topk_empty_and_all_equal(J):
+    T, k = 9000, 300
+    s = np.zeros((2, 1, T), np.float32)
+    s[1, 0] = 2.5
+    got = _topk_case(J, 2, 1, T, k, [0, T], s)
+    assert np.all(got[0] == -1)
+    np.testing.assert_array_equal(got[1, 0], np.arange(k))
+
+
+# ---------------------------------------------------------------------------
+# whole sparse step, dense, gather ablation, combine
+# ---------------------------------------------------------------------------
+def _sparse_and_check(J, PL, inp, k, S, units=None):
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=k, S=S)
+    st.run()
+    torch.cuda.synchronize()
+    idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
+    cfg = inp.cfg
+    swaps = 0
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            if units is not None and (b, j) not in units:
+                continue
+            K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+            swaps += U.check_indices(idx[b, j], s, k)
+            sel = idx[b, j][idx[b, j] >= 0]
+            U.check_attention(inp, b, j, hs, K, V, sel, out, lse, c.scale)
+    return c, st, swaps
+
+
+@pytest.mark.parametrize("cfg,k,S", [(synth.TINY, 256, 8), (synth.LLAMA8B_32K, 256, 8),
+                                     (synth.LLAMA8B_32K, 256, 1), (synth.LLAMA8B_32K, 1, 4)])
+def test_sparse_step_parity(J, PL, cfg, k, S):
+    _sparse_and_check(J, PL, synth.make_gqa(cfg), k, S)
+
+
+def test_sparse_step_ragged(J, PL):
+    _sparse_and_check(J, PL, ragged_inputs(), 256, 8)
+
+
+@pytest.mark.parametrize("k", [256, 1024, 2048])
+def test_sparse_step_paged_qwen(J, PL, k):
+    cfg = replace(synth.PAGED_QWEN14B, B=3, T=20000, len_lo=9000, len_hi=20000, seed=50 + k)
+    _sparse_and_check(J, PL, synth.make_gqa(cfg), k, 8)
+
+
+def test_sparse_k_equals_T_is_dense(J, PL):
+    cfg = replace(synth.TINY, T=2048, B=2)
+    inp = synth.make_gqa(cfg)
+    c, st, _ = _sparse_and_check(J, PL, inp, cfg.T, 16)
+    np.testing.assert_array_equal(_np(st.idx), np.broadcast_to(np.arange(cfg.T), st.idx.shape))
+    dn = PL.DenseStep(c, S=16)
+    dn.run()
+    torch.cuda.synchronize()
+    U.check_close(_np(dn.out), _np(st.out), tol=1e-5, what="k=T sparse vs dense")
+
+
+@pytest.mark.parametrize("cfg,S", [(synth.TINY, 7), (synth.LLAMA8B_32K, 64), (RAGGED, 16)])
+def test_dense_parity(J, PL, cfg, S):
+    inp = ragged_inputs() if cfg is RAGGED else synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    dn = PL.DenseStep(c, S=S)
+    dn.run()
+    torch.cuda.synchronize()
+    out, lse = _np(dn.out), _np(dn.lse)
+    for b in range(inp.cfg.B):
+        for j in range(inp.cfg.Hkv):
+            K, V = U.unit_rows(inp, b, j)
+            hs = list(O.group_heads(j, inp.cfg.G))
+            o_ref, lse_ref = O.dense_unit(inp.q[b, hs], K, V, c.scale)
+            U.check_close(out[b, hs], o_ref, what=f"dense b={b} j={j}")
+            U.check_close(lse[b, hs], lse_ref, what=f"dense lse b={b} j={j}")
+
+
+def test_dense_paged(J, PL):
+    cfg = replace(synth.PAGED_QWEN14B, B=2, T=6000, len_lo=3000, len_hi=6000, seed=61)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    dn = PL.DenseStep(c, S=32)
+    dn.run()
+    torch.cuda.synchronize()
+    out = _np(dn.out)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            K, V = U.unit_rows(inp, b, j)
+            hs = list(O.group_heads(j, cfg.G))
+            U.check_close(out[b, hs], O.dense_unit(inp.q[b, hs], K, V, c.scale)[0], what="dense paged")
+
+
+def test_gather_ablation(J, PL):
+    inp = ragged_inputs()
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=256, S=8)
+    st.run()
+    ga = PL.GatherStep(st, S=4)
+    ga.run()
+    torch.cuda.synchronize()
+    idx, Kg, Vg, lens = _np(st.idx), _np(ga.Kg), _np(ga.Vg), _np(ga.lens)
+    for b in range(inp.cfg.B):
+        assert lens[b] == min(256, int(inp.seq_lens[b]))
+        for j in range(inp.cfg.Hkv):
+            K, V = U.unit_rows(inp, b, j)
+            sel = idx[b, j]
+            ok = sel >= 0
+            np.testing.assert_array_equal(Kg[b, j][ok], K[sel[ok]])
+            np.testing.assert_array_equal(Vg[b, j][ok], V[sel[ok]])
+            assert np.all(Kg[b, j][~ok] == 0)
+            hs = list(O.group_heads(j, inp.cfg.G))
+            U.check_attention(inp, b, j, hs, K, V, sel[ok], _np(ga.out), _np(ga.lse), c.scale)
+
+
+@pytest.mark.parametrize("S,dv", [(1, 128), (8, 128), (64, 128), (5, 512)])
+def test_combine_parity(J, S, dv):
+    rng = np.random.default_rng(S * 7 + dv)
+    B, H = 3, 5
+    po = rng.standard_normal((B, H, S, dv)).astype(np.float32)
+    pl = (rng.standard_normal((B, H, S)) * 3).astype(np.float32)
+    pl[0, 0, :] = -np.inf                        # an all-empty row
+    if S > 1:
+        pl[1, 2, 0] = -np.inf                    # one empty split
+    out = torch.empty((B, H, dv), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    J.jssa_combine(B, H, S, dv, torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, 0, lse)
+    outb = torch.empty((B, H, dv), dtype=torch.int16, device="cuda")
+    J.jssa_combine(B, H, S, dv, torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), outb, 1, None)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ro, rl = O.combine(po[b, h], pl[b, h])
+            U.check_close(o[b, h], ro, tol=1e-5, what="combine")
+            U.check_close(l[b, h], rl, tol=1e-5, what="combine lse")
+    ob = synth.bf16_bits_to_f32(outb.cpu().numpy().view(np.uint16))
+    np.testing.assert_array_equal(ob, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(o)))
+
+
+def test_deterministic_repeat(J, PL):
+    inp = synth.make_gqa(synth.LLAMA8B_32K)
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=256, S=8)
+    st.run()
+    torch.cuda.synchronize()
+    a = (_np(st.idx).copy(), _np(st.out).copy(), _np(st.scores).copy())
+    st.run()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(st.idx), a[0])
+    np.testing.assert_array_equal(_np(st.out), a[1])
+    np.testing.assert_array_equal(_np(st.scores), a[2])
+
+
+def test_invalid_page_entries_are_absent(J, PL):
+    """A page-table entry outside [0, num_pages) inside T_b hides its 16
+    tokens: never scored above -inf, never selected, never attended."""
+    cfg = replace(synth.PAGED_QWEN14B, B=2, T=2048, len_lo=2048, len_hi=2048, seed=71)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    table = inp.page_table.copy()
+    table[0, 3] = -1
+    table[1, 10] = inp.num_pages + 5
+    c.page_table.copy_(torch.from_numpy(table).cuda())
+    st = PL.SparseStep(c, k=256, S=8)
+    st.run()
+    torch.cuda.synchronize()
+    S_ = _np(st.scores)
+    assert np.all(np.isneginf(S_[0, :, 48:64])) and np.all(np.isneginf(S_[1, :, 160:176]))
+    idx = _np(st.idx)
+    assert not np.any((idx[0] >= 48) & (idx[0] < 64))
+    assert not np.any((idx[1] >= 160) & (idx[1] < 176))
+    assert np.all(np.isfinite(_np(st.out)))
+
+
+# ---------------------------------------------------------------------------
+# MLA
+# ---------------------------------------------------------------------------
+def test_mla_parity(J, PL):
+    cfg = replace(synth.MLA_DSV3, B=2, T=6000, k=512)
+    inp = synth.make_mla(cfg)
+    st = PL.MlaStep(inp, S=4)
+    st.project()
+    torch.cuda.synchronize()
+    Kp = _np(st.Kp)
+    for b in range(cfg.B):
+        np.testing.assert_array_equal(Kp[b], O.project_keys(inp.latent[b], inp.P))
+    st.run()
+    torch.cuda.synchronize()
+    qa = O.mla_absorbed_query(inp.q_nope[0], inp.q_rope[0], inp.W_uk)
+    U.check_close(_np(st.q_abs)[0], qa, tol=1e-4, what="absorbed query")
+    idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
+    for b in range(cfg.B):
+        s = O.mla_scores(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.P, O.project_keys(inp.latent[b], inp.P))
+        U.check_indices(idx[b], s, cfg.k)
+        sel = idx[b][idx[b] >= 0]
+        o, _, l = O.mla_attend_explicit(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.W_uv, inp.latent[b][sel],
+                                        st.scale)
+        U.check_close(out[b], o, what=f"mla out b={b}")
+        U.check_close(lse[b], l, what=f"mla lse b={b}")

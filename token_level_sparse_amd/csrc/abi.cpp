@@ -1,0 +1,304 @@
+// C ABI of the JSSA library: host-side validation, then one launch per call.
+// Declarations and the contract of every entry point are in include/jssa.h.
+#include "../../include/jssa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+jssa_status fail(jssa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+jssa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return JSSA_OK;
+  }
+  return fail(JSSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                          \
+  do {                                                                          \
+    if (!(p)) return fail(JSSA_ERR_NULL, "%s: %s is NULL", __func__, #p);       \
+    if (!aligned(p)) return fail(JSSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p); \
+  } while (0)
+#define REQUIRE_ALIGNED_OPT(p)                                                  \
+  do {                                                                          \
+    if ((p) && !aligned(p))                                                     \
+      return fail(JSSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+constexpr int32_t kMaxSeq = 1 << 24;
+
+jssa_status check_desc(const char* fn, const jssa_gqa_desc* d, bool need_rank) {
+  if (!d) return fail(JSSA_ERR_NULL, "%s: desc is NULL", fn);
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1)
+    return fail(JSSA_ERR_SHAPE, "%s: B, Hq, Hkv must be >= 1 (got %d, %d, %d)", fn, d->B, d->Hq, d->Hkv);
+  if (d->Hq % d->Hkv != 0)
+    return fail(JSSA_ERR_SHAPE, "%s: Hq (%d) is not a multiple of Hkv (%d)", fn, d->Hq, d->Hkv);
+  if (d->Hq / d->Hkv > 16)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: group size %d > 16", fn, d->Hq / d->Hkv);
+  if (d->d != 128) return fail(JSSA_ERR_UNSUPPORTED, "%s: head width %d (only 128)", fn, d->d);
+  if (need_rank && d->r != 16 && d->r != 32 && d->r != 48 && d->r != 64 && d->r != 128)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: rank %d (16, 32, 48, 64 or 128)", fn, d->r);
+  if (d->max_seq < 1 || d->max_seq > kMaxSeq)
+    return fail(JSSA_ERR_SHAPE, "%s: max_seq %d outside [1, 2^24]", fn, d->max_seq);
+  if (int64_t(d->B) * d->Hq > (1 << 24))
+    return fail(JSSA_ERR_SHAPE, "%s: B*Hq too large", fn);
+  if (d->page_size != 0 && d->page_size != 16)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: page_size %d (0 or 16)", fn, d->page_size);
+  if (d->page_size == 16) {
+    if (!d->page_table) return fail(JSSA_ERR_NULL, "%s: page_table is NULL for a paged cache", fn);
+    if (d->num_pages < 1) return fail(JSSA_ERR_SHAPE, "%s: num_pages %d", fn, d->num_pages);
+    if (d->max_pages_per_seq < (d->max_seq + 15) / 16)
+      return fail(JSSA_ERR_SHAPE, "%s: max_pages_per_seq %d < ceil(max_seq/16)", fn, d->max_pages_per_seq);
+  }
+  return JSSA_OK;
+}
+
+jssa::GqaDev to_dev(const jssa_gqa_desc* d) {
+  jssa::GqaDev g;
+  g.B = d->B;
+  g.Hq = d->Hq;
+  g.Hkv = d->Hkv;
+  g.G = d->Hq / d->Hkv;
+  g.d = d->d;
+  g.r = d->r;
+  g.max_seq = d->max_seq;
+  g.page_size = d->page_size;
+  g.num_pages = d->page_size ? d->num_pages : 0;
+  g.max_pages = d->page_size ? d->max_pages_per_seq : 0;
+  g.page_table = d->page_size ? d->page_table : nullptr;
+  g.seq_lens = d->seq_lens;
+  return g;
+}
+
+hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+jssa_status check_mla(const char* fn, const jssa_mla_desc* m) {
+  if (!m) return fail(JSSA_ERR_NULL, "%s: desc is NULL", fn);
+  if (m->B < 1 || m->H < 1) return fail(JSSA_ERR_SHAPE, "%s: B and H must be >= 1", fn);
+  if (m->H % 16 != 0 || m->H > 1024)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: H %d (a multiple of 16, <= 1024)", fn, m->H);
+  if (m->d_latent != 512 || m->d_rope != 64 || m->d_nope != 128 || m->d_v != 128)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: widths latent/rope/nope/v must be 512/64/128/128", fn);
+  if (m->r != 16 && m->r != 32 && m->r != 64)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: rank %d (16, 32 or 64)", fn, m->r);
+  if (m->max_seq < 1 || m->max_seq > kMaxSeq)
+    return fail(JSSA_ERR_SHAPE, "%s: max_seq %d outside [1, 2^24]", fn, m->max_seq);
+  return JSSA_OK;
+}
+
+jssa::MlaDev to_mla(const jssa_mla_desc* m) {
+  return jssa::MlaDev{m->B, m->H, m->d_latent, m->d_rope, m->d_nope, m->d_v, m->r, m->max_seq,
+                      m->seq_lens};
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t jssa_version(void) { return 100; }
+
+const char* jssa_last_error(void) { return g_err; }
+
+const char* jssa_status_string(jssa_status s) {
+  switch (s) {
+    case JSSA_OK: return "ok";
+    case JSSA_ERR_NULL: return "null pointer";
+    case JSSA_ERR_SHAPE: return "bad shape";
+    case JSSA_ERR_UNSUPPORTED: return "unsupported size";
+    case JSSA_ERR_ALIGN: return "misaligned pointer";
+    case JSSA_ERR_WORKSPACE: return "workspace too small";
+    case JSSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+jssa_status jssa_append_kv(const jssa_gqa_desc* desc, void* K, void* V, void* Kp, const void* k_new,
+                           const void* v_new, const float* P, const int32_t* pos, int32_t n_new,
+                           void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(Kp); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new);
+  REQUIRE_PTR(P); REQUIRE_PTR(pos);
+  if (n_new < 1 || n_new > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: n_new %d outside [1, max_seq]", __func__, n_new);
+  return hip_status(jssa::launch_project(to_dev(desc), static_cast<const uint16_t*>(k_new), 0, pos,
+                                         n_new, true, static_cast<uint16_t*>(K),
+                                         static_cast<uint16_t*>(V),
+                                         static_cast<const uint16_t*>(v_new), P,
+                                         static_cast<uint16_t*>(Kp), S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_project_keys(const jssa_gqa_desc* desc, const void* K, const float* P, void* Kp,
+                              void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  REQUIRE_PTR(K); REQUIRE_PTR(P); REQUIRE_PTR(Kp);
+  return hip_status(jssa::launch_project(to_dev(desc), static_cast<const uint16_t*>(K), 0, nullptr,
+                                         desc->max_seq, false, nullptr, nullptr, nullptr, P,
+                                         static_cast<uint16_t*>(Kp), S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_score(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                       float* scores, void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(scores);
+  return hip_status(jssa::launch_score(to_dev(desc), static_cast<const uint16_t*>(q), P,
+                                       static_cast<const uint16_t*>(Kp), scores, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_topk_workspace_size(int32_t B, int32_t H, int32_t max_seq, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
+  if (B < 1 || H < 1 || int64_t(B) * H > (1 << 24))
+    return fail(JSSA_ERR_SHAPE, "%s: B %d, H %d", __func__, B, H);
+  if (max_seq < 1 || max_seq > kMaxSeq)
+    return fail(JSSA_ERR_SHAPE, "%s: max_seq %d outside [1, 2^24]", __func__, max_seq);
+  if (k < 1 || k > 4096 || k > max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
+  *bytes = jssa::topk_workspace_bytes(B * H, max_seq, k);
+  return JSSA_OK;
+}
+
+jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int32_t* seq_lens,
+                      const float* scores, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                      void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_topk_workspace_size(B, H, max_seq, k, &need)) return s;
+  REQUIRE_PTR(scores); REQUIRE_PTR(idx); REQUIRE_ALIGNED_OPT(seq_lens);
+  if (need > 0) REQUIRE_PTR(ws);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  return hip_status(jssa::launch_topk(B, H, max_seq, seq_lens, scores, k, idx, ws, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* q, const void* K, const void* V,
+                                const int32_t* idx, int32_t k, int32_t S_, float scale, float* part_o,
+                                float* part_lse, void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, false)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(idx); REQUIRE_PTR(part_o);
+  REQUIRE_PTR(part_lse);
+  if (k < 1 || k > 4096 || k > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
+  if (S_ < 1 || S_ > 64) return fail(JSSA_ERR_SHAPE, "%s: S %d outside [1, 64]", __func__, S_);
+  return hip_status(jssa::launch_indexed(to_dev(desc), static_cast<const uint16_t*>(q),
+                                         static_cast<const uint16_t*>(K),
+                                         static_cast<const uint16_t*>(V), idx, k, S_, scale, part_o,
+                                         part_lse, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_combine(int32_t B, int32_t H, int32_t S_, int32_t dv, const float* part_o,
+                         const float* part_lse, void* out, int32_t out_bf16, float* lse,
+                         void* stream) {
+  if (B < 1 || H < 1 || int64_t(B) * H > (1 << 24))
+    return fail(JSSA_ERR_SHAPE, "%s: B %d, H %d", __func__, B, H);
+  if (S_ < 1 || S_ > 256) return fail(JSSA_ERR_SHAPE, "%s: S %d outside [1, 256]", __func__, S_);
+  if (dv < 4 || dv > 1024 || dv % 4)
+    return fail(JSSA_ERR_UNSUPPORTED, "%s: dv %d (a multiple of 4, <= 1024)", __func__, dv);
+  REQUIRE_PTR(part_o); REQUIRE_PTR(part_lse); REQUIRE_PTR(out);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(JSSA_ERR_ALIGN, "%s: lse is not 4-byte aligned", __func__);
+  return hip_status(jssa::launch_combine(B, H, S_, dv, part_o, part_lse, out, out_bf16 != 0, lse,
+                                         S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_dense_decode(const jssa_gqa_desc* desc, const void* q, const void* K, const void* V,
+                              int32_t S_, float scale, float* part_o, float* part_lse, void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, false)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(part_o); REQUIRE_PTR(part_lse);
+  if (S_ < 1 || S_ > 256) return fail(JSSA_ERR_SHAPE, "%s: S %d outside [1, 256]", __func__, S_);
+  return hip_status(jssa::launch_dense(to_dev(desc), static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(K),
+                                       static_cast<const uint16_t*>(V), S_, scale, part_o, part_lse,
+                                       S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_gather_kv(const jssa_gqa_desc* desc, const void* K, const void* V,
+                           const int32_t* idx, int32_t k, void* Kg, void* Vg, int32_t* lens_out,
+                           void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, false)) return s;
+  REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(idx); REQUIRE_PTR(Kg); REQUIRE_PTR(Vg);
+  REQUIRE_ALIGNED_OPT(lens_out);
+  if (k < 1 || k > 4096 || k > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
+  return hip_status(jssa::launch_gather(to_dev(desc), static_cast<const uint16_t*>(K),
+                                        static_cast<const uint16_t*>(V), idx, k,
+                                        static_cast<uint16_t*>(Kg), static_cast<uint16_t*>(Vg),
+                                        lens_out, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const void* latent, const float* P,
+                                    void* Kp_lat, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(latent); REQUIRE_PTR(P); REQUIRE_PTR(Kp_lat); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  return hip_status(jssa::launch_mla_project(to_mla(desc), static_cast<const uint16_t*>(latent), P,
+                                             static_cast<uint16_t*>(Kp_lat), S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
+                              const void* W_uk, float* q_abs, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(q_nope); REQUIRE_PTR(q_rope); REQUIRE_PTR(W_uk); REQUIRE_PTR(q_abs);
+  return hip_status(jssa::launch_mla_absorb(to_mla(desc), static_cast<const uint16_t*>(q_nope),
+                                            static_cast<const uint16_t*>(q_rope),
+                                            static_cast<const uint16_t*>(W_uk), q_abs, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_abs, const float* P,
+                           const void* Kp_lat, float* scores, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(q_abs); REQUIRE_PTR(P); REQUIRE_PTR(Kp_lat); REQUIRE_PTR(scores);
+  REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  return hip_status(jssa::launch_mla_score(to_mla(desc), q_abs, P,
+                                           static_cast<const uint16_t*>(Kp_lat), scores, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_indexed_decode(const jssa_mla_desc* desc, const float* q_abs,
+                                    const void* latent, const int32_t* idx, int32_t k, int32_t S_,
+                                    float scale, float* part_o, float* part_lse, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(q_abs); REQUIRE_PTR(latent); REQUIRE_PTR(idx); REQUIRE_PTR(part_o);
+  REQUIRE_PTR(part_lse); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  if (k < 1 || k > 4096 || k > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
+  if (S_ < 1 || S_ > 64) return fail(JSSA_ERR_SHAPE, "%s: S %d outside [1, 64]", __func__, S_);
+  return hip_status(jssa::launch_mla_indexed(to_mla(desc), q_abs,
+                                             static_cast<const uint16_t*>(latent), idx, k, S_,
+                                             scale, part_o, part_lse, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const void* W_uv,
+                          float* out, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(o_lat); REQUIRE_PTR(W_uv); REQUIRE_PTR(out);
+  return hip_status(jssa::launch_mla_up_v(to_mla(desc), o_lat, static_cast<const uint16_t*>(W_uv),
+                                          out, S(stream)),
+                    __func__);
+}
+
+}  // extern "C"

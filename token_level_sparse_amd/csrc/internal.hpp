@@ -1,0 +1,50 @@
+// Launchers shared between the kernel sources and the C-ABI layer. Every
+// launcher assumes its arguments were validated by abi.cpp and returns the
+// status of the launch (hipGetLastError after the launch).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace jssa {
+
+hipError_t launch_project(const GqaDev& g, const uint16_t* src, int64_t src_row_stride_tok,
+                          const int32_t* pos, int n_tok, bool append, uint16_t* K, uint16_t* V,
+                          const uint16_t* v_src, const float* P, uint16_t* Kp, hipStream_t st);
+
+hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
+                        float* scores, hipStream_t st);
+
+size_t topk_workspace_bytes(int rows, int max_seq, int k);
+hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
+                       int k, int32_t* idx, void* ws, hipStream_t st);
+
+hipError_t launch_indexed(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                          const int32_t* idx, int k, int S, float scale, float* part_o,
+                          float* part_lse, hipStream_t st);
+hipError_t launch_dense(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                        int S, float scale, float* part_o, float* part_lse, hipStream_t st);
+hipError_t launch_combine(int B, int H, int S, int dv, const float* part_o, const float* part_lse,
+                          void* out, bool out_bf16, float* lse, hipStream_t st);
+hipError_t launch_gather(const GqaDev& g, const uint16_t* K, const uint16_t* V, const int32_t* idx,
+                         int k, uint16_t* Kg, uint16_t* Vg, int32_t* lens_out, hipStream_t st);
+
+struct MlaDev {
+  int B, H, d_latent, d_rope, d_nope, d_v, r, max_seq;
+  const int32_t* seq_lens;
+};
+hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const float* P,
+                              uint16_t* Kp, hipStream_t st);
+hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
+                             const uint16_t* W_uk, float* q_abs, hipStream_t st);
+hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P,
+                            const uint16_t* Kp, float* scores, hipStream_t st);
+hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_t* latent,
+                              const int32_t* idx, int k, int S, float scale, float* part_o,
+                              float* part_lse, hipStream_t st);
+hipError_t launch_mla_up_v(const MlaDev& m, const float* o_lat, const uint16_t* W_uv, float* out,
+                           hipStream_t st);
+
+}  // namespace jssa

@@ -1,0 +1,94 @@
+// Log-sum-exp combine of split partials, and the gather ablation copy.
+//
+// Combine: split-K decode produces per-split (o_s, lse_s); the exact softmax
+// over the union of the splits weights each o_s by exp(lse_s - max lse).
+// Gather: the common token-sparse implementation copies the selected K/V rows
+// into a contiguous buffer and then runs a dense kernel; JSSA's digest
+// (Interpretation) reports that this copy is comparable to the reduced
+// attention itself. It is built here only to measure that ablation.
+#include "internal.hpp"
+
+namespace jssa {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(int H, int S, int dv,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse,
+                                                      void* __restrict__ out, int out_bf16,
+                                                      float* __restrict__ lse_out) {
+  const int bh = blockIdx.x;
+  const float* pl = part_lse + int64_t(bh) * S;
+  float M = -__builtin_inff();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
+  float L = 0.f;
+  if (M != -__builtin_inff())
+    for (int s = 0; s < S; ++s) L += __expf(pl[s] - M);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int c4 = threadIdx.x; c4 * 4 < dv; c4 += blockDim.x) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (L > 0.f) {
+      for (int s = 0; s < S; ++s) {
+        const float wgt = __expf(pl[s] - M);
+        if (wgt == 0.f) continue;
+        const f32x4 v = reinterpret_cast<const f32x4*>(part_o + (int64_t(bh) * S + s) * dv)[c4];
+        acc += wgt * v;
+      }
+      acc *= inv;
+    }
+    if (out_bf16) {
+      uint16_t* o = static_cast<uint16_t*>(out) + int64_t(bh) * dv + c4 * 4;
+      u32x2 pk = {uint32_t(f32_to_bf16_rne(acc.x)) | (uint32_t(f32_to_bf16_rne(acc.y)) << 16),
+                  uint32_t(f32_to_bf16_rne(acc.z)) | (uint32_t(f32_to_bf16_rne(acc.w)) << 16)};
+      *reinterpret_cast<u32x2*>(o) = pk;
+    } else {
+      reinterpret_cast<f32x4*>(static_cast<float*>(out) + int64_t(bh) * dv)[c4] = acc;
+    }
+  }
+  if (lse_out && threadIdx.x == 0) lse_out[bh] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+}
+
+// One 16-lane group per selected row; 16 rows per 256-thread block.
+__global__ __launch_bounds__(256) void gather_kernel(GqaDev g, const uint16_t* __restrict__ K,
+                                                     const uint16_t* __restrict__ V,
+                                                     const int32_t* __restrict__ idx, int k,
+                                                     uint16_t* __restrict__ Kg,
+                                                     uint16_t* __restrict__ Vg,
+                                                     int32_t* __restrict__ lens_out) {
+  const int b = blockIdx.z, j = blockIdx.y;
+  const int i = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int Tb = seq_len(g, b);
+  if (lens_out && j == 0 && blockIdx.x == 0 && threadIdx.x == 0) lens_out[b] = min(k, Tb);
+  if (i >= k) return;
+  const int t = idx[(int64_t(b) * g.Hkv + j) * k + i];
+  int64_t off = -1;
+  if (t >= 0 && t < Tb) off = row_off(g, b, j, t, 128);
+  u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+  if (off >= 0) {
+    kv = reinterpret_cast<const u32x4*>(K + off)[sub];
+    vv = reinterpret_cast<const u32x4*>(V + off)[sub];
+  }
+  const int64_t d = ((int64_t(b) * g.Hkv + j) * k + i) * 128;
+  reinterpret_cast<u32x4*>(Kg + d)[sub] = kv;
+  reinterpret_cast<u32x4*>(Vg + d)[sub] = vv;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int B, int H, int S, int dv, const float* part_o, const float* part_lse,
+                          void* out, bool out_bf16, float* lse, hipStream_t st) {
+  int threads = dv / 4;
+  threads = threads < 64 ? 64 : (threads > 256 ? 256 : ((threads + 63) / 64) * 64);
+  hipLaunchKernelGGL(combine_kernel, dim3(B * H), dim3(threads), 0, st, H, S, dv, part_o, part_lse,
+                     out, out_bf16 ? 1 : 0, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GqaDev& g, const uint16_t* K, const uint16_t* V, const int32_t* idx,
+                         int k, uint16_t* Kg, uint16_t* Vg, int32_t* lens_out, hipStream_t st) {
+  dim3 grid((k + 15) / 16, g.Hkv, g.B);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, st, g, K, V, idx, k, Kg, Vg, lens_out);
+  return hipGetLastError();
+}
+
+}  // namespace jssa

@@ -1,0 +1,204 @@
+"""Device-side plumbing around the C ABI: upload seeded inputs, allocate the
+buffers each stage writes, and chain the entry points of one decode step.
+
+PyTorch is used for device memory and streams only; every step of the path
+runs in the HIP library. The chains follow the JSSA decode step (score ->
+top-k -> indexed attention -> combine), the dense full-KV baseline
+(dense -> combine) and the gather ablation (score -> top-k -> gather ->
+dense over the gathered rows -> combine).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import jssa
+from .synth import GqaInputs, MlaInputs, PAGE
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a numpy array; bf16 bit patterns (uint16) become int16 tensors."""
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class GqaCache:
+    """One layer's cache and inputs on the GPU (contiguous or paged)."""
+
+    def __init__(self, inp: GqaInputs, device="cuda"):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.B, self.Hq, self.Hkv, self.d, self.T, self.r = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.T, cfg.r
+        self.q = to_device(inp.q, device)
+        self.P = to_device(inp.P, device)
+        self.K = to_device(inp.K, device)
+        self.V = to_device(inp.V, device)
+        self.seq_lens = to_device(inp.seq_lens.astype(np.int32), device)
+        self.paged = inp.page_table is not None
+        if self.paged:
+            self.page_table = to_device(inp.page_table.astype(np.int32), device)
+            self.num_pages = inp.num_pages
+            self.Kp = torch.zeros((inp.num_pages, cfg.Hkv, PAGE, cfg.r), dtype=torch.int16, device=device)
+            self.desc = jssa.gqa_desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.r, cfg.T, cfg.d, PAGE, inp.num_pages,
+                                      inp.page_table.shape[1], self.page_table, self.seq_lens)
+        else:
+            self.page_table = None
+            self.num_pages = 0
+            self.Kp = torch.zeros((cfg.B, cfg.Hkv, cfg.T, cfg.r), dtype=torch.int16, device=device)
+            self.desc = jssa.gqa_desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.r, cfg.T, cfg.d, 0, 0, 0, None,
+                                      self.seq_lens)
+        self.scale = 1.0 / math.sqrt(cfg.d)
+
+    def project(self, stream=None):
+        jssa.jssa_project_keys(self.desc, self.K, self.P, self.Kp, stream)
+
+
+class SparseStep:
+    """score -> top-k -> gather-free indexed split-K attention -> combine."""
+
+    def __init__(self, c: GqaCache, k: int, S: int = 8):
+        dev = c.q.device
+        self.c, self.k, self.S = c, k, S
+        self.scores = torch.empty((c.B, c.Hkv, c.T), dtype=torch.float32, device=dev)
+        nbytes = jssa.jssa_topk_workspace_size(c.B, c.Hkv, c.T, k)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty((c.B, c.Hkv, k), dtype=torch.int32, device=dev)
+        self.part_o = torch.empty((c.B, c.Hq, S, c.d), dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty((c.B, c.Hq, S), dtype=torch.float32, device=dev)
+        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+
+    def score(self, stream=None):
+        c = self.c
+        jssa.jssa_score(c.desc, c.q, c.P, c.Kp, self.scores, stream)
+
+    def topk(self, stream=None):
+        c = self.c
+        jssa.jssa_topk(c.B, c.Hkv, c.T, c.seq_lens, self.scores, self.k, self.idx, self.ws, None, stream)
+
+    def attend(self, stream=None):
+        c = self.c
+        jssa.jssa_indexed_decode(c.desc, c.q, c.K, c.V, self.idx, self.k, self.S, c.scale, self.part_o,
+                                 self.part_lse, stream)
+
+    def combine(self, stream=None):
+        c = self.c
+        jssa.jssa_combine(c.B, c.Hq, self.S, c.d, self.part_o, self.part_lse, self.out, 0, self.lse, stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.topk(stream)
+        self.attend(stream)
+        self.combine(stream)
+
+
+class DenseStep:
+    """Full-KV split-K attention -> combine."""
+
+    def __init__(self, c: GqaCache, S: int = 64):
+        dev = c.q.device
+        self.c, self.S = c, S
+        self.part_o = torch.empty((c.B, c.Hq, S, c.d), dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty((c.B, c.Hq, S), dtype=torch.float32, device=dev)
+        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+
+    def attend(self, stream=None):
+        c = self.c
+        jssa.jssa_dense_decode(c.desc, c.q, c.K, c.V, self.S, c.scale, self.part_o, self.part_lse, stream)
+
+    def combine(self, stream=None):
+        c = self.c
+        jssa.jssa_combine(c.B, c.Hq, self.S, c.d, self.part_o, self.part_lse, self.out, 0, self.lse, stream)
+
+    def run(self, stream=None):
+        self.attend(stream)
+        self.combine(stream)
+
+
+class GatherStep:
+    """Gather ablation: score -> top-k -> copy the selected rows into a
+    contiguous [B,Hkv,k,d] buffer -> dense attention over it -> combine."""
+
+    def __init__(self, sparse: SparseStep, S: int | None = None):
+        c = sparse.c
+        dev = c.q.device
+        self.sp, self.c = sparse, c
+        self.S = S or sparse.S
+        k = sparse.k
+        self.Kg = torch.empty((c.B, c.Hkv, k, c.d), dtype=torch.int16, device=dev)
+        self.Vg = torch.empty_like(self.Kg)
+        self.lens = torch.empty(c.B, dtype=torch.int32, device=dev)
+        self.gdesc = jssa.gqa_desc(c.B, c.Hq, c.Hkv, c.r, k, c.d, 0, 0, 0, None, self.lens)
+        self.part_o = torch.empty((c.B, c.Hq, self.S, c.d), dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty((c.B, c.Hq, self.S), dtype=torch.float32, device=dev)
+        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+
+    def gather(self, stream=None):
+        c = self.c
+        jssa.jssa_gather_kv(c.desc, c.K, c.V, self.sp.idx, self.sp.k, self.Kg, self.Vg, self.lens, stream)
+
+    def attend(self, stream=None):
+        c = self.c
+        jssa.jssa_dense_decode(self.gdesc, c.q, self.Kg, self.Vg, self.S, c.scale, self.part_o,
+                               self.part_lse, stream)
+
+    def combine(self, stream=None):
+        c = self.c
+        jssa.jssa_combine(c.B, c.Hq, self.S, c.d, self.part_o, self.part_lse, self.out, 0, self.lse, stream)
+
+    def run(self, stream=None):
+        self.sp.score(stream)
+        self.sp.topk(stream)
+        self.gather(stream)
+        self.attend(stream)
+        self.combine(stream)
+
+
+class MlaStep:
+    """MLA: absorb -> score -> top-k (one set per sequence) -> indexed MFMA
+    attention over the latent rows -> combine -> value up-projection."""
+
+    def __init__(self, inp: MlaInputs, S: int = 8, device="cuda"):
+        cfg = inp.cfg
+        self.cfg, self.S, self.k = cfg, S, cfg.k
+        self.q_nope = to_device(inp.q_nope, device)
+        self.q_rope = to_device(inp.q_rope, device)
+        self.W_uk = to_device(inp.W_uk, device)
+        self.W_uv = to_device(inp.W_uv, device)
+        self.P = to_device(inp.P, device)
+        self.latent = to_device(inp.latent, device)
+        self.seq_lens = to_device(inp.seq_lens.astype(np.int32), device)
+        self.desc = jssa.mla_desc(cfg.B, cfg.H, cfg.r, cfg.T, cfg.d_latent, cfg.d_rope, cfg.d_nope, cfg.d_v,
+                                  self.seq_lens)
+        self.scale = 1.0 / math.sqrt(cfg.d_nope + cfg.d_rope)
+        B, H = cfg.B, cfg.H
+        self.Kp = torch.zeros((B, cfg.T, cfg.r), dtype=torch.int16, device=device)
+        self.q_abs = torch.empty((B, H, cfg.d_c), dtype=torch.float32, device=device)
+        self.scores = torch.empty((B, cfg.T), dtype=torch.float32, device=device)
+        nbytes = jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        self.idx = torch.empty((B, cfg.k), dtype=torch.int32, device=device)
+        self.part_o = torch.empty((B, H, S, cfg.d_latent), dtype=torch.float32, device=device)
+        self.part_lse = torch.empty((B, H, S), dtype=torch.float32, device=device)
+        self.o_lat = torch.empty((B, H, cfg.d_latent), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=device)
+
+    def project(self, stream=None):
+        jssa.jssa_mla_project_latent(self.desc, self.latent, self.P, self.Kp, stream)
+
+    def run(self, stream=None):
+        cfg = self.cfg
+        jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.q_abs, stream)
+        jssa.jssa_mla_score(self.desc, self.q_abs, self.P, self.Kp, self.scores, stream)
+        jssa.jssa_topk(cfg.B, 1, cfg.T, self.seq_lens, self.scores, self.k, self.idx, self.ws, None, stream)
+        jssa.jssa_mla_indexed_decode(self.desc, self.q_abs, self.latent, self.idx, self.k, self.S,
+                                     self.scale, self.part_o, self.part_lse, stream)
+        jssa.jssa_combine(cfg.B, cfg.H, self.S, cfg.d_latent, self.part_o, self.part_lse, self.o_lat, 0,
+                          self.lse, stream)
+        jssa.jssa_mla_up_v(self.desc, self.o_lat, self.W_uv, self.out, stream)
