@@ -32,7 +32,7 @@ def parse():
                     choices=["gqa_128k_b16", "gqa_128k_b4", "llama3.1-8b_layer_32k", "qwen3-14b_paged_ragged",
                              "deepseek-v3_mla_128k"])
     ap.add_argument("--k", type=int, default=0, help="override the budget (paged workload sweep)")
-    ap.add_argument("--splits", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=0, help="splits of the selected set (0: by k)")
     ap.add_argument("--dense-splits", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
@@ -53,24 +53,31 @@ def workload(name: str):
     return synth.MLA_DSV3
 
 
-def time_loop(fns, steps, warmup, torch, stream):
-    """Run `fns` (a list of stage callables) warmup + steps times; returns
-    (total seconds of the timed steps, per-stage mean microseconds measured
-    with events on the launch stream)."""
+def time_loop(fns, steps, warmup, torch, stream, graph=None):
+    """Run `fns` (a list of stage callables) warmup + steps times. Returns
+    (seconds of the timed steps, per-stage mean microseconds).
+
+    The timed steps run back to back with nothing between them (bracketed by
+    device synchronisation); when `graph` (a captured torch CUDAGraph of the
+    same stages) is given, each step is one replay of it. The per-stage times
+    come from a second pass of eager steps with an event pair around every
+    stage on the launch stream."""
+    run = graph.replay if graph is not None else (lambda: [f() for f in fns])
     for _ in range(warmup):
-        for f in fns:
-            f()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     for s in range(steps):
         ev[s][0].record(stream)
         for i, f in enumerate(fns):
             f()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    total = time.perf_counter() - t0
     stage_us = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]) * 1e3)
                 for i in range(len(fns))]
     return total, stage_us
@@ -122,26 +129,44 @@ def main():
     c.project()
     torch.cuda.synchronize()
     print("[bench] projected keys on GPU", file=sys.stderr, flush=True)
-    k, S = cfg.k, args.splits
-    sp = pipeline.SparseStep(c, k=k, S=S)
-    total, st_us = time_loop([sp.score, sp.topk, sp.attend, sp.combine], args.steps, args.warmup, torch, stream)
-    ms = total / args.steps * 1e3
-    steps_s = args.steps / total
-    print(f"[bench] sparse {ms:.3f} ms/step", file=sys.stderr, flush=True)
-
+    k = cfg.k
     B, Hkv, Hq, d, r, T = cfg.B, cfg.Hkv, cfg.Hq, cfg.d, cfg.r, cfg.T
     tot_tok = int(np.sum(inp.seq_lens)) * Hkv            # (token, KV head) pairs scanned
-    score_bytes = tot_tok * 2 * r + B * Hq * d * 2 + Hkv * d * r * 4 + B * Hkv * T * 4
-    topk_bytes = B * Hkv * T * 4 + B * Hkv * k * 4
     nsel = int(np.sum(np.minimum(k, inp.seq_lens))) * Hkv
-    idx_bytes = nsel * 4 * d + B * Hkv * k * 4 + B * Hq * d * 2 + B * Hq * S * (d + 1) * 4
-    comb_bytes = B * Hq * S * (d + 1) * 4 + B * Hq * (d + 1) * 4
-    stage_names = ["score", "topk", "indexed", "combine"]
-    stage_bytes = [score_bytes, topk_bytes, idx_bytes, comb_bytes]
-    stages = {n: {"us": round(u, 2), "bytes": int(bb), "GB_s": round(bb / (u * 1e-6) / 1e9, 1),
-                  "frac_hbm": round(bb / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
-              for n, u, bb in zip(stage_names, st_us, stage_bytes)}
-    achieved = score_bytes / (st_us[0] * 1e-6) / 1e9
+    # the headline step: fused score -> top-k, then gather-free indexed attention
+    sp = pipeline.SparseStep(c, k=k, S=args.splits or None, fused=True, keep_scores=False)
+    S = sp.S
+    total, st_us = time_loop(sp.stages(), args.steps, args.warmup, torch, stream)
+    ms = total / args.steps * 1e3
+    steps_s = args.steps / total
+    print(f"[bench] sparse (fused score+top-k) {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    # the same step through the separate jssa_score / jssa_topk entry points
+    sp2 = pipeline.SparseStep(c, k=k, S=S, fused=False)
+    total2, st2_us = time_loop(sp2.stages(), args.steps, args.warmup, torch, stream)
+    print(f"[bench] sparse (separate score, top-k) {total2 / args.steps * 1e3:.3f} ms/step", file=sys.stderr,
+          flush=True)
+    comb_us = st_us[2] if S > 1 else 0.0
+
+    kp_bytes = tot_tok * 2 * r
+    q_bytes = B * Hq * d * 2
+    p_bytes = Hkv * d * r * 4
+    fused_bytes = kp_bytes + q_bytes + p_bytes            # the fused pass writes no score row
+    score_bytes = kp_bytes + q_bytes + p_bytes + B * Hkv * T * 4
+    topk_bytes = B * Hkv * T * 4 + B * Hkv * k * 4
+    idx_bytes = nsel * 4 * d + B * Hkv * k * 4 + q_bytes + B * Hq * S * (d + 1) * 4
+    comb_bytes = B * Hq * S * (d + 1) * 4 + B * Hq * (d + 1) * 4 if S > 1 else 0
+
+    def stage(us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9 if us > 0 else None
+        return {"us": round(us, 2), "bytes": int(nbytes), "GB_s": round(gbs, 1) if gbs else None,
+                "frac_hbm": round(gbs / HBM_PEAK_GBS, 3) if gbs else None}
+
+    stages = {"score_topk_fused": stage(st_us[0], fused_bytes), "indexed": stage(st_us[1], idx_bytes),
+              "combine": stage(comb_us, comb_bytes)}
+    stages_split = {"score": stage(st2_us[0], score_bytes), "topk": stage(st2_us[1], topk_bytes),
+                    "indexed": stage(st2_us[2], idx_bytes), "ms_per_step": round(total2 / args.steps * 1e3, 4),
+                    "steps_per_s": round(args.steps / total2, 2)}
+    achieved = fused_bytes / (st_us[0] * 1e-6) / 1e9
 
     result = {
         "metric": "sparse decode-attn steps/s at 128K,B=16 (Hkv=8,d=128,k=256); HBM GB/s vs peak",
@@ -152,10 +177,11 @@ def main():
                    "S": S, "paged": bool(cfg.paged)},
         "tokens_per_s": round(B * steps_s, 1),
         "context_tokens_scanned_per_s": round(tot_tok * steps_s, 1),
-        "roofline": {"bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "score_kernel (fused score + top-k chunk stage)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "stages": stages,
+        "separate_entry_points": stages_split,
     }
 
     if not args.no_compare:
@@ -168,16 +194,15 @@ def main():
                            "GB_s": round(dense_bytes / (dst_us[0] * 1e-6) / 1e9, 1),
                            "frac_hbm": round(dense_bytes / (dst_us[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 3)}
         result["speedup_vs_dense"] = round((dtotal / dsteps) / (total / args.steps), 3)
-        ga = pipeline.GatherStep(sp, S=S)
-        gtotal, gst_us = time_loop([sp.score, sp.topk, ga.gather, ga.attend, ga.combine], max(3, args.steps // 5),
-                                   2, torch, stream)
+        ga = pipeline.GatherStep(sp, S=max(S, 4))
         gsteps = max(3, args.steps // 5)
-        sparse_attn_us = st_us[2] + st_us[3]
-        gather_attn_us = gst_us[2] + gst_us[3] + gst_us[4]
+        gtotal, gst_us = time_loop([sp.score_topk, ga.gather, ga.attend, ga.combine], gsteps, 2, torch, stream)
+        sparse_attn_us = st_us[1] + comb_us
+        gather_attn_us = gst_us[1] + gst_us[2] + gst_us[3]
         dense_attn_us = dst_us[0] + dst_us[1]
         result["gather_ablation"] = {
-            "ms_per_step": round(gtotal / gsteps * 1e3, 4), "gather_us": round(gst_us[2], 2),
-            "dense_on_gathered_us": round(gst_us[3], 2),
+            "ms_per_step": round(gtotal / gsteps * 1e3, 4), "gather_us": round(gst_us[1], 2),
+            "dense_on_gathered_us": round(gst_us[2], 2), "combine_us": round(gst_us[3], 2),
             "attention_stage_us": {"gather_free": round(sparse_attn_us, 2), "gather": round(gather_attn_us, 2),
                                    "dense_full_kv": round(dense_attn_us, 2)},
             "attention_stage_speedup_vs_dense": {"gather_free": round(dense_attn_us / sparse_attn_us, 2),

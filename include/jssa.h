@@ -147,6 +147,24 @@ JSSA_API jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int3
                       void* stream);
 
 /*
+ * Fused score -> top-k: the subspace score stream of jssa_score and the
+ * selection of jssa_topk in one pass over the projected key cache. Each
+ * 8192-token chunk keeps its scores in registers and emits only the tokens
+ * that can still be among its row's k best, so the fp32 score row is never
+ * written and read back (unless `scores` is given).
+ *  q, P, Kp  as jssa_score; k as jssa_topk (1 <= k <= min(4096, max_seq))
+ *  scores    device fp32 [B,Hkv,max_seq] or NULL: if given, written exactly
+ *            as by jssa_score
+ *  idx       device int32 [B,Hkv,k]: exactly what jssa_topk returns for the
+ *            scores jssa_score computes
+ *  ws        device workspace of at least jssa_score_topk_workspace_size bytes
+ */
+JSSA_API jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes);
+JSSA_API jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                     int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/*
  * Gather-free indexed attention, split-K partials (digest Interpretation:
  * selected tokens are read where they lie through scattered indices rather
  * than copied into a contiguous buffer; JSSA abstract).

@@ -85,12 +85,11 @@ def test_desc_validation(J):
 def test_topk_workspace(J):
     n = J.jssa_topk_workspace_size(16, 8, 131072, 256)
     assert n > 16 * 8 * 256 * 8           # at least one candidate list per row
-    assert J.jssa_topk_workspace_size(1, 1, 1000, 10) == 0   # one chunk: no workspace
+    assert J.jssa_topk_workspace_size(1, 1, 1000, 10) > 0
     assert _status(J.jssa_topk_workspace_size, 1, 1, 100, 101) == J.ERR_SHAPE
     assert _status(J.jssa_topk_workspace_size, 1, 1, 10000, 4097) == J.ERR_SHAPE
     assert _status(J.jssa_topk, 16, 8, 131072, None, A, 256, A, A, n - 1) == J.ERR_WORKSPACE
     assert _status(J.jssa_topk, 16, 8, 131072, None, None, 256, A, A, n) == J.ERR_NULL
-    # long rows with a large budget take extra merge rounds; the plan still fits
     for T, k in [(1 << 24, 4096), (1 << 24, 1), (262144, 4096), (131072, 2048)]:
         assert J.jssa_topk_workspace_size(4, 2, T, k) > 0
 

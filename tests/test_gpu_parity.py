@@ -189,10 +189,10 @@ def test_topk_empty_and_all_equal(J):
 # ---------------------------------------------------------------------------
 # whole sparse step, dense, gather ablation, combine
 # ---------------------------------------------------------------------------
-def _sparse_and_check(J, PL, inp, k, S, units=None):
+def _sparse_and_check(J, PL, inp, k, S, units=None, fused=False):
     c = PL.GqaCache(inp)
     c.project()
-    st = PL.SparseStep(c, k=k, S=S)
+    st = PL.SparseStep(c, k=k, S=S, fused=fused)
     st.run()
     torch.cuda.synchronize()
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
@@ -217,6 +217,41 @@ def test_sparse_step_parity(J, PL, cfg, k, S):
 
 def test_sparse_step_ragged(J, PL):
     _sparse_and_check(J, PL, ragged_inputs(), 256, 8)
+
+
+@pytest.mark.parametrize("cfg,k,S", [(synth.TINY, 256, 1), (synth.LLAMA8B_32K, 256, 1), (RAGGED, 300, 2)])
+def test_sparse_step_fused(J, PL, cfg, k, S):
+    inp = ragged_inputs() if cfg is RAGGED else synth.make_gqa(cfg)
+    _sparse_and_check(J, PL, inp, k, S, fused=True)
+
+
+@pytest.mark.parametrize("case", ["ragged32", "r48_paged_k2048", "r128_k4096", "tiny_k1", "r16_T100"])
+def test_score_topk_fused_equals_split(J, PL, case):
+    """The fused score + top-k pass returns exactly the indices (and, when
+    asked, the scores) of jssa_score followed by jssa_topk."""
+    if case == "ragged32":
+        inp, k = ragged_inputs(), 256
+    elif case == "r48_paged_k2048":
+        inp, k = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=40000, len_lo=20000, len_hi=40000, seed=81)), 2048
+    elif case == "r128_k4096":
+        inp, k = synth.make_gqa(replace(synth.TINY, r=128, T=20000, B=2, seed=82)), 4096
+    elif case == "tiny_k1":
+        inp, k = synth.make_gqa(synth.TINY), 1
+    else:
+        inp, k = synth.make_gqa(replace(synth.TINY, r=16, T=100, seed=83)), 60
+    c = PL.GqaCache(inp)
+    c.project()
+    a = PL.SparseStep(c, k=k, fused=False)
+    a.score()
+    a.topk()
+    b = PL.SparseStep(c, k=k, fused=True, keep_scores=True)
+    b.score_topk()
+    nb = PL.SparseStep(c, k=k, fused=True, keep_scores=False)
+    nb.score_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(b.idx), _np(a.idx))
+    np.testing.assert_array_equal(_np(nb.idx), _np(a.idx))
+    np.testing.assert_array_equal(_np(b.scores), _np(a.scores))
 
 
 @pytest.mark.parametrize("k", [256, 1024, 2048])
@@ -378,3 +413,27 @@ def test_mla_parity(J, PL):
                                         st.scale)
         U.check_close(out[b], o, what=f"mla out b={b}")
         U.check_close(lse[b], l, what=f"mla lse b={b}")
+
+
+# ---------------------------------------------------------------------------
+# full size: the 128K x B=16 workload in the launch configuration the
+# benchmark times; sampled units against the oracle, properties everywhere
+# ---------------------------------------------------------------------------
+def test_full_size_128k_b16_sampled(J, PL):
+    cfg = synth.BATCHED_128K
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=cfg.k)
+    st.run()
+    torch.cuda.synchronize()
+    idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
+    assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < cfg.T
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(0)
+    rows = rng.choice(cfg.T, 2048, replace=False)
+    for b, j in [(0, 0), (3, 5), (7, 2), (12, 7), (15, 1)]:
+        K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+        np.testing.assert_array_equal(_np(c.Kp[b, j, torch.from_numpy(rows).cuda()]), Kp[rows])
+        U.check_indices(idx[b, j], s, cfg.k)
+        U.check_attention(inp, b, j, hs, K, V, idx[b, j], out, lse, c.scale)

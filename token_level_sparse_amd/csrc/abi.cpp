@@ -189,6 +189,32 @@ jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int32_t* seq_
                     __func__);
 }
 
+jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
+  if (k < 1 || k > 4096 || k > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
+  jssa::carve_segs(nullptr, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
+                   jssa::score_topk_segment_cap(), bytes);
+  return JSSA_OK;
+}
+
+jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp, int32_t k,
+                            float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(idx); REQUIRE_PTR(ws);
+  REQUIRE_ALIGNED_OPT(scores);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
+                                         jssa::score_topk_segment_cap(), nullptr);
+  return hip_status(jssa::launch_score_topk(to_dev(desc), static_cast<const uint16_t*>(q), P,
+                                            static_cast<const uint16_t*>(Kp), k, scores, idx, segs,
+                                            S(stream)),
+                    __func__);
+}
+
 jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* q, const void* K, const void* V,
                                 const int32_t* idx, int32_t k, int32_t S_, float scale, float* part_o,
                                 float* part_lse, void* stream) {

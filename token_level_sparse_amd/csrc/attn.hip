@@ -23,6 +23,11 @@ namespace {
 constexpr int kD = 128;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Reinterpret one dword (two packed bf16) as a bf16 pair. Takes the dword by
+// value: bit-casting a vector-element lvalue (v.y) directly reads element 0.
+__device__ __forceinline__ bf16x2 as_pair(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
 template <int GT, int STEPS, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t* __restrict__ q,
@@ -54,17 +59,19 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
   }
   const int32_t* irow = DENSE ? nullptr : idx + (int64_t(b) * g.Hkv + j) * k;
 
-  // query slice (dims sub*8..+8) of each head, pre-scaled into the log2 domain
-  float qf[GT][8];
+  // query slice (dims sub*8..+8) of each head as bf16 pairs; logits use
+  // v_dot2_f32_bf16 (exact bf16 products, fp32 sums) and are scaled into the
+  // log2 domain after the row reduction
+  bf16x2 qv[GT][4];
   const float qs = scale * kLog2e;
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
     if (h < nh) v = *reinterpret_cast<const u32x4*>(q + (int64_t(b) * g.Hq + h0 + h) * kD + sub * 8);
-    qf[h][0] = bf_lo(v.x) * qs; qf[h][1] = bf_hi(v.x) * qs;
-    qf[h][2] = bf_lo(v.y) * qs; qf[h][3] = bf_hi(v.y) * qs;
-    qf[h][4] = bf_lo(v.z) * qs; qf[h][5] = bf_hi(v.z) * qs;
-    qf[h][6] = bf_lo(v.w) * qs; qf[h][7] = bf_hi(v.w) * qs;
+    qv[h][0] = as_pair(v.x);
+    qv[h][1] = as_pair(v.y);
+    qv[h][2] = as_pair(v.z);
+    qv[h][3] = as_pair(v.w);
   }
 
   float m[GT], l[GT], o[GT][8];
@@ -99,14 +106,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const u32x4 v = kr[st];
-      float kf[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                     bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+      const bf16x2 k0 = as_pair(v.x), k1 = as_pair(v.y), k2 = as_pair(v.z), k3 = as_pair(v.w);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(qf[h][e], kf[e], a);
-        a = row16_sum(a);
+        float a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][0], k0, 0.f, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][1], k1, a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][2], k2, a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][3], k3, a, false);
+        a = row16_sum(a) * qs;
         lg[st][h] = ok[st] ? a : -__builtin_inff();
       }
     }
@@ -220,19 +227,17 @@ hipError_t launch_attn_t(const GqaDev& g, const uint16_t* q, const uint16_t* K, 
 }
 
 template <bool DENSE, int NW>
-hipError_t launch_attn(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                       const int32_t* idx, int k, int S, float scale, float* po, float* pl,
-                       hipStream_t st) {
+hipError_t launch_attn_g(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                         const int32_t* idx, int k, int S, float scale, float* po, float* pl,
+                         hipStream_t st) {
   switch (g.G) {
     case 1: return launch_attn_t<1, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
     case 2: return launch_attn_t<2, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
     case 3: case 6: case 9: case 12: case 15:
       return launch_attn_t<3, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
-    case 4: case 8: case 16:
-      return launch_attn_t<4, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
     case 5: case 10:
       return launch_attn_t<5, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
-    default:   // 7, 11, 13, 14: groups of up to 4 heads, the last one partial
+    default:   // 4, 8, 16 and 7, 11, 13, 14: groups of up to 4 heads
       return launch_attn_t<4, 8, NW, DENSE>(g, q, K, V, idx, k, S, scale, po, pl, st);
   }
 }
@@ -242,12 +247,17 @@ hipError_t launch_attn(const GqaDev& g, const uint16_t* q, const uint16_t* K, co
 hipError_t launch_indexed(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                           const int32_t* idx, int k, int S, float scale, float* part_o,
                           float* part_lse, hipStream_t st) {
-  return launch_attn<false, 1>(g, q, K, V, idx, k, S, scale, part_o, part_lse, st);
+  // one wave per 32 rows of a split, up to 8 waves merged in LDS
+  const int rows = (k + S - 1) / S;
+  if (rows > 128) return launch_attn_g<false, 8>(g, q, K, V, idx, k, S, scale, part_o, part_lse, st);
+  if (rows > 64) return launch_attn_g<false, 4>(g, q, K, V, idx, k, S, scale, part_o, part_lse, st);
+  if (rows > 32) return launch_attn_g<false, 2>(g, q, K, V, idx, k, S, scale, part_o, part_lse, st);
+  return launch_attn_g<false, 1>(g, q, K, V, idx, k, S, scale, part_o, part_lse, st);
 }
 
 hipError_t launch_dense(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                         int S, float scale, float* part_o, float* part_lse, hipStream_t st) {
-  return launch_attn<true, 4>(g, q, K, V, nullptr, 0, S, scale, part_o, part_lse, st);
+  return launch_attn_g<true, 4>(g, q, K, V, nullptr, 0, S, scale, part_o, part_lse, st);
 }
 
 }  // namespace jssa

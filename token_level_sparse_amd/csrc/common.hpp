@@ -87,9 +87,11 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 // Ordering fence for data exchanged through LDS between lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  // Fences limited to LDS ("local"): they order the wave's LDS accesses
+  // without waiting for its global loads in flight.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

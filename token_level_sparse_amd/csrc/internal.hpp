@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "select.hpp"
 
 namespace jssa {
 
@@ -18,6 +19,11 @@ hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, cons
                         float* scores, hipStream_t st);
 
 size_t topk_workspace_bytes(int rows, int max_seq, int k);
+CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total);
+int score_topk_segments(int max_seq);
+int score_topk_segment_cap();
+hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
+                             float* scores, int32_t* idx, CandSegs segs, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
 

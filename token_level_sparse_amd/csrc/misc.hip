@@ -11,40 +11,52 @@
 namespace jssa {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(int H, int S, int dv,
+// One row (b, h) per tpr = dv/4 threads, several rows per 256-thread block.
+// Loads of the partials are issued 8 splits at a time so their latencies
+// overlap.
+__global__ __launch_bounds__(256) void combine_kernel(int rows, int S, int dv,
                                                       const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       void* __restrict__ out, int out_bf16,
                                                       float* __restrict__ lse_out) {
-  const int bh = blockIdx.x;
+  const int tpr = dv / 4;
+  const int rpb = 256 / tpr;
+  const int bh = blockIdx.x * rpb + threadIdx.x / tpr;
+  const int c4 = threadIdx.x % tpr;
+  if (bh >= rows || threadIdx.x >= rpb * tpr) return;
   const float* pl = part_lse + int64_t(bh) * S;
   float M = -__builtin_inff();
   for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (M != -__builtin_inff())
-    for (int s = 0; s < S; ++s) L += __expf(pl[s] - M);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int c4 = threadIdx.x; c4 * 4 < dv; c4 += blockDim.x) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (L > 0.f) {
-      for (int s = 0; s < S; ++s) {
-        const float wgt = __expf(pl[s] - M);
-        if (wgt == 0.f) continue;
-        const f32x4 v = reinterpret_cast<const f32x4*>(part_o + (int64_t(bh) * S + s) * dv)[c4];
-        acc += wgt * v;
+  if (M != -__builtin_inff()) {
+    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + int64_t(bh) * S * dv) + c4;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      f32x4 v[8];
+      float wgt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = s0 + i;
+        wgt[i] = s < S ? __expf(pl[s] - M) : 0.f;
+        v[i] = (s < S && wgt[i] != 0.f) ? po[int64_t(s) * tpr] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      acc *= inv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        L += wgt[i];
+        acc += wgt[i] * v[i];
+      }
     }
-    if (out_bf16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + int64_t(bh) * dv + c4 * 4;
-      u32x2 pk = {uint32_t(f32_to_bf16_rne(acc.x)) | (uint32_t(f32_to_bf16_rne(acc.y)) << 16),
-                  uint32_t(f32_to_bf16_rne(acc.z)) | (uint32_t(f32_to_bf16_rne(acc.w)) << 16)};
-      *reinterpret_cast<u32x2*>(o) = pk;
-    } else {
-      reinterpret_cast<f32x4*>(static_cast<float*>(out) + int64_t(bh) * dv)[c4] = acc;
-    }
+    acc *= 1.f / L;
   }
-  if (lse_out && threadIdx.x == 0) lse_out[bh] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+  if (out_bf16) {
+    uint16_t* o = static_cast<uint16_t*>(out) + int64_t(bh) * dv + c4 * 4;
+    u32x2 pk = {uint32_t(f32_to_bf16_rne(acc.x)) | (uint32_t(f32_to_bf16_rne(acc.y)) << 16),
+                uint32_t(f32_to_bf16_rne(acc.z)) | (uint32_t(f32_to_bf16_rne(acc.w)) << 16)};
+    *reinterpret_cast<u32x2*>(o) = pk;
+  } else {
+    reinterpret_cast<f32x4*>(static_cast<float*>(out) + int64_t(bh) * dv)[c4] = acc;
+  }
+  if (lse_out && c4 == 0) lse_out[bh] = L > 0.f ? M + __logf(L) : -__builtin_inff();
 }
 
 // One 16-lane group per selected row; 16 rows per 256-thread block.
@@ -77,10 +89,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GqaDev g, const uint16_t* _
 
 hipError_t launch_combine(int B, int H, int S, int dv, const float* part_o, const float* part_lse,
                           void* out, bool out_bf16, float* lse, hipStream_t st) {
-  int threads = dv / 4;
-  threads = threads < 64 ? 64 : (threads > 256 ? 256 : ((threads + 63) / 64) * 64);
-  hipLaunchKernelGGL(combine_kernel, dim3(B * H), dim3(threads), 0, st, H, S, dv, part_o, part_lse,
-                     out, out_bf16 ? 1 : 0, lse);
+  const int rows = B * H;
+  const int tpr = dv / 4;
+  const int rpb = tpr >= 256 ? 1 : 256 / tpr;
+  if (tpr > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, rows, S, dv, part_o,
+                     part_lse, out, out_bf16 ? 1 : 0, lse);
   return hipGetLastError();
 }
 

@@ -111,71 +111,6 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// Selection score stream: s[b,t] = (P^T sum_h q_abs[b,h]) . Kp_lat[b,t], one
-// set per sequence (all heads share the latent cache). Same streaming scheme
-// as the GQA score kernel: coalesced 16-byte pieces, partial dots via LDS.
-// ---------------------------------------------------------------------------
-template <int R>
-__global__ __launch_bounds__(256) void mla_score_kernel(MlaDev m, const float* __restrict__ qa,
-                                                        const float* __restrict__ P,
-                                                        const uint16_t* __restrict__ Kp,
-                                                        float* __restrict__ scores, int tpw) {
-  constexpr int PP = R / 8;
-  __shared__ float qbar[kDc];
-  __shared__ float qp[R];
-  __shared__ float part[4][64 * PP];
-  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int Tb = mla_len(m, b);
-  // prologue: qbar over heads, then qp. The summed query is H x 576 floats
-  // per sequence; blocks of one sequence read it from L2.
-  for (int c = tid; c < kDc; c += 256) {
-    float s = 0.f;
-    for (int h = 0; h < m.H; ++h) s += qa[(int64_t(b) * m.H + h) * kDc + c];
-    qbar[c] = s;
-  }
-  __syncthreads();
-  if (tid < R) {
-    float s = 0.f;
-    for (int i = 0; i < kDc; ++i) s = __builtin_fmaf(P[i * R + tid], qbar[i], s);
-    qp[tid] = s;
-  }
-  __syncthreads();
-  float qr[8];
-  const int sl = lane % PP;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qr[e] = qp[sl * 8 + e];
-  const int chunk = 4 * 64 * tpw;
-  float* srow = scores + int64_t(b) * m.max_seq;
-  for (int tile = 0; tile < tpw; ++tile) {
-    const int t0 = blockIdx.x * chunk + (tile * 4 + w) * 64;
-    const u32x4* base = reinterpret_cast<const u32x4*>(Kp + (int64_t(b) * m.max_seq + t0) * R);
-#pragma unroll
-    for (int mm = 0; mm < PP; ++mm) {
-      const int p = mm * 64 + lane;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + p / PP < Tb) v = __builtin_nontemporal_load(base + p);
-      float a = 0.f;
-      a = __builtin_fmaf(qr[0], bf_lo(v.x), a);
-      a = __builtin_fmaf(qr[1], bf_hi(v.x), a);
-      a = __builtin_fmaf(qr[2], bf_lo(v.y), a);
-      a = __builtin_fmaf(qr[3], bf_hi(v.y), a);
-      a = __builtin_fmaf(qr[4], bf_lo(v.z), a);
-      a = __builtin_fmaf(qr[5], bf_hi(v.z), a);
-      a = __builtin_fmaf(qr[6], bf_lo(v.w), a);
-      a = __builtin_fmaf(qr[7], bf_hi(v.w), a);
-      part[w][p] = a;
-    }
-    wave_lds_sync();
-    float s = 0.f;
-#pragma unroll
-    for (int pc = 0; pc < PP; ++pc) s += part[w][lane * PP + pc];
-    wave_lds_sync();
-    const int t = t0 + lane;
-    if (t < m.max_seq) srow[t] = t < Tb ? s : -__builtin_inff();
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Indexed MLA attention on MFMA. Block = 1 wave = 16 heads x one split of the
 // selected slots, processed 32 tokens at a time.
 //  QK^T: S^T[16 tok x 16 heads] += C[16 tok x 32 dims] . Qt[32 dims x 16 heads]
@@ -379,23 +314,6 @@ hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const flo
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
                              const uint16_t* W_uk, float* q_abs, hipStream_t st) {
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(m.H), dim3(256), 0, st, m, q_nope, q_rope, W_uk, q_abs);
-  return hipGetLastError();
-}
-
-hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P, const uint16_t* Kp,
-                            float* scores, hipStream_t st) {
-  const int64_t tiles = (m.max_seq + 63) / 64;
-  int64_t tpw = (int64_t(m.B) * tiles + 2048 * 4 - 1) / (2048 * 4);
-  if (tpw < 16) tpw = 16;
-  if (tpw > 64) tpw = 64;
-  const int64_t chunk = 4 * 64 * tpw;
-  dim3 grid(unsigned((m.max_seq + chunk - 1) / chunk), m.B);
-  switch (m.r) {
-    case 16: hipLaunchKernelGGL(mla_score_kernel<16>, grid, dim3(256), 0, st, m, q_abs, P, Kp, scores, int(tpw)); break;
-    case 32: hipLaunchKernelGGL(mla_score_kernel<32>, grid, dim3(256), 0, st, m, q_abs, P, Kp, scores, int(tpw)); break;
-    case 64: hipLaunchKernelGGL(mla_score_kernel<64>, grid, dim3(256), 0, st, m, q_abs, P, Kp, scores, int(tpw)); break;
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -1,163 +1,310 @@
-// Subspace score stream: scores[b,j,t] = qp(b,j) . Kp[b,j,t,:].
+// Subspace score stream: scores[b,j,t] = qp(b,j) . Kp[b,j,t,:], and the
+// same stream fused with the chunk stage of the top-k selection.
 //
 // JSSA ranks candidate tokens in a low-dimensional space that holds queries
 // and keys together (ai4snews digest, Synopsis and Interpretation). A KV
 // head's score sums its G query heads' scores; by linearity that is one dot of
 // qp = P_j^T (sum_h q_h) with the stored projected key, so the stream reads
-// 2r bytes per token and does r FMAs.
+// 2r bytes per token and does r FMAs. For the MLA latent cache the same
+// stream runs with qp = P^T (sum over all heads of the absorbed query).
 //
 // HBM-bound streaming kernel. Each wave reads a tile of 64 tokens' projected
 // keys as 64*r/8 contiguous 16-byte pieces, one coalesced dwordx4 load per
-// piece column (1 KB per wave instruction), so every load instruction covers
-// whole cache lines. Lane l of load m holds piece m*64+l; its 8-element
-// partial dot goes through LDS and lane t then sums the r/8 partials of token
-// t and writes one fp32 score (a coalesced 256-byte store per wave). The next
-// tile's loads are issued before the current tile is reduced.
+// piece column (1 KB per wave instruction, whole cache lines). Lane l of load
+// m holds piece 64m+l; the r/8 lanes holding one token's pieces are adjacent,
+// so their 8-element partial dots are summed with DPP moves, and one
+// ds_bpermute per load column hands token i's score to lane i: every lane
+// then owns one token of the tile and the scores leave as one coalesced
+// 256-byte store per wave. The next tile's loads are in flight while the
+// current tile is reduced, and the first tile's loads are issued before the
+// qp prologue. r = 48 (6 lanes per token, not aligned to DPP rows) sums its
+// partials through LDS instead.
+//
+// Fused variant (score -> top-k chunk stage): after the stream the block runs the
+// chunk selection of the top-k (chunk_select) on its 8192 tokens and writes
+// the surviving candidates, so the row's final selection never has to read
+// the whole score row back. Writing the scores themselves is optional.
 #include "internal.hpp"
+#include "select.hpp"
 
 namespace jssa {
 namespace {
 
 constexpr int kD = 128;
+constexpr int kDc = 576;
 constexpr int kWaves = 4;
+constexpr int kFusedTiles = 32;            // tiles of 64 tokens per wave: 8192-token chunks
+constexpr int kPlainTiles = 16;            // 4096-token chunks for the score-only stream
+constexpr int kDepth = 2;                  // tiles per wave whose loads are in flight together
 
-template <int R>
-struct ScoreShape {
-  static constexpr int PP = R / 8;                 // 16-byte pieces per token
-  static constexpr int M = PP;                     // loads per lane per 64-token tile
-  static constexpr bool kUniformSlice = (64 % PP) == 0;
+// sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16)
+template <int PP>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (PP >= 2) x += dpp_mov<0xb1>(x);     // quad_perm [1,0,3,2]
+  if constexpr (PP >= 4) x += dpp_mov<0x4e>(x);     // quad_perm [2,3,0,1]
+  if constexpr (PP >= 8) x += dpp_mov<0x141>(x);    // row_half_mirror
+  if constexpr (PP >= 16) x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float dot8(const float (&q)[8], u32x4 v) {
+  float a = 0.f;
+  a = __builtin_fmaf(q[0], bf_lo(v.x), a);
+  a = __builtin_fmaf(q[1], bf_hi(v.x), a);
+  a = __builtin_fmaf(q[2], bf_lo(v.y), a);
+  a = __builtin_fmaf(q[3], bf_hi(v.y), a);
+  a = __builtin_fmaf(q[4], bf_lo(v.z), a);
+  a = __builtin_fmaf(q[5], bf_hi(v.z), a);
+  a = __builtin_fmaf(q[6], bf_lo(v.w), a);
+  a = __builtin_fmaf(q[7], bf_hi(v.w), a);
+  return a;
+}
+
+enum Mode { kGqa = 0, kMla = 1 };
+
+struct FusedOut {
+  CandSegs segs;
+  int k;
+  int write_scores;
 };
 
 template <int R>
+struct ScoreSmem {
+  float qbar[kDc];
+  float qpart[256];
+  float qp[R];
+  float part[(R / 8) & (R / 8 - 1) ? kWaves * 8 * R : 1];   // LDS reduction (r = 48 only)
+};
+
+template <int R, int MODE, bool FUSED>
 __global__ __launch_bounds__(256) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
+                                                    const float* __restrict__ qabs, int Hmla,
                                                     const float* __restrict__ P,
                                                     const uint16_t* __restrict__ Kp,
-                                                    float* __restrict__ scores, int tiles_per_wave) {
-  using S = ScoreShape<R>;
-  __shared__ float qbar[kD];
-  __shared__ float qpart[256];
-  __shared__ float qp[R];
-  __shared__ float part[kWaves][64 * S::M];
+                                                    float* __restrict__ scores, FusedOut fo) {
+  constexpr int PP = R / 8;                   // lanes (16-byte pieces) per token
+  constexpr bool kDpp = (PP & (PP - 1)) == 0; // power of two -> DPP groups
+  constexpr int DIN = MODE == kGqa ? kD : kDc;
+  constexpr int NSL = kDpp ? 1 : PP;          // qp slices held per lane
+  constexpr int TPW = FUSED ? kFusedTiles : kPlainTiles;
+  __shared__ ScoreSmem<R> sm;
+  // Fused: token o of the chunk is staged at (o % TPW) * (256 + 1) + o / TPW,
+  // so thread i later reads its TPW consecutive tokens o = i*TPW + e at
+  // e*257 + i; the +1 pad keeps both the tile writes and those reads free of
+  // LDS bank conflicts. Score-only: staged at o.
+  static_assert(!FUSED || kWaves * 64 == 256, "fused staging assumes 256 threads");
+  constexpr int kStageBytes = FUSED ? TPW * 257 * 4 : kWaves * 64 * TPW * 4;
+  constexpr int kBufBytes = kStageBytes > int(sizeof(ChunkSmem<256, TPW>)) ? kStageBytes : int(sizeof(ChunkSmem<256, TPW>));
+  __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
 
   const int b = blockIdx.z, j = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, kept scalar
   const int Tb = seq_len(g, b);
+  const int chunk = kWaves * 64 * TPW;
+  const int t_begin = blockIdx.x * chunk;
+  float* srow = scores ? scores + (int64_t(b) * g.Hkv + j) * g.max_seq : nullptr;
+  const bool paged = g.page_size != 0;
+  const int64_t ubase = (int64_t(b) * g.Hkv + j) * int64_t(g.max_seq) * R;   // contiguous unit base
 
-  // ---- prologue: qp = P_j^T sum_{h in group} q_h (fp32)
-  if (tid < kD) {
-    const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + tid;
-    float s = 0.f;
-    for (int h = 0; h < g.G; ++h) s += bf(qg[h * kD]);
-    qbar[tid] = s;
+  const int64_t seg = FUSED ? int64_t(b * g.Hkv + j) * fo.segs.nseg + blockIdx.x : 0;
+  if (t_begin >= Tb) {                       // whole chunk past the sequence's end
+    if (!FUSED || fo.write_scores) {
+      const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
+      for (int i = tid; i < lim; i += 256) srow[t_begin + i] = -__builtin_inff();
+    }
+    if (FUSED && tid == 0) fo.segs.cnt[seg] = 0;
+    return;
+  }
+  // Tokens of this block are [t_begin, tend); loads of later positions are
+  // clamped to token tend - 1 (a cache hit) and masked out of the result, so
+  // every tile's loads are issued without a branch.
+  const int tend = Tb - t_begin < chunk ? Tb : t_begin + chunk;
+  __shared__ int pid[FUSED ? kWaves * 64 * kFusedTiles / kPage : kWaves * 64 * kPlainTiles / kPage];
+  if (paged) {                               // page ids of the chunk (-1: no valid page)
+    for (int i = tid; i < chunk / kPage; i += 256) {
+      int t = t_begin + i * kPage;
+      t = t < tend ? t : tend - 1;
+      const int pg = g.page_table[int64_t(b) * g.max_pages + (t >> 4)];
+      pid[i] = pg >= 0 && pg < g.num_pages ? pg : -1;
+    }
+    __syncthreads();
+  }
+  auto load_tile = [&](int tile, u32x4 (&buf)[PP]) {
+    const int t0 = t_begin + (tile * kWaves + w) * 64;
+#pragma unroll
+    for (int m = 0; m < PP; ++m) {
+      const int p = m * 64 + lane;
+      int t = t0 + p / PP;
+      t = t < tend ? t : tend - 1;
+      int64_t off;
+      if (!paged) {
+        off = ubase + int64_t(t) * R;
+      } else {
+        int pg = pid[(t - t_begin) >> 4];
+        pg = pg < 0 ? 0 : pg;
+        off = ((int64_t(pg) * g.Hkv + j) * kPage + (t & (kPage - 1))) * R;
+      }
+      buf[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kp + off) + p % PP);
+    }
+  };
+  auto token_ok = [&](int t) -> bool {
+    if (t >= tend) return false;
+    return !paged || pid[(t - t_begin) >> 4] >= 0;
+  };
+
+  u32x4 bufs[kDepth][PP];
+  load_tile(0, bufs[0]);                       // in flight during the prologue
+
+  // ---- prologue: qp = P_j^T qbar (fp32). Loops are unrolled so that their
+  // loads are all in flight together rather than one round trip each.
+  if constexpr (MODE == kGqa) {
+    if (tid < kD) {
+      const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + tid;
+      float s = 0.f;
+      int h = 0;
+      for (; h + 4 <= g.G; h += 4) {
+        const float a0 = bf(qg[h * kD]), a1 = bf(qg[(h + 1) * kD]);
+        const float a2 = bf(qg[(h + 2) * kD]), a3 = bf(qg[(h + 3) * kD]);
+        s += a0; s += a1; s += a2; s += a3;
+      }
+      for (; h < g.G; ++h) s += bf(qg[h * kD]);
+      sm.qbar[tid] = s;
+    }
+  } else {
+    for (int c = tid; c < kDc; c += 256) {
+      const float* qc = qabs + int64_t(b) * Hmla * kDc + c;
+      float s = 0.f;
+      int h = 0;
+      for (; h + 8 <= Hmla; h += 8) {
+        float a[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = qc[int64_t(h + u) * kDc];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += a[u];
+      }
+      for (; h < Hmla; ++h) s += qc[int64_t(h) * kDc];
+      sm.qbar[c] = s;
+    }
   }
   __syncthreads();
   {
-    constexpr int NS = 256 / R;          // i-slices per output column
+    constexpr int NS = 256 / R;
+    constexpr int NI = (DIN + NS - 1) / NS;
     const int c = tid % R, sl = tid / R;
     if (sl < NS) {
-      const float* Pj = P + int64_t(j) * kD * R;
+      const float* Pj = P + int64_t(j) * DIN * R;
       float s = 0.f;
-      for (int i = sl; i < kD; i += NS) s = __builtin_fmaf(Pj[i * R + c], qbar[i], s);
-      qpart[sl * R + c] = s;
+#pragma unroll 16
+      for (int ii = 0; ii < NI; ++ii) {
+        const int i = sl + ii * NS;
+        const int ic = i < DIN ? i : DIN - 1;      // unconditional load, zero weight past DIN
+        const float pv = Pj[ic * R + c];
+        s = __builtin_fmaf(pv, i < DIN ? sm.qbar[ic] : 0.f, s);
+      }
+      sm.qpart[sl * R + c] = s;
     }
     __syncthreads();
     if (tid < R) {
       float s = 0.f;
-      for (int k = 0; k < NS; ++k) s += qpart[k * R + tid];
-      qp[tid] = s;
+      for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
+      sm.qp[tid] = s;
     }
     __syncthreads();
   }
-
-  // per-load qp slices held in registers
-  constexpr int NSL = S::kUniformSlice ? 1 : S::M;
   float qr[NSL][8];
 #pragma unroll
   for (int m = 0; m < NSL; ++m) {
-    const int sl = (m * 64 + lane) % S::PP;
+    const int sl = (m * 64 + lane) % PP;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qr[m][e] = qp[sl * 8 + e];
+    for (int e = 0; e < 8; ++e) qr[m][e] = sm.qp[sl * 8 + e];
   }
 
-  const int chunk = kWaves * 64 * tiles_per_wave;
-  const int t_begin = blockIdx.x * chunk;
-  float* srow = scores + (int64_t(b) * g.Hkv + j) * g.max_seq;
-  const bool paged = g.page_size != 0;
-
-  auto load_tile = [&](int tile, u32x4 (&buf)[S::M]) {
-    const int t0 = t_begin + (tile * kWaves + w) * 64;
+  // score of token t0 + lane of the current tile
+  auto tile_scores = [&](const u32x4 (&v)[PP]) -> float {
+    if constexpr (kDpp) {
+      constexpr int TPI = 64 / PP;            // tokens per load column
+      float mine = 0.f;
 #pragma unroll
-    for (int m = 0; m < S::M; ++m) {
-      const int p = m * 64 + lane;
-      const int t = t0 + p / S::PP;
-      const int pc = p % S::PP;
-      buf[m] = u32x4{0u, 0u, 0u, 0u};
-      if (t < Tb) {
-        if (!paged) {
-          const u32x4* base = reinterpret_cast<const u32x4*>(
-              Kp + ((int64_t(b) * g.Hkv + j) * g.max_seq + t0) * R);
-          buf[m] = __builtin_nontemporal_load(base + p);
-        } else {
-          const int64_t off = row_off(g, b, j, t, R);
-          if (off >= 0) buf[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kp + off) + pc);
-        }
+      for (int m = 0; m < PP; ++m) {
+        const float s = group_sum<PP>(dot8(qr[0], v[m]));
+        const float x = __shfl(s, (lane % TPI) * PP, 64);
+        if (lane / TPI == m) mine = x;
       }
+      return mine;
+    } else {
+      float* pw = sm.part + w * 64 * PP;
+#pragma unroll
+      for (int m = 0; m < PP; ++m) pw[m * 64 + lane] = dot8(qr[m], v[m]);
+      wave_lds_sync();
+      float s = 0.f;
+#pragma unroll
+      for (int pc = 0; pc < PP; ++pc) s += pw[lane * PP + pc];
+      wave_lds_sync();
+      return s;
     }
   };
 
-  u32x4 cur[S::M];
-  load_tile(0, cur);
-  for (int tile = 0; tile < tiles_per_wave; ++tile) {
-    const int t0 = t_begin + (tile * kWaves + w) * 64;
-    u32x4 nxt[S::M];
-    if (tile + 1 < tiles_per_wave) load_tile(tile + 1, nxt);
+  // Stream the chunk's tiles; the scores are staged in LDS and leave only
+  // after the stream. (A store inside the loop would sit in the in-order
+  // vmcnt queue between tile loads, so every wait for a tile would also wait
+  // for the previous store's write acknowledgement; holding them in
+  // registers would cost occupancy.)
+  float* stage = reinterpret_cast<float*>(sbuf);
+  auto sidx = [](int o) { return FUSED ? (o % TPW) * 257 + o / TPW : o; };
+  auto stage_tile = [&](int tile, const u32x4 (&buf)[PP]) {
+    const int off = (tile * kWaves + w) * 64;
+    const float x = tile_scores(buf);
+    stage[sidx(off + lane)] = token_ok(t_begin + off + lane) ? x : -__builtin_inff();
+  };
+  // kDepth register buffers rotate with no copies between them (a copy of a
+  // buffer whose loads are in flight would wait for them): while one tile's
+  // scores are computed, the loads of the next kDepth - 1 tiles are in flight.
+  static_assert(TPW % kDepth == 0, "tiles are streamed in groups of kDepth");
 #pragma unroll
-    for (int m = 0; m < S::M; ++m) {
-      const float* qs = qr[S::kUniformSlice ? 0 : m];
-      const u32x4 v = cur[m];
-      float a = 0.f;
-      a = __builtin_fmaf(qs[0], bf_lo(v.x), a);
-      a = __builtin_fmaf(qs[1], bf_hi(v.x), a);
-      a = __builtin_fmaf(qs[2], bf_lo(v.y), a);
-      a = __builtin_fmaf(qs[3], bf_hi(v.y), a);
-      a = __builtin_fmaf(qs[4], bf_lo(v.z), a);
-      a = __builtin_fmaf(qs[5], bf_hi(v.z), a);
-      a = __builtin_fmaf(qs[6], bf_lo(v.w), a);
-      a = __builtin_fmaf(qs[7], bf_hi(v.w), a);
-      part[w][m * 64 + lane] = a;
+  for (int u = 1; u < kDepth - 1; ++u) load_tile(u, bufs[u]);
+  for (int tile = 0; tile < TPW; tile += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      // past the chunk on the last group: clamped, unused
+      load_tile(tile + u + kDepth - 1, bufs[(u + kDepth - 1) % kDepth]);
+      stage_tile(tile + u, bufs[u]);
     }
-    wave_lds_sync();
-    float s = 0.f;
-#pragma unroll
-    for (int pc = 0; pc < S::PP; ++pc) s += part[w][lane * S::PP + pc];
-    wave_lds_sync();
-    const int t = t0 + lane;
-    if (t < g.max_seq) srow[t] = (t < Tb) ? s : -__builtin_inff();
-    if (tile + 1 < tiles_per_wave) {
-#pragma unroll
-      for (int m = 0; m < S::M; ++m) cur[m] = nxt[m];
+  }
+  __syncthreads();
+  if (!FUSED || fo.write_scores) {
+    float* dst = srow + t_begin;
+    const int lim = g.max_seq - t_begin;                 // > 0
+    if ((g.max_seq & 3) == 0) {                          // 16-byte aligned row chunk
+      for (int i = tid * 4; i < chunk && i < lim; i += 1024)
+        *reinterpret_cast<f32x4*>(dst + i) =
+            f32x4{stage[sidx(i)], stage[sidx(i + 1)], stage[sidx(i + 2)], stage[sidx(i + 3)]};
+    } else {
+      for (int i = tid; i < chunk && i < lim; i += 256) dst[i] = stage[sidx(i)];
     }
+  }
+  if constexpr (FUSED) {
+    uint32_t key[TPW];
+#pragma unroll
+    for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[e * 257 + tid]);   // token tid*TPW + e
+    __syncthreads();                                     // stage is reused below
+    ChunkSmem<256, TPW>& csm = *reinterpret_cast<ChunkSmem<256, TPW>*>(sbuf);
+    int n = Tb - t_begin;
+    n = n < 0 ? 0 : (n > chunk ? chunk : n);
+    chunk_select<256, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
   }
 }
 
-}  // namespace
-
-hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
-                        float* scores, hipStream_t st) {
-  // Aim for about 8 blocks of 4 waves per CU over the whole grid; at least 4
-  // tiles per wave so the prologue is amortised.
-  const int64_t units = int64_t(g.B) * g.Hkv;
-  const int64_t tiles_total = (g.max_seq + 63) / 64;
-  int64_t want_blocks = 2048;
-  int64_t tpw = (units * tiles_total + want_blocks * kWaves - 1) / (want_blocks * kWaves);
-  if (tpw < 4) tpw = 4;
-  if (tpw > 64) tpw = 64;
-  const int64_t chunk = kWaves * 64 * tpw;
+template <int MODE, bool FUSED>
+hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qabs, int Hmla, const float* P,
+                          const uint16_t* Kp, float* scores, hipStream_t st, FusedOut fo) {
+  const int64_t chunk = kWaves * 64 * (FUSED ? kFusedTiles : kPlainTiles);
   dim3 grid(unsigned((g.max_seq + chunk - 1) / chunk), g.Hkv, g.B);
   switch (g.r) {
-#define JSSA_CASE(R)                                                                             \
-  case R:                                                                                        \
-    hipLaunchKernelGGL(score_kernel<R>, grid, dim3(256), 0, st, g, q, P, Kp, scores, int(tpw)); \
+#define JSSA_CASE(R)                                                                                  \
+  case R:                                                                                             \
+    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(256), 0, st, g, q, qabs, Hmla, P,   \
+                       Kp, scores, fo);                                                               \
     break;
     JSSA_CASE(16) JSSA_CASE(32) JSSA_CASE(48) JSSA_CASE(64) JSSA_CASE(128)
 #undef JSSA_CASE
@@ -165,6 +312,42 @@ hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, cons
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
+                        float* scores, hipStream_t st) {
+  return launch_score_t<kGqa, false>(g, q, nullptr, 0, P, Kp, scores, st, FusedOut{});
+}
+
+hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P, const uint16_t* Kp,
+                            float* scores, hipStream_t st) {
+  GqaDev g{};
+  g.B = m.B;
+  g.Hq = 1;
+  g.Hkv = 1;
+  g.G = 1;
+  g.d = kDc;
+  g.r = m.r;
+  g.max_seq = m.max_seq;
+  g.seq_lens = m.seq_lens;
+  return launch_score_t<kMla, false>(g, nullptr, q_abs, m.H, P, Kp, scores, st, FusedOut{});
+}
+
+int score_topk_segments(int max_seq) {
+  const int chunk = kWaves * 64 * kFusedTiles;
+  return (max_seq + chunk - 1) / chunk;
+}
+
+int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
+
+hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
+                             float* scores, int32_t* idx, CandSegs segs, hipStream_t st) {
+  FusedOut fo{segs, k, scores ? 1 : 0};
+  hipError_t e = launch_score_t<kGqa, true>(g, q, nullptr, 0, P, Kp, scores, st, fo);
+  if (e != hipSuccess) return e;
+  return launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx, st);
 }
 
 }  // namespace jssa

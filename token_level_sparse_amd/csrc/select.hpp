@@ -1,0 +1,235 @@
+// Block-level building blocks of the top-k selection (shared by the
+// standalone top-k and the fused score + select kernel).
+//
+// Keys are order-preserving uint32 images of fp32 scores (score_key). A
+// chunk keeps every token whose key is at or above a threshold at or below
+// the chunk's own k-th largest key (found with at most two LDS histogram
+// levels): any token below it has at least k better tokens in the same chunk
+// and cannot be among the row's k best. The kept tokens and their keys go to
+// the chunk's segment of a workspace; a per-row final pass resolves the exact
+// threshold.
+#pragma once
+#include "common.hpp"
+
+namespace jssa {
+
+constexpr int kSelBins = 2048;
+
+// Segmented candidate lists: segment (row, s) holds cnt[row*nseg+s] entries
+// at key/idx + (row*nseg+s)*cap.
+struct CandSegs {
+  int32_t* cnt;
+  uint32_t* key;
+  int32_t* idx;
+  int nseg, cap;
+};
+
+template <int NT>
+struct ScanSmem {
+  int sc[NT / 64];
+};
+
+// Inclusive scan over the NT threads of the block; total in *tot.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, ScanSmem<NT>& s, int* tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) s.sc[w] = v;
+  __syncthreads();
+  int pre = 0, t = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int x = s.sc[i];
+    pre += i < w ? x : 0;
+    t += x;
+  }
+  __syncthreads();
+  *tot = t;
+  return v + pre;
+}
+
+// Over a histogram of NT*BPT bins, the bin D such that fewer than `need`
+// counted items come before D in scan order and at least `need` come before
+// or in D. desc scans from the top bin down (largest keys first), otherwise
+// from bin 0 up. Result: res[0] = D, res[1] = items before D. Every thread
+// must call it; res is valid after the call.
+template <int NT, int BPT>
+__device__ __forceinline__ void pick_bin(const uint32_t* h, int need, bool desc, ScanSmem<NT>& s,
+                                         int* res) {
+  const int tid = threadIdx.x;
+  int loc[BPT];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int pos = tid * BPT + i;
+    loc[i] = int(h[desc ? (NT * BPT - 1 - pos) : pos]);
+    mine += loc[i];
+  }
+  int tot;
+  int before = block_scan<NT>(mine, s, &tot) - mine;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    if (before < need && before + loc[i] >= need) {
+      const int pos = tid * BPT + i;
+      res[0] = desc ? (NT * BPT - 1 - pos) : pos;
+      res[1] = before;
+    }
+    before += loc[i];
+  }
+  __syncthreads();
+}
+
+template <int NT, int E>
+struct ChunkSmem {
+  uint32_t hist[kSelBins];
+  ScanSmem<NT> scan;
+  uint32_t red[4][NT / 64];
+  int res[2];
+};
+
+// Extra candidates a chunk may keep in its threshold bin before a second,
+// finer histogram level pays for itself (they only cost the final pass work).
+constexpr int kSelSlack = 32;
+
+// Chunk-local selection. Each thread holds E keys; key e of thread tid is
+// token base + tid*E + e, a real token iff it is below `lim`. n = number of
+// real tokens in the block (block-uniform). Writes the kept (key, index)
+// pairs to segment `seg`, in ascending token order, and its count; every
+// real token whose key is at or above the chunk's k-th largest key is kept.
+//
+// The histogram is adaptive: its 2048 bins split [lo, hi] linearly in key
+// space, so one level usually brackets the k-th key to a few candidates. lo
+// is the best of the cheap lower bounds on the chunk's k-th key that apply:
+//  - in a full chunk with k <= NT, the smallest per-thread maximum (each of
+//    the NT threads holds a key at or above it);
+//  - in a full chunk with k <= 2*64*NW, the smallest over the NW waves of the
+//    wave's r-th largest per-thread second maximum, r = ceil(k / (2*NW)):
+//    each wave then has r threads holding two keys at or above it;
+//  - otherwise the smallest real key.
+template <int NT, int E>
+__device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n, int k, ChunkSmem<NT, E>& sm,
+                             CandSegs out, int64_t seg) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  auto real = [&](int e) { return base + tid * E + e < lim; };
+  const bool keep_all = n <= k;
+  const bool full = n == NT * E;
+  uint32_t thr = 0;                          // keep real keys >= thr
+  if (!keep_all) {
+    uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (real(e)) {
+        const uint32_t x = key[e];
+        m2 = x > m1 ? m1 : (x > m2 ? x : m2);
+        m1 = x > m1 ? x : m1;
+        tmin = x < tmin ? x : tmin;
+      }
+    uint32_t bound2 = 0u;                    // the wave's r-th largest m2 (0: not usable)
+    const int r = (k + 2 * NW - 1) / (2 * NW);
+    if (full && r <= 64) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = bound2 | (1u << bit);
+        if (__popcll(__ballot(m2 >= c)) >= r) bound2 = c;
+      }
+    }
+    uint32_t mx = m1, mnmx = m1, mn = tmin;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
+      const uint32_t c = uint32_t(__shfl_xor(int(mnmx), o, 64));
+      const uint32_t d = uint32_t(__shfl_xor(int(mn), o, 64));
+      mx = a > mx ? a : mx;
+      mnmx = c < mnmx ? c : mnmx;
+      mn = d < mn ? d : mn;
+    }
+    if (lane == 0) {
+      sm.red[0][wv] = mx;
+      sm.red[1][wv] = mnmx;
+      sm.red[2][wv] = mn;
+      sm.red[3][wv] = bound2;
+    }
+    for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
+    __syncthreads();
+    uint32_t hi = sm.red[0][0], lo_full = sm.red[1][0], lo_any = sm.red[2][0], lo2 = sm.red[3][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
+      lo_full = sm.red[1][i] < lo_full ? sm.red[1][i] : lo_full;
+      lo_any = sm.red[2][i] < lo_any ? sm.red[2][i] : lo_any;
+      lo2 = sm.red[3][i] < lo2 ? sm.red[3][i] : lo2;
+    }
+    uint32_t lo = lo_any;
+    if (full && k <= NT) lo = lo_full > lo ? lo_full : lo;
+    if (full && r <= 64) lo = lo2 > lo ? lo2 : lo;
+    const uint32_t range = hi - lo;
+    const int sh0 = range < uint32_t(kSelBins) ? 0 : (32 - __builtin_clz(range)) - 11;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (real(e) && key[e] >= lo) atomicAdd(&sm.hist[(key[e] - lo) >> sh0], 1u);
+    __syncthreads();
+    pick_bin<NT, kSelBins / NT>(sm.hist, k, true, sm.scan, sm.res);
+    const uint32_t d0 = uint32_t(sm.res[0]);
+    const int need = k - sm.res[1];
+    const int cnt0 = int(sm.hist[d0]);
+    thr = lo + (d0 << sh0);
+    __syncthreads();
+    if (sh0 > 0 && cnt0 - need > kSelSlack) {          // block-uniform
+      const int sh1 = sh0 > 11 ? sh0 - 11 : 0;
+      for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (real(e) && key[e] >= thr && ((key[e] - lo) >> sh0) == d0)
+          atomicAdd(&sm.hist[(key[e] - thr) >> sh1], 1u);
+      __syncthreads();
+      pick_bin<NT, kSelBins / NT>(sm.hist, need, true, sm.scan, sm.res);
+      thr += uint32_t(sm.res[0]) << sh1;
+    }
+  }
+  // Compaction in token order: a thread's tokens are consecutive, so one
+  // block scan of the per-thread counts places every kept key. The kept
+  // pairs are gathered in LDS (over the histogram, which is no longer read)
+  // and leave as coalesced stores; more than fit go out directly.
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += (real(e) && key[e] >= thr) ? 1 : 0;
+  int tot;
+  int at = block_scan<NT>(mine, sm.scan, &tot) - mine;
+  uint32_t* okey = out.key + seg * out.cap;
+  int32_t* oidx = out.idx + seg * out.cap;
+  constexpr int kStaged = kSelBins / 2;
+  const bool staged = tot <= kStaged;                  // block-uniform
+  uint32_t* skey = sm.hist;
+  int32_t* sidx = reinterpret_cast<int32_t*>(sm.hist + kStaged);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (real(e) && key[e] >= thr) {
+      if (staged) {
+        skey[at] = key[e];
+        sidx[at] = base + tid * E + e;
+      } else {
+        okey[at] = key[e];
+        oidx[at] = base + tid * E + e;
+      }
+      ++at;
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < tot; i += NT) {
+      okey[i] = skey[i];
+      oidx[i] = sidx[i];
+    }
+  }
+  if (tid == 0) out.cnt[seg] = tot;
+}
+
+hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
+                               int32_t* idx, hipStream_t st);
+
+}  // namespace jssa

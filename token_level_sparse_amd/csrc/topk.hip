@@ -4,393 +4,332 @@
 // ai4snews digest, Synopsis). The result is the first min(k, T_b) tokens of
 // the total order (score descending, index ascending), listed ascending.
 //
-// Two-level deterministic selection, no global sorting:
-//  round 0: each block takes one chunk of C scores of one row, keeps them in
-//           registers (256 or 1024 threads x 4..16 each) as order-preserving uint32 keys and radix-selects the
-//           chunk's own top-k (three digit levels, 11+11+10 bits, with LDS
-//           histograms; the last digit level is skipped once the threshold
-//           bin holds exactly the tokens still needed). Ties at the threshold
-//           key are resolved by position, so the chunk's list is the chunk's
-//           prefix of the total order. Survivors are written in position
-//           order (ballot ranks + a prefix over (element, wave) blocks).
-//  merge:   a 1024-thread block concatenates the chunk lists of a row (still
-//           ascending by token) and runs the same selection; a token dropped
-//           inside a chunk has k better tokens in that chunk, so the union of
-//           chunk lists contains the row's top-k. Long rows with small k take
-//           extra merge rounds.
-// Every decision depends only on keys and positions, so results do not
-// depend on scheduling.
+// Radix selection over order-preserving uint32 keys, two kernels, no global
+// atomics (same-address atomics serialise across the XCDs):
+//  chunk   one 256-thread block per 8192 scores of a row (32 per thread)
+//          keeps every token at or above a bound on the chunk's own k-th key
+//          (chunk_select: a token below that key cannot be in the row's
+//          top-k) and writes them to the chunk's workspace segment.
+//  final   one block per row loads the row's candidate list (its segments
+//          in order, which is ascending token order) into registers, finds
+//          the exact threshold key with adaptive LDS histogram levels (each
+//          splits the current key bracket into 4096 linear bins), and writes
+//          the taken tokens in list order: every key above the threshold,
+//          and the lowest-index tokens of a tied threshold key.
+// Every decision depends only on keys and indices, so the result does not
+// depend on scheduling. Rows whose candidate count exceeds the register
+// capacity re-read their segments at each level (slower, same result).
 #include "internal.hpp"
+#include "select.hpp"
 
 namespace jssa {
 namespace {
 
-constexpr int kBins = 2048;
+constexpr int kCT = 256;              // threads of the chunk kernel
+constexpr int kCE = 32;               // scores per thread
+constexpr int kChunk = kCT * kCE;     // 8192
+constexpr int kFinBits = 12;
+constexpr int kFinBins = 1 << kFinBits;
+constexpr int kMaxSeg = 4096;
 
-template <int NT>
-struct SelectSmem {
-  int hist[kBins];
-  int blk[(NT / 64) * 64 + 1];
-  int scan_tot[NT / 64];
-  int sel_bin, sel_gt, total;
-  int offs[1025];
-};
-
-// Inclusive scan over threads (tid order); returns inclusive value, writes
-// the block total to *total (visible after the call).
-template <int NT>
-__device__ int block_incl_scan(int v, SelectSmem<NT>& sm) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) sm.scan_tot[w] = v;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int x = sm.scan_tot[i];
-    pre += (i < w) ? x : 0;
-    tot += x;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) sm.total = tot;
-  return v + pre;
+__device__ __forceinline__ int row_len(int max_seq, const int32_t* seq_lens, int b) {
+  int t = seq_lens ? seq_lens[b] : max_seq;
+  return t < 0 ? 0 : (t > max_seq ? max_seq : t);
 }
 
-// Position-order rank of set flags; element e of thread tid has position
-// e*NT + tid. Returns ranks in rank[], count of set flags via return.
-template <int NT, int E>
-__device__ int ordered_rank(const bool (&flag)[E], int (&rank)[E], SelectSmem<NT>& sm) {
-  constexpr int NW = NT / 64;
-  constexpr int NB = E * NW;                 // (element, wave) blocks in position order
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint64_t lt = lanemask_lt();
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint64_t ball = __ballot(flag[e]);
-    rank[e] = __popcll(ball & lt);
-    if (lane == 0) sm.blk[e * NW + w] = __popcll(ball);
-  }
-  __syncthreads();
-  if (w == 0) {
-    constexpr int PER = (NB + 63) / 64;
-    int loc[PER];
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int ix = lane * PER + i;
-      loc[i] = ix < NB ? sm.blk[ix] : 0;
-      s += loc[i];
-    }
-    int incl = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - s;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int ix = lane * PER + i;
-      if (ix < NB) sm.blk[ix] = run;
-      run += loc[i];
-    }
-    if (lane == 63) sm.blk[NB] = incl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < E; ++e) rank[e] += sm.blk[e * NW + w];
-  const int tot = sm.blk[NB];
-  __syncthreads();
-  return tot;
-}
-
-// Selects `need` = min(k, n) elements; on return take[e] marks them.
-template <int NT, int E>
-__device__ void select_top(const uint32_t (&key)[E], const bool (&valid)[E], int n, int k,
-                           bool (&take)[E], SelectSmem<NT>& sm) {
-  const int tid = threadIdx.x;
-  if (n <= k) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) take[e] = valid[e];
+// ---------------------------------------------------------------------------
+// chunk pass over a score buffer
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
+                                                    const float* __restrict__ scores, int k, CandSegs segs) {
+  __shared__ ChunkSmem<kCT, kCE> sm;
+  const int tid = threadIdx.x, row = blockIdx.y, chunk = blockIdx.x;
+  const int Tb = row_len(max_seq, seq_lens, row / H);
+  const int start = chunk * kChunk;
+  int n = Tb - start;
+  n = n < 0 ? 0 : (n > kChunk ? kChunk : n);
+  const float* src = scores + int64_t(row) * max_seq + start;
+  if (n == 0) {
+    if (tid == 0) segs.cnt[int64_t(row) * segs.nseg + chunk] = 0;
     return;
   }
-  int rem = k;
-  uint32_t pre = 0;
-  int res_shift = 0;
-  constexpr int BPT = kBins / NT;
-  for (int L = 0; L < 3; ++L) {
-    const int shift = L == 0 ? 21 : (L == 1 ? 10 : 0);
-    const int bits = L == 2 ? 10 : 11;
-    const uint32_t mask = (1u << bits) - 1u;
-    for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0;
-    __syncthreads();
+  // Thread i takes the chunk's scores i*kCE .. i*kCE+kCE-1 (consecutive
+  // tokens per thread, as chunk_select expects). All loads are issued
+  // together; positions past the row's end re-read its last score and are
+  // masked out as keys.
+  float v[kCE];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool in = valid[e] && (L == 0 || (key[e] >> (shift + bits)) == pre);
-      if (in) atomicAdd(&sm.hist[(key[e] >> shift) & mask], 1);
-    }
-    __syncthreads();
-    int loc[BPT];
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      loc[i] = sm.hist[tid * BPT + i];
-      mine += loc[i];
-    }
-    const int incl = block_incl_scan<NT>(mine, sm);
-    __syncthreads();
-    int running = sm.total - incl;          // elements in higher bins (higher threads)
-#pragma unroll
-    for (int i = BPT - 1; i >= 0; --i) {
-      if (running < rem && running + loc[i] >= rem) {
-        sm.sel_bin = tid * BPT + i;
-        sm.sel_gt = running;
-      }
-      running += loc[i];
-    }
-    __syncthreads();
-    const int D = sm.sel_bin;
-    rem -= sm.sel_gt;
-    const int cntD = sm.hist[D];
-    pre = (pre << bits) | uint32_t(D);
-    res_shift = shift;
-    __syncthreads();
-    if (cntD == rem) break;
+  for (int e = 0; e < kCE; ++e) {
+    const int p = tid * kCE + e;
+    v[e] = src[p < n ? p : n - 1];
   }
-  bool gt[E], eq[E];
+  uint32_t key[kCE];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t top = key[e] >> res_shift;
-    gt[e] = valid[e] && top > pre;
-    eq[e] = valid[e] && top == pre;
-  }
-  int rk[E];
-  ordered_rank<NT, E>(eq, rk, sm);
-#pragma unroll
-  for (int e = 0; e < E; ++e) take[e] = gt[e] || (eq[e] && rk[e] < rem);
+  for (int e = 0; e < kCE; ++e) key[e] = tid * kCE + e < n ? score_key(v[e]) : 0u;
+  chunk_select<kCT, kCE>(key, start, start + n, n, k, sm, segs, int64_t(row) * segs.nseg + chunk);
 }
 
-struct SegIn {
-  const int32_t* cnt;    // [rows][nseg]
-  const uint32_t* key;   // [rows][nseg][k]
-  const int32_t* idx;
-  int nseg, spc;
-};
-struct SegOut {
-  int32_t* cnt;          // [rows][gridDim.x]
-  uint32_t* key;         // [rows][gridDim.x][k]
-  int32_t* idx;
+// ---------------------------------------------------------------------------
+// final pass
+// ---------------------------------------------------------------------------
+template <int NT>
+struct FinalSmem {
+  uint32_t hist[kFinBins];
+  int offs[kMaxSeg + 1];
+  ScanSmem<NT> scan;
+  uint32_t red[2][NT / 64];
+  int res[2];
 };
 
-template <int NT, int E, bool FROM_SCORES, bool FINAL>
-__global__ __launch_bounds__(NT) void select_kernel(int H, int max_seq, const int32_t* seq_lens,
-                                                    const float* __restrict__ scores, SegIn in,
-                                                    int k, SegOut out, int32_t* __restrict__ idx_out) {
-  __shared__ SelectSmem<NT> sm;
-  const int tid = threadIdx.x;
-  const int row = blockIdx.y, chunk = blockIdx.x;
-  uint32_t key[E];
-  int32_t idx[E];
-  bool valid[E];
+template <int NT, int EF>
+__global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
+                                                   CandSegs segs, int32_t* __restrict__ out) {
+  constexpr int NW = NT / 64;
+  __shared__ FinalSmem<NT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, row = blockIdx.x;
+  const int Tb = row_len(max_seq, seq_lens, row / H);
+  const int need_all = min(k, Tb);
+  const int nseg = segs.nseg;
+
+  // segment offsets: each thread scans SPT consecutive segments
+  constexpr int SPT = kMaxSeg / NT;
+  int c[SPT];
+  int mine = 0;
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) {
+    const int s = tid * SPT + x;
+    c[x] = segs.cnt[int64_t(row) * nseg + (s < nseg ? s : nseg - 1)];
+  }
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) {
+    c[x] = tid * SPT + x < nseg ? c[x] : 0;
+    mine += c[x];
+  }
   int n;
-  if constexpr (FROM_SCORES) {
-    const int b = row / H;
-    int Tb = seq_lens ? seq_lens[b] : max_seq;
-    Tb = Tb < 0 ? 0 : (Tb > max_seq ? max_seq : Tb);
-    const int start = chunk * (NT * E);
-    n = Tb - start;
-    n = n < 0 ? 0 : (n > NT * E ? NT * E : n);
-    const float* src = scores + int64_t(row) * max_seq + start;
+  int run = block_scan<NT>(mine, sm.scan, &n) - mine;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int p = e * NT + tid;
-      valid[e] = p < n;
-      key[e] = valid[e] ? score_key(src[p]) : 0u;
-      idx[e] = start + p;
+  for (int x = 0; x < SPT; ++x) {
+    const int s = tid * SPT + x;
+    if (s < nseg) sm.offs[s] = run;
+    run += c[x];
+  }
+  if (tid == 0) sm.offs[nseg] = n;
+  __syncthreads();
+  // The row's candidate list is its segments one after the other: ascending
+  // token order (segments cover ascending token ranges, each in token order).
+  const uint32_t* gkey = segs.key + int64_t(row) * nseg * segs.cap;
+  const int32_t* gidx = segs.idx + int64_t(row) * nseg * segs.cap;
+  auto locate = [&](int i) -> int {      // segment holding list position i < n
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
     }
-  } else {
-    const int s0 = chunk * in.spc;
-    const int ns = min(in.spc, in.nseg - s0);
-    int c = 0;
-    if (tid < ns) c = in.cnt[int64_t(row) * in.nseg + s0 + tid];
-    const int incl = block_incl_scan<NT>(c, sm);
-    if (tid < ns) sm.offs[tid + 1] = incl;
-    if (tid == 0) sm.offs[0] = 0;
-    __syncthreads();
-    n = sm.offs[ns];
+    return lo;
+  };
+  // list positions i0 .. i0+EF-1 (idx -1 past the end). Addresses first,
+  // then every load at once; positions past the end re-read entry n - 1.
+  auto fetch = [&](int i0, uint32_t (&ck)[EF], int32_t (&ci)[EF]) {
+    int64_t o[EF];
+    int s = locate(i0 < n ? i0 : n - 1);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int p = e * NT + tid;
-      valid[e] = p < n;
-      key[e] = 0u;
-      idx[e] = -1;
-      if (valid[e]) {
-        int lo = 0, hi = ns - 1;         // largest s with offs[s] <= p
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sm.offs[mid] <= p) lo = mid; else hi = mid - 1;
-        }
-        const int64_t at = (int64_t(row) * in.nseg + s0 + lo) * k + (p - sm.offs[lo]);
-        key[e] = in.key[at];
-        idx[e] = in.idx[at];
-      }
+    for (int e = 0; e < EF; ++e) {
+      const int i = i0 + e < n ? i0 + e : n - 1;
+      while (i >= sm.offs[s + 1]) ++s;
+      o[e] = int64_t(s) * segs.cap + (i - sm.offs[s]);
     }
-    __syncthreads();
-  }
-
-  bool take[E];
-  select_top<NT, E>(key, valid, n, k, take, sm);
-  int rk[E];
-  const int cnt = ordered_rank<NT, E>(take, rk, sm);
-  if constexpr (FINAL) {
-    int32_t* dst = idx_out + int64_t(row) * k;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (take[e]) dst[rk[e]] = idx[e];
-    for (int i = cnt + tid; i < k; i += NT) dst[i] = -1;
+    for (int e = 0; e < EF; ++e) {
+      ck[e] = gkey[o[e]];
+      ci[e] = gidx[o[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < EF; ++e)
+      if (i0 + e >= n) ci[e] = -1;
+  };
+
+  // candidates live in registers when they fit (block-uniform choice), each
+  // thread holding EF consecutive list positions
+  constexpr int kRegCap = NT * EF;
+  const bool reg = n <= kRegCap;
+  uint32_t rkey[EF];
+  int32_t ridx[EF];
+  if (reg && n > 0) {
+    fetch(tid * EF, rkey, ridx);
   } else {
-    const int64_t seg = int64_t(row) * gridDim.x + chunk;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (take[e]) {
-        out.key[seg * k + rk[e]] = key[e];
-        out.idx[seg * k + rk[e]] = idx[e];
-      }
-    if (tid == 0) out.cnt[seg] = cnt;
+    for (int e = 0; e < EF; ++e) {
+      rkey[e] = 0u;
+      ridx[e] = -1;
+    }
   }
-}
-
-constexpr int kMergeCap = 16384;   // candidates one merge block holds (1024 x 16)
-
-int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-struct TopkPlan {
-  int C0, n0;                       // round-0 chunk length and chunk count
-  int rounds;                       // merge rounds after round 0 (last one final)
-  int nseg[8], spc[8];              // per merge round: input segments, segments per block
-  size_t seg_bytes[2];              // ping-pong segment buffers
-};
-
-TopkPlan plan(int rows, int max_seq, int k) {
-  TopkPlan p{};
-  int C0 = next_pow2(16 * k);
-  C0 = C0 < 1024 ? 1024 : (C0 > 16384 ? 16384 : C0);
-  if (max_seq <= C0) {
-    C0 = next_pow2(max_seq);
-    if (C0 < 1024) C0 = 1024;
-  }
-  p.C0 = C0;
-  p.n0 = (max_seq + C0 - 1) / C0;
-  auto bytes = [&](int nseg) { return size_t(rows) * nseg * (size_t(k) * 8 + 4) + 256; };
-  p.seg_bytes[0] = p.n0 > 1 ? bytes(p.n0) : 0;
-  p.seg_bytes[1] = 0;
-  int nseg = p.n0;
-  p.rounds = 0;
-  while (nseg > 1) {
-    int spc;
-    if (int64_t(nseg) * k <= kMergeCap && nseg <= 1024) {
-      spc = nseg;
+  auto for_each_key = [&](auto&& fn) {
+    if (reg) {
+#pragma unroll
+      for (int e = 0; e < EF; ++e)
+        if (ridx[e] >= 0) fn(rkey[e]);
     } else {
-      spc = kMergeCap / k;
-      if (spc > 1024) spc = 1024;
+      for (int i = tid; i < n; i += NT) {
+        const int s = locate(i);
+        fn(gkey[int64_t(s) * segs.cap + (i - sm.offs[s])]);
+      }
     }
-    p.nseg[p.rounds] = nseg;
-    p.spc[p.rounds] = spc;
-    const int next = (nseg + spc - 1) / spc;
-    if (next > 1) {
-      const size_t nb = bytes(next);
-      size_t& slot = p.seg_bytes[(p.rounds + 1) & 1];
-      if (nb > slot) slot = nb;
+  };
+
+  // Selection rule: take key > tkey, and the first trem candidates (in list
+  // order, i.e. lowest token indices) whose key equals tkey.
+  uint32_t tkey = 0u;
+  int trem = 0x7fffffff;
+  if (n > need_all && need_all > 0) {
+    uint32_t mx = 0u, mn = 0xffffffffu;
+    for_each_key([&](uint32_t key) {
+      mx = key > mx ? key : mx;
+      mn = key < mn ? key : mn;
+    });
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
+      const uint32_t c = uint32_t(__shfl_xor(int(mn), o, 64));
+      mx = a > mx ? a : mx;
+      mn = c < mn ? c : mn;
     }
-    ++p.rounds;
-    nseg = next;
+    if (lane == 0) {
+      sm.red[0][wv] = mx;
+      sm.red[1][wv] = mn;
+    }
+    __syncthreads();
+    uint64_t hi = 0, lo = 0xffffffffull;
+    for (int i = 0; i < NW; ++i) {
+      hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
+      lo = sm.red[1][i] < lo ? sm.red[1][i] : lo;
+    }
+    // Adaptive levels: kFinBins linear bins over the current bracket
+    // [lo, hi] of keys; the bin holding the rem-th largest key becomes the
+    // next bracket. Every level narrows the bracket by 2^12, so at most three
+    // levels reach a single key value.
+    int rem = need_all;
+    for (;;) {
+      const uint64_t range = hi - lo;
+      const int sh = range < uint64_t(kFinBins) ? 0 : (64 - __builtin_clzll(range)) - kFinBits;
+      for (int i = tid; i < kFinBins; i += NT) sm.hist[i] = 0u;
+      __syncthreads();
+      for_each_key([&](uint32_t key) {
+        if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> sh], 1u);
+      });
+      __syncthreads();
+      pick_bin<NT, kFinBins / NT>(sm.hist, rem, true, sm.scan, sm.res);
+      const uint64_t D = uint64_t(sm.res[0]);
+      rem -= sm.res[1];
+      const int cnt = int(sm.hist[D]);
+      __syncthreads();
+      const uint64_t blo = lo + (D << sh);
+      if (cnt == rem) {                  // the whole bin is taken
+        tkey = uint32_t(blo);
+        break;
+      }
+      if (sh == 0) {                     // a single key value, tied
+        tkey = uint32_t(blo);
+        trem = rem;
+        break;
+      }
+      const uint64_t bhi = blo + (uint64_t(1) << sh) - 1;
+      lo = blo;
+      hi = bhi < hi ? bhi : hi;
+    }
   }
-  return p;
+
+  // Output in list order, which is ascending token order: two block scans
+  // per page of candidates, one ranking the tied candidates and one placing
+  // the taken ones.
+  int32_t* dst = out + int64_t(row) * k;
+  int tie_base = 0, out_base = 0;
+  auto emit = [&](const uint32_t (&ck)[EF], const int32_t (&ci)[EF]) {
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < EF; ++e) nt += (ci[e] >= 0 && ck[e] == tkey) ? 1 : 0;
+    int tt;
+    int tr = block_scan<NT>(nt, sm.scan, &tt) - nt + tie_base;
+    bool take[EF];
+    int ns = 0;
+#pragma unroll
+    for (int e = 0; e < EF; ++e) {
+      bool t = false;
+      if (ci[e] >= 0) {
+        if (ck[e] > tkey) t = true;
+        else if (ck[e] == tkey) t = tr++ < trem;
+      }
+      take[e] = t;
+      ns += t ? 1 : 0;
+    }
+    int st;
+    int at = block_scan<NT>(ns, sm.scan, &st) - ns + out_base;
+#pragma unroll
+    for (int e = 0; e < EF; ++e)
+      if (take[e]) dst[at++] = ci[e];
+    tie_base += tt;
+    out_base += st;
+  };
+  if (n == 0) {
+  } else if (reg) {
+    emit(rkey, ridx);
+  } else {
+    for (int p0 = 0; p0 < n; p0 += kRegCap) {
+      uint32_t ck[EF];
+      int32_t ci[EF];
+      fetch(p0 + tid * EF, ck, ci);
+      emit(ck, ci);
+    }
+  }
+  for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
 }
 
-template <int NT, int E>
-void launch_round0(dim3 grid, bool final_, int H, int max_seq, const int32_t* seq_lens,
-                   const float* scores, int k, SegOut out, int32_t* idx, hipStream_t st) {
-  SegIn none{nullptr, nullptr, nullptr, 0, 0};
-  if (final_)
-    hipLaunchKernelGGL((select_kernel<NT, E, true, true>), grid, dim3(NT), 0, st, H, max_seq,
-                       seq_lens, scores, none, k, out, idx);
-  else
-    hipLaunchKernelGGL((select_kernel<NT, E, true, false>), grid, dim3(NT), 0, st, H, max_seq,
-                       seq_lens, scores, none, k, out, idx);
-}
-
-template <int E>
-void launch_merge(dim3 grid, bool final_, int H, SegIn in, int k, SegOut out, int32_t* idx,
-                  hipStream_t st) {
-  if (final_)
-    hipLaunchKernelGGL((select_kernel<1024, E, false, true>), grid, dim3(1024), 0, st, H, 0,
-                       nullptr, nullptr, in, k, out, idx);
-  else
-    hipLaunchKernelGGL((select_kernel<1024, E, false, false>), grid, dim3(1024), 0, st, H, 0,
-                       nullptr, nullptr, in, k, out, idx);
-}
-
-SegOut seg_view(void* base, int rows, int nseg, int k) {
-  char* p = static_cast<char*>(base);
-  SegOut s;
-  s.key = reinterpret_cast<uint32_t*>(p);
-  s.idx = reinterpret_cast<int32_t*>(p + size_t(rows) * nseg * k * 4);
-  s.cnt = reinterpret_cast<int32_t*>(p + size_t(rows) * nseg * k * 8);
-  return s;
-}
+int chunks_of(int max_seq) { return (max_seq + kChunk - 1) / kChunk; }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int rows, int max_seq, int k) {
-  TopkPlan p = plan(rows, max_seq, k);
-  return p.seg_bytes[0] + p.seg_bytes[1];
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total) {
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* q = p ? p + off : nullptr; off += align256(bytes); return q; };
+  CandSegs w;
+  w.cnt = reinterpret_cast<int32_t*>(take(size_t(rows) * nseg * 4));
+  w.key = reinterpret_cast<uint32_t*>(take(size_t(rows) * nseg * cap * 4));
+  w.idx = reinterpret_cast<int32_t*>(take(size_t(rows) * nseg * cap * 4));
+  w.nseg = nseg;
+  w.cap = cap;
+  if (total) *total = off;
+  return w;
 }
 
-hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
-                       int k, int32_t* idx, void* ws, hipStream_t st) {
+hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
+                               int32_t* idx, hipStream_t st) {
+  if (segs.nseg > kMaxSeg) return hipErrorInvalidValue;
+  // candidates per row ~ nseg * (k + a few): 8192 held in registers for
+  // small budgets, 32768 for large ones; more are read from memory
+  if (k <= 512)
+    hipLaunchKernelGGL((final_kernel<1024, 8>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
+  else
+    hipLaunchKernelGGL((final_kernel<1024, 32>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
+  return hipGetLastError();
+}
+
+size_t topk_workspace_bytes(int rows, int max_seq, int) {
+  size_t total = 0;
+  carve_segs(nullptr, rows, chunks_of(max_seq), kChunk, &total);
+  return total;
+}
+
+hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+                       int32_t* idx, void* wsp, hipStream_t st) {
   const int rows = B * H;
-  TopkPlan p = plan(rows, max_seq, k);
-  void* buf[2] = {ws, static_cast<char*>(ws) + p.seg_bytes[0]};
-  const bool single = p.n0 == 1;
-  SegOut out0 = single ? SegOut{nullptr, nullptr, nullptr} : seg_view(buf[0], rows, p.n0, k);
-  dim3 g0(p.n0, rows);
-  switch (p.C0) {
-    case 1024: launch_round0<256, 4>(g0, single, H, max_seq, seq_lens, scores, k, out0, idx, st); break;
-    case 2048: launch_round0<256, 8>(g0, single, H, max_seq, seq_lens, scores, k, out0, idx, st); break;
-    case 4096: launch_round0<256, 16>(g0, single, H, max_seq, seq_lens, scores, k, out0, idx, st); break;
-    case 8192: launch_round0<1024, 8>(g0, single, H, max_seq, seq_lens, scores, k, out0, idx, st); break;
-    case 16384: launch_round0<1024, 16>(g0, single, H, max_seq, seq_lens, scores, k, out0, idx, st); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  SegOut cur = out0;
-  for (int r = 0; r < p.rounds; ++r) {
-    const int nseg = p.nseg[r], spc = p.spc[r];
-    const int next = (nseg + spc - 1) / spc;
-    const bool fin = next == 1;
-    SegIn in{cur.cnt, cur.key, cur.idx, nseg, spc};
-    SegOut o = fin ? SegOut{nullptr, nullptr, nullptr} : seg_view(buf[(r + 1) & 1], rows, next, k);
-    const int64_t cap = int64_t(spc) * k;
-    if (cap <= 8192)
-      launch_merge<8>(dim3(next, rows), fin, H, in, k, o, idx, st);
-    else
-      launch_merge<16>(dim3(next, rows), fin, H, in, k, o, idx, st);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    cur = o;
-  }
-  return hipSuccess;
+  const int nchunks = chunks_of(max_seq);
+  CandSegs segs = carve_segs(wsp, rows, nchunks, kChunk, nullptr);
+  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, st);
 }
 
 }  // namespace jssa

@@ -56,20 +56,40 @@ class GqaCache:
         jssa.jssa_project_keys(self.desc, self.K, self.P, self.Kp, stream)
 
 
-class SparseStep:
-    """score -> top-k -> gather-free indexed split-K attention -> combine."""
+def default_splits(k: int) -> int:
+    """Splits of the selected set: one 8-wave block covers 256 rows."""
+    return max(1, min(64, k // 256))
 
-    def __init__(self, c: GqaCache, k: int, S: int = 8):
+
+class SparseStep:
+    """score -> top-k -> gather-free indexed split-K attention -> combine.
+
+    fused=True runs score and top-k as one pass (jssa_score_topk, which does
+    not write the fp32 score row); fused=False runs jssa_score then jssa_topk.
+    Both give the same indices. With S = 1 the single partial is already the
+    normalised output and its log-sum-exp (the combine of one split is the
+    identity), so out/lse are views of the partial buffers and no combine is
+    launched."""
+
+    def __init__(self, c: GqaCache, k: int, S: int | None = None, fused: bool = False,
+                 keep_scores: bool = True):
         dev = c.q.device
-        self.c, self.k, self.S = c, k, S
-        self.scores = torch.empty((c.B, c.Hkv, c.T), dtype=torch.float32, device=dev)
+        S = default_splits(k) if S is None else S
+        self.c, self.k, self.S, self.fused = c, k, S, fused
+        self.scores = torch.empty((c.B, c.Hkv, c.T), dtype=torch.float32, device=dev) \
+            if (keep_scores or not fused) else None
         nbytes = jssa.jssa_topk_workspace_size(c.B, c.Hkv, c.T, k)
-        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        nf = jssa.jssa_score_topk_workspace_size(c.desc, k)
+        self.ws = torch.empty(max(nbytes, nf, 16), dtype=torch.uint8, device=dev)
         self.idx = torch.empty((c.B, c.Hkv, k), dtype=torch.int32, device=dev)
         self.part_o = torch.empty((c.B, c.Hq, S, c.d), dtype=torch.float32, device=dev)
         self.part_lse = torch.empty((c.B, c.Hq, S), dtype=torch.float32, device=dev)
-        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+        if S == 1:
+            self.out = self.part_o.view(c.B, c.Hq, c.d)
+            self.lse = self.part_lse.view(c.B, c.Hq)
+        else:
+            self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
 
     def score(self, stream=None):
         c = self.c
@@ -86,13 +106,21 @@ class SparseStep:
 
     def combine(self, stream=None):
         c = self.c
-        jssa.jssa_combine(c.B, c.Hq, self.S, c.d, self.part_o, self.part_lse, self.out, 0, self.lse, stream)
+        if self.S > 1:
+            jssa.jssa_combine(c.B, c.Hq, self.S, c.d, self.part_o, self.part_lse, self.out, 0, self.lse, stream)
+
+    def score_topk(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topk(c.desc, c.q, c.P, c.Kp, self.k, self.scores, self.idx, self.ws, None, stream)
+
+    def stages(self):
+        """The launches of one step, in order."""
+        head = [self.score_topk] if self.fused else [self.score, self.topk]
+        return head + [self.attend] + ([self.combine] if self.S > 1 else [])
 
     def run(self, stream=None):
-        self.score(stream)
-        self.topk(stream)
-        self.attend(stream)
-        self.combine(stream)
+        for f in self.stages():
+            f(stream)
 
 
 class DenseStep:
