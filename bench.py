@@ -21,6 +21,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -81,6 +82,20 @@ def time_loop(fns, steps, warmup, torch, stream, graph=None):
     stage_us = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]) * 1e3)
                 for i in range(len(fns))]
     return total, stage_us
+
+
+def time_launches(fn, n, torch, stream):
+    """Mean microseconds per launch of `fn` over n back-to-back launches,
+    from one HIP event pair on the launch stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
 def cpu_oracle_gqa(inp, k, units):
@@ -145,7 +160,9 @@ def main():
     total2, st2_us = time_loop(sp2.stages(), args.steps, args.warmup, torch, stream)
     print(f"[bench] sparse (separate score, top-k) {total2 / args.steps * 1e3:.3f} ms/step", file=sys.stderr,
           flush=True)
-    comb_us = st_us[2] if S > 1 else 0.0
+    # fused stages: [chunk pass (score stream + chunk select), final select, indexed attention, (combine)]
+    chunk_us, final_us, attn_us = st_us[0], st_us[1], st_us[2]
+    comb_us = st_us[3] if S > 1 else 0.0
 
     kp_bytes = tot_tok * 2 * r
     q_bytes = B * Hq * d * 2
@@ -161,12 +178,26 @@ def main():
         return {"us": round(us, 2), "bytes": int(nbytes), "GB_s": round(gbs, 1) if gbs else None,
                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 3) if gbs else None}
 
-    stages = {"score_topk_fused": stage(st_us[0], fused_bytes), "indexed": stage(st_us[1], idx_bytes),
+    cand_bytes = B * Hkv * -(-T // 8192) * 8 * (k + 1)     # about k kept (key, index) pairs per 8192-token chunk
+    stages = {"score_topk_chunks": stage(chunk_us, fused_bytes),
+              "select_final": stage(final_us, cand_bytes + B * Hkv * k * 4),
+              "indexed": stage(attn_us, idx_bytes),
               "combine": stage(comb_us, comb_bytes)}
     stages_split = {"score": stage(st2_us[0], score_bytes), "topk": stage(st2_us[1], topk_bytes),
                     "indexed": stage(st2_us[2], idx_bytes), "ms_per_step": round(total2 / args.steps * 1e3, 4),
                     "steps_per_s": round(args.steps / total2, 2)}
-    achieved = fused_bytes / (st_us[0] * 1e-6) / 1e9
+    # the dominant kernel's launch duration: back-to-back launches of the chunk pass
+    kern_us = time_launches(sp.score_chunks, args.steps, torch, stream)
+    achieved = fused_bytes / (kern_us * 1e-6) / 1e9
+    # measured HBM bytes per launch of the chunk-pass kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    # calibrated on a plain copy), reported only while the kernel sources match the measurement
+    traffic = None
+    if cfg.name == "gqa_128k_b16" and args.k is None:
+        from token_level_sparse_amd.prof_summary import read_traffic
+        t = read_traffic(os.path.join(ROOT, "profiles", "score_kernel_fused_gqa_128k_b16_hbm_traffic.txt"),
+                         f"score_kernel<{r},0,true>")
+        if t is not None:
+            traffic = t["bytes"]
 
     result = {
         "metric": "sparse decode-attn steps/s at 128K,B=16 (Hkv=8,d=128,k=256); HBM GB/s vs peak",
@@ -179,7 +210,10 @@ def main():
         "context_tokens_scanned_per_s": round(tot_tok * steps_s, 1),
         "roofline": {"bound": "hbm", "kernel": "score_kernel (fused score + top-k chunk stage)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(fused_bytes), "duration_us": round(kern_us, 2),
+                     "duration_source": f"HIP event pair around {args.steps} back-to-back jssa_score_topk_chunks "
+                                        "launches on their stream"},
         "stages": stages,
         "separate_entry_points": stages_split,
     }
@@ -197,7 +231,7 @@ def main():
         ga = pipeline.GatherStep(sp, S=max(S, 4))
         gsteps = max(3, args.steps // 5)
         gtotal, gst_us = time_loop([sp.score_topk, ga.gather, ga.attend, ga.combine], gsteps, 2, torch, stream)
-        sparse_attn_us = st_us[1] + comb_us
+        sparse_attn_us = attn_us + comb_us
         gather_attn_us = gst_us[1] + gst_us[2] + gst_us[3]
         dense_attn_us = dst_us[0] + dst_us[1]
         result["gather_ablation"] = {
@@ -235,7 +269,8 @@ def main():
 
 def bench_mla(args, cfg, torch, pipeline, synth, stream):
     inp = synth.make_mla(cfg)
-    st = pipeline.MlaStep(inp, S=args.splits)
+    S = args.splits or 8
+    st = pipeline.MlaStep(inp, S=S)
     st.project()
     torch.cuda.synchronize()
     from token_level_sparse_amd import jssa
@@ -268,7 +303,7 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
            "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(total / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16-mfma/f32", "data": "synthetic",
-           "config": {"workload": c.name, "B": c.B, "H": c.H, "T": c.T, "r": c.r, "k": c.k, "S": args.splits},
+           "config": {"workload": c.name, "B": c.B, "H": c.H, "T": c.T, "r": c.r, "k": c.k, "S": S},
            "stages_us": {n: round(u, 2) for n, u in zip(names, us)},
            "indexed_mfma_TFLOP_s": round(core_flops / (us[3] * 1e-6) / 1e12, 2)}
     print(json.dumps(res), flush=True)

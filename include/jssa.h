@@ -149,9 +149,11 @@ JSSA_API jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int3
 /*
  * Fused score -> top-k: the subspace score stream of jssa_score and the
  * selection of jssa_topk in one pass over the projected key cache. Each
- * 8192-token chunk keeps its scores in registers and emits only the tokens
+ * 8192-token chunk keeps its scores on chip (LDS) and emits only the tokens
  * that can still be among its row's k best, so the fp32 score row is never
- * written and read back (unless `scores` is given).
+ * written and read back (unless `scores` is given). Two launches: the chunk
+ * pass (jssa_score_topk_chunks) and the per-row final pass
+ * (jssa_score_topk_final); jssa_score_topk issues both.
  *  q, P, Kp  as jssa_score; k as jssa_topk (1 <= k <= min(4096, max_seq))
  *  scores    device fp32 [B,Hkv,max_seq] or NULL: if given, written exactly
  *            as by jssa_score
@@ -163,6 +165,22 @@ JSSA_API jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, i
 JSSA_API jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
                                      int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/*
+ * The two halves of jssa_score_topk, for callers that schedule or time them
+ * separately. jssa_score_topk_chunks streams Kp once and leaves, per 8192-
+ * token chunk of each (sequence, KV head) row, that chunk's candidates in
+ * `ws`; jssa_score_topk_final reads them back and writes idx. Between the two
+ * calls `ws` must not be modified, and both calls must get the same desc
+ * (shapes and seq_lens contents) and k; the pair then writes exactly what
+ * jssa_score_topk writes. Arguments, errors and workspace size as
+ * jssa_score_topk.
+ */
+JSSA_API jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, const float* P,
+                                            const void* Kp, int32_t k, float* scores, void* ws,
+                                            size_t ws_bytes, void* stream);
+JSSA_API jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const void* ws, size_t ws_bytes,
+                                           int32_t* idx, void* stream);
 
 /*
  * Gather-free indexed attention, split-K partials (digest Interpretation:

@@ -248,10 +248,16 @@ def test_score_topk_fused_equals_split(J, PL, case):
     b.score_topk()
     nb = PL.SparseStep(c, k=k, fused=True, keep_scores=False)
     nb.score_topk()
+    # the two halves of the fused call, issued separately
+    h = PL.SparseStep(c, k=k, fused=True, keep_scores=True)
+    h.score_chunks()
+    h.select_final()
     torch.cuda.synchronize()
     np.testing.assert_array_equal(_np(b.idx), _np(a.idx))
     np.testing.assert_array_equal(_np(nb.idx), _np(a.idx))
+    np.testing.assert_array_equal(_np(h.idx), _np(a.idx))
     np.testing.assert_array_equal(_np(b.scores), _np(a.scores))
+    np.testing.assert_array_equal(_np(h.scores), _np(a.scores))
 
 
 @pytest.mark.parametrize("k", [256, 1024, 2048])

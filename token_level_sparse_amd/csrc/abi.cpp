@@ -215,6 +215,36 @@ jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const floa
                     __func__);
 }
 
+jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                   int32_t k, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(ws);
+  REQUIRE_ALIGNED_OPT(scores);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
+                                         jssa::score_topk_segment_cap(), nullptr);
+  return hip_status(jssa::launch_score_chunks(to_dev(desc), static_cast<const uint16_t*>(q), P,
+                                              static_cast<const uint16_t*>(Kp), k, scores, segs, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const void* ws, size_t ws_bytes,
+                                  int32_t* idx, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(idx); REQUIRE_PTR(ws);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv,
+                                         jssa::score_topk_segments(desc->max_seq),
+                                         jssa::score_topk_segment_cap(), nullptr);
+  return hip_status(jssa::launch_select_final(desc->B * desc->Hkv, desc->Hkv, desc->max_seq, desc->seq_lens, k,
+                                              segs, idx, S(stream)),
+                    __func__);
+}
+
 jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* q, const void* K, const void* V,
                                 const int32_t* idx, int32_t k, int32_t S_, float scale, float* part_o,
                                 float* part_lse, void* stream) {

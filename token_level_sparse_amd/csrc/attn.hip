@@ -85,22 +85,38 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
 
   constexpr int RB = STEPS * 4;                 // rows per wave batch
   for (int base = r0 + w * RB; base < r1; base += NW * RB) {
+    // Every load of the batch is issued without a data-dependent branch (a
+    // load under one would be waited for before the next is issued): the
+    // batch's indices, then (paged) their page ids, then the K and V rows.
+    // Rows past the split or with no valid token read a valid row (token 0,
+    // or page 0) and are masked out.
     u32x4 kr[STEPS], vr[STEPS];
     bool ok[STEPS];
+    int tt[STEPS];
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int rr = base + st * 4 + gi;
-      int t = -1;
-      if (rr < r1) t = DENSE ? rr : irow[rr];
-      int64_t off = -1;
-      if (t >= 0 && t < Tb) off = row_off(g, b, j, t, kD);
-      ok[st] = off >= 0;
-      kr[st] = u32x4{0u, 0u, 0u, 0u};
-      vr[st] = u32x4{0u, 0u, 0u, 0u};
-      if (ok[st]) {
-        kr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K + off) + sub);
-        vr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off) + sub);
+      tt[st] = DENSE ? rr : irow[rr < r1 ? rr : r1 - 1];
+    }
+    int pg[STEPS];                              // page ids (paged cache), also loaded together
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int rr = base + st * 4 + gi;
+      ok[st] = rr < r1 && tt[st] >= 0 && tt[st] < Tb;
+      tt[st] = ok[st] ? tt[st] : 0;
+      pg[st] = g.page_size ? g.page_table[int64_t(b) * g.max_pages + (tt[st] >> 4)] : 0;
+    }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      int64_t off;
+      if (g.page_size) {
+        ok[st] = ok[st] && pg[st] >= 0 && pg[st] < g.num_pages;
+        off = ((int64_t(ok[st] ? pg[st] : 0) * g.Hkv + j) * kPage + (tt[st] & (kPage - 1))) * kD;
+      } else {
+        off = ((int64_t(b) * g.Hkv + j) * g.max_seq + tt[st]) * kD;
       }
+      kr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K + off) + sub);
+      vr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off) + sub);
     }
     float lg[STEPS][GT];
 #pragma unroll

@@ -24,6 +24,8 @@ int score_topk_segments(int max_seq);
 int score_topk_segment_cap();
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                              float* scores, int32_t* idx, CandSegs segs, hipStream_t st);
+hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
+                               float* scores, CandSegs segs, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
 

@@ -342,10 +342,15 @@ int score_topk_segments(int max_seq) {
 
 int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
 
+hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
+                               float* scores, CandSegs segs, hipStream_t st) {
+  FusedOut fo{segs, k, scores ? 1 : 0};
+  return launch_score_t<kGqa, true>(g, q, nullptr, 0, P, Kp, scores, st, fo);
+}
+
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                              float* scores, int32_t* idx, CandSegs segs, hipStream_t st) {
-  FusedOut fo{segs, k, scores ? 1 : 0};
-  hipError_t e = launch_score_t<kGqa, true>(g, q, nullptr, 0, P, Kp, scores, st, fo);
+  hipError_t e = launch_score_chunks(g, q, P, Kp, k, scores, segs, st);
   if (e != hipSuccess) return e;
   return launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx, st);
 }

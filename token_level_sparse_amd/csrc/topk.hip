@@ -129,15 +129,18 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   };
   // list positions i0 .. i0+EF-1 (idx -1 past the end). Addresses first,
   // then every load at once; positions past the end re-read entry n - 1.
-  auto fetch = [&](int i0, uint32_t (&ck)[EF], int32_t (&ci)[EF]) {
-    int64_t o[EF];
+  auto offsets = [&](int i0, int32_t (&o)[EF]) {   // row-relative offsets of positions i0..
     int s = locate(i0 < n ? i0 : n - 1);
 #pragma unroll
     for (int e = 0; e < EF; ++e) {
       const int i = i0 + e < n ? i0 + e : n - 1;
       while (i >= sm.offs[s + 1]) ++s;
-      o[e] = int64_t(s) * segs.cap + (i - sm.offs[s]);
+      o[e] = s * segs.cap + (i - sm.offs[s]);
     }
+  };
+  auto fetch = [&](int i0, uint32_t (&ck)[EF], int32_t (&ci)[EF]) {
+    int32_t o[EF];
+    offsets(i0, o);
 #pragma unroll
     for (int e = 0; e < EF; ++e) {
       ck[e] = gkey[o[e]];
@@ -168,10 +171,16 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
 #pragma unroll
       for (int e = 0; e < EF; ++e)
         if (ridx[e] >= 0) fn(rkey[e]);
-    } else {
-      for (int i = tid; i < n; i += NT) {
-        const int s = locate(i);
-        fn(gkey[int64_t(s) * segs.cap + (i - sm.offs[s])]);
+    } else {                             // page by page, as held in registers
+      for (int p0 = 0; p0 < n; p0 += kRegCap) {
+        const int i0 = p0 + tid * EF;
+        int32_t o[EF];
+        offsets(i0, o);
+#pragma unroll
+        for (int e = 0; e < EF; ++e) rkey[e] = gkey[o[e]];   // the register list is free here
+#pragma unroll
+        for (int e = 0; e < EF; ++e)
+          if (i0 + e < n) fn(rkey[e]);
       }
     }
   };
@@ -249,8 +258,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     for (int e = 0; e < EF; ++e) nt += (ci[e] >= 0 && ck[e] == tkey) ? 1 : 0;
     int tt;
     int tr = block_scan<NT>(nt, sm.scan, &tt) - nt + tie_base;
-    bool take[EF];
-    int ns = 0;
+    static_assert(EF <= 32, "taken flags are one bit each");
+    uint32_t take = 0u;
 #pragma unroll
     for (int e = 0; e < EF; ++e) {
       bool t = false;
@@ -258,14 +267,14 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
         if (ck[e] > tkey) t = true;
         else if (ck[e] == tkey) t = tr++ < trem;
       }
-      take[e] = t;
-      ns += t ? 1 : 0;
+      take |= t ? 1u << e : 0u;
     }
+    const int ns = __popc(take);
     int st;
     int at = block_scan<NT>(ns, sm.scan, &st) - ns + out_base;
 #pragma unroll
     for (int e = 0; e < EF; ++e)
-      if (take[e]) dst[at++] = ci[e];
+      if (take >> e & 1u) dst[at++] = ci[e];
     tie_base += tt;
     out_base += st;
   };
@@ -274,10 +283,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     emit(rkey, ridx);
   } else {
     for (int p0 = 0; p0 < n; p0 += kRegCap) {
-      uint32_t ck[EF];
-      int32_t ci[EF];
-      fetch(p0 + tid * EF, ck, ci);
-      emit(ck, ci);
+      fetch(p0 + tid * EF, rkey, ridx);
+      emit(rkey, ridx);
     }
   }
   for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
@@ -307,11 +314,12 @@ hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_
                                int32_t* idx, hipStream_t st) {
   if (segs.nseg > kMaxSeg) return hipErrorInvalidValue;
   // candidates per row ~ nseg * (k + a few): 8192 held in registers for
-  // small budgets, 32768 for large ones; more are read from memory
+  // small budgets (1024 threads x 8), 16384 for large ones (1024 x 16); rows
+  // with more are streamed from memory page by page
   if (k <= 512)
     hipLaunchKernelGGL((final_kernel<1024, 8>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
   else
-    hipLaunchKernelGGL((final_kernel<1024, 32>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
+    hipLaunchKernelGGL((final_kernel<1024, 16>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
   return hipGetLastError();
 }
 

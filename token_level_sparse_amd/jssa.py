@@ -27,7 +27,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = ra
 
 ENTRY_POINTS = (
     "jssa_append_kv", "jssa_project_keys", "jssa_score", "jssa_topk_workspace_size", "jssa_topk",
-    "jssa_score_topk_workspace_size", "jssa_score_topk",
+    "jssa_score_topk_workspace_size", "jssa_score_topk", "jssa_score_topk_chunks", "jssa_score_topk_final",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_status_string", "jssa_last_error", "jssa_version",
@@ -64,6 +64,8 @@ _SIGS = {
     "jssa_topk": [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
     "jssa_score_topk_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
     "jssa_score_topk": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
+    "jssa_score_topk_chunks": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
+    "jssa_score_topk_final": [_P(GqaDesc), _i32, _vp, _sz, _vp, _vp],
     "jssa_indexed_decode": [_P(GqaDesc), _vp, _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_combine": [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp],
     "jssa_dense_decode": [_P(GqaDesc), _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp],
@@ -171,6 +173,20 @@ def jssa_score_topk(desc, q, P, Kp, k, scores, idx, ws, ws_bytes=None, stream=No
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.jssa_score_topk(ctypes.byref(desc), _p(q), _p(P), _p(Kp), k, _p(scores), _p(idx), _p(ws),
                                 ws_bytes, _s(stream)), "jssa_score_topk")
+
+
+def jssa_score_topk_chunks(desc, q, P, Kp, k, scores, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topk_chunks(ctypes.byref(desc), _p(q), _p(P), _p(Kp), k, _p(scores), _p(ws), ws_bytes,
+                                       _s(stream)), "jssa_score_topk_chunks")
+
+
+def jssa_score_topk_final(desc, k, ws, idx, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topk_final(ctypes.byref(desc), k, _p(ws), ws_bytes, _p(idx), _s(stream)),
+           "jssa_score_topk_final")
 
 
 def jssa_indexed_decode(desc, q, K, V, idx, k, S, scale, part_o, part_lse, stream=None):

@@ -113,9 +113,17 @@ class SparseStep:
         c = self.c
         jssa.jssa_score_topk(c.desc, c.q, c.P, c.Kp, self.k, self.scores, self.idx, self.ws, None, stream)
 
+    def score_chunks(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topk_chunks(c.desc, c.q, c.P, c.Kp, self.k, self.scores, self.ws, None, stream)
+
+    def select_final(self, stream=None):
+        jssa.jssa_score_topk_final(self.c.desc, self.k, self.ws, self.idx, None, stream)
+
     def stages(self):
-        """The launches of one step, in order."""
-        head = [self.score_topk] if self.fused else [self.score, self.topk]
+        """The launches of one step, in order (the fused score + top-k as its
+        two halves, the same launches jssa_score_topk issues)."""
+        head = [self.score_chunks, self.select_final] if self.fused else [self.score, self.topk]
         return head + [self.attend] + ([self.combine] if self.S > 1 else [])
 
     def run(self, stream=None):
