@@ -38,6 +38,7 @@ def kernel_source_hash(sources=SCORE_KERNEL_SOURCES) -> str:
 
 def _short(name: str) -> str:
     name = name.replace("jssa::(anonymous namespace)::", "")
+    name = name[5:] if name.startswith("void ") else name
     name = name.split("(")[0] if "(" in name else name
     return name.replace(" ", "")
 
