@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--dense-splits", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
+    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     return ap.parse_args()
 
 
@@ -151,7 +152,11 @@ def main():
     # the headline step: fused score -> top-k, then gather-free indexed attention
     sp = pipeline.SparseStep(c, k=k, S=args.splits or None, fused=True, keep_scores=False)
     S = sp.S
-    total, st_us = time_loop(sp.stages(), args.steps, args.warmup, torch, stream)
+    # timed steps: eager launches (measured faster here than replaying a HIP graph of the same
+    # launches, which --graph times instead; the eager time is then reported beside it)
+    graph = sp.capture() if args.graph else None
+    total, st_us = time_loop(sp.stages(), args.steps, args.warmup, torch, stream, graph=graph)
+    total_eager = time_loop(sp.stages(), args.steps, args.warmup, torch, stream)[0] if graph is not None else total
     ms = total / args.steps * 1e3
     steps_s = args.steps / total
     print(f"[bench] sparse (fused score+top-k) {ms:.3f} ms/step", file=sys.stderr, flush=True)
@@ -192,7 +197,7 @@ def main():
     # measured HBM bytes per launch of the chunk-pass kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE,
     # calibrated on a plain copy), reported only while the kernel sources match the measurement
     traffic = None
-    if cfg.name == "gqa_128k_b16" and args.k is None:
+    if cfg.name == "gqa_128k_b16" and not args.k:
         from token_level_sparse_amd.prof_summary import read_traffic
         t = read_traffic(os.path.join(ROOT, "profiles", "score_kernel_fused_gqa_128k_b16_hbm_traffic.txt"),
                          f"score_kernel<{r},0,true>")
@@ -206,6 +211,8 @@ def main():
         "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "T": T, "r": r, "k": k,
                    "S": S, "paged": bool(cfg.paged)},
+        "timed_as": "HIP graph replay of the step" if graph is not None else "eager launches",
+        "eager_ms_per_step": round(total_eager / args.steps * 1e3, 4),
         "tokens_per_s": round(B * steps_s, 1),
         "context_tokens_scanned_per_s": round(tot_tok * steps_s, 1),
         "roofline": {"bound": "hbm", "kernel": "score_kernel (fused score + top-k chunk stage)",
@@ -277,10 +284,10 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
     c = cfg
 
     def absorb():
-        jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.q_abs, stream)
+        jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.P, st.q_abs, st.q_sel, stream)
 
     def score():
-        jssa.jssa_mla_score(st.desc, st.q_abs, st.P, st.Kp, st.scores, stream)
+        jssa.jssa_mla_score(st.desc, st.q_sel, st.Kp, st.scores, stream)
 
     def topk():
         jssa.jssa_topk(c.B, 1, c.T, st.seq_lens, st.scores, st.k, st.idx, st.ws, None, stream)

@@ -254,19 +254,26 @@ JSSA_API jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const vo
                                     void* Kp_lat, void* stream);
 
 /*
- * Absorbed query: q_abs[b,h] = [W_uk[h]^T q_nope[b,h] ; q_rope[b,h]] (fp32).
+ * Absorbed query and selection query (digest Perspective: selection over the
+ * shared latent cache).
+ *  q_abs[b,h] = [W_uk[h]^T q_nope[b,h] ; q_rope[b,h]] (fp32): the attention
+ *               query of head h against latent rows;
+ *  q_sel[b]   = P^T sum_h q_abs[b,h] (fp32, fixed summation order): the one
+ *               subspace query of sequence b that jssa_mla_score streams with.
  *  q_nope device bf16 [B,H,d_nope], q_rope device bf16 [B,H,d_rope],
- *  W_uk device bf16 [H,d_nope,d_latent], q_abs device fp32 [B,H,d_c] (written)
+ *  W_uk device bf16 [H,d_nope,d_latent], P device fp32 [d_c,r],
+ *  q_abs device fp32 [B,H,d_c] (written), q_sel device fp32 [B,r] (written)
  */
 JSSA_API jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
-                              const void* W_uk, float* q_abs, void* stream);
+                              const void* W_uk, const float* P, float* q_abs, float* q_sel, void* stream);
 
 /*
- * MLA selection scores: scores[b,t] = (P^T sum_h q_abs[b,h]) . Kp_lat[b,t]
- * for t < T_b, -inf beyond. scores device fp32 [B,max_seq].
+ * MLA selection scores: scores[b,t] = q_sel[b] . Kp_lat[b,t] for t < T_b,
+ * -inf beyond. q_sel device fp32 [B,r] (from jssa_mla_absorb_q), scores
+ * device fp32 [B,max_seq].
  */
-JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_abs, const float* P,
-                           const void* Kp_lat, float* scores, void* stream);
+JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat,
+                           float* scores, void* stream);
 
 /*
  * MLA attention over the selected latent rows, read in place (bf16 MFMA):

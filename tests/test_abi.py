@@ -101,7 +101,8 @@ def test_combine_and_mla_validation(J):
     m_ok = J.mla_desc(4, 128, 64, 131072)
     m_badh = J.mla_desc(4, 100, 64, 131072)
     m_badr = J.mla_desc(4, 128, 48, 131072)
-    assert _status(J.jssa_mla_score, m_badh, A, A, A, A) == J.ERR_UNSUPPORTED
-    assert _status(J.jssa_mla_score, m_badr, A, A, A, A) == J.ERR_UNSUPPORTED
+    assert _status(J.jssa_mla_score, m_badh, A, A, A) == J.ERR_UNSUPPORTED
+    assert _status(J.jssa_mla_score, m_badr, A, A, A) == J.ERR_UNSUPPORTED
+    assert _status(J.jssa_mla_absorb_q, m_ok, A, A, A, None, A, A) == J.ERR_NULL
     assert _status(J.jssa_mla_indexed_decode, m_ok, A, A, A, 2048, 0, 0.1, A, A) == J.ERR_SHAPE
     assert _status(J.jssa_mla_up_v, m_ok, A, None, A) == J.ERR_NULL

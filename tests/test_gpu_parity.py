@@ -357,6 +357,32 @@ def test_combine_parity(J, S, dv):
     np.testing.assert_array_equal(ob, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(o)))
 
 
+def test_graph_replay_matches_eager(J, PL):
+    """The fused step captured in a HIP graph gives the eager result on every
+    replay, with eager work and synchronisation between replays and the
+    outputs cleared before each one."""
+    inp = synth.make_gqa(replace(synth.LLAMA8B_32K, B=2, T=20000, seed=91))
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=256, S=2, fused=True, keep_scores=False)
+    st.run()
+    torch.cuda.synchronize()
+    ref_idx, ref_out, ref_lse = st.idx.clone(), st.out.clone(), st.lse.clone()
+    st.capture()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        st.idx.fill_(-7)
+        st.out.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        junk.mul_(1.0001).add_(0.5)                 # unrelated eager work between replays
+        torch.cuda.synchronize()
+        st.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.idx, ref_idx), rep
+        assert torch.equal(st.out, ref_out), rep
+        assert torch.equal(st.lse, ref_lse), rep
+
+
 def test_deterministic_repeat(J, PL):
     inp = synth.make_gqa(synth.LLAMA8B_32K)
     c = PL.GqaCache(inp)
@@ -408,8 +434,12 @@ def test_mla_parity(J, PL):
         np.testing.assert_array_equal(Kp[b], O.project_keys(inp.latent[b], inp.P))
     st.run()
     torch.cuda.synchronize()
-    qa = O.mla_absorbed_query(inp.q_nope[0], inp.q_rope[0], inp.W_uk)
-    U.check_close(_np(st.q_abs)[0], qa, tol=1e-4, what="absorbed query")
+    qsel = _np(st.q_sel)
+    for b in range(cfg.B):
+        qa = O.mla_absorbed_query(inp.q_nope[b], inp.q_rope[b], inp.W_uk)
+        U.check_close(_np(st.q_abs)[b], qa, tol=1e-4, what="absorbed query")
+        # the selection query is the projected head sum of the absorbed query
+        U.check_close(qsel[b], inp.P.astype(np.float64).T @ qa.sum(0), tol=1e-4, what="selection query")
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
     for b in range(cfg.B):
         s = O.mla_scores(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.P, O.project_keys(inp.latent[b], inp.P))

@@ -194,8 +194,9 @@ jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k,
   if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
   if (k < 1 || k > 4096 || k > desc->max_seq)
     return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
-  jssa::carve_segs(nullptr, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                   jssa::score_topk_segment_cap(), bytes);
+  const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
+  jssa::carve_segs(nullptr, rows, nseg, jssa::score_topk_segment_cap(), bytes);
+  *bytes += jssa::merge_workspace_bytes(rows, nseg, k);
   return JSSA_OK;
 }
 
@@ -207,11 +208,12 @@ jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const floa
   REQUIRE_ALIGNED_OPT(scores);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  size_t main_bytes = 0;
   jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), nullptr);
+                                         jssa::score_topk_segment_cap(), &main_bytes);
   return hip_status(jssa::launch_score_topk(to_dev(desc), static_cast<const uint16_t*>(q), P,
                                             static_cast<const uint16_t*>(Kp), k, scores, idx, segs,
-                                            S(stream)),
+                                            static_cast<char*>(ws) + main_bytes, S(stream)),
                     __func__);
 }
 
@@ -237,11 +239,13 @@ jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const vo
   REQUIRE_PTR(idx); REQUIRE_PTR(ws);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  size_t main_bytes = 0;
   jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv,
                                          jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), nullptr);
+                                         jssa::score_topk_segment_cap(), &main_bytes);
   return hip_status(jssa::launch_select_final(desc->B * desc->Hkv, desc->Hkv, desc->max_seq, desc->seq_lens, k,
-                                              segs, idx, S(stream)),
+                                              segs, idx, static_cast<char*>(const_cast<void*>(ws)) + main_bytes,
+                                              S(stream)),
                     __func__);
 }
 
@@ -314,22 +318,23 @@ jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const void* laten
 }
 
 jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
-                              const void* W_uk, float* q_abs, void* stream) {
+                              const void* W_uk, const float* P, float* q_abs, float* q_sel, void* stream) {
   if (jssa_status s = check_mla(__func__, desc)) return s;
-  REQUIRE_PTR(q_nope); REQUIRE_PTR(q_rope); REQUIRE_PTR(W_uk); REQUIRE_PTR(q_abs);
+  REQUIRE_PTR(q_nope); REQUIRE_PTR(q_rope); REQUIRE_PTR(W_uk); REQUIRE_PTR(P); REQUIRE_PTR(q_abs);
+  REQUIRE_PTR(q_sel);
   return hip_status(jssa::launch_mla_absorb(to_mla(desc), static_cast<const uint16_t*>(q_nope),
                                             static_cast<const uint16_t*>(q_rope),
-                                            static_cast<const uint16_t*>(W_uk), q_abs, S(stream)),
+                                            static_cast<const uint16_t*>(W_uk), P, q_abs, q_sel, S(stream)),
                     __func__);
 }
 
-jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_abs, const float* P,
-                           const void* Kp_lat, float* scores, void* stream) {
+jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat, float* scores,
+                           void* stream) {
   if (jssa_status s = check_mla(__func__, desc)) return s;
-  REQUIRE_PTR(q_abs); REQUIRE_PTR(P); REQUIRE_PTR(Kp_lat); REQUIRE_PTR(scores);
+  REQUIRE_PTR(q_sel); REQUIRE_PTR(Kp_lat); REQUIRE_PTR(scores);
   REQUIRE_ALIGNED_OPT(desc->seq_lens);
-  return hip_status(jssa::launch_mla_score(to_mla(desc), q_abs, P,
-                                           static_cast<const uint16_t*>(Kp_lat), scores, S(stream)),
+  return hip_status(jssa::launch_mla_score(to_mla(desc), q_sel, static_cast<const uint16_t*>(Kp_lat), scores,
+                                           S(stream)),
                     __func__);
 }
 

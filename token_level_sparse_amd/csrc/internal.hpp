@@ -23,7 +23,7 @@ CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total);
 int score_topk_segments(int max_seq);
 int score_topk_segment_cap();
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
-                             float* scores, int32_t* idx, CandSegs segs, hipStream_t st);
+                             float* scores, int32_t* idx, CandSegs segs, void* merge_ws, hipStream_t st);
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
@@ -46,9 +46,9 @@ struct MlaDev {
 hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const float* P,
                               uint16_t* Kp, hipStream_t st);
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
-                             const uint16_t* W_uk, float* q_abs, hipStream_t st);
-hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P,
-                            const uint16_t* Kp, float* scores, hipStream_t st);
+                             const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st);
+hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
+                            hipStream_t st);
 hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_t* latent,
                               const int32_t* idx, int k, int S, float scale, float* part_o,
                               float* part_lse, hipStream_t st);

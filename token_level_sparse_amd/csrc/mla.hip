@@ -70,8 +70,11 @@ __global__ __launch_bounds__(256) void mla_project_kernel(MlaDev m, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Absorbed query. Block per head h: q_abs[b,h,c] = sum_i q_nope[b,h,i] W_uk[h,i,c]
-// for c < 512 (fp32), then the rope part copied.
+// Absorbed query: q_abs[b,h,c] = sum_i q_nope[b,h,i] W_uk[h,i,c] for c < 512
+// (fp32), then the rope part copied. Block (h, column quarter): 128 columns
+// as 64 bf16 pairs; wave w sums rows i = 32w .. 32w+31, whose 32 pair loads
+// per lane are all issued before any is used; the four partial sums meet in
+// LDS. Each W_uk element is read once and serves every sequence.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_t* __restrict__ qn,
                                                          const uint16_t* __restrict__ qr,
@@ -79,8 +82,13 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_
                                                          float* __restrict__ qa) {
   constexpr int BT = 8;                  // sequences per pass
   __shared__ float qs[BT][128];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* W = Wuk + int64_t(h) * 128 * kDl;
+  __shared__ float part[4][BT][128];
+  const int h = blockIdx.x, cq = blockIdx.y, tid = threadIdx.x;
+  const int cp = tid & 63, w = tid >> 6;
+  const uint16_t* W = Wuk + (int64_t(h) * 128 + w * 32) * kDl + cq * 128 + 2 * cp;
+  uint32_t wr[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) wr[i] = *reinterpret_cast<const uint32_t*>(W + int64_t(i) * kDl);
   for (int b0 = 0; b0 < m.B; b0 += BT) {
     const int nb = min(BT, m.B - b0);
     __syncthreads();
@@ -92,21 +100,87 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_
     float acc[BT][2];
 #pragma unroll
     for (int bb = 0; bb < BT; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
-    for (int i = 0; i < 128; ++i) {
-      const uint32_t w2 = reinterpret_cast<const uint32_t*>(W + int64_t(i) * kDl)[tid];
-      const float w0 = bf_lo(w2), w1 = bf_hi(w2);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float w0 = bf_lo(wr[i]), w1 = bf_hi(wr[i]);
 #pragma unroll
       for (int bb = 0; bb < BT; ++bb) {
-        acc[bb][0] = __builtin_fmaf(qs[bb][i], w0, acc[bb][0]);
-        acc[bb][1] = __builtin_fmaf(qs[bb][i], w1, acc[bb][1]);
+        const float q = qs[bb][w * 32 + i];
+        acc[bb][0] = __builtin_fmaf(q, w0, acc[bb][0]);
+        acc[bb][1] = __builtin_fmaf(q, w1, acc[bb][1]);
       }
     }
-    for (int bb = 0; bb < nb; ++bb) {
-      float* dst = qa + (int64_t(b0 + bb) * m.H + h) * kDc;
-      dst[2 * tid] = acc[bb][0];
-      dst[2 * tid + 1] = acc[bb][1];
-      if (tid < 64) dst[kDl + tid] = bf(qr[(int64_t(b0 + bb) * m.H + h) * 64 + tid]);
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb) {
+      part[w][bb][2 * cp] = acc[bb][0];
+      part[w][bb][2 * cp + 1] = acc[bb][1];
     }
+    __syncthreads();
+    for (int e = tid; e < nb * 128; e += 256) {
+      const int bb = e / 128, c = e % 128;
+      const float v = ((part[0][bb][c] + part[1][bb][c]) + part[2][bb][c]) + part[3][bb][c];
+      qa[(int64_t(b0 + bb) * m.H + h) * kDc + cq * 128 + c] = v;
+    }
+    if (cq == 0)
+      for (int e = tid; e < nb * 64; e += 256) {
+        const int bb = e / 64, j = e % 64;
+        qa[(int64_t(b0 + bb) * m.H + h) * kDc + kDl + j] = bf(qr[(int64_t(b0 + bb) * m.H + h) * 64 + j]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection query of a sequence: q_sel[b,:] = P^T (sum_h q_abs[b,h,:]), the
+// subspace query the latent score stream dots with every projected row
+// (fixed summation order: deterministic). Block per sequence, 1024 threads:
+// the head sum is split over 4 head quarters (unrolled loads) and merged in
+// LDS, then R columns x 1024/R row slices of P.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(1024) void mla_selq_kernel(MlaDev m, const float* __restrict__ qa,
+                                                        const float* __restrict__ P,
+                                                        float* __restrict__ qsel) {
+  __shared__ float part[4][kDc];
+  __shared__ float qbar[kDc];
+  __shared__ float ppart[1024];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int hq = tid >> 8, ct = tid & 255;              // head quarter, column thread
+  const int hpq = (m.H + 3) / 4;
+  const int h0 = hq * hpq, h1 = min(m.H, h0 + hpq);
+  for (int c = ct; c < kDc; c += 256) {
+    const float* qc = qa + int64_t(b) * m.H * kDc + c;
+    float s = 0.f;
+    int h = h0;
+    for (; h + 8 <= h1; h += 8) {
+      float a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = qc[int64_t(h + u) * kDc];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += a[u];
+    }
+    for (; h < h1; ++h) s += qc[int64_t(h) * kDc];
+    part[hq][c] = s;
+  }
+  __syncthreads();
+  for (int c = tid; c < kDc; c += 1024) qbar[c] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+  __syncthreads();
+  constexpr int NS = 1024 / R;                          // row slices
+  constexpr int NI = (kDc + NS - 1) / NS;
+  const int c = tid % R, sl = tid / R;
+  float s = 0.f;
+#pragma unroll 8
+  for (int ii = 0; ii < NI; ++ii) {
+    const int i = sl + ii * NS;
+    const int ic = i < kDc ? i : kDc - 1;
+    const float pv = P[ic * R + c];
+    s = __builtin_fmaf(pv, i < kDc ? qbar[ic] : 0.f, s);
+  }
+  ppart[sl * R + c] = s;
+  __syncthreads();
+  if (tid < R) {
+    float t = 0.f;
+    for (int x = 0; x < NS; ++x) t += ppart[x * R + tid];
+    qsel[int64_t(b) * R + tid] = t;
   }
 }
 
@@ -139,8 +213,10 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
   const int r0 = min(s * cs, k), r1 = min(r0 + cs, k);
   const int h = ht * 16 + n;                       // this lane's head in the QK B operand
 
-  // B operand of QK^T (Q^T): lane holds Q[head n][dims kb*32 + 8g .. +8], as hi and lo bf16.
-  bf16x8 qhi[18], qlo[18];
+  // B operand of QK^T (Q^T): lane holds Q[head n][dims kb*32 + 8g .. +8], as hi and lo bf16;
+  // the lo parts wait in LDS (registers go to the accumulators and loads in flight).
+  __shared__ bf16x8 qlo_s[18][64];
+  bf16x8 qhi[18];
   {
     const float* qrow = qa + (int64_t(b) * m.H + h) * kDc;
     const float qs = scale * kLog2e;
@@ -149,13 +225,15 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
       const f32x4v* p = reinterpret_cast<const f32x4v*>(qrow + kb * 32 + 8 * g);
       const f32x4v a = p[0], c = p[1];
       float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      bf16x8 lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = x[e] * qs;
         const __bf16 hi = __bf16(v);
         qhi[kb][e] = hi;
-        qlo[kb][e] = __bf16(v - float(hi));
+        lo[e] = __bf16(v - float(hi));
       }
+      qlo_s[kb][lane] = lo;
     }
   }
 
@@ -165,37 +243,62 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
   float mrun = -__builtin_inff();    // running max for head n (log2 domain), uniform over g
   float lrun = 0.f;                  // partial sum over this lane group's tokens
 
+  // Loads are pipelined by half tiles: while one half's 18 pieces per lane
+  // are multiplied, the other half's (or the next tile's first half's) are
+  // in flight. No load sits under a data-dependent branch: rows past the
+  // split or with an invalid index read token 0 of the sequence (finite
+  // data) and are masked out of the softmax.
   const int32_t* irow = idx + int64_t(b) * k;
+  const uint16_t* lrow = lat + int64_t(b) * m.max_seq * kDc;
+  auto tile_index = [&](int base) -> int {           // lane l < 32: index of slot base + l
+    const int sl = base + (lane & 31);
+    return irow[sl < r1 ? sl : r1 - 1];
+  };
+  auto row_of = [&](int base, int tv, int hf, bool& ok) -> const uint16_t* {
+    const int tl = 8 * (n >> 2) + 4 * hf + (n & 3);  // token of MFMA row n in half hf
+    const int t = __shfl(tv, tl, 64);
+    ok = base + tl < r1 && t >= 0 && t < Tb;
+    return lrow + int64_t(ok ? t : 0) * kDc + 8 * g;
+  };
+  auto load_half = [&](const uint16_t* crow, u32x4 (&A)[18]) {
+#pragma unroll
+    for (int kb = 0; kb < 18; ++kb) A[kb] = *reinterpret_cast<const u32x4*>(crow + kb * 32);
+  };
+  // QK^T of one half tile; stashes the value part transposed in LDS
+  auto qk_half = [&](const u32x4 (&A)[18], int hf) -> f32x4v {
+    const int tl = 8 * (n >> 2) + 4 * hf + (n & 3);
+    f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 18; ++kb) {
+      if (kb < 16) {
+        const u32x4 raw = A[kb];
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Vt[(kb * 32 + 8 * g + e) * kVtStride + tl] = e16[e];
+      }
+      const bf16x8 a = __builtin_bit_cast(bf16x8, A[kb]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kb], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo_s[kb][lane], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+
+  u32x4 A0[18], A1[18];
+  int tv = r0 < r1 ? tile_index(r0) : 0;
+  bool ok0 = false, ok1 = false;
+  if (r0 < r1) load_half(row_of(r0, tv, 0, ok0), A0);
   for (int base = r0; base < r1; base += 32) {
+    load_half(row_of(base, tv, 1, ok1), A1);
+    const int nb = base + 32 < r1 ? base + 32 : base;    // next tile (or this one again: unused)
+    const int tvn = tile_index(nb);
     f32x4v St[2];
     bool okrow[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // token handled by MFMA row n of half hf
-      const int tok_local = 8 * (n >> 2) + 4 * hf + (n & 3);
-      const int slot = base + tok_local;
-      int t = -1;
-      if (slot < r1) t = irow[slot];
-      const bool ok = t >= 0 && t < Tb;
-      okrow[hf] = ok;
-      const uint16_t* crow = lat + (int64_t(b) * m.max_seq + (ok ? t : 0)) * kDc;
-      f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 18; ++kb) {
-        u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-        if (ok) raw = *reinterpret_cast<const u32x4*>(crow + kb * 32 + 8 * g);
-        if (kb < 16) {
-          // transposed stash of the value part: Vt[dim][token]
-          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&raw);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) Vt[(kb * 32 + 8 * g + e) * kVtStride + tok_local] = e16[e];
-        }
-        const bf16x8 a = __builtin_bit_cast(bf16x8, raw);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[kb], acc, 0, 0, 0);
-      }
-      St[hf] = acc;
-    }
+    St[0] = qk_half(A0, 0);
+    okrow[0] = ok0;
+    load_half(row_of(nb, tvn, 0, ok0), A0);            // next tile's first half
+    St[1] = qk_half(A1, 1);
+    okrow[1] = ok1;
+    tv = tvn;
     // St[hf][i] = logit (log2 domain) of head n, token 8g + 4hf + i.
     // validity of those tokens: rows 4g+i of each half belong to lanes n' = 4g+i
     float lg[8];
@@ -269,30 +372,47 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
 }
 
 // ---------------------------------------------------------------------------
-// out[b,h,v] = sum_c W_uv[h,v,c] o_lat[b,h,c]. Block per head, wave per 32 v.
+// out[b,h,v] = sum_c W_uv[h,v,c] o_lat[b,h,c]. Block (h, quarter of v): each
+// wave takes 8 rows of W_uv[h] (lane l holds dims 8l..8l+7 of each, all 8
+// rows loaded before any is used) and applies them to every sequence, four
+// at a time, reducing each dot over the 64 lanes.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_up_v_kernel(MlaDev m, const float* __restrict__ olat,
                                                        const uint16_t* __restrict__ Wuv,
                                                        float* __restrict__ out) {
-  const int h = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint16_t* W = Wuv + int64_t(h) * 128 * kDl;
-  for (int b = 0; b < m.B; ++b) {
-    const f32x4v* op = reinterpret_cast<const f32x4v*>(olat + (int64_t(b) * m.H + h) * kDl + lane * 8);
-    const f32x4v o0 = op[0], o1 = op[1];
-    for (int v = w * 32; v < w * 32 + 32; ++v) {
-      const u32x4 wr = reinterpret_cast<const u32x4*>(W + int64_t(v) * kDl)[lane];
-      float a = 0.f;
-      a = __builtin_fmaf(o0.x, bf_lo(wr.x), a);
-      a = __builtin_fmaf(o0.y, bf_hi(wr.x), a);
-      a = __builtin_fmaf(o0.z, bf_lo(wr.y), a);
-      a = __builtin_fmaf(o0.w, bf_hi(wr.y), a);
-      a = __builtin_fmaf(o1.x, bf_lo(wr.z), a);
-      a = __builtin_fmaf(o1.y, bf_hi(wr.z), a);
-      a = __builtin_fmaf(o1.z, bf_lo(wr.w), a);
-      a = __builtin_fmaf(o1.w, bf_hi(wr.w), a);
-      a = row16_sum(a);
-      a = xor_sum(xor_sum(a, 16), 32);
-      if (lane == 0) out[(int64_t(b) * m.H + h) * 128 + v] = a;
+  const int h = blockIdx.x, vq = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int v0 = vq * 32 + w * 8;
+  const uint16_t* W = Wuv + (int64_t(h) * 128 + v0) * kDl;
+  u32x4 wr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wr[j] = reinterpret_cast<const u32x4*>(W + int64_t(j) * kDl)[lane];
+  for (int b0 = 0; b0 < m.B; b0 += 4) {
+    f32x4v o[4][2];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int b = b0 + bb < m.B ? b0 + bb : m.B - 1;
+      const f32x4v* op = reinterpret_cast<const f32x4v*>(olat + (int64_t(b) * m.H + h) * kDl + lane * 8);
+      o[bb][0] = op[0];
+      o[bb][1] = op[1];
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 r = wr[j];
+        float a = 0.f;
+        a = __builtin_fmaf(o[bb][0].x, bf_lo(r.x), a);
+        a = __builtin_fmaf(o[bb][0].y, bf_hi(r.x), a);
+        a = __builtin_fmaf(o[bb][0].z, bf_lo(r.y), a);
+        a = __builtin_fmaf(o[bb][0].w, bf_hi(r.y), a);
+        a = __builtin_fmaf(o[bb][1].x, bf_lo(r.z), a);
+        a = __builtin_fmaf(o[bb][1].y, bf_hi(r.z), a);
+        a = __builtin_fmaf(o[bb][1].z, bf_lo(r.w), a);
+        a = __builtin_fmaf(o[bb][1].w, bf_hi(r.w), a);
+        a = row16_sum(a);
+        a = xor_sum(xor_sum(a, 16), 32);
+        if (lane == 0 && b0 + bb < m.B) out[(int64_t(b0 + bb) * m.H + h) * 128 + v0 + j] = a;
+      }
     }
   }
 }
@@ -312,8 +432,16 @@ hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const flo
 }
 
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
-                             const uint16_t* W_uk, float* q_abs, hipStream_t st) {
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(m.H), dim3(256), 0, st, m, q_nope, q_rope, W_uk, q_abs);
+                             const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st) {
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(m.H, kDl / 128), dim3(256), 0, st, m, q_nope, q_rope, W_uk, q_abs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (m.r) {
+    case 16: hipLaunchKernelGGL(mla_selq_kernel<16>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
+    case 32: hipLaunchKernelGGL(mla_selq_kernel<32>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
+    case 64: hipLaunchKernelGGL(mla_selq_kernel<64>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -328,7 +456,7 @@ hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_
 
 hipError_t launch_mla_up_v(const MlaDev& m, const float* o_lat, const uint16_t* W_uv, float* out,
                            hipStream_t st) {
-  hipLaunchKernelGGL(mla_up_v_kernel, dim3(m.H), dim3(256), 0, st, m, o_lat, W_uv, out);
+  hipLaunchKernelGGL(mla_up_v_kernel, dim3(m.H, 128 / 32), dim3(256), 0, st, m, o_lat, W_uv, out);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // head's score sums its G query heads' scores; by linearity that is one dot of
 // qp = P_j^T (sum_h q_h) with the stored projected key, so the stream reads
 // 2r bytes per token and does r FMAs. For the MLA latent cache the same
-// stream runs with qp = P^T (sum over all heads of the absorbed query).
+// stream runs with the selection query qp = P^T (sum over all heads of the
+// absorbed query), which the absorb step computes once per sequence.
 //
 // HBM-bound streaming kernel. Each wave reads a tile of 64 tokens' projected
 // keys as 64*r/8 contiguous 16-byte pieces, one coalesced dwordx4 load per
@@ -35,6 +36,7 @@ constexpr int kDc = 576;
 constexpr int kWaves = 4;
 constexpr int kFusedTiles = 32;            // tiles of 64 tokens per wave: 8192-token chunks
 constexpr int kPlainTiles = 16;            // 4096-token chunks for the score-only stream
+constexpr int kMlaTiles = 4;               // 1024-token chunks: the latent cache has only B rows
 constexpr int kDepth = 2;                  // tiles per wave whose loads are in flight together
 
 // sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16)
@@ -62,6 +64,10 @@ __device__ __forceinline__ float dot8(const float (&q)[8], u32x4 v) {
 
 enum Mode { kGqa = 0, kMla = 1 };
 
+constexpr int tiles_per_wave(int mode, bool fused) {
+  return fused ? kFusedTiles : (mode == kMla ? kMlaTiles : kPlainTiles);
+}
+
 struct FusedOut {
   CandSegs segs;
   int k;
@@ -70,7 +76,7 @@ struct FusedOut {
 
 template <int R>
 struct ScoreSmem {
-  float qbar[kDc];
+  float qbar[kD];
   float qpart[256];
   float qp[R];
   float part[(R / 8) & (R / 8 - 1) ? kWaves * 8 * R : 1];   // LDS reduction (r = 48 only)
@@ -78,15 +84,14 @@ struct ScoreSmem {
 
 template <int R, int MODE, bool FUSED>
 __global__ __launch_bounds__(256) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
-                                                    const float* __restrict__ qabs, int Hmla,
+                                                    const float* __restrict__ qsel,
                                                     const float* __restrict__ P,
                                                     const uint16_t* __restrict__ Kp,
                                                     float* __restrict__ scores, FusedOut fo) {
   constexpr int PP = R / 8;                   // lanes (16-byte pieces) per token
   constexpr bool kDpp = (PP & (PP - 1)) == 0; // power of two -> DPP groups
-  constexpr int DIN = MODE == kGqa ? kD : kDc;
   constexpr int NSL = kDpp ? 1 : PP;          // qp slices held per lane
-  constexpr int TPW = FUSED ? kFusedTiles : kPlainTiles;
+  constexpr int TPW = tiles_per_wave(MODE, FUSED);
   __shared__ ScoreSmem<R> sm;
   // Fused: token o of the chunk is staged at (o % TPW) * (256 + 1) + o / TPW,
   // so thread i later reads its TPW consecutive tokens o = i*TPW + e at
@@ -171,45 +176,34 @@ __global__ __launch_bounds__(256) void score_kernel(GqaDev g, const uint16_t* __
       for (; h < g.G; ++h) s += bf(qg[h * kD]);
       sm.qbar[tid] = s;
     }
-  } else {
-    for (int c = tid; c < kDc; c += 256) {
-      const float* qc = qabs + int64_t(b) * Hmla * kDc + c;
-      float s = 0.f;
-      int h = 0;
-      for (; h + 8 <= Hmla; h += 8) {
-        float a[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) a[u] = qc[int64_t(h + u) * kDc];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s += a[u];
-      }
-      for (; h < Hmla; ++h) s += qc[int64_t(h) * kDc];
-      sm.qbar[c] = s;
-    }
-  }
-  __syncthreads();
-  {
-    constexpr int NS = 256 / R;
-    constexpr int NI = (DIN + NS - 1) / NS;
-    const int c = tid % R, sl = tid / R;
-    if (sl < NS) {
-      const float* Pj = P + int64_t(j) * DIN * R;
-      float s = 0.f;
-#pragma unroll 16
-      for (int ii = 0; ii < NI; ++ii) {
-        const int i = sl + ii * NS;
-        const int ic = i < DIN ? i : DIN - 1;      // unconditional load, zero weight past DIN
-        const float pv = Pj[ic * R + c];
-        s = __builtin_fmaf(pv, i < DIN ? sm.qbar[ic] : 0.f, s);
-      }
-      sm.qpart[sl * R + c] = s;
-    }
     __syncthreads();
-    if (tid < R) {
-      float s = 0.f;
-      for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
-      sm.qp[tid] = s;
+    {
+      constexpr int NS = 256 / R;
+      constexpr int NI = (kD + NS - 1) / NS;
+      const int c = tid % R, sl = tid / R;
+      if (sl < NS) {
+        const float* Pj = P + int64_t(j) * kD * R;
+        float s = 0.f;
+#pragma unroll 16
+        for (int ii = 0; ii < NI; ++ii) {
+          const int i = sl + ii * NS;
+          const int ic = i < kD ? i : kD - 1;      // unconditional load, zero weight past d
+          const float pv = Pj[ic * R + c];
+          s = __builtin_fmaf(pv, i < kD ? sm.qbar[ic] : 0.f, s);
+        }
+        sm.qpart[sl * R + c] = s;
+      }
+      __syncthreads();
+      if (tid < R) {
+        float s = 0.f;
+        for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
+        sm.qp[tid] = s;
+      }
+      __syncthreads();
     }
+  } else {
+    // MLA: the selection query qp = P^T sum_h q_abs[b,h] comes precomputed
+    if (tid < R) sm.qp[tid] = qsel[int64_t(b) * R + tid];
     __syncthreads();
   }
   float qr[NSL][8];
@@ -296,15 +290,15 @@ __global__ __launch_bounds__(256) void score_kernel(GqaDev g, const uint16_t* __
 }
 
 template <int MODE, bool FUSED>
-hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qabs, int Hmla, const float* P,
+hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qsel, const float* P,
                           const uint16_t* Kp, float* scores, hipStream_t st, FusedOut fo) {
-  const int64_t chunk = kWaves * 64 * (FUSED ? kFusedTiles : kPlainTiles);
+  const int64_t chunk = kWaves * 64 * tiles_per_wave(MODE, FUSED);
   dim3 grid(unsigned((g.max_seq + chunk - 1) / chunk), g.Hkv, g.B);
   switch (g.r) {
 #define JSSA_CASE(R)                                                                                  \
   case R:                                                                                             \
-    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(256), 0, st, g, q, qabs, Hmla, P,   \
-                       Kp, scores, fo);                                                               \
+    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(256), 0, st, g, q, qsel, P, Kp,     \
+                       scores, fo);                                                                   \
     break;
     JSSA_CASE(16) JSSA_CASE(32) JSSA_CASE(48) JSSA_CASE(64) JSSA_CASE(128)
 #undef JSSA_CASE
@@ -318,11 +312,11 @@ hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qabs,
 
 hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
                         float* scores, hipStream_t st) {
-  return launch_score_t<kGqa, false>(g, q, nullptr, 0, P, Kp, scores, st, FusedOut{});
+  return launch_score_t<kGqa, false>(g, q, nullptr, P, Kp, scores, st, FusedOut{});
 }
 
-hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P, const uint16_t* Kp,
-                            float* scores, hipStream_t st) {
+hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
+                            hipStream_t st) {
   GqaDev g{};
   g.B = m.B;
   g.Hq = 1;
@@ -332,7 +326,7 @@ hipError_t launch_mla_score(const MlaDev& m, const float* q_abs, const float* P,
   g.r = m.r;
   g.max_seq = m.max_seq;
   g.seq_lens = m.seq_lens;
-  return launch_score_t<kMla, false>(g, nullptr, q_abs, m.H, P, Kp, scores, st, FusedOut{});
+  return launch_score_t<kMla, false>(g, nullptr, q_sel, nullptr, Kp, scores, st, FusedOut{});
 }
 
 int score_topk_segments(int max_seq) {
@@ -345,14 +339,14 @@ int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st) {
   FusedOut fo{segs, k, scores ? 1 : 0};
-  return launch_score_t<kGqa, true>(g, q, nullptr, 0, P, Kp, scores, st, fo);
+  return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores, st, fo);
 }
 
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
-                             float* scores, int32_t* idx, CandSegs segs, hipStream_t st) {
+                             float* scores, int32_t* idx, CandSegs segs, void* merge_ws, hipStream_t st) {
   hipError_t e = launch_score_chunks(g, q, P, Kp, k, scores, segs, st);
   if (e != hipSuccess) return e;
-  return launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx, st);
+  return launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx, merge_ws, st);
 }
 
 }  // namespace jssa

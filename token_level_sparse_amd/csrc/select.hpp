@@ -229,7 +229,10 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   if (tid == 0) out.cnt[seg] = tot;
 }
 
+// Per-row final selection over candidate segments (merging groups of
+// segments first when a row's list is long). merge_ws: merge_workspace_bytes.
+size_t merge_workspace_bytes(int rows, int nseg, int k);
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
-                               int32_t* idx, hipStream_t st);
+                               int32_t* idx, void* merge_ws, hipStream_t st);
 
 }  // namespace jssa

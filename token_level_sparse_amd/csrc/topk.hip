@@ -81,15 +81,50 @@ struct FinalSmem {
   int res[2];
 };
 
-template <int NT, int EF>
+// One block per (row, group of gs consecutive segments). MERGE = false: the
+// group is the whole row (gs = nseg) and the block writes the row's selected
+// indices. MERGE = true: the block writes its group's first min(k, n)
+// candidates of the (key desc, index asc) order, as (key, index) pairs in
+// token order, to segment (row, group) of `outs`: a smaller candidate list
+// for the next level that still holds the row's top k.
+template <int NT, int EF, bool MERGE>
 __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
-                                                   CandSegs segs, int32_t* __restrict__ out) {
+                                                   CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs) {
   constexpr int NW = NT / 64;
   __shared__ FinalSmem<NT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ng = (segs.nseg + gs - 1) / gs;
+  const int row = blockIdx.x / ng, grp = blockIdx.x % ng;
   const int Tb = row_len(max_seq, seq_lens, row / H);
-  const int need_all = min(k, Tb);
-  const int nseg = segs.nseg;
+  const int need_all = MERGE ? k : min(k, Tb);
+  const int s0 = grp * gs;
+  const int nseg = min(gs, segs.nseg - s0);             // segments in this block's list
+  const int64_t seg0 = int64_t(row) * segs.nseg + s0;
+  const uint32_t* gkey = segs.key + seg0 * segs.cap;
+  const int32_t* gidx = segs.idx + seg0 * segs.cap;
+
+  // Direct layout: segment s is read by TPS = NT/nseg threads, EF slots each,
+  // at fixed positions, so these loads go out together with the segment
+  // counts instead of after them. Thread order is then list order. Used when
+  // every segment fits its TPS*EF slots; otherwise the list is re-read below
+  // by list position.
+  static_assert(EF % 4 == 0, "direct slots are read 16 bytes at a time");
+  const int TPS = NT / nseg;
+  const bool try_direct = TPS > 0 && TPS * EF <= segs.cap && segs.cap % 4 == 0;   // block-uniform
+  const int dseg = TPS > 0 ? tid / TPS : nseg;
+  const int dj = TPS > 0 ? (tid % TPS) * EF : 0;
+  uint32_t rkey[EF];
+  int32_t ridx[EF];
+  if (try_direct) {
+    const int64_t o = int64_t(dseg < nseg ? dseg : 0) * segs.cap + dj;
+#pragma unroll
+    for (int e = 0; e < EF; e += 4) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(gkey + o + e);
+      const u32x4 iv = *reinterpret_cast<const u32x4*>(gidx + o + e);
+      rkey[e] = kv.x; rkey[e + 1] = kv.y; rkey[e + 2] = kv.z; rkey[e + 3] = kv.w;
+      ridx[e] = int32_t(iv.x); ridx[e + 1] = int32_t(iv.y); ridx[e + 2] = int32_t(iv.z); ridx[e + 3] = int32_t(iv.w);
+    }
+  }
 
   // segment offsets: each thread scans SPT consecutive segments
   constexpr int SPT = kMaxSeg / NT;
@@ -98,7 +133,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
 #pragma unroll
   for (int x = 0; x < SPT; ++x) {
     const int s = tid * SPT + x;
-    c[x] = segs.cnt[int64_t(row) * nseg + (s < nseg ? s : nseg - 1)];
+    c[x] = segs.cnt[seg0 + (s < nseg ? s : nseg - 1)];
   }
 #pragma unroll
   for (int x = 0; x < SPT; ++x) {
@@ -114,11 +149,12 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     run += c[x];
   }
   if (tid == 0) sm.offs[nseg] = n;
-  __syncthreads();
+  bool over = false;
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) over = over || c[x] > TPS * EF;
+  const bool direct = !__syncthreads_or(over) && try_direct;   // (the barrier also orders the offs writes)
   // The row's candidate list is its segments one after the other: ascending
   // token order (segments cover ascending token ranges, each in token order).
-  const uint32_t* gkey = segs.key + int64_t(row) * nseg * segs.cap;
-  const int32_t* gidx = segs.idx + int64_t(row) * nseg * segs.cap;
   auto locate = [&](int i) -> int {      // segment holding list position i < n
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
@@ -151,13 +187,17 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       if (i0 + e >= n) ci[e] = -1;
   };
 
-  // candidates live in registers when they fit (block-uniform choice), each
-  // thread holding EF consecutive list positions
+  // candidates live in registers when they fit (block-uniform choice): in
+  // the direct layout, or else each thread holding EF consecutive list
+  // positions
   constexpr int kRegCap = NT * EF;
-  const bool reg = n <= kRegCap;
-  uint32_t rkey[EF];
-  int32_t ridx[EF];
-  if (reg && n > 0) {
+  const bool reg = direct || n <= kRegCap;
+  if (direct) {
+    const int cnt = dseg < nseg ? sm.offs[dseg + 1] - sm.offs[dseg] : 0;
+#pragma unroll
+    for (int e = 0; e < EF; ++e)
+      if (dj + e >= cnt) ridx[e] = -1;
+  } else if (reg && n > 0) {
     fetch(tid * EF, rkey, ridx);
   } else {
 #pragma unroll
@@ -250,7 +290,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   // Output in list order, which is ascending token order: two block scans
   // per page of candidates, one ranking the tied candidates and one placing
   // the taken ones.
-  int32_t* dst = out + int64_t(row) * k;
+  int32_t* dst = MERGE ? outs.idx + (int64_t(row) * ng + grp) * outs.cap : out + int64_t(row) * k;
+  uint32_t* dkey = MERGE ? outs.key + (int64_t(row) * ng + grp) * outs.cap : nullptr;
   int tie_base = 0, out_base = 0;
   auto emit = [&](const uint32_t (&ck)[EF], const int32_t (&ci)[EF]) {
     int nt = 0;
@@ -274,7 +315,10 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     int at = block_scan<NT>(ns, sm.scan, &st) - ns + out_base;
 #pragma unroll
     for (int e = 0; e < EF; ++e)
-      if (take >> e & 1u) dst[at++] = ci[e];
+      if (take >> e & 1u) {
+        if constexpr (MERGE) dkey[at] = ck[e];
+        dst[at++] = ci[e];
+      }
     tie_base += tt;
     out_base += st;
   };
@@ -287,7 +331,11 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       emit(rkey, ridx);
     }
   }
-  for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+  if constexpr (MERGE) {
+    if (tid == 0) outs.cnt[int64_t(row) * ng + grp] = out_base;
+  } else {
+    for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+  }
 }
 
 int chunks_of(int max_seq) { return (max_seq + kChunk - 1) / kChunk; }
@@ -310,34 +358,72 @@ CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total) {
   return w;
 }
 
+// A row's list goes straight to the final pass when it fits the final
+// block's registers at the small configuration; otherwise groups of segments
+// are first merged down to k candidates each, level after level.
+namespace {
+constexpr int kFinalDirect = 8192;
+int merge_group(int k) { return max(2, kFinalDirect / k); }
+bool needs_merge(int nseg, int k) { return nseg > 1 && int64_t(nseg) * k > kFinalDirect; }
+}  // namespace
+
+size_t merge_workspace_bytes(int rows, int nseg, int k) {
+  if (!needs_merge(nseg, k)) return 0;
+  const int ng = (nseg + merge_group(k) - 1) / merge_group(k);
+  size_t one = 0;
+  carve_segs(nullptr, rows, ng, k, &one);
+  return 2 * one;                                      // two alternating levels
+}
+
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
-                               int32_t* idx, hipStream_t st) {
+                               int32_t* idx, void* merge_ws, hipStream_t st) {
   if (segs.nseg > kMaxSeg) return hipErrorInvalidValue;
-  // candidates per row ~ nseg * (k + a few): 8192 held in registers for
-  // small budgets (1024 threads x 8), 16384 for large ones (1024 x 16); rows
-  // with more are streamed from memory page by page
-  if (k <= 512)
-    hipLaunchKernelGGL((final_kernel<1024, 8>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
+  CandSegs cur = segs;
+  if (needs_merge(segs.nseg, k)) {
+    const int gs = merge_group(k);
+    size_t one = 0;
+    carve_segs(nullptr, rows, (segs.nseg + gs - 1) / gs, k, &one);
+    int level = 0;
+    while (needs_merge(cur.nseg, k)) {
+      const int ng = (cur.nseg + gs - 1) / gs;
+      CandSegs nxt = carve_segs(static_cast<char*>(merge_ws) + (level & 1) * one, rows, ng, k, nullptr);
+      // a group holds about gs * k <= 8192 candidates (+ ties): 16384 in registers
+      hipLaunchKernelGGL((final_kernel<1024, 16, true>), dim3(rows * ng), dim3(1024), 0, st, H, max_seq,
+                         seq_lens, k, cur, gs, nullptr, nxt);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      cur = nxt;
+      ++level;
+    }
+  }
+  // candidates per row ~ nseg * (k + a few): up to 8192 held in registers by
+  // 1024 threads x 8, more by 1024 x 16; rows with more than 16384 (ties)
+  // are streamed from memory page by page
+  if (int64_t(cur.nseg) * k <= kFinalDirect)
+    hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
+                       cur, cur.nseg, idx, CandSegs{});
   else
-    hipLaunchKernelGGL((final_kernel<1024, 16>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs, idx);
+    hipLaunchKernelGGL((final_kernel<1024, 16, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
+                       cur, cur.nseg, idx, CandSegs{});
   return hipGetLastError();
 }
 
-size_t topk_workspace_bytes(int rows, int max_seq, int) {
+size_t topk_workspace_bytes(int rows, int max_seq, int k) {
   size_t total = 0;
   carve_segs(nullptr, rows, chunks_of(max_seq), kChunk, &total);
-  return total;
+  return total + merge_workspace_bytes(rows, chunks_of(max_seq), k);
 }
 
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
                        int32_t* idx, void* wsp, hipStream_t st) {
   const int rows = B * H;
   const int nchunks = chunks_of(max_seq);
-  CandSegs segs = carve_segs(wsp, rows, nchunks, kChunk, nullptr);
+  size_t main_bytes = 0;
+  CandSegs segs = carve_segs(wsp, rows, nchunks, kChunk, &main_bytes);
   hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, st);
+  return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, static_cast<char*>(wsp) + main_bytes, st);
 }
 
 }  // namespace jssa

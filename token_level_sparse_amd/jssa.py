@@ -71,8 +71,8 @@ _SIGS = {
     "jssa_dense_decode": [_P(GqaDesc), _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp],
     "jssa_gather_kv": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp],
     "jssa_mla_project_latent": [_P(MlaDesc), _vp, _vp, _vp, _vp],
-    "jssa_mla_absorb_q": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp],
-    "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp],
+    "jssa_mla_absorb_q": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_mla_indexed_decode": [_P(MlaDesc), _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_mla_up_v": [_P(MlaDesc), _vp, _vp, _vp, _vp],
 }
@@ -214,13 +214,13 @@ def jssa_mla_project_latent(desc, latent, P, Kp_lat, stream=None):
            "jssa_mla_project_latent")
 
 
-def jssa_mla_absorb_q(desc, q_nope, q_rope, W_uk, q_abs, stream=None):
-    _check(_lib.jssa_mla_absorb_q(ctypes.byref(desc), _p(q_nope), _p(q_rope), _p(W_uk), _p(q_abs),
-                                  _s(stream)), "jssa_mla_absorb_q")
+def jssa_mla_absorb_q(desc, q_nope, q_rope, W_uk, P, q_abs, q_sel, stream=None):
+    _check(_lib.jssa_mla_absorb_q(ctypes.byref(desc), _p(q_nope), _p(q_rope), _p(W_uk), _p(P), _p(q_abs),
+                                  _p(q_sel), _s(stream)), "jssa_mla_absorb_q")
 
 
-def jssa_mla_score(desc, q_abs, P, Kp_lat, scores, stream=None):
-    _check(_lib.jssa_mla_score(ctypes.byref(desc), _p(q_abs), _p(P), _p(Kp_lat), _p(scores), _s(stream)),
+def jssa_mla_score(desc, q_sel, Kp_lat, scores, stream=None):
+    _check(_lib.jssa_mla_score(ctypes.byref(desc), _p(q_sel), _p(Kp_lat), _p(scores), _s(stream)),
            "jssa_mla_score")
 
 

@@ -130,6 +130,21 @@ class SparseStep:
         for f in self.stages():
             f(stream)
 
+    def capture(self):
+        """Record one step's launches into a HIP graph (replayed by replay()).
+        The entry points allocate, synchronise and memset nothing, so the
+        whole step is capturable; it reads the current contents of q, the
+        caches and seq_lens at every replay."""
+        self.run()                                   # warm: first launches outside the capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        return self.graph
+
+    def replay(self):
+        self.graph.replay()
+
 
 class DenseStep:
     """Full-KV split-K attention -> combine."""
@@ -215,6 +230,7 @@ class MlaStep:
         B, H = cfg.B, cfg.H
         self.Kp = torch.zeros((B, cfg.T, cfg.r), dtype=torch.int16, device=device)
         self.q_abs = torch.empty((B, H, cfg.d_c), dtype=torch.float32, device=device)
+        self.q_sel = torch.empty((B, cfg.r), dtype=torch.float32, device=device)
         self.scores = torch.empty((B, cfg.T), dtype=torch.float32, device=device)
         nbytes = jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -230,8 +246,9 @@ class MlaStep:
 
     def run(self, stream=None):
         cfg = self.cfg
-        jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.q_abs, stream)
-        jssa.jssa_mla_score(self.desc, self.q_abs, self.P, self.Kp, self.scores, stream)
+        jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.P, self.q_abs, self.q_sel,
+                               stream)
+        jssa.jssa_mla_score(self.desc, self.q_sel, self.Kp, self.scores, stream)
         jssa.jssa_topk(cfg.B, 1, cfg.T, self.seq_lens, self.scores, self.k, self.idx, self.ws, None, stream)
         jssa.jssa_mla_indexed_decode(self.desc, self.q_abs, self.latent, self.idx, self.k, self.S,
                                      self.scale, self.part_o, self.part_lse, stream)
