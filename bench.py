@@ -165,9 +165,15 @@ def main():
     total2, st2_us = time_loop(sp2.stages(), args.steps, args.warmup, torch, stream)
     print(f"[bench] sparse (separate score, top-k) {total2 / args.steps * 1e3:.3f} ms/step", file=sys.stderr,
           flush=True)
-    # fused stages: [chunk pass (score stream + chunk select), final select, indexed attention, (combine)]
-    chunk_us, final_us, attn_us = st_us[0], st_us[1], st_us[2]
-    comb_us = st_us[3] if S > 1 else 0.0
+    # fused stages: S == 1: [chunk pass (score stream + chunk select), final select + attention];
+    # S > 1: [chunk pass, final select, indexed split attention, combine]
+    chunk_us = st_us[0]
+    if S == 1:
+        final_attend_us = st_us[1]
+    else:
+        final_us, attn_us, comb_us = st_us[1], st_us[2], st_us[3]
+    # the separate entry points: [jssa_score, jssa_topk, jssa_indexed_decode, (jssa_combine)]
+    sep_attn_us = st2_us[2] + (st2_us[3] if S > 1 else 0.0)
 
     kp_bytes = tot_tok * 2 * r
     q_bytes = B * Hq * d * 2
@@ -184,12 +190,17 @@ def main():
                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 3) if gbs else None}
 
     cand_bytes = B * Hkv * -(-T // 8192) * 8 * (k + 1)     # about k kept (key, index) pairs per 8192-token chunk
-    stages = {"score_topk_chunks": stage(chunk_us, fused_bytes),
-              "select_final": stage(final_us, cand_bytes + B * Hkv * k * 4),
-              "indexed": stage(attn_us, idx_bytes),
-              "combine": stage(comb_us, comb_bytes)}
+    stages = {"score_topk_chunks": stage(chunk_us, fused_bytes)}
+    if S == 1:
+        stages["select_final_attend"] = stage(final_attend_us, cand_bytes + idx_bytes)
+    else:
+        stages["select_final"] = stage(final_us, cand_bytes + B * Hkv * k * 4)
+        stages["indexed"] = stage(attn_us, idx_bytes)
+        stages["combine"] = stage(comb_us, comb_bytes)
     stages_split = {"score": stage(st2_us[0], score_bytes), "topk": stage(st2_us[1], topk_bytes),
-                    "indexed": stage(st2_us[2], idx_bytes), "ms_per_step": round(total2 / args.steps * 1e3, 4),
+                    "indexed": stage(st2_us[2], idx_bytes),
+                    "combine": stage(st2_us[3] if S > 1 else 0.0, comb_bytes),
+                    "ms_per_step": round(total2 / args.steps * 1e3, 4),
                     "steps_per_s": round(args.steps / total2, 2)}
     # the dominant kernel's launch duration: back-to-back launches of the chunk pass
     kern_us = time_launches(sp.score_chunks, args.steps, torch, stream)
@@ -238,7 +249,7 @@ def main():
         ga = pipeline.GatherStep(sp, S=max(S, 4))
         gsteps = max(3, args.steps // 5)
         gtotal, gst_us = time_loop([sp.score_topk, ga.gather, ga.attend, ga.combine], gsteps, 2, torch, stream)
-        sparse_attn_us = attn_us + comb_us
+        sparse_attn_us = sep_attn_us                    # jssa_indexed_decode (+ combine) alone
         gather_attn_us = gst_us[1] + gst_us[2] + gst_us[3]
         dense_attn_us = dst_us[0] + dst_us[1]
         result["gather_ablation"] = {

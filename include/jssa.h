@@ -183,6 +183,27 @@ JSSA_API jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k,
                                            int32_t* idx, void* stream);
 
 /*
+ * The final half of jssa_score_topk fused with jssa_indexed_decode at one
+ * split: each (sequence, KV head) row's block selects its k tokens from the
+ * candidates jssa_score_topk_chunks left in `ws` and at once runs the
+ * gather-free attention of the row's query heads over them (digest
+ * Interpretation: selected rows read in place through the indices).
+ *  desc, k, ws, ws_bytes  as jssa_score_topk_final (same desc and k as the
+ *                         jssa_score_topk_chunks call that filled ws)
+ *  q, K, V, scale         as jssa_indexed_decode
+ *  idx  device int32 [B,Hkv,k] (written, as jssa_topk)
+ *  out  device fp32 [B,Hq,d] (written): softmax-weighted values
+ *  lse  device fp32 [B,Hq] (written): log-sum-exp (-inf for an empty set)
+ * out/lse equal jssa_indexed_decode's partials for S = 1 on the same idx.
+ * Fused in one kernel when k <= 512, the row's candidates need no merge
+ * level and G <= 16; otherwise the same results come from the separate
+ * launches (final select, then indexed attention).
+ */
+JSSA_API jssa_status jssa_score_topk_final_attend(const jssa_gqa_desc* desc, int32_t k, const void* ws,
+                                                  size_t ws_bytes, const void* q, const void* K, const void* V,
+                                                  float scale, int32_t* idx, float* out, float* lse, void* stream);
+
+/*
  * Gather-free indexed attention, split-K partials (digest Interpretation:
  * selected tokens are read where they lie through scattered indices rather
  * than copied into a contiguous buffer; JSSA abstract).

@@ -260,6 +260,46 @@ def test_score_topk_fused_equals_split(J, PL, case):
     np.testing.assert_array_equal(_np(h.scores), _np(a.scores))
 
 
+@pytest.mark.parametrize("case", ["llama_k256", "ragged_k100", "qwen_paged_k256_G5", "tiny_k512", "G8_k300", "k1024_split"])
+def test_final_attend_matches_separate(J, PL, case):
+    """jssa_score_topk_final_attend writes the indices of the separate final
+    selection and, within float rounding, the one-split attention of
+    jssa_indexed_decode on them; outputs also checked against the oracle."""
+    if case == "llama_k256":
+        inp, k = synth.make_gqa(replace(synth.LLAMA8B_32K, B=2, T=20000, seed=95)), 256
+    elif case == "ragged_k100":
+        inp, k = ragged_inputs(), 100
+    elif case == "qwen_paged_k256_G5":
+        inp, k = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=20000, len_lo=9000, len_hi=20000, seed=96)), 256
+    elif case == "tiny_k512":
+        inp, k = synth.make_gqa(synth.TINY), 512
+    elif case == "G8_k300":
+        inp, k = synth.make_gqa(replace(synth.TINY, Hq=16, Hkv=2, seed=97)), 300
+    else:                                                 # falls back to separate launches inside the call
+        inp, k = synth.make_gqa(replace(synth.LLAMA8B_32K, B=1, T=30000, seed=98)), 1024
+    c = PL.GqaCache(inp)
+    c.project()
+    a = PL.SparseStep(c, k=k, S=1, fused=True, keep_scores=False)
+    a.score_chunks()
+    a.select_final()
+    a.attend()
+    f = PL.SparseStep(c, k=k, S=1, fused=True, keep_scores=False)
+    f.score_chunks()
+    f.final_attend()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(f.idx), _np(a.idx))
+    U.check_close(_np(f.out), _np(a.out), tol=1e-5, what="fused vs separate out")
+    U.check_close(_np(f.lse), _np(a.lse), tol=1e-5, what="fused vs separate lse")
+    cfg = inp.cfg
+    idx, out, lse = _np(f.idx), _np(f.out), _np(f.lse)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+            U.check_indices(idx[b, j], s, k)
+            sel = idx[b, j][idx[b, j] >= 0]
+            U.check_attention(inp, b, j, hs, K, V, sel, out, lse, c.scale)
+
+
 @pytest.mark.parametrize("k", [256, 1024, 2048])
 def test_sparse_step_paged_qwen(J, PL, k):
     cfg = replace(synth.PAGED_QWEN14B, B=3, T=20000, len_lo=9000, len_hi=20000, seed=50 + k)

@@ -249,6 +249,32 @@ jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const vo
                     __func__);
 }
 
+jssa_status jssa_score_topk_final_attend(const jssa_gqa_desc* desc, int32_t k, const void* ws, size_t ws_bytes,
+                                         const void* q, const void* K, const void* V, float scale, int32_t* idx,
+                                         float* out, float* lse, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(ws); REQUIRE_PTR(q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(idx); REQUIRE_PTR(out);
+  REQUIRE_PTR(lse);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  size_t main_bytes = 0;
+  const int nseg = jssa::score_topk_segments(desc->max_seq);
+  jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv, nseg,
+                                         jssa::score_topk_segment_cap(), &main_bytes);
+  const jssa::GqaDev g = to_dev(desc);
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* K16 = static_cast<const uint16_t*>(K);
+  const auto* V16 = static_cast<const uint16_t*>(V);
+  if (jssa::select_attend_fused(nseg, k, g.G))
+    return hip_status(jssa::launch_select_attend(g, k, segs, q16, K16, V16, scale, idx, out, lse, S(stream)),
+                      __func__);
+  hipError_t e = jssa::launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx,
+                                           static_cast<char*>(const_cast<void*>(ws)) + main_bytes, S(stream));
+  if (e == hipSuccess) e = jssa::launch_indexed(g, q16, K16, V16, idx, k, 1, scale, out, lse, S(stream));
+  return hip_status(e, __func__);
+}
+
 jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* q, const void* K, const void* V,
                                 const int32_t* idx, int32_t k, int32_t S_, float scale, float* part_o,
                                 float* part_lse, void* stream) {

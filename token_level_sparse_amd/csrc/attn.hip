@@ -16,18 +16,10 @@
 // fp32 in the log2 domain. Multi-wave blocks merge their waves in LDS.
 // Outputs are per-split partials (o, lse); jssa_combine merges the splits.
 #include "internal.hpp"
+#include "attn_core.hpp"
 
 namespace jssa {
 namespace {
-
-constexpr int kD = 128;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLog2e = 1.4426950408889634f;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Reinterpret one dword (two packed bf16) as a bf16 pair. Takes the dword by
-// value: bit-casting a vector-element lvalue (v.y) directly reads element 0.
-__device__ __forceinline__ bf16x2 as_pair(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
 template <int GT, int STEPS, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t* __restrict__ q,
@@ -41,7 +33,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
   const int j = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int gi = lane >> 4, sub = lane & 15;
   const int Tb = seq_len(g, b);
   const int h0 = j * g.G + hg * GT;             // first global query head of this block
   const int nh = min(GT, g.G - hg * GT);        // valid heads in the group
@@ -59,176 +50,26 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
   }
   const int32_t* irow = DENSE ? nullptr : idx + (int64_t(b) * g.Hkv + j) * k;
 
-  // query slice (dims sub*8..+8) of each head as bf16 pairs; logits use
-  // v_dot2_f32_bf16 (exact bf16 products, fp32 sums) and are scaled into the
-  // log2 domain after the row reduction
   bf16x2 qv[GT][4];
-  const float qs = scale * kLog2e;
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (h < nh) v = *reinterpret_cast<const u32x4*>(q + (int64_t(b) * g.Hq + h0 + h) * kD + sub * 8);
-    qv[h][0] = as_pair(v.x);
-    qv[h][1] = as_pair(v.y);
-    qv[h][2] = as_pair(v.z);
-    qv[h][3] = as_pair(v.w);
-  }
-
-  float m[GT], l[GT], o[GT][8];
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    m[h] = -__builtin_inff();
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  }
-
+  attn_load_q<GT>(qv, q, int64_t(b) * g.Hq + h0, nh, lane & 15);
+  const float qs = scale * kAttnLog2e;
+  AttnAcc<GT> A;
+  attn_init(A);
   constexpr int RB = STEPS * 4;                 // rows per wave batch
   for (int base = r0 + w * RB; base < r1; base += NW * RB) {
-    // Every load of the batch is issued without a data-dependent branch (a
-    // load under one would be waited for before the next is issued): the
-    // batch's indices, then (paged) their page ids, then the K and V rows.
-    // Rows past the split or with no valid token read a valid row (token 0,
-    // or page 0) and are masked out.
-    u32x4 kr[STEPS], vr[STEPS];
-    bool ok[STEPS];
-    int tt[STEPS];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int rr = base + st * 4 + gi;
-      tt[st] = DENSE ? rr : irow[rr < r1 ? rr : r1 - 1];
-    }
-    int pg[STEPS];                              // page ids (paged cache), also loaded together
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int rr = base + st * 4 + gi;
-      ok[st] = rr < r1 && tt[st] >= 0 && tt[st] < Tb;
-      tt[st] = ok[st] ? tt[st] : 0;
-      pg[st] = g.page_size ? g.page_table[int64_t(b) * g.max_pages + (tt[st] >> 4)] : 0;
-    }
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      int64_t off;
-      if (g.page_size) {
-        ok[st] = ok[st] && pg[st] >= 0 && pg[st] < g.num_pages;
-        off = ((int64_t(ok[st] ? pg[st] : 0) * g.Hkv + j) * kPage + (tt[st] & (kPage - 1))) * kD;
-      } else {
-        off = ((int64_t(b) * g.Hkv + j) * g.max_seq + tt[st]) * kD;
-      }
-      kr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K + off) + sub);
-      vr[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off) + sub);
-    }
-    float lg[STEPS][GT];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const u32x4 v = kr[st];
-      const bf16x2 k0 = as_pair(v.x), k1 = as_pair(v.y), k2 = as_pair(v.z), k3 = as_pair(v.w);
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        float a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][0], k0, 0.f, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][1], k1, a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][2], k2, a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(qv[h][3], k3, a, false);
-        a = row16_sum(a) * qs;
-        lg[st][h] = ok[st] ? a : -__builtin_inff();
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float mb = lg[0][h];
-#pragma unroll
-      for (int st = 1; st < STEPS; ++st) mb = fmaxf(mb, lg[st][h]);
-      mb = xor_max(mb, 16);
-      mb = xor_max(mb, 32);
-      const float mn = fmaxf(m[h], mb);
-      if (mn == -__builtin_inff()) continue;      // nothing valid yet (wave-uniform)
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-      m[h] = mn;
-      float ls = 0.f;
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = o[h][e] * alpha;
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-        const float p = __builtin_amdgcn_exp2f(lg[st][h] - mn);
-        ls += p;
-        const u32x4 v = vr[st];
-        acc[0] = __builtin_fmaf(p, bf_lo(v.x), acc[0]);
-        acc[1] = __builtin_fmaf(p, bf_hi(v.x), acc[1]);
-        acc[2] = __builtin_fmaf(p, bf_lo(v.y), acc[2]);
-        acc[3] = __builtin_fmaf(p, bf_hi(v.y), acc[3]);
-        acc[4] = __builtin_fmaf(p, bf_lo(v.z), acc[4]);
-        acc[5] = __builtin_fmaf(p, bf_hi(v.z), acc[5]);
-        acc[6] = __builtin_fmaf(p, bf_lo(v.w), acc[6]);
-        acc[7] = __builtin_fmaf(p, bf_hi(v.w), acc[7]);
-      }
-      l[h] = l[h] * alpha + ls;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = acc[e];
-    }
+    if constexpr (DENSE)
+      attn_batch<GT, STEPS>(g, b, j, Tb, K, V, qv, qs, base, r1, [](int rr) { return rr; }, A);
+    else
+      attn_batch<GT, STEPS>(g, b, j, Tb, K, V, qv, qs, base, r1, [&](int rr) { return irow[rr]; }, A);
   }
-
-  // reduce the four 16-lane row groups of the wave
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    l[h] = xor_sum(xor_sum(l[h], 16), 32);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = xor_sum(xor_sum(o[h][e], 16), 32);
-  }
-
+  attn_wave_reduce(A);
   if constexpr (NW > 1) {
-    __shared__ float sm_m[NW][GT], sm_l[NW][GT];
-    __shared__ float sm_o[NW][GT][kD];
-    if (lane < 16) {
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm_o[w][h][sub * 8 + e] = o[h][e];
-      }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < GT; ++h) { sm_m[w][h] = m[h]; sm_l[w][h] = l[h]; }
-    }
-    __syncthreads();
+    __shared__ AttnMergeSmem<GT, NW> msm;
+    attn_block_merge(A, msm);
     if (w != 0) return;
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int x = 0; x < NW; ++x) M = fmaxf(M, sm_m[x][h]);
-      float L = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (M != -__builtin_inff()) {
-#pragma unroll
-        for (int x = 0; x < NW; ++x) {
-          const float f = __builtin_amdgcn_exp2f(sm_m[x][h] - M);
-          L += sm_l[x][h] * f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += sm_o[x][h][sub * 8 + e] * f;
-        }
-      }
-      m[h] = M;
-      l[h] = L;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = acc[e];
-    }
   }
-
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      if (h >= nh) break;
-      const int64_t ob = ((int64_t(b) * g.Hq + h0 + h) * S + s);
-      const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
-      f32x4 a = {o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv};
-      f32x4 c = {o[h][4] * inv, o[h][5] * inv, o[h][6] * inv, o[h][7] * inv};
-      f32x4* dst = reinterpret_cast<f32x4*>(part_o + ob * kD + sub * 8);
-      dst[0] = a;
-      dst[1] = c;
-      if (sub == 0)
-        part_lse[ob] = l[h] > 0.f ? (m[h] + __builtin_log2f(l[h])) * kLn2 : -__builtin_inff();
-    }
-  }
+  attn_store(A, nh, [&](int h) { return part_o + ((int64_t(b) * g.Hq + h0 + h) * S + s) * kAttnD; },
+             [&](int h) { return part_lse + (int64_t(b) * g.Hq + h0 + h) * S + s; });
 }
 
 template <int GT, int STEPS, int NW, bool DENSE>

@@ -83,7 +83,7 @@ struct ScoreSmem {
 };
 
 template <int R, int MODE, bool FUSED>
-__global__ __launch_bounds__(256) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R <= 64 ? 4 : 1))) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
                                                     const float* __restrict__ qsel,
                                                     const float* __restrict__ P,
                                                     const uint16_t* __restrict__ Kp,

@@ -234,5 +234,11 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
 size_t merge_workspace_bytes(int rows, int nseg, int k);
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
                                int32_t* idx, void* merge_ws, hipStream_t st);
+// Final selection fused with the attention of each row's query heads over the
+// selected tokens (one split), when select_attend_fused(nseg, k, G) holds.
+bool select_attend_fused(int nseg, int k, int G);
+hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
+                                const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
+                                hipStream_t st);
 
 }  // namespace jssa

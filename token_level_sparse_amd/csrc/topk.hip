@@ -21,6 +21,7 @@
 // capacity re-read their segments at each level (slower, same result).
 #include "internal.hpp"
 #include "select.hpp"
+#include "attn_core.hpp"
 
 namespace jssa {
 namespace {
@@ -87,9 +88,26 @@ struct FinalSmem {
 // candidates of the (key desc, index asc) order, as (key, index) pairs in
 // token order, to segment (row, group) of `outs`: a smaller candidate list
 // for the next level that still holds the row's top k.
-template <int NT, int EF, bool MERGE>
+// With GT > 0 (final mode only) the block then runs the attention of the
+// row's query heads over the selected tokens, read in place, and writes the
+// normalised outputs and log-sum-exps (split-K with one split): the indices
+// never make a round trip through memory before the attention reads them.
+struct AttendArgs {
+  GqaDev g;
+  const uint16_t* q;
+  const uint16_t* K;
+  const uint16_t* V;
+  float scale;
+  float* out;
+  float* lse;
+};
+constexpr int kAttendMaxK = 512;
+
+template <int NT, int EF, bool MERGE, int GT = 0>
 __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
-                                                   CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs) {
+                                                   CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs,
+                                                   AttendArgs at = AttendArgs{}) {
+  static_assert(GT == 0 || !MERGE, "attention follows the row's final selection only");
   constexpr int NW = NT / 64;
   __shared__ FinalSmem<NT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -293,6 +311,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   int32_t* dst = MERGE ? outs.idx + (int64_t(row) * ng + grp) * outs.cap : out + int64_t(row) * k;
   uint32_t* dkey = MERGE ? outs.key + (int64_t(row) * ng + grp) * outs.cap : nullptr;
   int tie_base = 0, out_base = 0;
+  __shared__ int32_t sel[GT > 0 ? kAttendMaxK : 1];   // the selected tokens, for the attention
   auto emit = [&](const uint32_t (&ck)[EF], const int32_t (&ci)[EF]) {
     int nt = 0;
 #pragma unroll
@@ -317,6 +336,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     for (int e = 0; e < EF; ++e)
       if (take >> e & 1u) {
         if constexpr (MERGE) dkey[at] = ck[e];
+        if constexpr (GT > 0) sel[at] = ci[e];
         dst[at++] = ci[e];
       }
     tie_base += tt;
@@ -335,6 +355,30 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     if (tid == 0) outs.cnt[int64_t(row) * ng + grp] = out_base;
   } else {
     for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+  }
+  if constexpr (GT > 0) {
+    constexpr int STEPS = 8, RB = STEPS * 4;
+    const GqaDev& g = at.g;
+    const int b = row / H, j = row % H, w = tid >> 6;
+    const int cnt = out_base;                           // selected tokens (<= kAttendMaxK)
+    const float qs = at.scale * kAttnLog2e;
+    __shared__ AttnMergeSmem<GT, NW> msm;
+    __syncthreads();                                    // sel complete
+    for (int hg = 0; hg * GT < g.G; ++hg) {
+      const int h0 = j * g.G + hg * GT, nh = min(GT, g.G - hg * GT);
+      bf16x2 qv[GT][4];
+      attn_load_q<GT>(qv, at.q, int64_t(b) * g.Hq + h0, nh, lane & 15);
+      AttnAcc<GT> A;
+      attn_init(A);
+      for (int base = w * RB; base < cnt; base += NW * RB)
+        attn_batch<GT, STEPS>(g, b, j, Tb, at.K, at.V, qv, qs, base, cnt, [&](int rr) { return sel[rr]; }, A);
+      attn_wave_reduce(A);
+      attn_block_merge(A, msm);
+      if (w == 0)
+        attn_store(A, nh, [&](int h) { return at.out + (int64_t(b) * g.Hq + h0 + h) * kAttnD; },
+                   [&](int h) { return at.lse + int64_t(b) * g.Hq + h0 + h; });
+      __syncthreads();                                  // msm is reused by the next head group
+    }
   }
 }
 
@@ -387,8 +431,8 @@ hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_
     while (needs_merge(cur.nseg, k)) {
       const int ng = (cur.nseg + gs - 1) / gs;
       CandSegs nxt = carve_segs(static_cast<char*>(merge_ws) + (level & 1) * one, rows, ng, k, nullptr);
-      // a group holds about gs * k <= 8192 candidates (+ ties): 16384 in registers
-      hipLaunchKernelGGL((final_kernel<1024, 16, true>), dim3(rows * ng), dim3(1024), 0, st, H, max_seq,
+      // a group holds about gs * k <= 8192 candidates (+ ties): 12288 in registers
+      hipLaunchKernelGGL((final_kernel<1024, 12, true>), dim3(rows * ng), dim3(1024), 0, st, H, max_seq,
                          seq_lens, k, cur, gs, nullptr, nxt);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -397,14 +441,40 @@ hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_
     }
   }
   // candidates per row ~ nseg * (k + a few): up to 8192 held in registers by
-  // 1024 threads x 8, more by 1024 x 16; rows with more than 16384 (ties)
+  // 1024 threads x 8, more by 1024 x 12; rows with more than 12288 (ties)
   // are streamed from memory page by page
   if (int64_t(cur.nseg) * k <= kFinalDirect)
     hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
                        cur, cur.nseg, idx, CandSegs{});
   else
-    hipLaunchKernelGGL((final_kernel<1024, 16, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
+    hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
                        cur, cur.nseg, idx, CandSegs{});
+  return hipGetLastError();
+}
+
+bool select_attend_fused(int nseg, int k, int G) {
+  return !needs_merge(nseg, k) && k <= kAttendMaxK && G <= 16;
+}
+
+hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
+                                const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
+                                hipStream_t st) {
+  if (segs.nseg > kMaxSeg || !select_attend_fused(segs.nseg, k, g.G)) return hipErrorInvalidValue;
+  const int rows = g.B * g.Hkv;
+  const AttendArgs aa{g, q, K, V, scale, out, lse};
+  // query heads per pass over the selected rows: the whole group when it has
+  // 1, 2 or 5 heads (or 10, 15), else 4 at a time
+  const int gt = g.G <= 2 ? g.G : (g.G % 5 == 0 ? 5 : 4);
+#define JSSA_FA(GT)                                                                                      \
+  hipLaunchKernelGGL((final_kernel<512, 16, false, GT>), dim3(rows), dim3(512), 0, st, g.Hkv, g.max_seq,   \
+                     g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa)
+  switch (gt) {
+    case 1: JSSA_FA(1); break;
+    case 2: JSSA_FA(2); break;
+    case 5: JSSA_FA(5); break;
+    default: JSSA_FA(4); break;
+  }
+#undef JSSA_FA
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = ra
 ENTRY_POINTS = (
     "jssa_append_kv", "jssa_project_keys", "jssa_score", "jssa_topk_workspace_size", "jssa_topk",
     "jssa_score_topk_workspace_size", "jssa_score_topk", "jssa_score_topk_chunks", "jssa_score_topk_final",
+    "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_status_string", "jssa_last_error", "jssa_version",
@@ -66,6 +67,7 @@ _SIGS = {
     "jssa_score_topk": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "jssa_score_topk_chunks": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
     "jssa_score_topk_final": [_P(GqaDesc), _i32, _vp, _sz, _vp, _vp],
+    "jssa_score_topk_final_attend": [_P(GqaDesc), _i32, _vp, _sz, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp],
     "jssa_indexed_decode": [_P(GqaDesc), _vp, _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_combine": [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp],
     "jssa_dense_decode": [_P(GqaDesc), _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp],
@@ -187,6 +189,13 @@ def jssa_score_topk_final(desc, k, ws, idx, ws_bytes=None, stream=None):
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.jssa_score_topk_final(ctypes.byref(desc), k, _p(ws), ws_bytes, _p(idx), _s(stream)),
            "jssa_score_topk_final")
+
+
+def jssa_score_topk_final_attend(desc, k, ws, q, K, V, scale, idx, out, lse, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topk_final_attend(ctypes.byref(desc), k, _p(ws), ws_bytes, _p(q), _p(K), _p(V), scale,
+                                             _p(idx), _p(out), _p(lse), _s(stream)), "jssa_score_topk_final_attend")
 
 
 def jssa_indexed_decode(desc, q, K, V, idx, k, S, scale, part_o, part_lse, stream=None):

@@ -120,9 +120,19 @@ class SparseStep:
     def select_final(self, stream=None):
         jssa.jssa_score_topk_final(self.c.desc, self.k, self.ws, self.idx, None, stream)
 
+    def final_attend(self, stream=None):
+        """Final selection and one-split attention in one call (S == 1)."""
+        c = self.c
+        jssa.jssa_score_topk_final_attend(c.desc, self.k, self.ws, c.q, c.K, c.V, c.scale, self.idx, self.out,
+                                          self.lse, None, stream)
+
     def stages(self):
-        """The launches of one step, in order (the fused score + top-k as its
-        two halves, the same launches jssa_score_topk issues)."""
+        """The launches of one step, in order. Fused with one split: the
+        chunk pass, then final selection + attention; fused with S splits:
+        the chunk pass, the final selection, the split attention and the
+        combine; unfused: jssa_score, jssa_topk, attention (+ combine)."""
+        if self.fused and self.S == 1:
+            return [self.score_chunks, self.final_attend]
         head = [self.score_chunks, self.select_final] if self.fused else [self.score, self.topk]
         return head + [self.attend] + ([self.combine] if self.S > 1 else [])
 
