@@ -77,13 +77,13 @@ struct FusedOut {
 template <int R>
 struct ScoreSmem {
   float qbar[kD];
-  float qpart[256];
+  float qpart[kWaves * 64];
   float qp[R];
   float part[(R / 8) & (R / 8 - 1) ? kWaves * 8 * R : 1];   // LDS reduction (r = 48 only)
 };
 
 template <int R, int MODE, bool FUSED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R <= 64 ? 4 : 1))) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUSED && R <= 64 ? 4 : 1))) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
                                                     const float* __restrict__ qsel,
                                                     const float* __restrict__ P,
                                                     const uint16_t* __restrict__ Kp,
@@ -93,13 +93,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
   constexpr int NSL = kDpp ? 1 : PP;          // qp slices held per lane
   constexpr int TPW = tiles_per_wave(MODE, FUSED);
   __shared__ ScoreSmem<R> sm;
-  // Fused: token o of the chunk is staged at (o % TPW) * (256 + 1) + o / TPW,
-  // so thread i later reads its TPW consecutive tokens o = i*TPW + e at
-  // e*257 + i; the +1 pad keeps both the tile writes and those reads free of
-  // LDS bank conflicts. Score-only: staged at o.
-  static_assert(!FUSED || kWaves * 64 == 256, "fused staging assumes 256 threads");
-  constexpr int kStageBytes = FUSED ? TPW * 257 * 4 : kWaves * 64 * TPW * 4;
-  constexpr int kBufBytes = kStageBytes > int(sizeof(ChunkSmem<256, TPW>)) ? kStageBytes : int(sizeof(ChunkSmem<256, TPW>));
+  // Fused: token o of the chunk is staged at (o % TPW) * SS + o / TPW with
+  // SS = NT + 64/TPW, so thread i later reads its TPW consecutive tokens
+  // o = i*TPW + e at e*SS + i; the pad makes both the tile writes (64
+  // consecutive o) and those reads hit 64 distinct LDS banks. Score-only:
+  // staged at o.
+  constexpr int NT = kWaves * 64;
+  static_assert(!FUSED || (64 % TPW == 0 || TPW % 64 == 0), "fused staging pad");
+  constexpr int SS = NT + (TPW <= 64 ? 64 / TPW : 1);
+  constexpr int kStageBytes = FUSED ? TPW * SS * 4 : NT * TPW * 4;
+  constexpr int kBufBytes = kStageBytes > int(sizeof(ChunkSmem<NT, TPW>)) ? kStageBytes : int(sizeof(ChunkSmem<NT, TPW>));
   __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
 
   const int b = blockIdx.z, j = blockIdx.y;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
   if (t_begin >= Tb) {                       // whole chunk past the sequence's end
     if (!FUSED || fo.write_scores) {
       const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
-      for (int i = tid; i < lim; i += 256) srow[t_begin + i] = -__builtin_inff();
+      for (int i = tid; i < lim; i += NT) srow[t_begin + i] = -__builtin_inff();
     }
     if (FUSED && tid == 0) fo.segs.cnt[seg] = 0;
     return;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
   const int tend = Tb - t_begin < chunk ? Tb : t_begin + chunk;
   __shared__ int pid[FUSED ? kWaves * 64 * kFusedTiles / kPage : kWaves * 64 * kPlainTiles / kPage];
   if (paged) {                               // page ids of the chunk (-1: no valid page)
-    for (int i = tid; i < chunk / kPage; i += 256) {
+    for (int i = tid; i < chunk / kPage; i += NT) {
       int t = t_begin + i * kPage;
       t = t < tend ? t : tend - 1;
       const int pg = g.page_table[int64_t(b) * g.max_pages + (t >> 4)];
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
     }
     __syncthreads();
     {
-      constexpr int NS = 256 / R;
+      constexpr int NS = NT / R;
       constexpr int NI = (kD + NS - 1) / NS;
       const int c = tid % R, sl = tid / R;
       if (sl < NS) {
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
   // for the previous store's write acknowledgement; holding them in
   // registers would cost occupancy.)
   float* stage = reinterpret_cast<float*>(sbuf);
-  auto sidx = [](int o) { return FUSED ? (o % TPW) * 257 + o / TPW : o; };
+  auto sidx = [](int o) { return FUSED ? (o % TPW) * SS + o / TPW : o; };
   auto stage_tile = [&](int tile, const u32x4 (&buf)[PP]) {
     const int off = (tile * kWaves + w) * 64;
     const float x = tile_scores(buf);
@@ -270,22 +273,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FUSED && R 
     float* dst = srow + t_begin;
     const int lim = g.max_seq - t_begin;                 // > 0
     if ((g.max_seq & 3) == 0) {                          // 16-byte aligned row chunk
-      for (int i = tid * 4; i < chunk && i < lim; i += 1024)
+      for (int i = tid * 4; i < chunk && i < lim; i += 4 * NT)
         *reinterpret_cast<f32x4*>(dst + i) =
             f32x4{stage[sidx(i)], stage[sidx(i + 1)], stage[sidx(i + 2)], stage[sidx(i + 3)]};
     } else {
-      for (int i = tid; i < chunk && i < lim; i += 256) dst[i] = stage[sidx(i)];
+      for (int i = tid; i < chunk && i < lim; i += NT) dst[i] = stage[sidx(i)];
     }
   }
   if constexpr (FUSED) {
     uint32_t key[TPW];
 #pragma unroll
-    for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[e * 257 + tid]);   // token tid*TPW + e
+    for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*TPW + e
     __syncthreads();                                     // stage is reused below
-    ChunkSmem<256, TPW>& csm = *reinterpret_cast<ChunkSmem<256, TPW>*>(sbuf);
+    ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
     int n = Tb - t_begin;
     n = n < 0 ? 0 : (n > chunk ? chunk : n);
-    chunk_select<256, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+    chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
   }
 }
 
@@ -297,7 +300,7 @@ hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qsel,
   switch (g.r) {
 #define JSSA_CASE(R)                                                                                  \
   case R:                                                                                             \
-    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(256), 0, st, g, q, qsel, P, Kp,     \
+    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(kWaves * 64), 0, st, g, q, qsel, P, Kp, \
                        scores, fo);                                                                   \
     break;
     JSSA_CASE(16) JSSA_CASE(32) JSSA_CASE(48) JSSA_CASE(64) JSSA_CASE(128)
