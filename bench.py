@@ -294,7 +294,7 @@ def main():
 
 def bench_mla(args, cfg, torch, pipeline, synth, stream):
     inp = synth.make_mla(cfg)
-    S = args.splits or 8
+    S = args.splits or 16
     st = pipeline.MlaStep(inp, S=S)
     st.project()
     torch.cuda.synchronize()

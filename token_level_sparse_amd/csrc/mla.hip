@@ -147,18 +147,21 @@ __global__ __launch_bounds__(1024) void mla_selq_kernel(MlaDev m, const float* _
   const int hq = tid >> 8, ct = tid & 255;              // head quarter, column thread
   const int hpq = (m.H + 3) / 4;
   const int h0 = hq * hpq, h1 = min(m.H, h0 + hpq);
+  // up to 32 heads per quarter: all loads of a column issued at once
+  // (clamped to a valid head, zero weight past the quarter)
   for (int c = ct; c < kDc; c += 256) {
     const float* qc = qa + int64_t(b) * m.H * kDc + c;
     float s = 0.f;
-    int h = h0;
-    for (; h + 8 <= h1; h += 8) {
-      float a[8];
+    for (int hb = h0; hb < h1; hb += 32) {
+      float a[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = qc[int64_t(h + u) * kDc];
+      for (int u = 0; u < 32; ++u) {
+        const int h = hb + u < h1 ? hb + u : h1 - 1;
+        a[u] = qc[int64_t(h) * kDc];
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += a[u];
+      for (int u = 0; u < 32; ++u) s += hb + u < h1 ? a[u] : 0.f;
     }
-    for (; h < h1; ++h) s += qc[int64_t(h) * kDc];
     part[hq][c] = s;
   }
   __syncthreads();
@@ -168,12 +171,16 @@ __global__ __launch_bounds__(1024) void mla_selq_kernel(MlaDev m, const float* _
   constexpr int NI = (kDc + NS - 1) / NS;
   const int c = tid % R, sl = tid / R;
   float s = 0.f;
-#pragma unroll 8
+  float pv[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {                   // every P load in flight at once
+    const int i = sl + ii * NS;
+    pv[ii] = P[(i < kDc ? i : kDc - 1) * R + c];
+  }
+#pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int i = sl + ii * NS;
-    const int ic = i < kDc ? i : kDc - 1;
-    const float pv = P[ic * R + c];
-    s = __builtin_fmaf(pv, i < kDc ? qbar[ic] : 0.f, s);
+    s = __builtin_fmaf(pv[ii], i < kDc ? qbar[i < kDc ? i : kDc - 1] : 0.f, s);
   }
   ppart[sl * R + c] = s;
   __syncthreads();
@@ -264,10 +271,14 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
 #pragma unroll
     for (int kb = 0; kb < 18; ++kb) A[kb] = *reinterpret_cast<const u32x4*>(crow + kb * 32);
   };
-  // QK^T of one half tile; stashes the value part transposed in LDS
+  // QK^T of one half tile; stashes the value part transposed in LDS. Four
+  // independent accumulator chains (hi/lo x even/odd dim blocks) keep the
+  // MFMA pipe busy instead of waiting on one chain's previous result.
   auto qk_half = [&](const u32x4 (&A)[18], int hf) -> f32x4v {
     const int tl = 8 * (n >> 2) + 4 * hf + (n & 3);
-    f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+    f32x4v acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 18; ++kb) {
       if (kb < 16) {
@@ -277,10 +288,10 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
         for (int e = 0; e < 8; ++e) Vt[(kb * 32 + 8 * g + e) * kVtStride + tl] = e16[e];
       }
       const bf16x8 a = __builtin_bit_cast(bf16x8, A[kb]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kb], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo_s[kb][lane], acc, 0, 0, 0);
+      acc[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kb], acc[kb & 1], 0, 0, 0);
+      acc[2 + (kb & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo_s[kb][lane], acc[2 + (kb & 1)], 0, 0, 0);
     }
-    return acc;
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
 
   u32x4 A0[18], A1[18];

@@ -224,7 +224,7 @@ class MlaStep:
     """MLA: absorb -> score -> top-k (one set per sequence) -> indexed MFMA
     attention over the latent rows -> combine -> value up-projection."""
 
-    def __init__(self, inp: MlaInputs, S: int = 8, device="cuda"):
+    def __init__(self, inp: MlaInputs, S: int = 16, device="cuda"):
         cfg = inp.cfg
         self.cfg, self.S, self.k = cfg, S, cfg.k
         self.q_nope = to_device(inp.q_nope, device)
