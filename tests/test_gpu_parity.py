@@ -496,13 +496,22 @@ def test_mla_parity(J, PL):
 # benchmark times; sampled units against the oracle, properties everywhere
 # ---------------------------------------------------------------------------
 def test_full_size_128k_b16_sampled(J, PL):
+    """The 128K x B=16 workload in the launch configuration the benchmark
+    times (fused chunk pass, then final selection + attention at one split),
+    checked on sampled units against the oracle and everywhere for the
+    properties that hold at any size; the separate entry points must give
+    the same indices."""
     cfg = synth.BATCHED_128K
     inp = synth.make_gqa(cfg)
     c = PL.GqaCache(inp)
     c.project()
-    st = PL.SparseStep(c, k=cfg.k)
+    st = PL.SparseStep(c, k=cfg.k, fused=True, keep_scores=False)
+    assert [f.__name__ for f in st.stages()] == ["score_chunks", "final_attend"]
     st.run()
+    sep = PL.SparseStep(c, k=cfg.k, fused=False)
+    sep.run()
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(st.idx), _np(sep.idx))
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
     assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < cfg.T
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
@@ -513,3 +522,51 @@ def test_full_size_128k_b16_sampled(J, PL):
         np.testing.assert_array_equal(_np(c.Kp[b, j, torch.from_numpy(rows).cuda()]), Kp[rows])
         U.check_indices(idx[b, j], s, cfg.k)
         U.check_attention(inp, b, j, hs, K, V, idx[b, j], out, lse, c.scale)
+
+
+def test_full_size_qwen_paged_k2048_sampled(J, PL):
+    """Paged, ragged Qwen3-14B-shaped workload at full size with the largest
+    budget of its sweep, in the benchmark's launch configuration (chunk pass,
+    merge levels + final selection, eight-split attention, combine)."""
+    cfg = replace(synth.PAGED_QWEN14B, k=2048)
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.SparseStep(c, k=cfg.k, fused=True, keep_scores=False)
+    assert st.S == 8
+    st.run()
+    torch.cuda.synchronize()
+    idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    for b, j in [(0, 0), (5, 3), (7, 7)]:
+        n = min(cfg.k, int(inp.seq_lens[b]))
+        assert np.all(np.diff(idx[b, j, :n]) > 0) and np.all(idx[b, j, n:] == -1)
+        K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+        U.check_indices(idx[b, j], s, cfg.k)
+        U.check_attention(inp, b, j, hs, K, V, idx[b, j][:n], out, lse, c.scale)
+
+
+def test_full_size_mla_sampled(J, PL):
+    """DeepSeek-V3-shaped MLA workload at full size (B=4, T=128K, k=2048) in
+    the benchmark's launch configuration (16 splits), two sequences checked
+    against the explicit (non-absorbed) oracle on the GPU's selected set."""
+    cfg = synth.MLA_DSV3
+    inp = synth.make_mla(cfg)
+    st = PL.MlaStep(inp)
+    assert st.S == 16
+    st.project()
+    st.run()
+    torch.cuda.synchronize()
+    idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    for b in (0, 3):
+        assert np.all(np.diff(idx[b]) > 0)
+        Kp = O.project_keys(inp.latent[b], inp.P)
+        rows = np.random.default_rng(b).choice(cfg.T, 1024, replace=False)
+        np.testing.assert_array_equal(_np(st.Kp[b, torch.from_numpy(rows).cuda()]), Kp[rows])
+        s = O.mla_scores(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.P, Kp)
+        U.check_indices(idx[b], s, cfg.k)
+        o, _, l = O.mla_attend_explicit(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.W_uv, inp.latent[b][idx[b]],
+                                        st.scale)
+        U.check_close(out[b], o, what=f"mla out b={b}")
+        U.check_close(lse[b], l, what=f"mla lse b={b}")

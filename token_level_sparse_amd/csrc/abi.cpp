@@ -1,4 +1,4 @@
-// C ABI of the JSSA library: host-side validation, then one launch per call.
+// C ABI of the JSSA library: host-side validation, then the call's launches.
 // Declarations and the contract of every entry point are in include/jssa.h.
 #include "../../include/jssa.h"
 

@@ -15,8 +15,8 @@
 // m holds piece 64m+l; the r/8 lanes holding one token's pieces are adjacent,
 // so their 8-element partial dots are summed with DPP moves, and one
 // ds_bpermute per load column hands token i's score to lane i: every lane
-// then owns one token of the tile and the scores leave as one coalesced
-// 256-byte store per wave. The next tile's loads are in flight while the
+// then owns one token of the tile. Scores are staged in LDS and leave after
+// the stream as 16-byte stores. The next tile's loads are in flight while the
 // current tile is reduced, and the first tile's loads are issued before the
 // qp prologue. r = 48 (6 lanes per token, not aligned to DPP rows) sums its
 // partials through LDS instead.
