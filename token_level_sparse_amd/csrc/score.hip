@@ -162,11 +162,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   };
 
   u32x4 bufs[kDepth][PP];
-  load_tile(0, bufs[0]);                       // in flight during the prologue
+#pragma unroll
+  for (int u = 0; u < kDepth - 1; ++u) load_tile(u, bufs[u]);   // in flight during the prologue
 
-  // ---- prologue: qp = P_j^T qbar (fp32). Loops are unrolled so that their
-  // loads are all in flight together rather than one round trip each.
+  // ---- prologue: qp = P_j^T qbar (fp32). The slice of P this thread needs
+  // and the group's query rows are loaded together (one round trip, not two),
+  // with every loop unrolled so that its loads are all in flight at once.
   if constexpr (MODE == kGqa) {
+    constexpr int NS = NT / R;                 // row slices of P
+    constexpr int NI = (kD + NS - 1) / NS;     // rows per slice
+    constexpr bool kPreP = NI <= 32;           // hold the slice in registers
+    const int c = tid % R, sl = tid / R;
+    const float* Pj = P + int64_t(j) * kD * R;
+    float pv[kPreP ? NI : 1];
+    if constexpr (kPreP) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        const int i = sl + ii * NS;
+        pv[ii] = Pj[(i < kD ? i : kD - 1) * R + c];   // unconditional load, zero weight past d
+      }
+    }
     if (tid < kD) {
       const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + tid;
       float s = 0.f;
@@ -180,30 +195,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       sm.qbar[tid] = s;
     }
     __syncthreads();
-    {
-      constexpr int NS = NT / R;
-      constexpr int NI = (kD + NS - 1) / NS;
-      const int c = tid % R, sl = tid / R;
-      if (sl < NS) {
-        const float* Pj = P + int64_t(j) * kD * R;
-        float s = 0.f;
+    if (sl < NS) {
+      float s = 0.f;
 #pragma unroll 16
-        for (int ii = 0; ii < NI; ++ii) {
-          const int i = sl + ii * NS;
-          const int ic = i < kD ? i : kD - 1;      // unconditional load, zero weight past d
-          const float pv = Pj[ic * R + c];
-          s = __builtin_fmaf(pv, i < kD ? sm.qbar[ic] : 0.f, s);
-        }
-        sm.qpart[sl * R + c] = s;
+      for (int ii = 0; ii < NI; ++ii) {
+        const int i = sl + ii * NS;
+        const int ic = i < kD ? i : kD - 1;
+        const float p = kPreP ? pv[kPreP ? ii : 0] : Pj[ic * R + c];
+        s = __builtin_fmaf(p, i < kD ? sm.qbar[ic] : 0.f, s);
       }
-      __syncthreads();
-      if (tid < R) {
-        float s = 0.f;
-        for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
-        sm.qp[tid] = s;
-      }
-      __syncthreads();
+      sm.qpart[sl * R + c] = s;
     }
+    __syncthreads();
+    if (tid < R) {
+      float s = 0.f;
+      for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
+      sm.qp[tid] = s;
+    }
+    __syncthreads();
   } else {
     // MLA: the selection query qp = P^T sum_h q_abs[b,h] comes precomputed
     if (tid < R) sm.qp[tid] = qsel[int64_t(b) * R + tid];
@@ -258,8 +267,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   // buffer whose loads are in flight would wait for them): while one tile's
   // scores are computed, the loads of the next kDepth - 1 tiles are in flight.
   static_assert(TPW % kDepth == 0, "tiles are streamed in groups of kDepth");
-#pragma unroll
-  for (int u = 1; u < kDepth - 1; ++u) load_tile(u, bufs[u]);
   for (int tile = 0; tile < TPW; tile += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
