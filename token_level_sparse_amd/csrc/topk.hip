@@ -92,6 +92,10 @@ struct FinalSmem {
 // row's query heads over the selected tokens, read in place, and writes the
 // normalised outputs and log-sum-exps (split-K with one split): the indices
 // never make a round trip through memory before the attention reads them.
+// hs blocks share a row: each makes the same (deterministic) selection and
+// attends for its own heads hpb*h .. hpb*h+hpb-1 of the row's group; only
+// the first writes the indices. A row's blocks are 8 launch positions apart,
+// so they land on one XCD and share its L2 for the candidates and K/V rows.
 struct AttendArgs {
   GqaDev g;
   const uint16_t* q;
@@ -100,6 +104,7 @@ struct AttendArgs {
   float scale;
   float* out;
   float* lse;
+  int hs, hpb;                                          // blocks per row, heads per block
 };
 constexpr int kAttendMaxK = 512;
 
@@ -112,7 +117,19 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   __shared__ FinalSmem<NT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ng = (segs.nseg + gs - 1) / gs;
-  const int row = blockIdx.x / ng, grp = blockIdx.x % ng;
+  int row = blockIdx.x / ng, grp = blockIdx.x % ng;
+  int hsplit = 0;                                       // this block's head share (GT > 0)
+  if constexpr (GT > 0) {
+    const int hs = at.hs, lin = blockIdx.x;
+    if (hs > 1 && (gridDim.x / hs) % 8 == 0) {          // lin = (q*hs + hsplit)*8 + row % 8
+      row = (lin / (8 * hs)) * 8 + lin % 8;
+      hsplit = (lin / 8) % hs;
+    } else {
+      row = lin / hs;
+      hsplit = lin % hs;
+    }
+    grp = 0;
+  }
   const int Tb = row_len(max_seq, seq_lens, row / H);
   const int need_all = MERGE ? k : min(k, Tb);
   const int s0 = grp * gs;
@@ -309,6 +326,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   // per page of candidates, one ranking the tied candidates and one placing
   // the taken ones.
   int32_t* dst = MERGE ? outs.idx + (int64_t(row) * ng + grp) * outs.cap : out + int64_t(row) * k;
+  const bool write_idx = MERGE || hsplit == 0;
   uint32_t* dkey = MERGE ? outs.key + (int64_t(row) * ng + grp) * outs.cap : nullptr;
   int tie_base = 0, out_base = 0;
   __shared__ int32_t sel[GT > 0 ? kAttendMaxK : 1];   // the selected tokens, for the attention
@@ -337,7 +355,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       if (take >> e & 1u) {
         if constexpr (MERGE) dkey[at] = ck[e];
         if constexpr (GT > 0) sel[at] = ci[e];
-        dst[at++] = ci[e];
+        if (write_idx) dst[at] = ci[e];
+        ++at;
       }
     tie_base += tt;
     out_base += st;
@@ -354,7 +373,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   if constexpr (MERGE) {
     if (tid == 0) outs.cnt[int64_t(row) * ng + grp] = out_base;
   } else {
-    for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+    if (write_idx)
+      for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
   }
   if constexpr (GT > 0) {
     constexpr int STEPS = 8, RB = STEPS * 4;
@@ -364,8 +384,9 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     const float qs = at.scale * kAttnLog2e;
     __shared__ AttnMergeSmem<GT, NW> msm;
     __syncthreads();                                    // sel complete
-    for (int hg = 0; hg * GT < g.G; ++hg) {
-      const int h0 = j * g.G + hg * GT, nh = min(GT, g.G - hg * GT);
+    const int hb0 = hsplit * at.hpb, hb1 = min(g.G, hb0 + at.hpb);   // heads of this block
+    for (int hl = hb0; hl < hb1; hl += GT) {
+      const int h0 = j * g.G + hl, nh = min(GT, hb1 - hl);
       bf16x2 qv[GT][4];
       attn_load_q<GT>(qv, at.q, int64_t(b) * g.Hq + h0, nh, lane & 15);
       AttnAcc<GT> A;
@@ -461,13 +482,20 @@ hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uin
                                 hipStream_t st) {
   if (segs.nseg > kMaxSeg || !select_attend_fused(segs.nseg, k, g.G)) return hipErrorInvalidValue;
   const int rows = g.B * g.Hkv;
-  const AttendArgs aa{g, q, K, V, scale, out, lse};
-  // query heads per pass over the selected rows: the whole group when it has
-  // 1, 2 or 5 heads (or 10, 15), else 4 at a time
-  const int gt = g.G <= 2 ? g.G : (g.G % 5 == 0 ? 5 : 4);
+  // Spread the row's query heads over hs blocks until the launch covers the
+  // CUs (256 blocks); the selection is repeated per block, the attention
+  // (the larger part) is split.
+  int hs = 1;
+  while (rows * hs < 256 && hs < g.G) ++hs;
+  const int hpb = (g.G + hs - 1) / hs;
+  hs = (g.G + hpb - 1) / hpb;
+  const AttendArgs aa{g, q, K, V, scale, out, lse, hs, hpb};
+  // query heads per pass over the selected rows: all of the block's heads
+  // when they are 1, 2 or 5 (or 10, 15), else 4 at a time
+  const int gt = hpb <= 2 ? hpb : (hpb % 5 == 0 ? 5 : 4);
 #define JSSA_FA(GT)                                                                                      \
-  hipLaunchKernelGGL((final_kernel<512, 16, false, GT>), dim3(rows), dim3(512), 0, st, g.Hkv, g.max_seq,   \
-                     g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa)
+  hipLaunchKernelGGL((final_kernel<512, 16, false, GT>), dim3(rows * hs), dim3(512), 0, st, g.Hkv,         \
+                     g.max_seq, g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa)
   switch (gt) {
     case 1: JSSA_FA(1); break;
     case 2: JSSA_FA(2); break;
