@@ -288,14 +288,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
   }
   if constexpr (FUSED) {
+    __shared__ Top2Smem<NT> tsm;
     uint32_t key[TPW];
 #pragma unroll
     for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*TPW + e
-    __syncthreads();                                     // stage is reused below
-    ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
     int n = Tb - t_begin;
     n = n < 0 ? 0 : (n > chunk ? chunk : n);
-    chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+    if (n == chunk && fo.k <= NT) {                      // block-uniform; the stage stays intact
+      chunk_select_top2<NT, TPW>(key, t_begin, fo.k, tsm, stage, SS, fo.segs, seg);
+    } else {
+      __syncthreads();                                   // stage is reused below
+      ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
+      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+    }
   }
 }
 

@@ -229,6 +229,96 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   if (tid == 0) out.cnt[seg] = tot;
 }
 
+constexpr int kTop2Bins = 256;
+
+template <int NT>
+struct Top2Smem {
+  uint32_t hist[kTop2Bins];
+  ScanSmem<NT> scan;
+  uint32_t red[2][NT / 64];
+  int res[2];
+};
+
+// Chunk-local selection for a full chunk (every one of the NT*E tokens real)
+// with k <= NT, whose keys also stay readable in LDS: key e of thread tid is
+// score_key(stage[e * SS + tid]), token base + tid*E + e. Same contract as
+// chunk_select, with a cheaper threshold.
+//
+// Let M be the multiset of every thread's two largest keys (2*NT values).
+// Any c with at least k values of M at or above it is at or below the
+// chunk's k-th largest key, since the values of M are distinct tokens'
+// keys. c is taken as the lower edge of the bin, in a linear histogram of M
+// over [min M, max M], that holds M's k-th largest value: two LDS atomics
+// per thread instead of a pass over all keys. Tokens above the chunk's k-th
+// key that M misses (a thread's third best and lower) are the only ones that
+// make c looser than the exact k-th key, and there are few: for Gaussian
+// scores, k = 256 and 8192 tokens, about 295 keys are kept on average.
+//
+// The kept keys are marked in a per-thread bit mask; a thread then visits
+// only its set bits, re-reading each key from LDS, instead of running a
+// divergent branch for every key.
+template <int NT, int E>
+__device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top2Smem<NT>& sm,
+                                  const float* stage, int SS, CandSegs out, int64_t seg) {
+  static_assert(E <= 32, "one mask bit per key");
+  static_assert(kTop2Bins == NT, "one histogram bin per thread");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t x = key[e];
+    const uint32_t y = x < m1 ? x : m1;
+    m2 = y > m2 ? y : m2;
+    m1 = x > m1 ? x : m1;
+  }
+  uint32_t hi = m1, lo = m2;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t a = uint32_t(__shfl_xor(int(hi), o, 64));
+    const uint32_t b = uint32_t(__shfl_xor(int(lo), o, 64));
+    hi = a > hi ? a : hi;
+    lo = b < lo ? b : lo;
+  }
+  if (lane == 0) {
+    sm.red[0][wv] = hi;
+    sm.red[1][wv] = lo;
+  }
+  sm.hist[tid] = 0u;
+  __syncthreads();
+  hi = sm.red[0][0];
+  lo = sm.red[1][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
+    lo = sm.red[1][i] < lo ? sm.red[1][i] : lo;
+  }
+  const uint32_t range = hi - lo;                 // M lies in [lo, hi]
+  const int sh = range < uint32_t(kTop2Bins) ? 0 : (32 - __builtin_clz(range)) - 8;
+  atomicAdd(&sm.hist[(m1 - lo) >> sh], 1u);
+  atomicAdd(&sm.hist[(m2 - lo) >> sh], 1u);
+  __syncthreads();
+  pick_bin<NT, 1>(sm.hist, k, true, sm.scan, sm.res);
+  const uint32_t c = lo + (uint32_t(sm.res[0]) << sh);
+
+  uint32_t mask = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mask |= key[e] >= c ? (1u << e) : 0u;
+  const int mine = __builtin_popcount(mask);
+  int tot;
+  int at = block_scan<NT>(mine, sm.scan, &tot) - mine;
+  uint32_t* okey = out.key + seg * out.cap;
+  int32_t* oidx = out.idx + seg * out.cap;
+  while (mask) {
+    const int e = __builtin_ctz(mask);
+    mask &= mask - 1u;
+    okey[at] = score_key(stage[e * SS + tid]);
+    oidx[at] = base + tid * E + e;
+    ++at;
+  }
+  if (tid == 0) out.cnt[seg] = tot;
+}
+
 // Per-row final selection over candidate segments (merging groups of
 // segments first when a row's list is long). merge_ws: merge_workspace_bytes.
 size_t merge_workspace_bytes(int rows, int nseg, int k);
