@@ -225,11 +225,37 @@ def test_sparse_step_fused(J, PL, cfg, k, S):
     _sparse_and_check(J, PL, inp, k, S, fused=True)
 
 
-@pytest.mark.parametrize("case", ["ragged32", "r48_paged_k2048", "r128_k4096", "tiny_k1", "r16_T100"])
+FULL16K = replace(synth.LLAMA8B_32K, B=1, T=16384, seed=84)
+
+
+@pytest.mark.parametrize("case", ["ragged32", "r48_paged_k2048", "r128_k4096", "tiny_k1", "r16_T100",
+                                  "full_k64", "full_k256_ties", "full_all_equal", "full_k257",
+                                  "paged_full_invalid"])
 def test_score_topk_fused_equals_split(J, PL, case):
     """The fused score + top-k pass returns exactly the indices (and, when
-    asked, the scores) of jssa_score followed by jssa_topk."""
-    if case == "ragged32":
+    asked, the scores) of jssa_score followed by jssa_topk. The full_* and
+    paged_full_* cases fill every 8192-token chunk, which takes the fused
+    kernel's top-two bound path for k <= 256 (ties, all-equal scores, -inf
+    tokens behind invalid pages) and the general path for k = 257."""
+    edit = None
+    if case.startswith("full_"):
+        inp = synth.make_gqa(FULL16K)
+        k = {"full_k64": 64, "full_k256_ties": 256, "full_all_equal": 200, "full_k257": 257}[case]
+        if case == "full_k256_ties":      # 37 distinct projected keys per (b, j): long runs of equal scores
+            edit = lambda c: c.Kp.copy_(c.Kp[:, :, torch.arange(c.Kp.shape[2], device=c.Kp.device) % 37])
+        elif case == "full_all_equal":
+            edit = lambda c: c.Kp.zero_()
+    elif case == "paged_full_invalid":
+        inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=16384, len_lo=16384, len_hi=16384, seed=85))
+        k = 256
+        table = inp.page_table.copy()
+        table[0, 7] = -1
+        table[0, 600] = -1
+        table[1, 1000] = inp.num_pages + 3
+
+        def edit(c):
+            c.page_table.copy_(torch.from_numpy(table).cuda())
+    elif case == "ragged32":
         inp, k = ragged_inputs(), 256
     elif case == "r48_paged_k2048":
         inp, k = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=40000, len_lo=20000, len_hi=40000, seed=81)), 2048
@@ -241,6 +267,9 @@ def test_score_topk_fused_equals_split(J, PL, case):
         inp, k = synth.make_gqa(replace(synth.TINY, r=16, T=100, seed=83)), 60
     c = PL.GqaCache(inp)
     c.project()
+    if edit is not None:
+        edit(c)
+        torch.cuda.synchronize()
     a = PL.SparseStep(c, k=k, fused=False)
     a.score()
     a.topk()
