@@ -39,6 +39,21 @@ R8 MLA: keys are [W_uk[h] c[:512]; c[512:]], values c[:512], output
    W_uv[h] (sum_t p_t c_t[:512]); the selection score projects the summed
    absorbed query [W_uk[h]^T q_nope; q_rope] and the latent row through one
    rank-r basis; one selected set per sequence.
+R9 subspace calibration ([JSSA-A]: the subspace minimises a token-score
+   preservation error, which is bounded by a marginal objective with a
+   closed-form spectral solution; the formulas are not on the pages). The
+   error of one (query, key) pair is e = qbar^T k - qbar^T P P^T k =
+   qbar^T Q k with Q = I - P P^T, qbar the group-summed query. Since Q is a
+   projector, |e| = |(Q qbar)^T (Q k)| <= |Q qbar| |Q k| <= (lam |Q qbar|^2 +
+   |Q k|^2 / lam) / 2 for any lam > 0 (Cauchy-Schwarz, then AM-GM), so
+   E|e| <= tr(Q (lam S_q + S_k / lam)) / 2 with S_q = E[qbar qbar^T] and
+   S_k = E[k k^T]: a bound that depends on the two marginal second moments
+   only and is linear in Q. Over orthonormal P [d,r] it is smallest when P
+   spans the top-r eigenvectors of M = lam S_q + S_k / lam (Ky Fan). lam =
+   sqrt(tr S_k / tr S_q) makes the two terms equal at P = 0; up to a
+   positive factor M is then S_q / tr S_q + S_k / tr S_k. Columns are
+   ordered by descending eigenvalue, each signed so that its entry of
+   largest magnitude (first such index on a tie) is positive.
 """
 from __future__ import annotations
 
@@ -232,3 +247,81 @@ def mla_attend_explicit(q_nope_bits, q_rope_bits, W_uk_bits, W_uv_bits, C_rows_b
         o[h] = Wv[h] @ o_lat[h]
         lse[h] = m + np.log(w.sum())
     return o, o_lat, lse
+
+
+# ---------------------------------------------------------------------------
+# Subspace calibration (R9)  [JSSA-A]; [JSSA-I] (queries and keys kept
+# together; oracle top-k recall as the measure of ranking quality);
+# [JSSA-P] (the marginal bound controls the exact score error)
+# ---------------------------------------------------------------------------
+def key_second_moment(K_rows_bits) -> np.ndarray:
+    """S_k = mean over the rows k of K [n, d] of k k^T (fp64); zeros if n = 0."""
+    K = bf16_to_f64(K_rows_bits).reshape(-1, np.asarray(K_rows_bits).shape[-1])
+    if K.shape[0] == 0:
+        return np.zeros((K.shape[1], K.shape[1]))
+    return K.T @ K / K.shape[0]
+
+
+def query_second_moment(q_samples_bits, j: int, G: int) -> np.ndarray:
+    """S_q = mean over samples n of qbar_n qbar_n^T, qbar_n = sum of the query
+    heads of KV head j's group in sample n (q [N, Hq, d], bf16 bits)."""
+    q = bf16_to_f64(q_samples_bits)[:, group_heads(j, G), :].sum(axis=1)   # [N, d]
+    if q.shape[0] == 0:
+        return np.zeros((q.shape[1], q.shape[1]))
+    return q.T @ q / q.shape[0]
+
+
+def marginal_operator(S_q, S_k) -> np.ndarray:
+    """M = S_q / tr S_q + S_k / tr S_k (R9); a zero-trace term is left out."""
+    M = np.zeros_like(np.asarray(S_q, np.float64))
+    for S in (S_q, S_k):
+        t = float(np.trace(S))
+        if t > 0:
+            M = M + np.asarray(S, np.float64) / t
+    return M
+
+
+def sign_fix(V) -> np.ndarray:
+    """Sign each column so that its entry of largest magnitude is positive."""
+    V = np.array(V, np.float64)
+    for c in range(V.shape[1]):
+        i = int(np.argmax(np.abs(V[:, c])))
+        if V[i, c] < 0:
+            V[:, c] = -V[:, c]
+    return V
+
+
+def calibrate_projection(S_q, S_k, r: int):
+    """P [d, r]: the top-r eigenvectors of the marginal operator (R9), columns
+    by descending eigenvalue, sign-fixed; also returns the r eigenvalues."""
+    M = marginal_operator(S_q, S_k)
+    w, V = np.linalg.eigh(M)                   # ascending
+    order = np.argsort(-w, kind="stable")[:r]
+    return sign_fix(V[:, order]), w[order]
+
+
+def marginal_bound(P, S_q, S_k) -> float:
+    """tr(Q (lam S_q + S_k / lam)) / 2 with Q = I - P P^T and lam =
+    sqrt(tr S_k / tr S_q): the upper bound on the mean |e| (R9)."""
+    P = np.asarray(P, np.float64)
+    Q = np.eye(P.shape[0]) - P @ P.T
+    lam = np.sqrt(np.trace(S_k) / np.trace(S_q))
+    return float(np.trace(Q @ (lam * np.asarray(S_q) + np.asarray(S_k) / lam)) / 2)
+
+
+def preservation_error(P, qbar, K) -> float:
+    """Mean over all (query, key) pairs of |qbar^T k - qbar^T P P^T k| for
+    queries qbar [Nq, d] and keys K [Nk, d] given as float arrays."""
+    P = np.asarray(P, np.float64)
+    qbar = np.asarray(qbar, np.float64)
+    K = np.asarray(K, np.float64)
+    exact = qbar @ K.T
+    approx = (qbar @ P) @ (K @ P).T
+    return float(np.abs(exact - approx).mean())
+
+
+def topk_recall(selected, reference) -> float:
+    """|selected & reference| / |reference| over the valid (>= 0) entries."""
+    a = set(int(x) for x in np.asarray(selected).ravel() if x >= 0)
+    b = set(int(x) for x in np.asarray(reference).ravel() if x >= 0)
+    return len(a & b) / len(b) if b else 1.0

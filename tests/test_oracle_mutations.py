@@ -66,8 +66,36 @@ def _mla_no_rope(qn, qr, Wk, Wv, C, scale):
     return _orig_mla(qn, np.zeros_like(qr), Wk, Wv, C, scale)
 
 
+def _marginal_unnormalised(S_q, S_k):
+    return np.asarray(S_q, np.float64) + np.asarray(S_k, np.float64)
+
+
+def _calib_bottom(S_q, S_k, r):
+    w, V = np.linalg.eigh(_orig_marginal(S_q, S_k))
+    return O.sign_fix(V[:, :r]), w[:r]
+
+
+def _query_moment_mean_heads(q_samples_bits, j, G):
+    return _orig_qmoment(q_samples_bits, j, G) / (G * G)
+
+
+def _key_moment_sum(K_rows_bits):
+    K = np.asarray(K_rows_bits)
+    return _orig_kmoment(K) * K.reshape(-1, K.shape[-1]).shape[0]
+
+
+def _bound_lam_inverted(P, S_q, S_k):
+    P = np.asarray(P, np.float64)
+    Q = np.eye(P.shape[0]) - P @ P.T
+    lam = np.sqrt(np.trace(S_q) / np.trace(S_k))
+    return float(np.trace(Q @ (lam * np.asarray(S_q) + np.asarray(S_k) / lam)) / 2)
+
+
 _orig_attend = O.attend
 _orig_mla = O.mla_attend_explicit
+_orig_marginal = O.marginal_operator
+_orig_qmoment = O.query_second_moment
+_orig_kmoment = O.key_second_moment
 
 MUTATIONS = [
     ("round_to_bf16", _truncate_bf16, [pins.test_bf16_golden_values]),
@@ -81,6 +109,11 @@ MUTATIONS = [
     ("group_heads", _group_strided, [pins.test_dense_matches_torch_sdpa]),
     ("paged_rows", _paged_swapped, [pins.test_paged_matches_contiguous]),
     ("mla_attend_explicit", _mla_no_rope, [pins.test_mla_brute_force_loops]),
+    ("marginal_operator", _marginal_unnormalised, [pins.test_calib_invariances, pins.test_calib_diagonal_closed_form]),
+    ("calibrate_projection", _calib_bottom, [pins.test_calib_diagonal_closed_form]),
+    ("query_second_moment", _query_moment_mean_heads, [pins.test_calib_second_moments_brute_force]),
+    ("key_second_moment", _key_moment_sum, [pins.test_calib_second_moments_brute_force]),
+    ("marginal_bound", _bound_lam_inverted, [pins.test_calib_minimises_bound_brute_force]),
 ]
 
 

@@ -394,3 +394,108 @@ def test_mla_score_is_summed_per_head_projection():
     Kpf = synth.bf16_bits_to_f32(Kp).astype(np.float64)
     ref = sum(Kpf @ (P.astype(np.float64).T @ qa[h]) for h in range(qa.shape[0]))
     np.testing.assert_allclose(s, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# subspace calibration (JSSA abstract on weekinpapers, Abstract: a shared
+# query-key subspace from a marginal bound on the score-preservation error
+# with a closed-form spectral solution; the reading is spelled out in the
+# oracle's header, R9)
+# ---------------------------------------------------------------------------
+def _orthonormal(rng, d, r):
+    q, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    return q
+
+
+def test_calib_second_moments_brute_force():
+    """Second moments against explicit Python loops over rows and heads."""
+    rng = np.random.default_rng(11)
+    K = bf16(rng.standard_normal((5, 4)))
+    Kf = [[O.bf16_to_f64(K[t, i]) for i in range(4)] for t in range(5)]
+    want = [[sum(float(Kf[t][a]) * float(Kf[t][b]) for t in range(5)) / 5 for b in range(4)] for a in range(4)]
+    np.testing.assert_allclose(O.key_second_moment(K), want, rtol=1e-15, atol=1e-15)
+    q = bf16(rng.standard_normal((3, 6, 4)))          # N=3 samples, Hq=6, G=3 -> 2 KV heads
+    for j in range(2):
+        qb = [[sum(float(O.bf16_to_f64(q[n, h, i])) for h in range(3 * j, 3 * j + 3)) for i in range(4)]
+              for n in range(3)]
+        want = [[sum(qb[n][a] * qb[n][b] for n in range(3)) / 3 for b in range(4)] for a in range(4)]
+        np.testing.assert_allclose(O.query_second_moment(q, j, 3), want, rtol=1e-14, atol=1e-14)
+
+
+def test_calib_diagonal_closed_form():
+    """Diagonal moments: the calibrated basis is the coordinate axes with the
+    largest a_i/sum(a) + b_i/sum(b), in that order, each +1."""
+    a = np.array([4.0, 1.0, 9.0, 0.5, 2.0, 3.5])
+    b = np.array([0.1, 6.0, 0.2, 0.3, 5.0, 0.4])
+    w = a / a.sum() + b / b.sum()
+    P, ev = O.calibrate_projection(np.diag(a), np.diag(b), 3)
+    want_axes = list(np.argsort(-w)[:3])
+    for c, ax in enumerate(want_axes):
+        e = np.zeros(6)
+        e[ax] = 1.0
+        np.testing.assert_allclose(P[:, c], e, atol=1e-12)
+        assert ev[c] == pytest.approx(w[ax], rel=1e-12)
+
+
+def test_calib_bound_holds_and_is_met_by_rank_r_data():
+    """The mean |score error| never exceeds the marginal bound (a theorem for
+    sample moments too); on data inside an r-dim subspace the calibrated basis
+    preserves every score exactly while a random one does not."""
+    rng = np.random.default_rng(12)
+    d, r = 16, 4
+    qb = rng.standard_normal((200, d)) * np.linspace(0.2, 2.0, d)
+    K = rng.standard_normal((300, d)) @ rng.standard_normal((d, d)) / 4
+    Sq, Sk = qb.T @ qb / 200, K.T @ K / 300
+    Pc, _ = O.calibrate_projection(Sq, Sk, r)
+    for P in [Pc] + [_orthonormal(rng, d, r) for _ in range(5)]:
+        assert O.preservation_error(P, qb, K) <= O.marginal_bound(P, Sq, Sk) * (1 + 1e-12)
+    B = _orthonormal(rng, d, r)                            # the data's subspace
+    qb = rng.standard_normal((50, r)) @ B.T
+    K = rng.standard_normal((80, r)) @ B.T
+    Sq, Sk = qb.T @ qb / 50, K.T @ K / 80
+    Pc, _ = O.calibrate_projection(Sq, Sk, r)
+    assert O.preservation_error(Pc, qb, K) < 1e-12
+    assert abs(O.marginal_bound(Pc, Sq, Sk)) < 1e-12
+    assert O.preservation_error(_orthonormal(rng, d, r), qb, K) > 1e-2
+
+
+def test_calib_minimises_bound_brute_force():
+    """d = 3, r = 1: a dense search over unit vectors on the half sphere finds
+    no basis with a smaller marginal bound than the calibrated one, and the
+    best grid point lies next to it."""
+    rng = np.random.default_rng(13)
+    A = rng.standard_normal((3, 3))
+    Bm = rng.standard_normal((3, 3))
+    Sq, Sk = A @ A.T, Bm @ Bm.T * 3
+    Pc, _ = O.calibrate_projection(Sq, Sk, 1)
+    best, arg = np.inf, None
+    for th in np.linspace(0, np.pi / 2, 181):
+        for ph in np.linspace(0, 2 * np.pi, 721):
+            v = np.array([[np.sin(th) * np.cos(ph)], [np.sin(th) * np.sin(ph)], [np.cos(th)]])
+            val = O.marginal_bound(v, Sq, Sk)
+            if val < best:
+                best, arg = val, v
+    assert O.marginal_bound(Pc, Sq, Sk) <= best + 1e-12
+    assert abs(float(arg[:, 0] @ Pc[:, 0])) > 0.999
+
+
+def test_calib_invariances():
+    """Scaling either moment leaves the basis unchanged (trace-normalised
+    operator); the basis is orthonormal and sign-fixed."""
+    rng = np.random.default_rng(14)
+    A = rng.standard_normal((8, 8))
+    Bm = rng.standard_normal((8, 3))
+    Sq, Sk = A @ A.T, Bm @ Bm.T + 0.1 * np.eye(8)
+    P1, _ = O.calibrate_projection(Sq, Sk, 3)
+    P2, _ = O.calibrate_projection(7.0 * Sq, 0.01 * Sk, 3)
+    np.testing.assert_allclose(P1, P2, atol=1e-10)
+    np.testing.assert_allclose(P1.T @ P1, np.eye(3), atol=1e-12)
+    for c in range(3):
+        i = int(np.argmax(np.abs(P1[:, c])))
+        assert P1[i, c] > 0
+
+
+def test_topk_recall_hand_values():
+    assert O.topk_recall([1, 2, 3, -1], [2, 3, 4, 5]) == 0.5
+    assert O.topk_recall([7, 8], [8, 7]) == 1.0
+    assert O.topk_recall([-1, -1], [-1, -1]) == 1.0

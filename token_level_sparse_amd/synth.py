@@ -15,7 +15,8 @@ a GQA KV cache; the digest on ai4snews, "Perspective": the model roster).
 Random streams: one numpy PCG64 stream per (seed, tensor id, index...), so a
 batch of 4 is a prefix of a batch of 16 and units can be drawn in parallel.
 Tensor ids: 0 key basis A, 1 keys, 2 queries, 3 values, 4 projection P,
-5 lengths and page tables, 6 MLA weights and queries.
+5 lengths and page tables, 6 MLA weights and queries, 7 calibration query
+samples.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-T_A, T_KEYS, T_Q, T_V, T_P, T_LEN, T_MLA = range(7)
+T_A, T_KEYS, T_Q, T_V, T_P, T_LEN, T_MLA, T_CALQ = range(8)
 LATENT_RANK = 24          # rank of the key/query basis A
 NOISE = 0.3               # isotropic noise added to keys and queries
 SINKS = 4                 # positions 0..3 carry keys scaled by SINK_SCALE
@@ -134,6 +135,19 @@ def gen_queries(cfg: GqaConfig) -> np.ndarray:
             w = g.standard_normal(LATENT_RANK)
             eps = g.standard_normal(cfg.d)
             q[b, h] = f32_to_bf16_bits(bases[h // cfg.G] @ w + NOISE * eps)
+    return q
+
+
+def gen_calib_queries(cfg: GqaConfig, n: int) -> np.ndarray:
+    """n decode-query samples [n, Hq, d] (bf16 bits) drawn like gen_queries
+    (basis of the head's KV group times a fresh latent, plus noise), from a
+    stream of their own: the sample set a subspace is calibrated on."""
+    q = np.empty((n, cfg.Hq, cfg.d), np.uint16)
+    for h in range(cfg.Hq):
+        g = stream(cfg.seed, T_CALQ, h)
+        w = g.standard_normal((n, LATENT_RANK))
+        eps = g.standard_normal((n, cfg.d))
+        q[:, h] = f32_to_bf16_bits(w @ key_basis(cfg, h // cfg.G).T + NOISE * eps)
     return q
 
 
