@@ -53,7 +53,8 @@ enum {
   JSSA_ERR_UNSUPPORTED = 3, /* a size outside the supported set below */
   JSSA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
   JSSA_ERR_WORKSPACE = 5,   /* workspace smaller than jssa_topk_workspace_size */
-  JSSA_ERR_HIP = 6          /* the HIP runtime reported an error */
+  JSSA_ERR_HIP = 6,         /* the HIP runtime reported an error */
+  JSSA_ERR_NUMERIC = 7      /* a host numerical routine did not converge */
 };
 
 /*
@@ -314,6 +315,64 @@ JSSA_API jssa_status jssa_mla_indexed_decode(const jssa_mla_desc* desc, const fl
  */
 JSSA_API jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const void* W_uv,
                           float* out, void* stream);
+
+/*
+ * Subspace calibration (JSSA abstract on weekinpapers, Abstract: the shared
+ * query-key subspace minimises a token-score preservation error through a
+ * marginal upper bound that has a closed-form spectral solution; the
+ * formulas are not on the pages). Reading used here: the error of a (query,
+ * key) pair is e = qbar^T (I - P P^T) k for the group-summed query qbar;
+ * Cauchy-Schwarz and AM-GM bound its mean by
+ * tr((I - P P^T)(lam S_q + S_k / lam)) / 2, with S_q = E[qbar qbar^T],
+ * S_k = E[k k^T], lam = sqrt(tr S_k / tr S_q). The bound is smallest for P =
+ * the top-r eigenvectors of M = S_q / tr S_q + S_k / tr S_k. These calls
+ * compute S_k and S_q per KV head on the GPU and P on the host; P [Hkv,d,r]
+ * from jssa_calib_projection (one head per call) is the projection that
+ * jssa_project_keys / jssa_score take. Offline: not part of a decode step.
+ */
+
+/* Workspace of jssa_calib_key_moments, in bytes (depends on desc->Hkv only). */
+JSSA_API jssa_status jssa_calib_workspace_size(const jssa_gqa_desc* desc, size_t* bytes);
+
+/*
+ * Key second moments over the cache:
+ *   moments[j] = (1/N_j) sum_{b, t < T_b, page valid} K[b,j,t] K[b,j,t]^T
+ * with N_j the number of those tokens (a zero matrix when N_j = 0).
+ *  K        device bf16, layout of desc (contiguous or paged, d = 128)
+ *  moments  device fp32 [Hkv,128,128], written (symmetric)
+ *  ws       device workspace of jssa_calib_workspace_size bytes (partials;
+ *           its contents need no initialisation and are overwritten)
+ * bf16 products are exact; sums are fp32 (MFMA accumulation, then a fixed-
+ * order sum of per-wave partials), so repeated calls give identical bits.
+ * desc->r is not used.
+ */
+JSSA_API jssa_status jssa_calib_key_moments(const jssa_gqa_desc* desc, const void* K, float* moments, void* ws,
+                                            size_t ws_bytes, void* stream);
+
+/*
+ * Query second moments over N decode-query samples:
+ *   moments[j] = (1/N) sum_n qbar_n qbar_n^T, qbar_n = sum_{h in group j} q[n,h]
+ *  q        device bf16 [N,Hq,128]; Hq a multiple of Hkv, Hq/Hkv <= 16
+ *  moments  device fp32 [Hkv,128,128], written
+ * qbar is summed in fp32; the outer products accumulate in fp32.
+ */
+JSSA_API jssa_status jssa_calib_query_moments(int32_t N, int32_t Hq, int32_t Hkv, const void* q, float* moments,
+                                              void* stream);
+
+/*
+ * Spectral step, HOST pointers (no GPU work): P = the top-r eigenvectors of
+ * M = S_q / tr S_q + S_k / tr S_k (a term with zero trace is left out),
+ * computed in fp64 by cyclic Jacobi rotations.
+ *  S_q, S_k  host fp32 [d,d] (symmetric)
+ *  P         host fp32 [d,r] row-major, written: orthonormal columns by
+ *            descending eigenvalue, each signed so that its entry of largest
+ *            magnitude (the first on a tie) is positive
+ *  eigvals   host fp64 [r] or NULL: the r eigenvalues of M
+ * JSSA_ERR_SHAPE if both traces are zero, JSSA_ERR_NUMERIC if the rotations
+ * do not converge.
+ */
+JSSA_API jssa_status jssa_calib_projection(int32_t d, int32_t r, const float* S_q, const float* S_k, float* P,
+                                           double* eigvals);
 
 /* Diagnostics (host only). */
 JSSA_API const char* jssa_status_string(jssa_status s);

@@ -106,3 +106,49 @@ def test_combine_and_mla_validation(J):
     assert _status(J.jssa_mla_absorb_q, m_ok, A, A, A, None, A, A) == J.ERR_NULL
     assert _status(J.jssa_mla_indexed_decode, m_ok, A, A, A, 2048, 0, 0.1, A, A) == J.ERR_SHAPE
     assert _status(J.jssa_mla_up_v, m_ok, A, None, A) == J.ERR_NULL
+
+
+def test_calib_validation(J):
+    ok = J.gqa_desc(2, 32, 8, 32, 4096)
+    need = J.jssa_calib_workspace_size(ok)
+    assert need > 0
+    assert _status(J.jssa_calib_key_moments, ok, A, A, A, need - 1) == J.ERR_WORKSPACE
+    assert _status(J.jssa_calib_key_moments, ok, None, A, A, need) == J.ERR_NULL
+    assert _status(J.jssa_calib_key_moments, ok, A, MIS, A, need) == J.ERR_ALIGN
+    assert _status(J.jssa_calib_query_moments, 0, 32, 8, A, A) == J.ERR_SHAPE
+    assert _status(J.jssa_calib_query_moments, 16, 30, 8, A, A) == J.ERR_SHAPE
+    import numpy as np
+    with pytest.raises(J.JssaError) as e:
+        J.jssa_calib_projection(np.eye(8), np.eye(8), 9)
+    assert e.value.status == J.ERR_SHAPE
+    with pytest.raises(J.JssaError) as e:
+        J.jssa_calib_projection(np.zeros((8, 8)), np.zeros((8, 8)), 2)
+    assert e.value.status == J.ERR_SHAPE
+    assert J.jssa_status_string(J.ERR_NUMERIC) == "numerical routine did not converge"
+
+
+def test_calib_projection_host_matches_oracle(J):
+    """The library's host spectral step (cyclic Jacobi) against the oracle's
+    (numpy eigh of the same marginal operator): eigenvalues, the spanned
+    subspace, orthonormality, and the closed-form diagonal case."""
+    import numpy as np
+    from oracle import jssa_oracle as O
+    rng = np.random.default_rng(21)
+    for d, r, rank_k in ((128, 32, 24), (128, 16, 128), (40, 8, 5)):
+        A_ = rng.standard_normal((d, d)) / np.sqrt(d)
+        B_ = rng.standard_normal((d, rank_k))
+        Sq = (A_ @ A_.T).astype(np.float32)
+        Sk = (B_ @ B_.T / rank_k + 0.09 * np.eye(d)).astype(np.float32)
+        P, w = J.jssa_calib_projection(Sq, Sk, r)
+        Po, wo = O.calibrate_projection(Sq.astype(np.float64), Sk.astype(np.float64), r)
+        np.testing.assert_allclose(w, wo, rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(P.astype(np.float64).T @ P, np.eye(r), atol=2e-6)
+        np.testing.assert_allclose(P @ P.T, Po @ Po.T, atol=2e-5)
+    a = np.array([4.0, 1.0, 9.0, 0.5, 2.0, 3.5], np.float32)
+    b = np.array([0.1, 6.0, 0.2, 0.3, 5.0, 0.4], np.float32)
+    P, _ = J.jssa_calib_projection(np.diag(a), np.diag(b), 3)
+    wgt = a / a.sum() + b / b.sum()
+    for c, ax in enumerate(np.argsort(-wgt)[:3]):
+        e = np.zeros(6, np.float32)
+        e[ax] = 1.0
+        np.testing.assert_allclose(P[:, c], e, atol=1e-7)

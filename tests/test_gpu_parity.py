@@ -490,6 +490,121 @@ def test_invalid_page_entries_are_absent(J, PL):
 
 
 # ---------------------------------------------------------------------------
+# subspace calibration: second moments (GPU), spectral step (host library),
+# oracle top-k recall of the calibrated subspace
+# ---------------------------------------------------------------------------
+def _valid_key_rows(inp, j):
+    """Every valid token's key row of KV head j (all sequences), skipping
+    tokens behind page-table entries outside [0, num_pages)."""
+    out = []
+    for b in range(inp.cfg.B):
+        n = int(inp.seq_lens[b])
+        if inp.page_table is None:
+            out.append(inp.K[b, j, :n])
+            continue
+        t = np.arange(n)
+        pg = inp.page_table[b][t // 16]
+        t = t[(pg >= 0) & (pg < inp.num_pages)]
+        out.append(O.paged_rows(inp.K, inp.page_table[b], j, t))
+    return np.concatenate(out, axis=0) if out else np.zeros((0, 128), np.uint16)
+
+
+def _moment_limit(S_ref, n_chain):
+    """Worst-case fp32 summation error of a mean of products x_a x_b over a
+    chain of n_chain roundings: n_chain * 2^-24 * mean|x_a x_b|, and
+    mean|x_a x_b| <= sqrt(S_aa S_bb) (Cauchy-Schwarz)."""
+    dg = np.sqrt(np.abs(np.diag(S_ref)))
+    return 1.01 * (n_chain + 2) * 2.0 ** -24 * np.outer(dg, dg) + 1e-30
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "paged_invalid", "llama32k"])
+def test_calib_key_moments(J, PL, case):
+    if case == "tiny":
+        inp = synth.make_gqa(synth.TINY)
+    elif case == "ragged":
+        inp = ragged_inputs()
+    elif case == "paged_invalid":
+        inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=3, T=20000, len_lo=1, len_hi=20000, seed=91))
+        inp.page_table[0, 2] = -1
+        inp.page_table[1, 0] = inp.num_pages + 7
+    else:
+        inp = synth.make_gqa(synth.LLAMA8B_32K)
+    c = PL.GqaCache(inp)
+    got = _np(PL.calib_key_moments(c))
+    again = _np(PL.calib_key_moments(c))
+    np.testing.assert_array_equal(got, again)              # fixed-order sums: same bits
+    cfg = inp.cfg
+    npb = max(1, 512 // cfg.Hkv)
+    units = cfg.B * ((cfg.T + 8191) // 8192)
+    n_chain = 32 * ((units + npb - 1) // npb) * 64 + npb * 4    # MFMA adds per wave + partial slots
+    for j in range(cfg.Hkv):
+        ref = O.key_second_moment(_valid_key_rows(inp, j))
+        err = np.abs(got[j] - ref)
+        assert np.all(err <= _moment_limit(ref, n_chain)), f"head {j}: max err {err.max():.3g}"
+        np.testing.assert_array_equal(got[j], got[j].T)
+
+
+def test_calib_query_moments(J, PL):
+    cfg = synth.LLAMA8B_32K
+    qs = synth.gen_calib_queries(cfg, 1000)                # 1000: a partial last batch of 64
+    got = _np(PL.calib_query_moments(torch.from_numpy(qs.view(np.int16)).cuda(), cfg.Hkv))
+    for j in range(cfg.Hkv):
+        ref = O.query_second_moment(qs, j, cfg.G)
+        err = np.abs(got[j] - ref)
+        assert np.all(err <= _moment_limit(ref, 1000 + cfg.G)), f"head {j}: max err {err.max():.3g}"
+
+
+def test_calib_end_to_end_recall(J, PL):
+    """Calibrate on the GPU, check the basis against the oracle through the
+    bound it minimises, then select with it: the indices obey the parity
+    rule for that basis, and they recover far more of the exact (full-width)
+    top-k than the random orthonormal basis does."""
+    cfg, k, r = synth.LLAMA8B_32K, 256, 32
+    inp = synth.make_gqa(cfg)
+    qs = synth.gen_calib_queries(cfg, 2048)
+    c = PL.GqaCache(inp)
+    P_cal, ev = PL.calibrate(c, torch.from_numpy(qs.view(np.int16)).cuda(), r)
+    Pn = _np(P_cal).astype(np.float64)
+    for j in range(cfg.Hkv):
+        Sk = O.key_second_moment(inp.K[0, j])
+        Sq = O.query_second_moment(qs, j, cfg.G)
+        Po, wo = O.calibrate_projection(Sq, Sk, r)
+        np.testing.assert_allclose(Pn[j].T @ Pn[j], np.eye(r), atol=2e-6)
+        assert O.marginal_bound(Pn[j], Sq, Sk) <= O.marginal_bound(Po, Sq, Sk) * (1 + 1e-4)
+        np.testing.assert_allclose(ev[j], wo, rtol=2e-4)
+        # the well-separated signal subspace (rank 24 in the synthetic keys) is the same one
+        P24 = Pn[j][:, :24]
+        np.testing.assert_allclose(P24 @ P24.T, Po[:, :24] @ Po[:, :24].T, atol=2e-3)
+    # selection with the calibrated basis (fp32 P as stored)
+    c.P = P_cal.contiguous()
+    c.project()
+    cal = PL.SparseStep(c, k=k, fused=True)
+    cal.score_topk()
+    # exact top-k: full-width scores, i.e. rank 128 with P = I on K itself
+    eye = torch.eye(128, dtype=torch.float32, device="cuda").repeat(cfg.Hkv, 1, 1).contiguous()
+    d_exact = J.gqa_desc(cfg.B, cfg.Hq, cfg.Hkv, 128, cfg.T, seq_lens=c.seq_lens)
+    idx_exact = torch.empty((cfg.B, cfg.Hkv, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(J.jssa_score_topk_workspace_size(d_exact, k), dtype=torch.uint8, device="cuda")
+    J.jssa_score_topk(d_exact, c.q, eye, c.K, k, None, idx_exact, ws)
+    rnd_c = PL.GqaCache(inp)
+    rnd_c.project()
+    rnd = PL.SparseStep(rnd_c, k=k, fused=True)
+    rnd.score_topk()
+    torch.cuda.synchronize()
+    gi, ge, gr = _np(cal.idx), _np(idx_exact), _np(rnd.idx)
+    rec_cal, rec_rnd = [], []
+    for j in range(cfg.Hkv):
+        hs = list(O.group_heads(j, cfg.G))
+        K = inp.K[0, j]
+        U.check_indices(gi[0, j], O.subspace_scores(inp.q[0, hs], Pn[j], O.project_keys(K, Pn[j])), k)
+        U.check_indices(ge[0, j], O.subspace_scores(inp.q[0, hs], np.eye(128), K), k)
+        rec_cal.append(O.topk_recall(gi[0, j], ge[0, j]))
+        rec_rnd.append(O.topk_recall(gr[0, j], ge[0, j]))
+    assert np.mean(rec_cal) >= 0.85, rec_cal
+    assert np.mean(rec_cal) >= np.mean(rec_rnd) + 0.4, (rec_cal, rec_rnd)
+
+
+# ---------------------------------------------------------------------------
 # MLA
 # ---------------------------------------------------------------------------
 def test_mla_parity(J, PL):

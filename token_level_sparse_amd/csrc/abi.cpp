@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <vector>
 
 #include "internal.hpp"
 
@@ -125,6 +126,7 @@ const char* jssa_status_string(jssa_status s) {
     case JSSA_ERR_ALIGN: return "misaligned pointer";
     case JSSA_ERR_WORKSPACE: return "workspace too small";
     case JSSA_ERR_HIP: return "HIP runtime error";
+    case JSSA_ERR_NUMERIC: return "numerical routine did not converge";
     default: return "unknown status";
   }
 }
@@ -386,6 +388,60 @@ jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const v
   return hip_status(jssa::launch_mla_up_v(to_mla(desc), o_lat, static_cast<const uint16_t*>(W_uv),
                                           out, S(stream)),
                     __func__);
+}
+
+jssa_status jssa_calib_workspace_size(const jssa_gqa_desc* desc, size_t* bytes) {
+  if (jssa_status s = check_desc(__func__, desc, false)) return s;
+  if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
+  *bytes = jssa::calib_workspace_bytes(desc->Hkv);
+  return JSSA_OK;
+}
+
+jssa_status jssa_calib_key_moments(const jssa_gqa_desc* desc, const void* K, float* moments, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_calib_workspace_size(desc, &need)) return s;
+  REQUIRE_PTR(K); REQUIRE_PTR(moments); REQUIRE_PTR(ws); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  return hip_status(jssa::launch_calib_key_moments(to_dev(desc), static_cast<const uint16_t*>(K), moments, ws,
+                                                   S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_calib_query_moments(int32_t N, int32_t Hq, int32_t Hkv, const void* q, float* moments,
+                                     void* stream) {
+  if (N < 1 || N > (1 << 24)) return fail(JSSA_ERR_SHAPE, "%s: N %d outside [1, 2^24]", __func__, N);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16 || int64_t(N) * Hq > (int64_t(1) << 31))
+    return fail(JSSA_ERR_SHAPE, "%s: Hq %d, Hkv %d", __func__, Hq, Hkv);
+  REQUIRE_PTR(q); REQUIRE_PTR(moments);
+  return hip_status(jssa::launch_calib_query_moments(N, Hq, Hkv, static_cast<const uint16_t*>(q), moments,
+                                                     S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_calib_projection(int32_t d, int32_t r, const float* S_q, const float* S_k, float* P,
+                                  double* eigvals) {
+  if (d < 1 || d > 1024 || r < 1 || r > d)
+    return fail(JSSA_ERR_SHAPE, "%s: d %d, r %d (need 1 <= r <= d <= 1024)", __func__, d, r);
+  if (!S_q || !S_k || !P) return fail(JSSA_ERR_NULL, "%s: S_q, S_k and P must be non-NULL", __func__);
+  double tq = 0.0, tk = 0.0;
+  for (int i = 0; i < d; ++i) {
+    tq += S_q[size_t(i) * d + i];
+    tk += S_k[size_t(i) * d + i];
+  }
+  if (!(tq > 0.0) && !(tk > 0.0))
+    return fail(JSSA_ERR_SHAPE, "%s: both moments have zero (or invalid) trace", __func__);
+  std::vector<double> M(size_t(d) * d, 0.0), V(size_t(d) * r), w(r);
+  for (size_t e = 0; e < M.size(); ++e)
+    M[e] = (tq > 0.0 ? double(S_q[e]) / tq : 0.0) + (tk > 0.0 ? double(S_k[e]) / tk : 0.0);
+  if (!jssa::symmetric_top_eigen(d, r, M.data(), V.data(), w.data()))
+    return fail(JSSA_ERR_NUMERIC, "%s: eigen-solver did not converge", __func__);
+  for (size_t e = 0; e < V.size(); ++e) P[e] = float(V[e]);
+  if (eigvals)
+    for (int c = 0; c < r; ++c) eigvals[c] = w[c];
+  g_err[0] = 0;
+  return JSSA_OK;
 }
 
 }  // extern "C"

@@ -39,6 +39,19 @@ hipError_t launch_combine(int B, int H, int S, int dv, const float* part_o, cons
 hipError_t launch_gather(const GqaDev& g, const uint16_t* K, const uint16_t* V, const int32_t* idx,
                          int k, uint16_t* Kg, uint16_t* Vg, int32_t* lens_out, hipStream_t st);
 
+size_t align256(size_t x);
+
+// Subspace calibration (calib.hip, calib_host.cpp).
+int calib_blocks_per_head(int Hkv);
+size_t calib_workspace_bytes(int Hkv);
+hipError_t launch_calib_key_moments(const GqaDev& g, const uint16_t* K, float* out, void* ws, hipStream_t st);
+hipError_t launch_calib_query_moments(int N, int Hq, int Hkv, const uint16_t* q, float* out, hipStream_t st);
+// Top-r eigenvectors of the symmetric d x d matrix M (row-major, fp64), by
+// cyclic Jacobi rotations; columns by descending eigenvalue, each signed so
+// its entry of largest magnitude (first on a tie) is positive. V: [d, r]
+// row-major; w: the r eigenvalues. Returns false if it did not converge.
+bool symmetric_top_eigen(int d, int r, const double* M, double* V, double* w);
+
 struct MlaDev {
   int B, H, d_latent, d_rope, d_nope, d_v, r, max_seq;
   const int32_t* seq_lens;

@@ -23,7 +23,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m token_level_sparse_amd.build`")
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_NUMERIC = range(8)
 
 ENTRY_POINTS = (
     "jssa_append_kv", "jssa_project_keys", "jssa_score", "jssa_topk_workspace_size", "jssa_topk",
@@ -31,7 +31,8 @@ ENTRY_POINTS = (
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
-    "jssa_mla_up_v", "jssa_status_string", "jssa_last_error", "jssa_version",
+    "jssa_mla_up_v", "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
+    "jssa_calib_projection", "jssa_status_string", "jssa_last_error", "jssa_version",
 )
 
 
@@ -77,6 +78,10 @@ _SIGS = {
     "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_mla_indexed_decode": [_P(MlaDesc), _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_mla_up_v": [_P(MlaDesc), _vp, _vp, _vp, _vp],
+    "jssa_calib_workspace_size": [_P(GqaDesc), _P(_sz)],
+    "jssa_calib_key_moments": [_P(GqaDesc), _vp, _vp, _vp, _sz, _vp],
+    "jssa_calib_query_moments": [_i32, _i32, _i32, _vp, _vp, _vp],
+    "jssa_calib_projection": [_i32, _i32, _vp, _vp, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -241,3 +246,36 @@ def jssa_mla_indexed_decode(desc, q_abs, latent, idx, k, S, scale, part_o, part_
 def jssa_mla_up_v(desc, o_lat, W_uv, out, stream=None):
     _check(_lib.jssa_mla_up_v(ctypes.byref(desc), _p(o_lat), _p(W_uv), _p(out), _s(stream)),
            "jssa_mla_up_v")
+
+
+def jssa_calib_workspace_size(desc) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_calib_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "jssa_calib_workspace_size")
+    return n.value
+
+
+def jssa_calib_key_moments(desc, K, moments, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_calib_key_moments(ctypes.byref(desc), _p(K), _p(moments), _p(ws), ws_bytes, _s(stream)),
+           "jssa_calib_key_moments")
+
+
+def jssa_calib_query_moments(N, Hq, Hkv, q, moments, stream=None):
+    _check(_lib.jssa_calib_query_moments(N, Hq, Hkv, _p(q), _p(moments), _s(stream)), "jssa_calib_query_moments")
+
+
+def jssa_calib_projection(S_q, S_k, r: int):
+    """Host call: S_q, S_k numpy [d, d] (converted to fp32). Returns (P [d, r]
+    fp32, eigenvalues [r] fp64)."""
+    import numpy as np
+    S_q = np.ascontiguousarray(S_q, dtype=np.float32)
+    S_k = np.ascontiguousarray(S_k, dtype=np.float32)
+    d = S_q.shape[0]
+    if S_q.shape != (d, d) or S_k.shape != (d, d):
+        raise ValueError("S_q and S_k must be square and of one size")
+    P = np.empty((d, r), np.float32)
+    w = np.empty(r, np.float64)
+    _check(_lib.jssa_calib_projection(d, r, S_q.ctypes.data, S_k.ctypes.data, P.ctypes.data, w.ctypes.data),
+           "jssa_calib_projection")
+    return P, w

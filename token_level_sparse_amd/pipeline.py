@@ -265,3 +265,36 @@ class MlaStep:
         jssa.jssa_combine(cfg.B, cfg.H, self.S, cfg.d_latent, self.part_o, self.part_lse, self.o_lat, 0,
                           self.lse, stream)
         jssa.jssa_mla_up_v(self.desc, self.o_lat, self.W_uv, self.out, stream)
+
+
+# ---------------------------------------------------------------------------
+# Subspace calibration (offline): second moments on the GPU, the spectral
+# step on the host, both in the library.
+# ---------------------------------------------------------------------------
+def calib_key_moments(c: GqaCache, stream=None) -> torch.Tensor:
+    """S_k per KV head [Hkv, d, d] fp32 over every valid token of the cache."""
+    ws = torch.empty(jssa.jssa_calib_workspace_size(c.desc), dtype=torch.uint8, device=c.K.device)
+    out = torch.empty((c.Hkv, c.d, c.d), dtype=torch.float32, device=c.K.device)
+    jssa.jssa_calib_key_moments(c.desc, c.K, out, ws, stream=stream)
+    return out
+
+
+def calib_query_moments(q_samples: torch.Tensor, Hkv: int, stream=None) -> torch.Tensor:
+    """S_q per KV head [Hkv, d, d] fp32 from decode-query samples [N, Hq, d]."""
+    N, Hq, d = q_samples.shape
+    out = torch.empty((Hkv, d, d), dtype=torch.float32, device=q_samples.device)
+    jssa.jssa_calib_query_moments(N, Hq, Hkv, q_samples, out, stream=stream)
+    return out
+
+
+def calibrate(c: GqaCache, q_samples: torch.Tensor, r: int):
+    """Calibrated projection P [Hkv, d, r] (fp32, on the cache's device) and
+    the kept eigenvalues [Hkv, r] of each head's marginal operator."""
+    Sk = calib_key_moments(c).cpu().numpy()
+    Sq = calib_query_moments(q_samples, c.Hkv).cpu().numpy()
+    Ps, ws = [], []
+    for j in range(c.Hkv):
+        P, w = jssa.jssa_calib_projection(Sq[j], Sk[j], r)
+        Ps.append(P)
+        ws.append(w)
+    return torch.from_numpy(np.stack(Ps)).to(c.K.device), np.stack(ws)
