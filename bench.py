@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--dense-splits", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
+    ap.add_argument("--no-calib", action="store_true", help="skip the subspace-calibration leg")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     return ap.parse_args()
 
@@ -268,6 +269,10 @@ def main():
                                                  "gather": round(dense_attn_us / gather_attn_us, 2)}}
         print("[bench] dense and gather comparisons done", file=sys.stderr, flush=True)
 
+    if not args.no_calib and not cfg.paged:
+        result["calibration"] = bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream)
+        print("[bench] calibration leg done", file=sys.stderr, flush=True)
+
     if not args.no_cpu:
         units = [(b, j) for b in range(min(2, B)) for j in range(Hkv)]
         dt, passes, res = cpu_oracle_gqa(inp, k, units)
@@ -290,6 +295,63 @@ def main():
         result["oracle_check"] = {"units": len(units), "index_parity": "ok", "tie_swaps": int(swaps)}
         print("[bench] cpu oracle leg done", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
+
+
+def bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream, n_queries=4096):
+    """Offline subspace calibration on the benchmark's own cache: key second
+    moments over every cached key (MFMA Gram kernel, HBM-bound), query second
+    moments over n_queries synthetic decode queries, the host spectral step,
+    then the recall of the exact (full-width) top-k by the calibrated basis
+    against the random orthonormal one the timed step uses."""
+    B, Hkv, Hq, d, r, k = cfg.B, cfg.Hkv, cfg.Hq, cfg.d, cfg.r, cfg.k
+    ws = torch.empty(jssa.jssa_calib_workspace_size(c.desc), dtype=torch.uint8, device="cuda")
+    Sk = torch.empty((Hkv, d, d), dtype=torch.float32, device="cuda")
+    km = lambda: jssa.jssa_calib_key_moments(c.desc, c.K, Sk, ws)   # noqa: E731
+    km_us = time_launches(km, max(5, args.steps // 5), torch, stream)
+    k_bytes = int(np.sum(inp.seq_lens)) * Hkv * d * 2
+    qs = torch.from_numpy(synth.gen_calib_queries(cfg, n_queries).view(np.int16)).cuda()
+    Sq = torch.empty((Hkv, d, d), dtype=torch.float32, device="cuda")
+    qm_us = time_launches(lambda: jssa.jssa_calib_query_moments(n_queries, Hq, Hkv, qs, Sq), 5, torch, stream)
+    torch.cuda.synchronize()
+    Skh, Sqh = Sk.cpu().numpy(), Sq.cpu().numpy()
+    t0 = time.perf_counter()
+    P = np.stack([jssa.jssa_calib_projection(Sqh[j], Skh[j], r)[0] for j in range(Hkv)])
+    host_ms = (time.perf_counter() - t0) * 1e3
+    # selection with the calibrated basis (a second projected cache)
+    cc = pipeline.GqaCache.__new__(pipeline.GqaCache)
+    cc.__dict__.update(c.__dict__)
+    cc.P = torch.from_numpy(P).cuda()
+    cc.Kp = torch.empty_like(c.Kp)
+    cc.project()
+    cal = pipeline.SparseStep(cc, k=k, fused=True)
+    cal.score_topk()
+    # exact top-k: full-width scores (rank 128, P = I, K itself as the projected cache)
+    eye = torch.eye(d, dtype=torch.float32, device="cuda").repeat(Hkv, 1, 1).contiguous()
+    dx = jssa.gqa_desc(B, Hq, Hkv, d, cfg.T, seq_lens=c.seq_lens)
+    idx_x = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
+    wx = torch.empty(jssa.jssa_score_topk_workspace_size(dx, k), dtype=torch.uint8, device="cuda")
+    jssa.jssa_score_topk(dx, c.q, eye, c.K, k, None, idx_x, wx)
+    rnd = pipeline.SparseStep(c, k=k, fused=True)
+    rnd.score_topk()
+    torch.cuda.synchronize()
+    gi, gx, gr = cal.idx.cpu().numpy(), idx_x.cpu().numpy(), rnd.idx.cpu().numpy()
+
+    def recall(a, x):
+        vals = []
+        for b in range(B):
+            for j in range(Hkv):
+                ref = x[b, j][x[b, j] >= 0]
+                vals.append(np.intersect1d(a[b, j], ref).size / max(1, ref.size))
+        return float(np.mean(vals))
+    del cc, cal
+    gbs = k_bytes / (km_us * 1e-6) / 1e9
+    return {"key_moments": {"us": round(km_us, 2), "bytes": k_bytes, "GB_s": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 3), "bound": "hbm",
+                            "kernels": "gram_kernel + gram_reduce_kernel (one jssa_calib_key_moments call)"},
+            "query_moments_us": round(qm_us, 2), "query_samples": n_queries,
+            "host_spectral_ms": round(host_ms, 1), "rank": r,
+            "recall_of_exact_topk": {"calibrated": round(recall(gi, gx), 4), "random": round(recall(gr, gx), 4),
+                                     "k": k, "units": B * Hkv}}
 
 
 def bench_mla(args, cfg, torch, pipeline, synth, stream):

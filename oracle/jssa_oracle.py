@@ -39,7 +39,8 @@ R8 MLA: keys are [W_uk[h] c[:512]; c[512:]], values c[:512], output
    W_uv[h] (sum_t p_t c_t[:512]); the selection score projects the summed
    absorbed query [W_uk[h]^T q_nope; q_rope] and the latent row through one
    rank-r basis; one selected set per sequence.
-R9 subspace calibration ([JSSA-A]: the subspace minimises a token-score
+(R9 to R11 fix the GPU side's precision and output type only.)
+R12 subspace calibration ([JSSA-A]: the subspace minimises a token-score
    preservation error, which is bounded by a marginal objective with a
    closed-form spectral solution; the formulas are not on the pages). The
    error of one (query, key) pair is e = qbar^T k - qbar^T P P^T k =
@@ -250,7 +251,7 @@ def mla_attend_explicit(q_nope_bits, q_rope_bits, W_uk_bits, W_uv_bits, C_rows_b
 
 
 # ---------------------------------------------------------------------------
-# Subspace calibration (R9)  [JSSA-A]; [JSSA-I] (queries and keys kept
+# Subspace calibration (R12)  [JSSA-A]; [JSSA-I] (queries and keys kept
 # together; oracle top-k recall as the measure of ranking quality);
 # [JSSA-P] (the marginal bound controls the exact score error)
 # ---------------------------------------------------------------------------
@@ -272,7 +273,7 @@ def query_second_moment(q_samples_bits, j: int, G: int) -> np.ndarray:
 
 
 def marginal_operator(S_q, S_k) -> np.ndarray:
-    """M = S_q / tr S_q + S_k / tr S_k (R9); a zero-trace term is left out."""
+    """M = S_q / tr S_q + S_k / tr S_k (R12); a zero-trace term is left out."""
     M = np.zeros_like(np.asarray(S_q, np.float64))
     for S in (S_q, S_k):
         t = float(np.trace(S))
@@ -292,7 +293,7 @@ def sign_fix(V) -> np.ndarray:
 
 
 def calibrate_projection(S_q, S_k, r: int):
-    """P [d, r]: the top-r eigenvectors of the marginal operator (R9), columns
+    """P [d, r]: the top-r eigenvectors of the marginal operator (R12), columns
     by descending eigenvalue, sign-fixed; also returns the r eigenvalues."""
     M = marginal_operator(S_q, S_k)
     w, V = np.linalg.eigh(M)                   # ascending
@@ -302,7 +303,7 @@ def calibrate_projection(S_q, S_k, r: int):
 
 def marginal_bound(P, S_q, S_k) -> float:
     """tr(Q (lam S_q + S_k / lam)) / 2 with Q = I - P P^T and lam =
-    sqrt(tr S_k / tr S_q): the upper bound on the mean |e| (R9)."""
+    sqrt(tr S_k / tr S_q): the upper bound on the mean |e| (R12)."""
     P = np.asarray(P, np.float64)
     Q = np.eye(P.shape[0]) - P @ P.T
     lam = np.sqrt(np.trace(S_k) / np.trace(S_q))

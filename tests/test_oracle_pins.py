@@ -400,7 +400,7 @@ def test_mla_score_is_summed_per_head_projection():
 # subspace calibration (JSSA abstract on weekinpapers, Abstract: a shared
 # query-key subspace from a marginal bound on the score-preservation error
 # with a closed-form spectral solution; the reading is spelled out in the
-# oracle's header, R9)
+# oracle's header, R12)
 # ---------------------------------------------------------------------------
 def _orthonormal(rng, d, r):
     q, _ = np.linalg.qr(rng.standard_normal((d, r)))
