@@ -16,6 +16,10 @@ blocks. Sources (page title, section):
             gather-free ...", Synopsis.
 * [JSSA-I]  same digest, Interpretation (scoring space, gather-free reads).
 * [JSSA-P]  same digest, Perspective (GQA / hybrid / MLA coverage).
+* [FFD]     "Faster Than Flash: Exploiting Attention Sparsity for Efficient
+            Long-Context Decoding" (evolve.pub review), Summary, Key claims
+            and FAQ (the top-delta rule, the sink/local pseudo-max and its
+            fail-safe property).
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -40,6 +44,16 @@ R8 MLA: keys are [W_uk[h] c[:512]; c[512:]], values c[:512], output
    absorbed query [W_uk[h]^T q_nope; q_rope] and the latent row through one
    rank-r basis; one selected set per sequence.
 (R9 to R11 fix the GPU side's precision and output type only.)
+R13 top-delta selection ([FFD], the top-delta rule and its fail-safe
+   pseudo-max, applied per token and per KV head instead of per block): the
+   approximate logit of token t is the group-mean subspace logit
+   l_t = scale * s_t / G. The pseudo-max m~ is the largest s_t over the
+   first n_sink and the last n_local positions of the sequence (valid tokens
+   only); a token is kept when scale * s_t / G >= scale * m~ / G - delta,
+   i.e. s_t >= m~ - delta * G / scale. The kept set is capped at k_max
+   tokens by the order of R3 and listed like R3's, with its size. No valid
+   special token (or T_b = 0): nothing is filtered. Decisions are taken on
+   scores rounded to fp32, the threshold in fp64.
 R12 subspace calibration ([JSSA-A]: the subspace minimises a token-score
    preservation error, which is bounded by a marginal objective with a
    closed-form spectral solution; the formulas are not on the pages). The
@@ -326,3 +340,38 @@ def topk_recall(selected, reference) -> float:
     a = set(int(x) for x in np.asarray(selected).ravel() if x >= 0)
     b = set(int(x) for x in np.asarray(reference).ravel() if x >= 0)
     return len(a & b) / len(b) if b else 1.0
+
+
+# ---------------------------------------------------------------------------
+# Top-delta selection (R13)  [FFD]
+# ---------------------------------------------------------------------------
+def topdelta_threshold(scores, delta: float, n_sink: int, n_local: int, scale: float, G: int,
+                       valid=None) -> float:
+    """s_thr = m~ - delta * G / scale, m~ the largest fp32-rounded score over
+    the first n_sink and last n_local positions that are valid; -inf when
+    there is none."""
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s32.shape[0]
+    t = np.arange(n)
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    special = ok & ((t < n_sink) | (t >= n - n_local))
+    if not special.any():
+        return -np.inf
+    return float(s32[special].max()) - delta * G / scale
+
+
+def select_topdelta(scores, k_max: int, delta: float, n_sink: int, n_local: int, scale: float, G: int,
+                    valid=None):
+    """(indices [k_max] ascending, -1 padded; count): the valid tokens with
+    fp32 score >= the top-delta threshold, at most k_max of them, chosen in
+    the order (score desc, index asc) (R13, R3)."""
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s32.shape[0]
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    thr = topdelta_threshold(scores, delta, n_sink, n_local, scale, G, ok)
+    cand = np.nonzero(ok & (s32 >= thr))[0]
+    order = cand[np.lexsort((cand, -s32[cand]))]
+    keep = np.sort(order[:k_max])
+    out = np.full(k_max, -1, np.int64)
+    out[:keep.shape[0]] = keep
+    return out, int(keep.shape[0])

@@ -91,6 +91,34 @@ def _bound_lam_inverted(P, S_q, S_k):
     return float(np.trace(Q @ (lam * np.asarray(S_q) + np.asarray(S_k) / lam)) / 2)
 
 
+def _topdelta_global_max(scores, k_max, delta, n_sink, n_local, scale, G, valid=None):
+    n = len(scores)
+    return _orig_topdelta(scores, k_max, delta, n, 0, scale, G, valid)
+
+
+def _topdelta_no_group(scores, k_max, delta, n_sink, n_local, scale, G, valid=None):
+    return _orig_topdelta(scores, k_max, delta, n_sink, n_local, scale, 1, valid)
+
+
+def _strict_impl(scores, k_max, delta, n_sink, n_local, scale, G, valid=None):
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s32.shape[0]
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    thr = O.topdelta_threshold(scores, delta, n_sink, n_local, scale, G, ok)
+    cand = np.nonzero(ok & (s32 > thr))[0]
+    order = cand[np.lexsort((cand, -s32[cand]))]
+    keep = np.sort(order[:k_max])
+    out = np.full(k_max, -1, np.int64)
+    out[:keep.shape[0]] = keep
+    return out, int(keep.shape[0])
+
+
+def _threshold_local_off_by_one(scores, delta, n_sink, n_local, scale, G, valid=None):
+    return _orig_threshold(scores, delta, n_sink, max(0, n_local - 1), scale, G, valid)
+
+
+_orig_topdelta = O.select_topdelta
+_orig_threshold = O.topdelta_threshold
 _orig_attend = O.attend
 _orig_mla = O.mla_attend_explicit
 _orig_marginal = O.marginal_operator
@@ -114,6 +142,10 @@ MUTATIONS = [
     ("query_second_moment", _query_moment_mean_heads, [pins.test_calib_second_moments_brute_force]),
     ("key_second_moment", _key_moment_sum, [pins.test_calib_second_moments_brute_force]),
     ("marginal_bound", _bound_lam_inverted, [pins.test_calib_minimises_bound_brute_force]),
+    ("select_topdelta", _topdelta_global_max, [pins.test_topdelta_golden_hand]),
+    ("select_topdelta", _topdelta_no_group, [pins.test_topdelta_golden_hand]),
+    ("select_topdelta", _strict_impl, [pins.test_topdelta_golden_hand]),
+    ("topdelta_threshold", _threshold_local_off_by_one, [pins.test_topdelta_golden_hand]),
 ]
 
 

@@ -499,3 +499,66 @@ def test_topk_recall_hand_values():
     assert O.topk_recall([1, 2, 3, -1], [2, 3, 4, 5]) == 0.5
     assert O.topk_recall([7, 8], [8, 7]) == 1.0
     assert O.topk_recall([-1, -1], [-1, -1]) == 1.0
+
+
+# ---------------------------------------------------------------------------
+# top-delta selection (Faster Than Flash review on evolve.pub, Summary and
+# FAQ: the top-delta rule with a sink/local pseudo-max; reading R13 in the
+# oracle's header)
+# ---------------------------------------------------------------------------
+def test_topdelta_golden_hand():
+    g = _golden("topdelta_hand.json")
+    s, valid = np.array(g["scores"]), np.array(g["valid"], bool)
+    for c in g["cases"]:
+        idx, cnt = O.select_topdelta(s, c["k_max"], c["delta"], c["n_sink"], c["n_local"], g["scale"], g["G"], valid)
+        np.testing.assert_array_equal(idx, c["idx"])
+        assert cnt == c["count"]
+
+
+def test_topdelta_infinite_delta_is_topk():
+    rng = np.random.default_rng(31)
+    for _ in range(10):
+        n = int(rng.integers(1, 300))
+        s = rng.integers(-5, 6, n) * 0.25 if rng.random() < 0.5 else rng.standard_normal(n)
+        k = int(rng.integers(1, 400))
+        idx, cnt = O.select_topdelta(s, k, np.inf, 4, 16, 0.1, 4)
+        np.testing.assert_array_equal(idx, O.select_topk(s, k))
+        assert cnt == min(k, n)
+
+
+def test_topdelta_failsafe_and_monotone():
+    """The pseudo-max never exceeds the true max, so the kept set (uncapped)
+    contains every token within delta of the true max; a larger delta keeps
+    a superset."""
+    rng = np.random.default_rng(32)
+    for _ in range(20):
+        n = int(rng.integers(8, 500))
+        s = rng.standard_normal(n) * 3
+        G, scale = int(rng.integers(1, 9)), float(rng.uniform(0.05, 1.0))
+        d1, d2 = sorted(rng.uniform(0, 10, 2))
+        i1, c1 = O.select_topdelta(s, n, d1, 4, 32, scale, G)
+        i2, c2 = O.select_topdelta(s, n, d2, 4, 32, scale, G)
+        k1, k2 = set(i1[:c1]), set(i2[:c2])
+        assert k1 <= k2
+        s32 = s.astype(np.float32).astype(np.float64)
+        true_set = set(np.nonzero(s32 >= s32.max() - d1 * G / scale)[0])
+        assert true_set <= k1
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topdelta_brute_force_small(seed):
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(0, 40))
+    s = rng.integers(-3, 4, n) * 0.5
+    valid = rng.random(n) < 0.8
+    ns, nl = int(rng.integers(0, 5)), int(rng.integers(0, 9))
+    delta, G, scale, k = float(rng.choice([0.0, 0.3, 1.0, 5.0])), 2, 0.5, int(rng.integers(1, 45))
+    m = None
+    for t in range(n):
+        if valid[t] and (t < ns or t >= n - nl):
+            m = s[t] if m is None else max(m, s[t])
+    kept = [t for t in range(n) if valid[t] and (m is None or s[t] >= m - delta * G / scale)]
+    kept = sorted(sorted(kept, key=lambda t: (-s[t], t))[:k])
+    idx, cnt = O.select_topdelta(s, k, delta, ns, nl, scale, G, valid)
+    assert cnt == len(kept)
+    np.testing.assert_array_equal(idx, kept + [-1] * (k - len(kept)))
