@@ -317,6 +317,57 @@ JSSA_API jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat
                           float* out, void* stream);
 
 /*
+ * Top-delta selection (Faster Than Flash review on evolve.pub, Summary, Key
+ * claims and FAQ: keep what lies within delta, in log space, of a pseudo-max
+ * estimated from sink and local tokens; the pseudo-max never exceeds the
+ * true max, so an error only enlarges the kept set). Applied here per token
+ * and per KV head to the subspace score s_t: the approximate logit is the
+ * group-mean scale * s_t / G; the pseudo-max m is the largest s_t over the
+ * first n_sink and the last n_local positions of the sequence; token t is
+ * kept iff s_t >= m - delta * G / scale, at most k_max of them, chosen by
+ * (score desc, index asc). Tokens without a valid page are never kept; with
+ * no special token (n_sink = n_local = 0) nothing is filtered. The result is
+ * the same as the top-k_max selection with its members below the threshold
+ * removed. Scores, m and the threshold are fp32.
+ */
+typedef struct {
+  float delta;       /* >= 0, in natural-log units of the group-mean logit; +inf: plain top-k */
+  int32_t n_sink;    /* >= 0: positions 0 .. n_sink-1 inform the pseudo-max */
+  int32_t n_local;   /* >= 0: positions T_b-n_local .. T_b-1 inform the pseudo-max */
+} jssa_topdelta_rule;
+
+/* Workspace of the top-delta calls (the score + top-k workspace plus one
+ * pseudo-max slot per 8192-token chunk). */
+JSSA_API jssa_status jssa_score_topdelta_workspace_size(const jssa_gqa_desc* desc, int32_t k_max, size_t* bytes);
+
+/*
+ * Score stream + top-delta selection (two launches or more: the fused chunk
+ * pass, then the final selection).
+ *  q, P, Kp  as jssa_score_topk; scale > 0 converts delta to score units
+ *  idx       device int32 [B,Hkv,k_max]: kept tokens ascending, -1 padded
+ *  counts    device int32 [B,Hkv] or NULL: number kept per (b, j)
+ * ws holds the candidate lists and pseudo-max slots; no initialisation.
+ */
+JSSA_API jssa_status jssa_score_topdelta(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                         int32_t k_max, const jssa_topdelta_rule* rule, float scale, int32_t* idx,
+                                         int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * jssa_score_topdelta followed by the attention of every query head over
+ * its KV head's kept tokens, read in place (one split: out is the
+ * normalised output, lse the log-sum-exp; an empty set gives 0 and -inf).
+ * The final selection and the attention share a kernel when the selection
+ * needs no merge level, k_max <= 512 and G <= 16; otherwise
+ * jssa_indexed_decode (S = 1) follows it.
+ *  K, V  device bf16 (layout of desc); out device fp32 [B,Hq,128]; lse [B,Hq]
+ */
+JSSA_API jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const void* q, const float* P,
+                                                const void* Kp, const void* K, const void* V, int32_t k_max,
+                                                const jssa_topdelta_rule* rule, float scale, int32_t* idx,
+                                                int32_t* counts, float* out, float* lse, void* ws, size_t ws_bytes,
+                                                void* stream);
+
+/*
  * Subspace calibration (JSSA abstract on weekinpapers, Abstract: the shared
  * query-key subspace minimises a token-score preservation error through a
  * marginal upper bound that has a closed-form spectral solution; the

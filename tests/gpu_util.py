@@ -80,3 +80,40 @@ def check_attention(inp, b, j, hs, K, V, sel, out, lse, scale):
 
 def scale_of(cfg) -> float:
     return 1.0 / math.sqrt(cfg.d)
+
+
+def unit_valid(inp: synth.GqaInputs, b: int) -> np.ndarray:
+    """Tokens of sequence b that have a valid page (all of them when contiguous)."""
+    n = int(inp.seq_lens[b])
+    if inp.page_table is None:
+        return np.ones(n, bool)
+    pg = inp.page_table[b][np.arange(n) // 16]
+    return (pg >= 0) & (pg < inp.num_pages)
+
+
+def check_topdelta(gpu_idx, gpu_cnt, s, valid, k_max, delta, n_sink, n_local, scale, G) -> int:
+    """Top-delta parity (reading R13): the GPU lists gpu_cnt distinct valid
+    tokens ascending, then -1; its set equals the oracle's except for tokens
+    whose oracle score lies within IDX_REL (relative) of the threshold or of
+    the last kept score (both sides decide on fp32 scores computed in
+    different orders). Returns the number of such tokens."""
+    o_idx, o_cnt = O.select_topdelta(s, k_max, delta, n_sink, n_local, scale, G, valid)
+    g = np.asarray(gpu_idx[:gpu_cnt], np.int64)
+    assert np.all(gpu_idx[gpu_cnt:] == -1), "padding past the count must be -1"
+    assert np.all(np.diff(g) > 0), "indices must be strictly ascending"
+    if gpu_cnt:
+        assert g[0] >= 0 and g[-1] < s.shape[0] and np.all(valid[g]), "kept tokens must be valid"
+    diff = np.setxor1d(g, o_idx[:o_cnt])
+    if diff.size == 0:
+        assert gpu_cnt == o_cnt
+        return 0
+    thr = O.topdelta_threshold(s, delta, n_sink, n_local, scale, G, valid)
+    s32 = s.astype(np.float32).astype(np.float64)
+    kept = o_idx[:o_cnt]
+    s_last = s32[kept].min() if o_cnt else -np.inf
+    m = thr + delta * G / scale
+    band_thr = IDX_REL * max(abs(m), abs(thr), 1e-30)
+    ok = (np.abs(s[diff] - thr) <= band_thr) | (np.abs(s[diff] - s_last) <= IDX_REL * max(abs(s_last), 1e-30))
+    assert np.all(ok), f"tokens {diff[~ok][:8]} differ outside the tie bands (thr={thr}, last={s_last})"
+    assert abs(gpu_cnt - o_cnt) <= diff.size
+    return int(diff.size)

@@ -490,6 +490,87 @@ def test_invalid_page_entries_are_absent(J, PL):
 
 
 # ---------------------------------------------------------------------------
+# top-delta selection (reading R13)
+# ---------------------------------------------------------------------------
+TD_CASES = {
+    "tiny_d0.5": (lambda: synth.make_gqa(synth.TINY), 256, 0.5, 4, 64),
+    "tiny_d2_capped": (lambda: synth.make_gqa(synth.TINY), 256, 2.0, 4, 64),
+    "tiny_d3": (lambda: synth.make_gqa(synth.TINY), 256, 3.0, 4, 64),
+    "tiny_no_special": (lambda: synth.make_gqa(synth.TINY), 256, 0.5, 0, 0),
+    "ragged_d2": (lambda: ragged_inputs(), 300, 2.0, 4, 64),
+    "llama_d1_k1024": (lambda: synth.make_gqa(synth.LLAMA8B_32K), 1024, 1.0, 4, 64),
+    "llama_d2_k4096_merge": (lambda: synth.make_gqa(synth.LLAMA8B_32K), 4096, 2.0, 4, 64),
+    "paged_hidden_sinks": (None, 512, 2.0, 4, 64),
+}
+
+
+def _td_inputs(case):
+    make = TD_CASES[case][0]
+    if make is not None:
+        return make()
+    inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=20000, len_lo=8000, len_hi=20000, seed=93))
+    inp.page_table[0, 0] = -1                       # sequence 0: its sink tokens have no page
+    last = (int(inp.seq_lens[1]) - 1) // 16
+    inp.page_table[1, last - 1] = -1                # sequence 1: part of its local window has no page
+    return inp
+
+
+@pytest.mark.parametrize("case", list(TD_CASES))
+def test_topdelta_parity(J, PL, case):
+    _, k_max, delta, ns, nl = TD_CASES[case]
+    inp = _td_inputs(case)
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.TopDeltaStep(c, k_max, delta, ns, nl)
+    st.select()
+    torch.cuda.synchronize()
+    idx, cnt = _np(st.idx), _np(st.counts)
+    cfg = inp.cfg
+    for b in range(cfg.B):
+        valid = U.unit_valid(inp, b)
+        for j in range(cfg.Hkv):
+            _, _, _, s, _ = U.oracle_unit(inp, b, j)
+            U.check_topdelta(idx[b, j], int(cnt[b, j]), s, valid, k_max, delta, ns, nl, c.scale, cfg.G)
+
+
+def test_topdelta_infinite_delta_is_topk(J, PL):
+    inp = synth.make_gqa(synth.LLAMA8B_32K)
+    c = PL.GqaCache(inp)
+    c.project()
+    st = PL.TopDeltaStep(c, 256, float("inf"))
+    st.select()
+    ref = PL.SparseStep(c, k=256, fused=True)
+    ref.score_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(st.idx), _np(ref.idx))
+    assert np.all(_np(st.counts) == 256)
+
+
+@pytest.mark.parametrize("case", ["tiny_d2_capped", "llama_d1_k1024", "paged_hidden_sinks"])
+def test_topdelta_attend(J, PL, case):
+    """Selection + attention (fused with the final selection when k_max <=
+    512, else followed by the indexed kernel): the indices equal the
+    selection-only call's, outputs match the oracle on the GPU's kept set."""
+    _, k_max, delta, ns, nl = TD_CASES[case]
+    inp = _td_inputs(case)
+    c = PL.GqaCache(inp)
+    c.project()
+    sel = PL.TopDeltaStep(c, k_max, delta, ns, nl)
+    sel.select()
+    st = PL.TopDeltaStep(c, k_max, delta, ns, nl)
+    st.run()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(st.idx), _np(sel.idx))
+    np.testing.assert_array_equal(_np(st.counts), _np(sel.counts))
+    idx, cnt, out, lse = _np(st.idx), _np(st.counts), _np(st.out), _np(st.lse)
+    cfg = inp.cfg
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            K, V, _, _, hs = U.oracle_unit(inp, b, j)
+            U.check_attention(inp, b, j, hs, K, V, idx[b, j][:cnt[b, j]], out, lse, c.scale)
+
+
+# ---------------------------------------------------------------------------
 # subspace calibration: second moments (GPU), spectral step (host library),
 # oracle top-k recall of the calibrated subspace
 # ---------------------------------------------------------------------------

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <vector>
@@ -388,6 +389,95 @@ jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const v
   return hip_status(jssa::launch_mla_up_v(to_mla(desc), o_lat, static_cast<const uint16_t*>(W_uv),
                                           out, S(stream)),
                     __func__);
+}
+
+jssa_status jssa_score_topdelta_workspace_size(const jssa_gqa_desc* desc, int32_t k_max, size_t* bytes) {
+  size_t base = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k_max, &base)) return s;
+  const size_t rows = size_t(desc->B) * desc->Hkv, nseg = size_t(jssa::score_topk_segments(desc->max_seq));
+  *bytes = jssa::align256(base) + jssa::align256(rows * nseg * sizeof(uint32_t));
+  return JSSA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks and set-up of the two top-delta entry points: the candidate
+// segments, the merge workspace, the pseudo-max slots and the filter.
+struct TopDelta {
+  jssa::CandSegs segs;
+  void* merge_ws;
+  uint32_t* pmax;
+  jssa::DeltaArgs dl;
+};
+
+jssa_status topdelta_setup(const char* fn, const jssa_gqa_desc* desc, int32_t k_max, const jssa_topdelta_rule* rule,
+                           float scale, int32_t* counts, void* ws, size_t ws_bytes, TopDelta* td) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topdelta_workspace_size(desc, k_max, &need)) return s;
+  if (!rule) return fail(JSSA_ERR_NULL, "%s: rule is NULL", fn);
+  if (!(rule->delta >= 0.0f)) return fail(JSSA_ERR_SHAPE, "%s: delta %g (must be >= 0)", fn, double(rule->delta));
+  if (rule->n_sink < 0 || rule->n_local < 0)
+    return fail(JSSA_ERR_SHAPE, "%s: n_sink %d, n_local %d (must be >= 0)", fn, rule->n_sink, rule->n_local);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(JSSA_ERR_SHAPE, "%s: scale %g", fn, double(scale));
+  if (!ws) return fail(JSSA_ERR_NULL, "%s: ws is NULL", fn);
+  if (!aligned(ws)) return fail(JSSA_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  if (counts && !aligned(counts)) return fail(JSSA_ERR_ALIGN, "%s: counts is not 16-byte aligned", fn);
+  if (ws_bytes < need) return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  size_t base = 0;
+  jssa_score_topk_workspace_size(desc, k_max, &base);
+  size_t main_bytes = 0;
+  const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
+  td->segs = jssa::carve_segs(ws, rows, nseg, jssa::score_topk_segment_cap(), &main_bytes);
+  td->merge_ws = static_cast<char*>(ws) + main_bytes;
+  td->pmax = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + jssa::align256(base));
+  td->dl = jssa::DeltaArgs{td->pmax, nseg, rule->delta * float(desc->Hq / desc->Hkv) / scale, counts};
+  return JSSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+jssa_status jssa_score_topdelta(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                int32_t k_max, const jssa_topdelta_rule* rule, float scale, int32_t* idx,
+                                int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  TopDelta td;
+  if (jssa_status s = topdelta_setup(__func__, desc, k_max, rule, scale, counts, ws, ws_bytes, &td)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(idx);
+  const jssa::GqaDev g = to_dev(desc);
+  hipError_t e = jssa::launch_score_chunks(g, static_cast<const uint16_t*>(q), P, static_cast<const uint16_t*>(Kp),
+                                           k_max, nullptr, td.segs, S(stream), td.pmax, rule->n_sink, rule->n_local);
+  if (e == hipSuccess)
+    e = jssa::launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k_max, td.segs, idx, td.merge_ws,
+                                  S(stream), td.dl);
+  return hip_status(e, __func__);
+}
+
+jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                       const void* K, const void* V, int32_t k_max, const jssa_topdelta_rule* rule,
+                                       float scale, int32_t* idx, int32_t* counts, float* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  TopDelta td;
+  if (jssa_status s = topdelta_setup(__func__, desc, k_max, rule, scale, counts, ws, ws_bytes, &td)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(idx);
+  REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  const jssa::GqaDev g = to_dev(desc);
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* K16 = static_cast<const uint16_t*>(K);
+  const auto* V16 = static_cast<const uint16_t*>(V);
+  hipError_t e = jssa::launch_score_chunks(g, q16, P, static_cast<const uint16_t*>(Kp), k_max, nullptr, td.segs,
+                                           S(stream), td.pmax, rule->n_sink, rule->n_local);
+  if (e != hipSuccess) return hip_status(e, __func__);
+  if (jssa::select_attend_fused(td.segs.nseg, k_max, g.G))
+    return hip_status(jssa::launch_select_attend(g, k_max, td.segs, q16, K16, V16, scale, idx, out, lse,
+                                                 S(stream), td.dl),
+                      __func__);
+  e = jssa::launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k_max, td.segs, idx, td.merge_ws,
+                                S(stream), td.dl);
+  if (e == hipSuccess) e = jssa::launch_indexed(g, q16, K16, V16, idx, k_max, 1, scale, out, lse, S(stream));
+  return hip_status(e, __func__);
 }
 
 jssa_status jssa_calib_workspace_size(const jssa_gqa_desc* desc, size_t* bytes) {

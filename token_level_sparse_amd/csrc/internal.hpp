@@ -25,7 +25,8 @@ int score_topk_segment_cap();
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                              float* scores, int32_t* idx, CandSegs segs, void* merge_ws, hipStream_t st);
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
-                               float* scores, CandSegs segs, hipStream_t st);
+                               float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax = nullptr,
+                               int n_sink = 0, int n_local = 0);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
 

@@ -72,6 +72,8 @@ struct FusedOut {
   CandSegs segs;
   int k;
   int write_scores;
+  uint32_t* pmax;           // top-delta: per segment, the largest key of the row's sink/local tokens in it
+  int n_sink, n_local;      // sink tokens: t < n_sink; local tokens: t >= T_b - n_local
 };
 
 template <int R>
@@ -121,7 +123,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
       for (int i = tid; i < lim; i += NT) srow[t_begin + i] = -__builtin_inff();
     }
-    if (FUSED && tid == 0) fo.segs.cnt[seg] = 0;
+    if (FUSED && tid == 0) {
+      fo.segs.cnt[seg] = 0;
+      if (fo.pmax) fo.pmax[seg] = 0u;
+    }
     return;
   }
   // Tokens of this block are [t_begin, tend); loads of later positions are
@@ -288,6 +293,33 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
   }
   if constexpr (FUSED) {
+    if (fo.pmax) {                                       // top-delta pseudo-max contribution of this chunk
+      const int e1 = fo.n_sink < tend ? fo.n_sink : tend;
+      const int s2 = Tb - fo.n_local > t_begin ? Tb - fo.n_local : t_begin;
+      uint32_t pm = 0u;
+      if (e1 > t_begin || tend > s2) {                   // block-uniform
+        __shared__ uint32_t pred[kWaves];
+        uint32_t v = 0u;
+        for (int t = t_begin + tid; t < e1; t += NT) {
+          const uint32_t x = score_key(stage[sidx(t - t_begin)]);
+          v = x > v ? x : v;
+        }
+        for (int t = s2 + tid; t < tend; t += NT) {
+          const uint32_t x = score_key(stage[sidx(t - t_begin)]);
+          v = x > v ? x : v;
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = uint32_t(__shfl_xor(int(v), o, 64));
+          v = y > v ? y : v;
+        }
+        if (lane == 0) pred[w] = v;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) pm = pred[i] > pm ? pred[i] : pm;
+      }
+      if (tid == 0) fo.pmax[seg] = pm;
+    }
     __shared__ Top2Smem<NT> tsm;
     uint32_t key[TPW];
 #pragma unroll
@@ -352,8 +384,9 @@ int score_topk_segments(int max_seq) {
 int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
 
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
-                               float* scores, CandSegs segs, hipStream_t st) {
-  FusedOut fo{segs, k, scores ? 1 : 0};
+                               float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax, int n_sink,
+                               int n_local) {
+  FusedOut fo{segs, k, scores ? 1 : 0, pmax, n_sink, n_local};
   return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores, st, fo);
 }
 

@@ -319,16 +319,40 @@ __device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
   if (tid == 0) out.cnt[seg] = tot;
 }
 
+// Top-delta filter of a row's final selection (Faster Than Flash review on
+// evolve.pub, Summary and FAQ: keep what lies within delta, in log space, of
+// a pseudo-max estimated from sink and local tokens). pmax[row * nseg0 + s]
+// is the largest score key of the row's sink or local tokens in segment s
+// (0: none there); the row's pseudo-max m is their maximum, and a selected
+// token stays only if its score is >= m - thr_off (thr_off = delta * G /
+// scale: the group-mean logit within delta of the pseudo-max's). Tokens
+// with a -inf score (no valid page) never stay. Because the kept set is an
+// upper set of scores, filtering the top-k selection gives exactly the
+// top-k of the kept set. counts[row] receives the number kept. pmax ==
+// nullptr: no filter.
+struct DeltaArgs {
+  const uint32_t* pmax;
+  int nseg0;
+  float thr_off;
+  int32_t* counts;
+};
+
+// Inverse of score_key.
+__device__ __forceinline__ float key_score(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  return __uint_as_float(u);
+}
+
 // Per-row final selection over candidate segments (merging groups of
 // segments first when a row's list is long). merge_ws: merge_workspace_bytes.
 size_t merge_workspace_bytes(int rows, int nseg, int k);
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
-                               int32_t* idx, void* merge_ws, hipStream_t st);
+                               int32_t* idx, void* merge_ws, hipStream_t st, DeltaArgs dl = DeltaArgs{});
 // Final selection fused with the attention of each row's query heads over the
 // selected tokens (one split), when select_attend_fused(nseg, k, G) holds.
 bool select_attend_fused(int nseg, int k, int G);
 hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
                                 const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
-                                hipStream_t st);
+                                hipStream_t st, DeltaArgs dl = DeltaArgs{});
 
 }  // namespace jssa

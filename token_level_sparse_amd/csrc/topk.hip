@@ -111,7 +111,7 @@ constexpr int kAttendMaxK = 512;
 template <int NT, int EF, bool MERGE, int GT = 0>
 __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
                                                    CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs,
-                                                   AttendArgs at = AttendArgs{}) {
+                                                   AttendArgs at = AttendArgs{}, DeltaArgs dl = DeltaArgs{}) {
   static_assert(GT == 0 || !MERGE, "attention follows the row's final selection only");
   constexpr int NW = NT / 64;
   __shared__ FinalSmem<NT> sm;
@@ -174,6 +174,31 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   for (int x = 0; x < SPT; ++x) {
     c[x] = tid * SPT + x < nseg ? c[x] : 0;
     mine += c[x];
+  }
+  // top-delta (final level only): the row's pseudo-max and the key a kept
+  // token must reach (0: no filter)
+  uint32_t thr_key = 0u;
+  if constexpr (!MERGE) {
+    if (dl.pmax) {                                      // block-uniform
+      __shared__ uint32_t pred[NW];
+      uint32_t pm = 0u;
+      for (int s = tid; s < dl.nseg0; s += NT) {
+        const uint32_t v = dl.pmax[int64_t(row) * dl.nseg0 + s];
+        pm = v > pm ? v : pm;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = uint32_t(__shfl_xor(int(pm), o, 64));
+        pm = y > pm ? y : pm;
+      }
+      if (lane == 0) pred[wv] = pm;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) pm = pred[i] > pm ? pred[i] : pm;
+      if (pm != 0u) thr_key = score_key(key_score(pm) - dl.thr_off);
+      const uint32_t neg_inf = score_key(-__builtin_inff());
+      thr_key = thr_key > neg_inf ? thr_key : neg_inf + 1u;      // -inf scores: no valid page
+    }
   }
   int n;
   int run = block_scan<NT>(mine, sm.scan, &n) - mine;
@@ -345,6 +370,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
         if (ck[e] > tkey) t = true;
         else if (ck[e] == tkey) t = tr++ < trem;
       }
+      t = t && ck[e] >= thr_key;                        // top-delta filter (thr_key 0: none)
       take |= t ? 1u << e : 0u;
     }
     const int ns = __popc(take);
@@ -375,6 +401,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   } else {
     if (write_idx)
       for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+    if (dl.counts && write_idx && tid == 0) dl.counts[row] = out_base;
   }
   if constexpr (GT > 0) {
     constexpr int STEPS = 8, RB = STEPS * 4;
@@ -441,7 +468,7 @@ size_t merge_workspace_bytes(int rows, int nseg, int k) {
 }
 
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
-                               int32_t* idx, void* merge_ws, hipStream_t st) {
+                               int32_t* idx, void* merge_ws, hipStream_t st, DeltaArgs dl) {
   if (segs.nseg > kMaxSeg) return hipErrorInvalidValue;
   CandSegs cur = segs;
   if (needs_merge(segs.nseg, k)) {
@@ -466,10 +493,10 @@ hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_
   // are streamed from memory page by page
   if (int64_t(cur.nseg) * k <= kFinalDirect)
     hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
-                       cur, cur.nseg, idx, CandSegs{});
+                       cur, cur.nseg, idx, CandSegs{}, AttendArgs{}, dl);
   else
     hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
-                       cur, cur.nseg, idx, CandSegs{});
+                       cur, cur.nseg, idx, CandSegs{}, AttendArgs{}, dl);
   return hipGetLastError();
 }
 
@@ -479,7 +506,7 @@ bool select_attend_fused(int nseg, int k, int G) {
 
 hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
                                 const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
-                                hipStream_t st) {
+                                hipStream_t st, DeltaArgs dl) {
   if (segs.nseg > kMaxSeg || !select_attend_fused(segs.nseg, k, g.G)) return hipErrorInvalidValue;
   const int rows = g.B * g.Hkv;
   // Spread the row's query heads over hs blocks until the launch covers the
@@ -495,7 +522,7 @@ hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uin
   const int gt = hpb <= 2 ? hpb : (hpb % 5 == 0 ? 5 : 4);
 #define JSSA_FA(GT)                                                                                      \
   hipLaunchKernelGGL((final_kernel<512, 16, false, GT>), dim3(rows * hs), dim3(512), 0, st, g.Hkv,         \
-                     g.max_seq, g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa)
+                     g.max_seq, g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa, dl)
   switch (gt) {
     case 1: JSSA_FA(1); break;
     case 2: JSSA_FA(2); break;

@@ -31,7 +31,8 @@ ENTRY_POINTS = (
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
-    "jssa_mla_up_v", "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
+    "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
+    "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
     "jssa_calib_projection", "jssa_status_string", "jssa_last_error", "jssa_version",
 )
 
@@ -56,6 +57,10 @@ class MlaDesc(ctypes.Structure):
                 ("r", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("seq_lens", ctypes.c_void_p)]
 
 
+class TopDeltaRule(ctypes.Structure):
+    _fields_ = [("delta", ctypes.c_float), ("n_sink", ctypes.c_int32), ("n_local", ctypes.c_int32)]
+
+
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _P = ctypes.POINTER
 _SIGS = {
@@ -78,6 +83,10 @@ _SIGS = {
     "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_mla_indexed_decode": [_P(MlaDesc), _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_mla_up_v": [_P(MlaDesc), _vp, _vp, _vp, _vp],
+    "jssa_score_topdelta_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
+    "jssa_score_topdelta": [_P(GqaDesc), _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp, _vp, _sz, _vp],
+    "jssa_score_topdelta_attend": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp,
+                                   _vp, _vp, _vp, _sz, _vp],
     "jssa_calib_workspace_size": [_P(GqaDesc), _P(_sz)],
     "jssa_calib_key_moments": [_P(GqaDesc), _vp, _vp, _vp, _sz, _vp],
     "jssa_calib_query_moments": [_i32, _i32, _i32, _vp, _vp, _vp],
@@ -279,3 +288,32 @@ def jssa_calib_projection(S_q, S_k, r: int):
     _check(_lib.jssa_calib_projection(d, r, S_q.ctypes.data, S_k.ctypes.data, P.ctypes.data, w.ctypes.data),
            "jssa_calib_projection")
     return P, w
+
+
+def topdelta_rule(delta: float, n_sink: int = 4, n_local: int = 64) -> TopDeltaRule:
+    return TopDeltaRule(delta, n_sink, n_local)
+
+
+def jssa_score_topdelta_workspace_size(desc, k_max) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_score_topdelta_workspace_size(ctypes.byref(desc), k_max, ctypes.byref(n)),
+           "jssa_score_topdelta_workspace_size")
+    return n.value
+
+
+def jssa_score_topdelta(desc, q, P, Kp, k_max, rule, scale, idx, counts, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topdelta(ctypes.byref(desc), _p(q), _p(P), _p(Kp), k_max,
+                                    None if rule is None else ctypes.byref(rule), scale, _p(idx), _p(counts),
+                                    _p(ws), ws_bytes, _s(stream)), "jssa_score_topdelta")
+
+
+def jssa_score_topdelta_attend(desc, q, P, Kp, K, V, k_max, rule, scale, idx, counts, out, lse, ws,
+                               ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topdelta_attend(ctypes.byref(desc), _p(q), _p(P), _p(Kp), _p(K), _p(V), k_max,
+                                           None if rule is None else ctypes.byref(rule), scale, _p(idx),
+                                           _p(counts), _p(out), _p(lse), _p(ws), ws_bytes, _s(stream)),
+           "jssa_score_topdelta_attend")

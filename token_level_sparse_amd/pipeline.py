@@ -298,3 +298,30 @@ def calibrate(c: GqaCache, q_samples: torch.Tensor, r: int):
         Ps.append(P)
         ws.append(w)
     return torch.from_numpy(np.stack(Ps)).to(c.K.device), np.stack(ws)
+
+
+# ---------------------------------------------------------------------------
+# Top-delta step: the fused chunk pass, then the final selection with the
+# top-delta filter and the attention over the kept tokens.
+# ---------------------------------------------------------------------------
+class TopDeltaStep:
+    def __init__(self, cache: GqaCache, k_max: int, delta: float, n_sink: int = 4, n_local: int = 64):
+        c = cache
+        self.c, self.k_max = c, k_max
+        self.rule = jssa.topdelta_rule(delta, n_sink, n_local)
+        dev = c.K.device
+        self.ws = torch.empty(jssa.jssa_score_topdelta_workspace_size(c.desc, k_max), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty((c.B, c.Hkv, k_max), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((c.B, c.Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+
+    def select(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topdelta(c.desc, c.q, c.P, c.Kp, self.k_max, self.rule, c.scale, self.idx, self.counts,
+                                 self.ws, stream=stream)
+
+    def run(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topdelta_attend(c.desc, c.q, c.P, c.Kp, c.K, c.V, self.k_max, self.rule, c.scale, self.idx,
+                                        self.counts, self.out, self.lse, self.ws, stream=stream)
