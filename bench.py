@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
     ap.add_argument("--no-calib", action="store_true", help="skip the subspace-calibration leg")
+    ap.add_argument("--no-topdelta", action="store_true", help="skip the top-delta leg")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     return ap.parse_args()
 
@@ -268,6 +269,21 @@ def main():
             "attention_stage_speedup_vs_dense": {"gather_free": round(dense_attn_us / sparse_attn_us, 2),
                                                  "gather": round(dense_attn_us / gather_attn_us, 2)}}
         print("[bench] dense and gather comparisons done", file=sys.stderr, flush=True)
+
+    if not args.no_topdelta:
+        td = {}
+        for delta in (1.0, 2.0, 3.0):
+            tds = pipeline.TopDeltaStep(c, k, delta, 4, 64)
+            tsteps = max(5, args.steps // 2)
+            ttotal, _ = time_loop([tds.run], tsteps, 2, torch, stream)
+            cnt = tds.counts.cpu().numpy()
+            td[f"delta_{delta:g}"] = {"ms_per_step": round(ttotal / tsteps * 1e3, 4),
+                                      "steps_per_s": round(tsteps / ttotal, 2),
+                                      "mean_kept": round(float(cnt.mean()), 1), "min_kept": int(cnt.min()),
+                                      "max_kept": int(cnt.max())}
+        result["topdelta"] = {"k_max": k, "n_sink": 4, "n_local": 64, "entry_point": "jssa_score_topdelta_attend",
+                              "topk_step_ms": round(ms, 4), "by_delta": td}
+        print("[bench] top-delta leg done", file=sys.stderr, flush=True)
 
     if not args.no_calib and not cfg.paged:
         result["calibration"] = bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream)
