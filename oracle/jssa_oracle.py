@@ -16,6 +16,9 @@ blocks. Sources (page title, section):
             gather-free ...", Synopsis.
 * [JSSA-I]  same digest, Interpretation (scoring space, gather-free reads).
 * [JSSA-P]  same digest, Perspective (GQA / hybrid / MLA coverage).
+* [DOSA]    "DoSA Makes Sparse Attention Selection Conditional Without
+            Approximation" (cctest.ai), How the method works (seed threshold,
+            upper-bound certificate, exact top-k preserved).
 * [FFD]     "Faster Than Flash: Exploiting Attention Sparsity for Efficient
             Long-Context Decoding" (evolve.pub review), Summary, Key claims
             and FAQ (the top-delta rule, the sink/local pseudo-max and its
@@ -54,6 +57,18 @@ R13 top-delta selection ([FFD], the top-delta rule and its fail-safe
    tokens by the order of R3 and listed like R3's, with its size. No valid
    special token (or T_b = 0): nothing is filtered. Decisions are taken on
    scores rounded to fp32, the threshold in fp64.
+R14 lossless screening ([DOSA]: a seed set gives a lower bound on the
+   winning threshold; candidates whose upper bound falls below it are
+   dropped before exact scoring, and the top-k is unchanged). Applied to the
+   one r-dim dot product s_t = qp . Kp_t: a tile of 64 consecutive tokens
+   has the box bound ub = sum_c max(qp_c lo_c, qp_c hi_c), lo and hi the
+   per-dimension minimum and maximum of its valid projected keys, so
+   ub >= s_t for each of its tokens. The seed set is a caller-given list of
+   token indices per (sequence, KV head) (in decoding, e.g. the previous
+   step's selection); tau is the k-th largest fp32 score over its distinct
+   valid entries (-inf with fewer than k). A tile with ub < tau holds no
+   token of the top-k (each of its scores is below tau <= the k-th score)
+   and is skipped.
 R12 subspace calibration ([JSSA-A]: the subspace minimises a token-score
    preservation error, which is bounded by a marginal objective with a
    closed-form spectral solution; the formulas are not on the pages). The
@@ -375,3 +390,70 @@ def select_topdelta(scores, k_max: int, delta: float, n_sink: int, n_local: int,
     out = np.full(k_max, -1, np.int64)
     out[:keep.shape[0]] = keep
     return out, int(keep.shape[0])
+
+
+# ---------------------------------------------------------------------------
+# Lossless screening (R14)  [DOSA]
+# ---------------------------------------------------------------------------
+SCREEN_TILE = 64
+
+
+def tile_bounds(Kp_bits, valid=None, tile: int = SCREEN_TILE):
+    """Per tile of `tile` consecutive tokens: (lo, hi) [ntiles, r], the
+    per-dimension min and max of the tile's valid projected keys (fp64);
+    a tile without a valid token gets lo = +inf, hi = -inf."""
+    Kp = bf16_to_f64(Kp_bits)
+    n, r = Kp.shape
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    nt = (n + tile - 1) // tile
+    lo = np.full((nt, r), np.inf)
+    hi = np.full((nt, r), -np.inf)
+    for i in range(nt):
+        rows = Kp[i * tile:(i + 1) * tile][ok[i * tile:(i + 1) * tile]]
+        if rows.shape[0]:
+            lo[i] = rows.min(axis=0)
+            hi[i] = rows.max(axis=0)
+    return lo, hi
+
+
+def tile_upper_bounds(qp, lo, hi) -> np.ndarray:
+    """ub per tile = sum_c max(qp_c lo_c, qp_c hi_c) (-inf for empty tiles)."""
+    qp = np.asarray(qp, np.float64)
+    empty = ~np.isfinite(lo).all(axis=1)
+    l = np.where(np.isfinite(lo), lo, 0.0)
+    h = np.where(np.isfinite(hi), hi, 0.0)
+    ub = np.maximum(l * qp, h * qp).sum(axis=1)
+    return np.where(empty, -np.inf, ub)
+
+
+def seed_threshold(scores, seeds, k: int, valid=None) -> float:
+    """tau: the k-th largest fp32-rounded score over the distinct valid
+    tokens listed in `seeds` (entries outside [0, T_b) ignored); -inf when
+    there are fewer than k."""
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    n = s32.shape[0]
+    sd = np.unique(np.asarray(seeds, np.int64).ravel())
+    sd = sd[(sd >= 0) & (sd < n)]
+    if valid is not None:
+        sd = sd[np.asarray(valid, bool)[sd]]
+    if sd.shape[0] < k:
+        return -np.inf
+    return float(np.sort(s32[sd])[::-1][k - 1])
+
+
+def screened_topk(scores, qp, Kp_bits, seeds, k: int, valid=None):
+    """(R3's selection restricted to the tokens of the tiles that survive
+    screening, the keep flag per tile)."""
+    lo, hi = tile_bounds(Kp_bits, valid)
+    keep_tile = tile_upper_bounds(qp, lo, hi) >= seed_threshold(scores, seeds, k, valid)
+    n = np.asarray(scores).shape[0]
+    ok = np.ones(n, bool) if valid is None else np.asarray(valid, bool)
+    alive = ok & np.repeat(keep_tile, SCREEN_TILE)[:n]
+    s = np.where(alive, np.asarray(scores, np.float64), -np.inf)
+    cand = np.nonzero(alive)[0]
+    s32 = s.astype(np.float32).astype(np.float64)
+    order = cand[np.lexsort((cand, -s32[cand]))]
+    keepi = np.sort(order[:k])
+    out = np.full(k, -1, np.int64)
+    out[:keepi.shape[0]] = keepi
+    return out, keep_tile

@@ -117,6 +117,32 @@ def _threshold_local_off_by_one(scores, delta, n_sink, n_local, scale, G, valid=
     return _orig_threshold(scores, delta, n_sink, max(0, n_local - 1), scale, G, valid)
 
 
+def _ub_min(qp, lo, hi):
+    qp = np.asarray(qp, np.float64)
+    l = np.where(np.isfinite(lo), lo, 0.0)
+    h = np.where(np.isfinite(hi), hi, 0.0)
+    return np.minimum(l * qp, h * qp).sum(axis=1)
+
+
+def _seed_with_duplicates(scores, seeds, k, valid=None):
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    sd = np.asarray(seeds, np.int64).ravel()
+    sd = sd[(sd >= 0) & (sd < s32.shape[0])]
+    if valid is not None:
+        sd = sd[np.asarray(valid, bool)[sd]]
+    return -np.inf if sd.shape[0] < k else float(np.sort(s32[sd])[::-1][k - 1])
+
+
+def _tile_bounds_all_rows(Kp_bits, valid=None, tile=64):
+    return _orig_tile_bounds(Kp_bits, None, tile)
+
+
+def _seed_threshold_kplus1(scores, seeds, k, valid=None):
+    return _orig_seed_threshold(scores, seeds, k + 1, valid)
+
+
+_orig_tile_bounds = O.tile_bounds
+_orig_seed_threshold = O.seed_threshold
 _orig_topdelta = O.select_topdelta
 _orig_threshold = O.topdelta_threshold
 _orig_attend = O.attend
@@ -146,6 +172,10 @@ MUTATIONS = [
     ("select_topdelta", _topdelta_no_group, [pins.test_topdelta_golden_hand]),
     ("select_topdelta", _strict_impl, [pins.test_topdelta_golden_hand]),
     ("topdelta_threshold", _threshold_local_off_by_one, [pins.test_topdelta_golden_hand]),
+    ("tile_upper_bounds", _ub_min, [lambda: pins.test_screen_bounds_sound_and_lossless(1)]),
+    ("seed_threshold", _seed_with_duplicates, [pins.test_screen_seed_closed_form]),
+    ("tile_bounds", _tile_bounds_all_rows, [pins.test_screen_hand_values]),
+    ("seed_threshold", _seed_threshold_kplus1, [pins.test_screen_seed_closed_form]),
 ]
 
 

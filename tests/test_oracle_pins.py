@@ -562,3 +562,76 @@ def test_topdelta_brute_force_small(seed):
     idx, cnt = O.select_topdelta(s, k, delta, ns, nl, scale, G, valid)
     assert cnt == len(kept)
     np.testing.assert_array_equal(idx, kept + [-1] * (k - len(kept)))
+
+
+# ---------------------------------------------------------------------------
+# lossless screening (DoSA article on cctest.ai, How the method works: seed
+# threshold, upper-bound certificate, unchanged top-k; reading R14 in the
+# oracle's header)
+# ---------------------------------------------------------------------------
+def _clustered_keys(rng, n, r, seg=256, noise=0.1):
+    """Keys in segments of `seg` tokens around their own random centre (a
+    topic per segment): tiles inside a segment are narrow boxes."""
+    c = rng.standard_normal(((n + seg - 1) // seg, r))
+    return bf16(np.repeat(c, seg, axis=0)[:n] + noise * rng.standard_normal((n, r)))
+
+
+def test_screen_hand_values():
+    """Two-token tile [[1, -2], [3, 0]], qp = [2, -1]: lo = [1, -2], hi = [3, 0],
+    ub = max(2, 6) + max(2, 0) = 8 >= the scores 4 and 6. A third, invalid
+    row does not widen the box."""
+    Kp = bf16([[1, -2], [3, 0], [100, 100]])
+    lo, hi = O.tile_bounds(Kp, valid=[1, 1, 0], tile=3)
+    np.testing.assert_array_equal(lo, [[1, -2]])
+    np.testing.assert_array_equal(hi, [[3, 0]])
+    assert O.tile_upper_bounds([2.0, -1.0], lo, hi)[0] == 8.0
+    lo, hi = O.tile_bounds(bf16([[2, 5]] * 4), tile=4)          # identical rows: the bound is attained
+    assert O.tile_upper_bounds([1.5, -0.5], lo, hi)[0] == 1.5 * 2 - 0.5 * 5
+
+
+def test_screen_seed_closed_form():
+    """tau is the k-th largest score over the distinct valid seeds: scores
+    s_t = t, seeds {990, 5, 700, 990, -1, 5000, 800}, k = 3 -> {990, 800,
+    700, 5} ranked, tau = 700; with token 800 invalid, tau = 5; fewer than k
+    valid seeds -> -inf."""
+    s = np.arange(1000.0)
+    seeds = [990, 5, 700, 990, -1, 5000, 800]
+    assert O.seed_threshold(s, seeds, 3) == 700.0
+    v = np.ones(1000, bool)
+    v[800] = False
+    assert O.seed_threshold(s, seeds, 3, v) == 5.0
+    assert O.seed_threshold(s, seeds, 5) == -np.inf
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_screen_bounds_sound_and_lossless(seed):
+    """Every tile bound covers its tokens' scores, tau never exceeds the
+    k-th score, and the screened selection equals the plain one, whatever
+    the seeds. With the previous step's selection as seeds (a nearby query)
+    and clustered keys, most tiles are skipped."""
+    rng = np.random.default_rng(300 + seed)
+    n, r = int(rng.integers(600, 6000)), 16
+    Kp = _clustered_keys(rng, n, r) if seed % 2 else bf16(rng.standard_normal((n, r)))
+    qp = rng.standard_normal(r) * 3
+    valid = rng.random(n) < 0.97
+    Kf = O.bf16_to_f64(Kp)
+    s = np.where(valid, Kf @ qp, -np.inf)
+    k = int(rng.integers(1, 80))
+    lo, hi = O.tile_bounds(Kp, valid)
+    ub = O.tile_upper_bounds(qp, lo, hi)
+    for i in range(ub.shape[0]):
+        seg = s[i * 64:(i + 1) * 64]
+        if np.isfinite(seg.max()):
+            assert ub[i] >= seg.max() - 1e-9 * (1 + abs(seg.max()))
+    qprev = qp + 0.3 * rng.standard_normal(r)                  # the previous step's query
+    seeds = O.select_topk(np.where(valid, Kf @ qprev, -np.inf), k)
+    seeds_rand = rng.integers(0, n, 3 * k)
+    s32 = s.astype(np.float32).astype(np.float64)
+    for sd in (seeds, seeds_rand):
+        tau = O.seed_threshold(s, sd, k, valid)
+        assert tau <= np.sort(s32)[::-1][k - 1]
+        got, keep = O.screened_topk(s, qp, Kp, sd, k, valid)
+        np.testing.assert_array_equal(got, O.select_topk(s, k))
+    if seed % 2:
+        _, keep = O.screened_topk(s, qp, Kp, seeds, k, valid)
+        assert keep.mean() < 0.7, f"clustered keys: {keep.mean():.2f} of tiles kept"
