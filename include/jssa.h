@@ -368,6 +368,52 @@ JSSA_API jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const
                                                 void* stream);
 
 /*
+ * Lossless tile screening ("DoSA Makes Sparse Attention Selection
+ * Conditional Without Approximation", cctest.ai, How the method works: a
+ * seed set bounds the winning threshold from below; candidates whose upper
+ * bound is lower are dropped before exact scoring; the top-k is unchanged).
+ * Tiles are 64 consecutive tokens of one (sequence, KV head). A tile's box
+ * bound ub = sum_c max(qp_c lo_c, qp_c hi_c), lo/hi the per-dimension min/max
+ * of its valid projected keys, is >= each of its scores. tau is the k-th
+ * largest score over the distinct valid seed tokens (caller-given, e.g. the
+ * previous decode step's selection), so tau <= the k-th score; a tile with
+ * ub < tau is not read by the score stream. The comparison carries a margin
+ * of 2^-16 * sum|qp_c Kp_c| on both sides so that fp32 rounding never drops
+ * a tile that exact arithmetic keeps. The selection is exactly that of
+ * jssa_score_topk; only the bytes read change. With fewer than k distinct
+ * valid seeds nothing is dropped.
+ */
+
+/* Size of the tile bounds: device bf16 [B,Hkv,ceil(max_seq/64),2,r], per tile
+ * the r minima then the r maxima (+inf / -inf for a tile with no valid token). */
+JSSA_API jssa_status jssa_tile_bounds_size(const jssa_gqa_desc* desc, size_t* bytes);
+
+/* Builds every tile's bounds from the projected cache Kp (layout of desc).
+ * Exact (the min and max of bf16 values). After appends, build again (the
+ * tiles holding new tokens change). */
+JSSA_API jssa_status jssa_build_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, void* bounds, void* stream);
+
+/* Workspace of jssa_score_topk_screened_chunks: the jssa_score_topk workspace
+ * (same layout, at the start) plus one keep bit per tile. */
+JSSA_API jssa_status jssa_score_topk_screened_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes);
+
+/*
+ * Screening, then the fused score stream + chunk selection over the kept
+ * tiles only. Finish with jssa_score_topk_final or
+ * jssa_score_topk_final_attend on the same workspace; the indices are those
+ * of jssa_score_topk.
+ *  bounds      from jssa_build_tile_bounds
+ *  seeds       device int32 [B,Hkv,n_seed] token indices (entries outside
+ *              [0, T_b), repeats and tokens without a page are ignored);
+ *              NULL allowed when n_seed = 0; 0 <= n_seed <= 4096
+ *  kept_tiles  device int32 [B,Hkv] or NULL: tiles read per (b, j)
+ */
+JSSA_API jssa_status jssa_score_topk_screened_chunks(const jssa_gqa_desc* desc, const void* q, const float* P,
+                                                     const void* Kp, const void* bounds, const int32_t* seeds,
+                                                     int32_t n_seed, int32_t k, int32_t* kept_tiles, void* ws,
+                                                     size_t ws_bytes, void* stream);
+
+/*
  * Subspace calibration (JSSA abstract on weekinpapers, Abstract: the shared
  * query-key subspace minimises a token-score preservation error through a
  * marginal upper bound that has a closed-form spectral solution; the

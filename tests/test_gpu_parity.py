@@ -571,6 +571,115 @@ def test_topdelta_attend(J, PL, case):
 
 
 # ---------------------------------------------------------------------------
+# lossless tile screening (reading R14)
+# ---------------------------------------------------------------------------
+def _prev_step_seeds(PL, c, inp, k, noise=0.1, rs=7):
+    """The previous decode step's selection: the top-k under a nearby query."""
+    rng = np.random.default_rng(rs)
+    q_prev = synth.f32_to_bf16_bits(O.bf16_to_f64(inp.q) + noise * rng.standard_normal(inp.q.shape))
+    q_keep = c.q
+    c.q = torch.from_numpy(q_prev.view(np.int16)).cuda()
+    st = PL.SparseStep(c, k=k, fused=True)
+    st.score_topk()
+    torch.cuda.synchronize()
+    c.q = q_keep
+    return st.idx.clone()
+
+
+def _screen_inputs(case):
+    if case == "tiny":
+        return synth.make_gqa(synth.TINY), 256
+    if case == "llama_random_seeds":
+        return synth.make_gqa(synth.LLAMA8B_32K), 256
+    if case == "clustered_32k":
+        return synth.make_gqa(replace(synth.LLAMA8B_32K, key_model="clustered", seed=95)), 256
+    if case == "clustered_paged_invalid":
+        inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=20000, len_lo=9000, len_hi=20000, seed=96,
+                                     key_model="clustered"))
+        inp.page_table[0, 5] = -1
+        inp.page_table[1, 40] = -1
+        return inp, 512
+    if case == "ragged_dup_seeds":
+        return ragged_inputs(), 100
+    return synth.make_gqa(synth.TINY), 64                     # no_seeds
+
+
+@pytest.mark.parametrize("case", ["tiny", "llama_random_seeds", "clustered_32k", "clustered_paged_invalid",
+                                  "ragged_dup_seeds", "no_seeds"])
+def test_screened_topk_lossless(J, PL, case):
+    inp, k = _screen_inputs(case)
+    cfg = inp.cfg
+    c = PL.GqaCache(inp)
+    c.project()
+    if case == "llama_random_seeds":
+        seeds = torch.randint(0, cfg.T, (cfg.B, cfg.Hkv, 3 * k), dtype=torch.int32, device="cuda")
+    elif case == "ragged_dup_seeds":
+        prev = _prev_step_seeds(PL, c, inp, k)
+        seeds = torch.cat([prev, prev[:, :, :40], torch.full_like(prev[:, :, :8], 10 ** 6)], dim=2).contiguous()
+    elif case == "no_seeds":
+        seeds = torch.zeros((cfg.B, cfg.Hkv, 0), dtype=torch.int32, device="cuda")
+    else:
+        seeds = _prev_step_seeds(PL, c, inp, k)
+    sc = PL.ScreenedStep(c, k, seeds)
+    sc.build_bounds()
+    sc.chunks()
+    sc.final()
+    plain = PL.SparseStep(c, k=k, fused=True)
+    plain.score_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(sc.idx), _np(plain.idx))          # the selection is unchanged
+    # bounds: exact bf16 min / max per tile
+    nt = (cfg.T + 63) // 64
+    bd = _np(sc.bounds).reshape(cfg.B, cfg.Hkv, nt, 2, cfg.r)
+    bdf = O.bf16_to_f64(bd)
+    # keep bits written after the jssa_score_topk workspace
+    base = J.jssa_score_topk_workspace_size(c.desc, k)
+    off = (base + 255) // 256 * 256
+    nwords = 2 * ((nt + 63) // 64)
+    kw = _np(sc.ws)[off:off + cfg.B * cfg.Hkv * nwords * 4].view(np.uint32).reshape(cfg.B, cfg.Hkv, nwords)
+    kept_gpu = _np(sc.kept_tiles)
+    sd = _np(seeds)
+    dropped, total = 0, 0
+    for b in range(cfg.B):
+        valid = U.unit_valid(inp, b)
+        Tb = int(inp.seq_lens[b])
+        ntb = (Tb + 63) // 64
+        for j in range(cfg.Hkv):
+            K, _, Kp, s, hs = U.oracle_unit(inp, b, j)
+            lo, hi = O.tile_bounds(Kp, valid)
+            np.testing.assert_array_equal(bdf[b, j, :ntb, 0], lo)
+            np.testing.assert_array_equal(bdf[b, j, :ntb, 1], hi)
+            qp = O.project_query(inp.q[b, hs], inp.P[j])
+            _, keep_o = O.screened_topk(np.where(valid, s, -np.inf), qp, Kp, sd[b, j], k, valid)
+            bits = np.unpackbits(kw[b, j].view(np.uint8), bitorder="little")[:ntb].astype(bool)
+            assert np.all(bits[keep_o]), "a tile the oracle keeps was dropped"
+            assert kept_gpu[b, j] == bits.sum()
+            dropped += ntb - bits.sum()
+            total += ntb
+    if case.startswith("clustered"):
+        assert dropped / total > 0.3, f"clustered keys: only {dropped}/{total} tiles dropped"
+    if case == "no_seeds":
+        assert dropped == 0
+
+
+def test_screened_final_attend_identical(J, PL):
+    inp = synth.make_gqa(replace(synth.LLAMA8B_32K, key_model="clustered", seed=97))
+    c = PL.GqaCache(inp)
+    c.project()
+    seeds = _prev_step_seeds(PL, c, inp, 256)
+    sc = PL.ScreenedStep(c, 256, seeds)
+    sc.build_bounds()
+    sc.chunks()
+    sc.final_attend()
+    plain = PL.SparseStep(c, k=256, S=1, fused=True)
+    plain.run()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(sc.idx), _np(plain.idx))
+    np.testing.assert_array_equal(_np(sc.out), _np(plain.out))
+    np.testing.assert_array_equal(_np(sc.lse), _np(plain.lse))
+
+
+# ---------------------------------------------------------------------------
 # subspace calibration: second moments (GPU), spectral step (host library),
 # oracle top-k recall of the calibrated subspace
 # ---------------------------------------------------------------------------

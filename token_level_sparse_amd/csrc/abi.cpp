@@ -480,6 +480,57 @@ jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const void* q,
   return hip_status(e, __func__);
 }
 
+jssa_status jssa_tile_bounds_size(const jssa_gqa_desc* desc, size_t* bytes) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
+  *bytes = size_t(desc->B) * desc->Hkv * jssa::screen_tiles(desc->max_seq) * 2 * desc->r * sizeof(uint16_t);
+  return JSSA_OK;
+}
+
+jssa_status jssa_build_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, void* bounds, void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  REQUIRE_PTR(Kp); REQUIRE_PTR(bounds); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  return hip_status(jssa::launch_tile_bounds(to_dev(desc), static_cast<const uint16_t*>(Kp),
+                                             static_cast<uint16_t*>(bounds), S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_score_topk_screened_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes) {
+  size_t base = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &base)) return s;
+  const size_t rows = size_t(desc->B) * desc->Hkv;
+  *bytes = jssa::align256(base) + jssa::align256(rows * jssa::screen_words(desc->max_seq) * sizeof(uint32_t));
+  return JSSA_OK;
+}
+
+jssa_status jssa_score_topk_screened_chunks(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                           const void* bounds, const int32_t* seeds, int32_t n_seed, int32_t k,
+                                           int32_t* kept_tiles, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_screened_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(bounds); REQUIRE_PTR(ws);
+  REQUIRE_ALIGNED_OPT(kept_tiles); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  if (n_seed < 0 || n_seed > jssa::screen_max_seeds())
+    return fail(JSSA_ERR_SHAPE, "%s: n_seed %d outside [0, %d]", __func__, n_seed, jssa::screen_max_seeds());
+  if (n_seed > 0) REQUIRE_PTR(seeds);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  size_t base = 0;
+  jssa_score_topk_workspace_size(desc, k, &base);
+  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
+                                         jssa::score_topk_segment_cap(), nullptr);
+  auto* keep = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + jssa::align256(base));
+  const jssa::GqaDev g = to_dev(desc);
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* Kp16 = static_cast<const uint16_t*>(Kp);
+  hipError_t e = jssa::launch_screen(g, q16, P, Kp16, static_cast<const uint16_t*>(bounds), seeds, n_seed, k, keep,
+                                     kept_tiles, S(stream));
+  if (e == hipSuccess)
+    e = jssa::launch_score_chunks(g, q16, P, Kp16, k, nullptr, segs, S(stream), nullptr, 0, 0, keep,
+                                  jssa::screen_words(desc->max_seq));
+  return hip_status(e, __func__);
+}
+
 jssa_status jssa_calib_workspace_size(const jssa_gqa_desc* desc, size_t* bytes) {
   if (jssa_status s = check_desc(__func__, desc, false)) return s;
   if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);

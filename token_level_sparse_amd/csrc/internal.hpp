@@ -26,7 +26,18 @@ hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P,
                              float* scores, int32_t* idx, CandSegs segs, void* merge_ws, hipStream_t st);
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax = nullptr,
-                               int n_sink = 0, int n_local = 0);
+                               int n_sink = 0, int n_local = 0, const uint32_t* keep = nullptr,
+                               int keep_words = 0);
+
+// Lossless tile screening (screen.hip): 64-token tile bounds of the projected
+// cache, and one keep bit per tile from a seed-set threshold.
+int screen_tiles(int max_seq);
+int screen_words(int max_seq);
+int screen_max_seeds();
+hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bounds, hipStream_t st);
+hipError_t launch_screen(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
+                         const uint16_t* bounds, const int32_t* seeds, int n_seed, int k, uint32_t* keep,
+                         int32_t* kept_tiles, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
 

@@ -74,7 +74,12 @@ struct FusedOut {
   int write_scores;
   uint32_t* pmax;           // top-delta: per segment, the largest key of the row's sink/local tokens in it
   int n_sink, n_local;      // sink tokens: t < n_sink; local tokens: t >= T_b - n_local
+  const uint32_t* keep;     // screening: one bit per 64-token tile ([rows, keep_words]); nullptr: all kept
+  int keep_words;
 };
+// A token of a dropped tile is staged with this value: a NaN whose score_key
+// is 0, the key of no token (finite scores map to keys above 0).
+constexpr uint32_t kDroppedBits = 0xffffffffu;
 
 template <int R>
 struct ScoreSmem {
@@ -143,13 +148,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
     __syncthreads();
   }
+  // Screening: the chunk's 128 tiles of 64 tokens have one keep bit each. A
+  // dropped tile's loads still go out (no branch) but all read the chunk's
+  // first row, a cache hit, so the tile costs no HBM bytes; its tokens are
+  // staged as dropped.
+  uint32_t kw[4] = {~0u, ~0u, ~0u, ~0u};
+  if (FUSED && fo.keep) {
+    const uint32_t* kp = fo.keep + int64_t(b * g.Hkv + j) * fo.keep_words;
+    const int w0 = t_begin / (64 * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kw[i] = w0 + i < fo.keep_words ? kp[w0 + i] : 0u;
+  }
+  auto dropped = [&](int tile) -> bool {            // wave-uniform
+    const int ct = tile * kWaves + w;
+    if (!FUSED || ct >= 128) return false;
+    const uint32_t word = ct < 32 ? kw[0] : (ct < 64 ? kw[1] : (ct < 96 ? kw[2] : kw[3]));
+    return ((word >> (ct & 31)) & 1u) == 0u;
+  };
   auto load_tile = [&](int tile, u32x4 (&buf)[PP]) {
     const int t0 = t_begin + (tile * kWaves + w) * 64;
+    const bool drop = dropped(tile);
 #pragma unroll
     for (int m = 0; m < PP; ++m) {
       const int p = m * 64 + lane;
       int t = t0 + p / PP;
       t = t < tend ? t : tend - 1;
+      t = drop ? t_begin : t;
       int64_t off;
       if (!paged) {
         off = ubase + int64_t(t) * R;
@@ -266,7 +290,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   auto stage_tile = [&](int tile, const u32x4 (&buf)[PP]) {
     const int off = (tile * kWaves + w) * 64;
     const float x = tile_scores(buf);
-    stage[sidx(off + lane)] = token_ok(t_begin + off + lane) ? x : -__builtin_inff();
+    const float v = token_ok(t_begin + off + lane) ? x : -__builtin_inff();
+    stage[sidx(off + lane)] = dropped(tile) ? __uint_as_float(kDroppedBits) : v;
   };
   // kDepth register buffers rotate with no copies between them (a copy of a
   // buffer whose loads are in flight would wait for them): while one tile's
@@ -385,8 +410,8 @@ int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
 
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax, int n_sink,
-                               int n_local) {
-  FusedOut fo{segs, k, scores ? 1 : 0, pmax, n_sink, n_local};
+                               int n_local, const uint32_t* keep, int keep_words) {
+  FusedOut fo{segs, k, scores ? 1 : 0, pmax, n_sink, n_local, keep, keep_words};
   return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores, st, fo);
 }
 

@@ -197,7 +197,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   // and leave as coalesced stores; more than fit go out directly.
   int mine = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) mine += (real(e) && key[e] >= thr) ? 1 : 0;
+  for (int e = 0; e < E; ++e) mine += (real(e) && key[e] >= thr && key[e] != 0u) ? 1 : 0;   // key 0: no token
   int tot;
   int at = block_scan<NT>(mine, sm.scan, &tot) - mine;
   uint32_t* okey = out.key + seg * out.cap;
@@ -208,7 +208,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   int32_t* sidx = reinterpret_cast<int32_t*>(sm.hist + kStaged);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (real(e) && key[e] >= thr) {
+    if (real(e) && key[e] >= thr && key[e] != 0u) {
       if (staged) {
         skey[at] = key[e];
         sidx[at] = base + tid * E + e;
@@ -303,7 +303,7 @@ __device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
 
   uint32_t mask = 0u;
 #pragma unroll
-  for (int e = 0; e < E; ++e) mask |= key[e] >= c ? (1u << e) : 0u;
+  for (int e = 0; e < E; ++e) mask |= (key[e] >= c && key[e] != 0u) ? (1u << e) : 0u;   // key 0: no token
   const int mine = __builtin_popcount(mask);
   int tot;
   int at = block_scan<NT>(mine, sm.scan, &tot) - mine;

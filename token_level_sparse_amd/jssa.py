@@ -32,7 +32,8 @@ ENTRY_POINTS = (
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
-    "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
+    "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_score_topk_screened_workspace_size",
+    "jssa_score_topk_screened_chunks", "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
     "jssa_calib_projection", "jssa_status_string", "jssa_last_error", "jssa_version",
 )
 
@@ -87,6 +88,10 @@ _SIGS = {
     "jssa_score_topdelta": [_P(GqaDesc), _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp, _vp, _sz, _vp],
     "jssa_score_topdelta_attend": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp,
                                    _vp, _vp, _vp, _sz, _vp],
+    "jssa_tile_bounds_size": [_P(GqaDesc), _P(_sz)],
+    "jssa_build_tile_bounds": [_P(GqaDesc), _vp, _vp, _vp],
+    "jssa_score_topk_screened_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
+    "jssa_score_topk_screened_chunks": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp],
     "jssa_calib_workspace_size": [_P(GqaDesc), _P(_sz)],
     "jssa_calib_key_moments": [_P(GqaDesc), _vp, _vp, _vp, _sz, _vp],
     "jssa_calib_query_moments": [_i32, _i32, _i32, _vp, _vp, _vp],
@@ -317,3 +322,29 @@ def jssa_score_topdelta_attend(desc, q, P, Kp, K, V, k_max, rule, scale, idx, co
                                            None if rule is None else ctypes.byref(rule), scale, _p(idx),
                                            _p(counts), _p(out), _p(lse), _p(ws), ws_bytes, _s(stream)),
            "jssa_score_topdelta_attend")
+
+
+def jssa_tile_bounds_size(desc) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_tile_bounds_size(ctypes.byref(desc), ctypes.byref(n)), "jssa_tile_bounds_size")
+    return n.value
+
+
+def jssa_build_tile_bounds(desc, Kp, bounds, stream=None):
+    _check(_lib.jssa_build_tile_bounds(ctypes.byref(desc), _p(Kp), _p(bounds), _s(stream)), "jssa_build_tile_bounds")
+
+
+def jssa_score_topk_screened_workspace_size(desc, k) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_score_topk_screened_workspace_size(ctypes.byref(desc), k, ctypes.byref(n)),
+           "jssa_score_topk_screened_workspace_size")
+    return n.value
+
+
+def jssa_score_topk_screened_chunks(desc, q, P, Kp, bounds, seeds, n_seed, k, kept_tiles, ws, ws_bytes=None,
+                                    stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_score_topk_screened_chunks(ctypes.byref(desc), _p(q), _p(P), _p(Kp), _p(bounds), _p(seeds),
+                                                n_seed, k, _p(kept_tiles), _p(ws), ws_bytes, _s(stream)),
+           "jssa_score_topk_screened_chunks")

@@ -325,3 +325,39 @@ class TopDeltaStep:
         c = self.c
         jssa.jssa_score_topdelta_attend(c.desc, c.q, c.P, c.Kp, c.K, c.V, self.k_max, self.rule, c.scale, self.idx,
                                         self.counts, self.out, self.lse, self.ws, stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# Screened step: tile bounds (kept with the cache), screening against a seed
+# set, the chunk pass over the kept tiles, then the usual final selection.
+# ---------------------------------------------------------------------------
+class ScreenedStep:
+    def __init__(self, cache: GqaCache, k: int, seeds: torch.Tensor):
+        c = cache
+        self.c, self.k = c, k
+        dev = c.K.device
+        self.seeds = seeds.contiguous()
+        self.n_seed = int(seeds.shape[-1]) if seeds is not None else 0
+        self.bounds = torch.empty(jssa.jssa_tile_bounds_size(c.desc) // 2, dtype=torch.int16, device=dev)
+        self.ws = torch.empty(jssa.jssa_score_topk_screened_workspace_size(c.desc, k), dtype=torch.uint8,
+                              device=dev)
+        self.idx = torch.empty((c.B, c.Hkv, k), dtype=torch.int32, device=dev)
+        self.kept_tiles = torch.empty((c.B, c.Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty((c.B, c.Hq, c.d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device=dev)
+
+    def build_bounds(self, stream=None):
+        jssa.jssa_build_tile_bounds(self.c.desc, self.c.Kp, self.bounds, stream)
+
+    def chunks(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topk_screened_chunks(c.desc, c.q, c.P, c.Kp, self.bounds, self.seeds, self.n_seed, self.k,
+                                             self.kept_tiles, self.ws, stream=stream)
+
+    def final(self, stream=None):
+        jssa.jssa_score_topk_final(self.c.desc, self.k, self.ws, self.idx, stream=stream)
+
+    def final_attend(self, stream=None):
+        c = self.c
+        jssa.jssa_score_topk_final_attend(c.desc, self.k, self.ws, c.q, c.K, c.V, c.scale, self.idx, self.out,
+                                          self.lse, stream=stream)

@@ -78,6 +78,12 @@ class GqaConfig:
     len_hi: int = 0
     sinks: bool = True
     ks: tuple = field(default=())
+    # key model: "lowrank" (i.i.d. tokens) or "clustered" (segments of
+    # cluster_len tokens share a latent centre; within a segment the latent
+    # moves by cluster_noise and the isotropic noise is cluster_noise too)
+    key_model: str = "lowrank"
+    cluster_len: int = 512
+    cluster_noise: float = 0.05
 
     @property
     def G(self) -> int:
@@ -113,6 +119,19 @@ def gen_keys_unit(cfg: GqaConfig, b: int, j: int, n: int, basis: np.ndarray | No
     """Keys of sequence b, KV head j, positions 0..n-1, as bf16 bits [n,d]."""
     A = key_basis(cfg, j) if basis is None else basis
     g = stream(cfg.seed, T_KEYS, b, j)
+    if cfg.key_model == "clustered":
+        # a stand-in for the locality of real caches (neighbouring tokens of
+        # one passage are alike): the latent is piecewise constant over
+        # segments, plus small per-token movement and noise
+        nseg = (n + cfg.cluster_len - 1) // cfg.cluster_len
+        centres = g.standard_normal((nseg, LATENT_RANK))
+        z = np.repeat(centres, cfg.cluster_len, axis=0)[:n]
+        z += cfg.cluster_noise * g.standard_normal((n, LATENT_RANK))
+        x = z @ A.T
+        x += cfg.cluster_noise * g.standard_normal((n, cfg.d))
+        if cfg.sinks:
+            x[:SINKS] *= SINK_SCALE
+        return f32_to_bf16_bits(x)
     z = g.standard_normal((n, LATENT_RANK))
     eps = g.standard_normal((n, cfg.d))
     x = z @ A.T
