@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-compare", action="store_true", help="skip the dense and gather comparisons")
     ap.add_argument("--no-calib", action="store_true", help="skip the subspace-calibration leg")
     ap.add_argument("--no-topdelta", action="store_true", help="skip the top-delta leg")
+    ap.add_argument("--no-screen", action="store_true", help="skip the lossless-screening leg")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     return ap.parse_args()
 
@@ -285,6 +286,20 @@ def main():
                               "topk_step_ms": round(ms, 4), "by_delta": td}
         print("[bench] top-delta leg done", file=sys.stderr, flush=True)
 
+    if not args.no_screen and not cfg.paged:
+        from dataclasses import replace as _replace
+        scr = {"seeds": "the previous step's selection (top-k under the query plus N(0, 0.1^2) noise)"}
+        scr[cfg.name] = bench_screening(args, cfg, inp, c, torch, pipeline, synth, stream)
+        del_cfg = _replace(cfg, B=min(cfg.B, 4), key_model="clustered", name=cfg.name + "_clustered")
+        inp_c = synth.make_gqa(del_cfg)
+        c_c = pipeline.GqaCache(inp_c)
+        c_c.project()
+        scr[del_cfg.name] = bench_screening(args, del_cfg, inp_c, c_c, torch, pipeline, synth, stream)
+        del c_c, inp_c
+        torch.cuda.empty_cache()
+        result["screening"] = scr
+        print("[bench] screening leg done", file=sys.stderr, flush=True)
+
     if not args.no_calib and not cfg.paged:
         result["calibration"] = bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream)
         print("[bench] calibration leg done", file=sys.stderr, flush=True)
@@ -311,6 +326,40 @@ def main():
         result["oracle_check"] = {"units": len(units), "index_parity": "ok", "tie_swaps": int(swaps)}
         print("[bench] cpu oracle leg done", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
+
+
+def bench_screening(args, cfg, inp, c, torch, pipeline, synth, stream):
+    """Lossless tile screening on one cache: the screened step (screen +
+    chunk pass over the kept tiles + final select/attend) against the plain
+    step, with the seeds taken from the previous step's selection."""
+    k = cfg.k
+    rng = np.random.default_rng(11)
+    q_prev = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.q) + 0.1 * rng.standard_normal(inp.q.shape))
+    q_keep = c.q
+    c.q = torch.from_numpy(q_prev.view(np.int16)).cuda()
+    prev = pipeline.SparseStep(c, k=k, fused=True)
+    prev.score_topk()
+    torch.cuda.synchronize()
+    c.q = q_keep
+    seeds = prev.idx.clone()
+    sc = pipeline.ScreenedStep(c, k, seeds)
+    b_us = time_launches(sc.build_bounds, 3, torch, stream)
+    plain = pipeline.SparseStep(c, k=k, S=1, fused=True, keep_scores=False)
+    steps = max(5, args.steps // 2)
+    p_total, _ = time_loop(plain.stages(), steps, 2, torch, stream)
+    s_total, s_us = time_loop([sc.chunks, sc.final_attend], steps, 2, torch, stream)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(sc.idx, plain.idx))
+    kept = sc.kept_tiles.cpu().numpy().astype(np.int64)
+    tiles = int(np.sum((inp.seq_lens.astype(np.int64) + 63) // 64)) * cfg.Hkv
+    kept_frac = float(kept.sum()) / tiles
+    read_bytes = int(kept.sum()) * 64 * 2 * cfg.r + tiles * 2 * cfg.r * 2 + seeds.numel() * (4 + 2 * cfg.r)
+    return {"B": cfg.B, "plain_ms_per_step": round(p_total / steps * 1e3, 4),
+            "screened_ms_per_step": round(s_total / steps * 1e3, 4),
+            "screen_plus_chunks_us": round(s_us[0], 2), "final_attend_us": round(s_us[1], 2),
+            "kept_tile_fraction": round(kept_frac, 4),
+            "chunk_pass_bytes": {"plain": int(tiles * 64 * 2 * cfg.r), "screened": read_bytes},
+            "bounds_build_us": round(b_us, 1), "indices_equal_plain": same}
 
 
 def bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream, n_queries=4096):

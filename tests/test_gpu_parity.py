@@ -230,13 +230,14 @@ FULL16K = replace(synth.LLAMA8B_32K, B=1, T=16384, seed=84)
 
 @pytest.mark.parametrize("case", ["ragged32", "r48_paged_k2048", "r128_k4096", "tiny_k1", "r16_T100",
                                   "full_k64", "full_k256_ties", "full_all_equal", "full_k257",
-                                  "paged_full_invalid"])
+                                  "paged_full_invalid", "clustered_full_k256"])
 def test_score_topk_fused_equals_split(J, PL, case):
     """The fused score + top-k pass returns exactly the indices (and, when
     asked, the scores) of jssa_score followed by jssa_topk. The full_* and
     paged_full_* cases fill every 8192-token chunk, which takes the fused
     kernel's top-two bound path for k <= 256 (ties, all-equal scores, -inf
-    tokens behind invalid pages) and the general path for k = 257."""
+    tokens behind invalid pages), its fallback to the histogram select on
+    clustered keys, and the general path for k = 257."""
     edit = None
     if case.startswith("full_"):
         inp = synth.make_gqa(FULL16K)
@@ -245,6 +246,8 @@ def test_score_topk_fused_equals_split(J, PL, case):
             edit = lambda c: c.Kp.copy_(c.Kp[:, :, torch.arange(c.Kp.shape[2], device=c.Kp.device) % 37])
         elif case == "full_all_equal":
             edit = lambda c: c.Kp.zero_()
+    elif case == "clustered_full_k256":       # neighbouring tokens alike: the top-two bound falls back
+        inp, k = synth.make_gqa(replace(FULL16K, key_model="clustered", cluster_len=256, seed=86)), 256
     elif case == "paged_full_invalid":
         inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=16384, len_lo=16384, len_hi=16384, seed=85))
         k = 256

@@ -89,7 +89,7 @@ struct ScoreSmem {
   float part[(R / 8) & (R / 8 - 1) ? kWaves * 8 * R : 1];   // LDS reduction (r = 48 only)
 };
 
-template <int R, int MODE, bool FUSED>
+template <int R, int MODE, bool FUSED, bool SCREEN>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUSED && R <= 64 ? 4 : 1))) void score_kernel(GqaDev g, const uint16_t* __restrict__ q,
                                                     const float* __restrict__ qsel,
                                                     const float* __restrict__ P,
@@ -148,12 +148,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
     __syncthreads();
   }
-  // Screening: the chunk's 128 tiles of 64 tokens have one keep bit each. A
-  // dropped tile's loads still go out (no branch) but all read the chunk's
-  // first row, a cache hit, so the tile costs no HBM bytes; its tokens are
-  // staged as dropped.
+  // Screening (SCREEN, a separate instantiation: the plain stream carries
+  // none of this): the chunk's 128 tiles of 64 tokens have one keep bit
+  // each. A dropped tile's loads still go out (no branch) but read the
+  // chunk's first tile again, a cache hit, so the tile costs no HBM bytes;
+  // its tokens are staged as dropped.
   uint32_t kw[4] = {~0u, ~0u, ~0u, ~0u};
-  if (FUSED && fo.keep) {
+  if (SCREEN) {
     const uint32_t* kp = fo.keep + int64_t(b * g.Hkv + j) * fo.keep_words;
     const int w0 = t_begin / (64 * 32);
 #pragma unroll
@@ -161,19 +162,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   }
   auto dropped = [&](int tile) -> bool {            // wave-uniform
     const int ct = tile * kWaves + w;
-    if (!FUSED || ct >= 128) return false;
+    if (!SCREEN || ct >= 128) return false;
     const uint32_t word = ct < 32 ? kw[0] : (ct < 64 ? kw[1] : (ct < 96 ? kw[2] : kw[3]));
     return ((word >> (ct & 31)) & 1u) == 0u;
   };
   auto load_tile = [&](int tile, u32x4 (&buf)[PP]) {
-    const int t0 = t_begin + (tile * kWaves + w) * 64;
-    const bool drop = dropped(tile);
+    const int t0 = t_begin + (dropped(tile) ? 0 : (tile * kWaves + w) * 64);
 #pragma unroll
     for (int m = 0; m < PP; ++m) {
       const int p = m * 64 + lane;
       int t = t0 + p / PP;
       t = t < tend ? t : tend - 1;
-      t = drop ? t_begin : t;
       int64_t off;
       if (!paged) {
         off = ubase + int64_t(t) * R;
@@ -291,7 +290,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     const int off = (tile * kWaves + w) * 64;
     const float x = tile_scores(buf);
     const float v = token_ok(t_begin + off + lane) ? x : -__builtin_inff();
-    stage[sidx(off + lane)] = dropped(tile) ? __uint_as_float(kDroppedBits) : v;
+    stage[sidx(off + lane)] = (SCREEN && dropped(tile)) ? __uint_as_float(kDroppedBits) : v;
   };
   // kDepth register buffers rotate with no copies between them (a copy of a
   // buffer whose loads are in flight would wait for them): while one tile's
@@ -351,9 +350,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*TPW + e
     int n = Tb - t_begin;
     n = n < 0 ? 0 : (n > chunk ? chunk : n);
-    if (n == chunk && fo.k <= NT) {                      // block-uniform; the stage stays intact
-      chunk_select_top2<NT, TPW>(key, t_begin, fo.k, tsm, stage, SS, fo.segs, seg);
-    } else {
+    // the top-two bound first (block-uniform; it leaves the stage intact),
+    // the histogram select when it does not apply or keeps too many
+    const bool done = n == chunk && fo.k <= NT &&
+                      chunk_select_top2<NT, TPW>(key, t_begin, fo.k, tsm, stage, SS, fo.segs, seg);
+    if (!done) {
       __syncthreads();                                   // stage is reused below
       ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
       chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   }
 }
 
-template <int MODE, bool FUSED>
+template <int MODE, bool FUSED, bool SCREEN = false>
 hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qsel, const float* P,
                           const uint16_t* Kp, float* scores, hipStream_t st, FusedOut fo) {
   const int64_t chunk = kWaves * 64 * tiles_per_wave(MODE, FUSED);
@@ -369,7 +370,7 @@ hipError_t launch_score_t(const GqaDev& g, const uint16_t* q, const float* qsel,
   switch (g.r) {
 #define JSSA_CASE(R)                                                                                  \
   case R:                                                                                             \
-    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED>), grid, dim3(kWaves * 64), 0, st, g, q, qsel, P, Kp, \
+    hipLaunchKernelGGL((score_kernel<R, MODE, FUSED, SCREEN>), grid, dim3(kWaves * 64), 0, st, g, q, qsel, P, Kp, \
                        scores, fo);                                                                   \
     break;
     JSSA_CASE(16) JSSA_CASE(32) JSSA_CASE(48) JSSA_CASE(64) JSSA_CASE(128)
@@ -412,6 +413,7 @@ hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* 
                                float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax, int n_sink,
                                int n_local, const uint32_t* keep, int keep_words) {
   FusedOut fo{segs, k, scores ? 1 : 0, pmax, n_sink, n_local, keep, keep_words};
+  if (keep) return launch_score_t<kGqa, true, true>(g, q, nullptr, P, Kp, scores, st, fo);
   return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores, st, fo);
 }
 

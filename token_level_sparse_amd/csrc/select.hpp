@@ -257,8 +257,15 @@ struct Top2Smem {
 // The kept keys are marked in a per-thread bit mask; a thread then visits
 // only its set bits, re-reading each key from LDS, instead of running a
 // divergent branch for every key.
+//
+// The bound assumes the chunk's best tokens are spread over many threads.
+// When they cluster (neighbouring tokens alike: a thread's 32 consecutive
+// tokens all near the top), M misses most of them and c falls far below the
+// k-th key. Then more than 2k keys pass; the function writes nothing and
+// returns false (block-uniform), and the caller runs chunk_select on the
+// same keys instead.
 template <int NT, int E>
-__device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top2Smem<NT>& sm,
+__device__ bool chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top2Smem<NT>& sm,
                                   const float* stage, int SS, CandSegs out, int64_t seg) {
   static_assert(E <= 32, "one mask bit per key");
   static_assert(kTop2Bins == NT, "one histogram bin per thread");
@@ -307,6 +314,7 @@ __device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
   const int mine = __builtin_popcount(mask);
   int tot;
   int at = block_scan<NT>(mine, sm.scan, &tot) - mine;
+  if (tot > 2 * k) return false;
   uint32_t* okey = out.key + seg * out.cap;
   int32_t* oidx = out.idx + seg * out.cap;
   while (mask) {
@@ -317,6 +325,7 @@ __device__ void chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
     ++at;
   }
   if (tid == 0) out.cnt[seg] = tot;
+  return true;
 }
 
 // Top-delta filter of a row's final selection (Faster Than Flash review on
