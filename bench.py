@@ -221,7 +221,7 @@ def main():
     if cfg.name == "gqa_128k_b16" and not args.k:
         from token_level_sparse_amd.prof_summary import read_traffic
         t = read_traffic(os.path.join(ROOT, "profiles", "score_kernel_fused_gqa_128k_b16_hbm_traffic.txt"),
-                         f"score_kernel<{r},0,true>")
+                         f"score_kernel<{r},0,true,false>")
         if t is not None:
             traffic = t["bytes"]
 
@@ -376,7 +376,8 @@ def bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, strea
     k_bytes = int(np.sum(inp.seq_lens)) * Hkv * d * 2
     qs = torch.from_numpy(synth.gen_calib_queries(cfg, n_queries).view(np.int16)).cuda()
     Sq = torch.empty((Hkv, d, d), dtype=torch.float32, device="cuda")
-    qm_us = time_launches(lambda: jssa.jssa_calib_query_moments(n_queries, Hq, Hkv, qs, Sq), 5, torch, stream)
+    qws = torch.empty(jssa.jssa_calib_query_workspace_size(Hkv), dtype=torch.uint8, device="cuda")
+    qm_us = time_launches(lambda: jssa.jssa_calib_query_moments(n_queries, Hq, Hkv, qs, Sq, qws), 5, torch, stream)
     torch.cuda.synchronize()
     Skh, Sqh = Sk.cpu().numpy(), Sq.cpu().numpy()
     t0 = time.perf_counter()

@@ -446,15 +446,20 @@ JSSA_API jssa_status jssa_calib_workspace_size(const jssa_gqa_desc* desc, size_t
 JSSA_API jssa_status jssa_calib_key_moments(const jssa_gqa_desc* desc, const void* K, float* moments, void* ws,
                                             size_t ws_bytes, void* stream);
 
+/* Workspace of jssa_calib_query_moments (per-slice partial sums). */
+JSSA_API jssa_status jssa_calib_query_workspace_size(int32_t Hkv, size_t* bytes);
+
 /*
  * Query second moments over N decode-query samples:
  *   moments[j] = (1/N) sum_n qbar_n qbar_n^T, qbar_n = sum_{h in group j} q[n,h]
  *  q        device bf16 [N,Hq,128]; Hq a multiple of Hkv, Hq/Hkv <= 16
  *  moments  device fp32 [Hkv,128,128], written
- * qbar is summed in fp32; the outer products accumulate in fp32.
+ *  ws       device workspace of jssa_calib_query_workspace_size bytes
+ * qbar is summed in fp32; the outer products accumulate in fp32 over 32
+ * slices of the samples, summed in a fixed order (repeatable bits).
  */
 JSSA_API jssa_status jssa_calib_query_moments(int32_t N, int32_t Hq, int32_t Hkv, const void* q, float* moments,
-                                              void* stream);
+                                              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Spectral step, HOST pointers (no GPU work): P = the top-r eigenvectors of

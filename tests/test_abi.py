@@ -115,8 +115,10 @@ def test_calib_validation(J):
     assert _status(J.jssa_calib_key_moments, ok, A, A, A, need - 1) == J.ERR_WORKSPACE
     assert _status(J.jssa_calib_key_moments, ok, None, A, A, need) == J.ERR_NULL
     assert _status(J.jssa_calib_key_moments, ok, A, MIS, A, need) == J.ERR_ALIGN
-    assert _status(J.jssa_calib_query_moments, 0, 32, 8, A, A) == J.ERR_SHAPE
-    assert _status(J.jssa_calib_query_moments, 16, 30, 8, A, A) == J.ERR_SHAPE
+    qneed = J.jssa_calib_query_workspace_size(8)
+    assert _status(J.jssa_calib_query_moments, 0, 32, 8, A, A, A, qneed) == J.ERR_SHAPE
+    assert _status(J.jssa_calib_query_moments, 16, 30, 8, A, A, A, qneed) == J.ERR_SHAPE
+    assert _status(J.jssa_calib_query_moments, 16, 32, 8, A, A, A, qneed - 1) == J.ERR_WORKSPACE
     import numpy as np
     with pytest.raises(J.JssaError) as e:
         J.jssa_calib_projection(np.eye(8), np.eye(8), 9)

@@ -550,13 +550,23 @@ jssa_status jssa_calib_key_moments(const jssa_gqa_desc* desc, const void* K, flo
                     __func__);
 }
 
-jssa_status jssa_calib_query_moments(int32_t N, int32_t Hq, int32_t Hkv, const void* q, float* moments,
-                                     void* stream) {
+jssa_status jssa_calib_query_workspace_size(int32_t Hkv, size_t* bytes) {
+  if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
+  if (Hkv < 1 || Hkv > 4096) return fail(JSSA_ERR_SHAPE, "%s: Hkv %d", __func__, Hkv);
+  *bytes = jssa::calib_query_workspace_bytes(Hkv);
+  return JSSA_OK;
+}
+
+jssa_status jssa_calib_query_moments(int32_t N, int32_t Hq, int32_t Hkv, const void* q, float* moments, void* ws,
+                                     size_t ws_bytes, void* stream) {
   if (N < 1 || N > (1 << 24)) return fail(JSSA_ERR_SHAPE, "%s: N %d outside [1, 2^24]", __func__, N);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16 || int64_t(N) * Hq > (int64_t(1) << 31))
     return fail(JSSA_ERR_SHAPE, "%s: Hq %d, Hkv %d", __func__, Hq, Hkv);
-  REQUIRE_PTR(q); REQUIRE_PTR(moments);
-  return hip_status(jssa::launch_calib_query_moments(N, Hq, Hkv, static_cast<const uint16_t*>(q), moments,
+  REQUIRE_PTR(q); REQUIRE_PTR(moments); REQUIRE_PTR(ws);
+  const size_t need = jssa::calib_query_workspace_bytes(Hkv);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  return hip_status(jssa::launch_calib_query_moments(N, Hq, Hkv, static_cast<const uint16_t*>(q), moments, ws,
                                                      S(stream)),
                     __func__);
 }

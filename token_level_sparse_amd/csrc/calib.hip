@@ -172,6 +172,7 @@ __global__ __launch_bounds__(64) void gram_reduce_kernel(const float* __restrict
   const float* src = partial + int64_t(j) * nslots * kTileFloats + x * 256 + lane * 4;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   int64_t n = 0;
+#pragma unroll 8
   for (int q = 0; q < nslots; ++q) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(src + int64_t(q) * kTileFloats);
     s = s + v;
@@ -191,40 +192,70 @@ __global__ __launch_bounds__(64) void gram_reduce_kernel(const float* __restrict
 }
 
 // Query moments: out[j] = (1/N) sum_n qbar_n qbar_n^T, qbar_n the fp32 sum of
-// the bf16 query rows of KV head j's group in sample n. Block (j, y) owns
-// output rows 32y .. 32y+31: thread tid holds column tid%128 of 16 of them.
-// Samples go through LDS 64 at a time.
+// the bf16 query rows of KV head j's group in sample n. Block (j, p) takes
+// the samples of slice p (kQSplit slices) 64 at a time through LDS; thread
+// tid accumulates the 8 x 8 patch of rows 8(tid/16).., columns 8(tid%16)..
+// of its slice's sum, written as a partial; qmoment_reduce_kernel sums the
+// slices in order and divides by N.
+constexpr int kQSplit = 32;
+
 __global__ __launch_bounds__(256) void qmoment_kernel(int N, int Hq, int Hkv, const uint16_t* __restrict__ q,
-                                                      float* __restrict__ out) {
-  __shared__ float qs[64][kCD];
-  const int j = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
+                                                      float* __restrict__ partial) {
+  __shared__ float qs[64][kCD + 4];
+  const int j = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   const int G = Hq / Hkv;
-  const int col = tid & (kCD - 1), r0 = 32 * y + (tid >> 7) * 16;
-  float acc[16];
+  const int per = (N + kQSplit - 1) / kQSplit;
+  const int n_lo = p * per, n_hi = N < n_lo + per ? N : n_lo + per;
+  const int r0 = 8 * (tid >> 4), c0 = 8 * (tid & 15);
+  float acc[8][8];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int n0 = 0; n0 < N; n0 += 64) {
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.f;
+  for (int n0 = n_lo; n0 < n_hi; n0 += 64) {
     __syncthreads();
     for (int e = tid; e < 64 * kCD; e += 256) {
       const int n = e / kCD, dim = e % kCD;
       float s = 0.f;
-      if (n0 + n < N) {
+      if (n0 + n < n_hi) {
         const uint16_t* row = q + (int64_t(n0 + n) * Hq + int64_t(j) * G) * kCD + dim;
         for (int h = 0; h < G; ++h) s += bf(row[h * kCD]);
       }
       qs[n][dim] = s;
     }
     __syncthreads();
-    const int nb = N - n0 < 64 ? N - n0 : 64;
+    const int nb = n_hi - n0 < 64 ? n_hi - n0 : 64;
     for (int n = 0; n < nb; ++n) {
-      const float xc = qs[n][col];
+      float ra[8], cb[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(qs[n][r0 + r], xc, acc[r]);
+      for (int a = 0; a < 8; ++a) {
+        ra[a] = qs[n][r0 + a];
+        cb[a] = qs[n][c0 + a];
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[a][c] = __builtin_fmaf(ra[a], cb[c], acc[a][c]);
     }
   }
-  const float inv = N > 0 ? float(1.0 / double(N)) : 0.f;
+  float* dst = partial + (int64_t(j) * kQSplit + p) * kCD * kCD;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) out[(int64_t(j) * kCD + r0 + r) * kCD + col] = acc[r] * inv;
+  for (int a = 0; a < 8; ++a) {
+    f32x4 lo = {acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+    f32x4 hi = {acc[a][4], acc[a][5], acc[a][6], acc[a][7]};
+    *reinterpret_cast<f32x4*>(dst + (r0 + a) * kCD + c0) = lo;
+    *reinterpret_cast<f32x4*>(dst + (r0 + a) * kCD + c0 + 4) = hi;
+  }
+}
+
+__global__ __launch_bounds__(256) void qmoment_reduce_kernel(int N, const float* __restrict__ partial,
+                                                             float* __restrict__ out) {
+  const int j = blockIdx.x;
+  const int e = blockIdx.y * 256 + threadIdx.x;        // element of the 128 x 128 matrix
+  float s = 0.f;
+#pragma unroll 8
+  for (int p = 0; p < kQSplit; ++p) s += partial[(int64_t(j) * kQSplit + p) * kCD * kCD + e];
+  out[int64_t(j) * kCD * kCD + e] = N > 0 ? s * float(1.0 / double(N)) : 0.f;
 }
 
 }  // namespace
@@ -248,8 +279,15 @@ hipError_t launch_calib_key_moments(const GqaDev& g, const uint16_t* K, float* o
   return hipGetLastError();
 }
 
-hipError_t launch_calib_query_moments(int N, int Hq, int Hkv, const uint16_t* q, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(qmoment_kernel, dim3(Hkv, kCD / 32), dim3(256), 0, st, N, Hq, Hkv, q, out);
+size_t calib_query_workspace_bytes(int Hkv) { return size_t(Hkv) * kQSplit * kCD * kCD * sizeof(float); }
+
+hipError_t launch_calib_query_moments(int N, int Hq, int Hkv, const uint16_t* q, float* out, void* ws,
+                                      hipStream_t st) {
+  float* partial = static_cast<float*>(ws);
+  hipLaunchKernelGGL(qmoment_kernel, dim3(Hkv, kQSplit), dim3(256), 0, st, N, Hq, Hkv, q, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qmoment_reduce_kernel, dim3(Hkv, kCD * kCD / 256), dim3(256), 0, st, N, partial, out);
   return hipGetLastError();
 }
 

@@ -57,7 +57,9 @@ size_t align256(size_t x);
 int calib_blocks_per_head(int Hkv);
 size_t calib_workspace_bytes(int Hkv);
 hipError_t launch_calib_key_moments(const GqaDev& g, const uint16_t* K, float* out, void* ws, hipStream_t st);
-hipError_t launch_calib_query_moments(int N, int Hq, int Hkv, const uint16_t* q, float* out, hipStream_t st);
+size_t calib_query_workspace_bytes(int Hkv);
+hipError_t launch_calib_query_moments(int N, int Hq, int Hkv, const uint16_t* q, float* out, void* ws,
+                                      hipStream_t st);
 // Top-r eigenvectors of the symmetric d x d matrix M (row-major, fp64), by
 // cyclic Jacobi rotations; columns by descending eigenvalue, each signed so
 // its entry of largest magnitude (first on a tie) is positive. V: [d, r]

@@ -33,7 +33,7 @@ ENTRY_POINTS = (
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
     "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_score_topk_screened_workspace_size",
-    "jssa_score_topk_screened_chunks", "jssa_calib_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
+    "jssa_score_topk_screened_chunks", "jssa_calib_workspace_size", "jssa_calib_query_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
     "jssa_calib_projection", "jssa_status_string", "jssa_last_error", "jssa_version",
 )
 
@@ -94,7 +94,8 @@ _SIGS = {
     "jssa_score_topk_screened_chunks": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp],
     "jssa_calib_workspace_size": [_P(GqaDesc), _P(_sz)],
     "jssa_calib_key_moments": [_P(GqaDesc), _vp, _vp, _vp, _sz, _vp],
-    "jssa_calib_query_moments": [_i32, _i32, _i32, _vp, _vp, _vp],
+    "jssa_calib_query_workspace_size": [_i32, _P(_sz)],
+    "jssa_calib_query_moments": [_i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp],
     "jssa_calib_projection": [_i32, _i32, _vp, _vp, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
@@ -275,8 +276,17 @@ def jssa_calib_key_moments(desc, K, moments, ws, ws_bytes=None, stream=None):
            "jssa_calib_key_moments")
 
 
-def jssa_calib_query_moments(N, Hq, Hkv, q, moments, stream=None):
-    _check(_lib.jssa_calib_query_moments(N, Hq, Hkv, _p(q), _p(moments), _s(stream)), "jssa_calib_query_moments")
+def jssa_calib_query_workspace_size(Hkv) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_calib_query_workspace_size(Hkv, ctypes.byref(n)), "jssa_calib_query_workspace_size")
+    return n.value
+
+
+def jssa_calib_query_moments(N, Hq, Hkv, q, moments, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_calib_query_moments(N, Hq, Hkv, _p(q), _p(moments), _p(ws), ws_bytes, _s(stream)),
+           "jssa_calib_query_moments")
 
 
 def jssa_calib_projection(S_q, S_k, r: int):

@@ -283,7 +283,8 @@ def calib_query_moments(q_samples: torch.Tensor, Hkv: int, stream=None) -> torch
     """S_q per KV head [Hkv, d, d] fp32 from decode-query samples [N, Hq, d]."""
     N, Hq, d = q_samples.shape
     out = torch.empty((Hkv, d, d), dtype=torch.float32, device=q_samples.device)
-    jssa.jssa_calib_query_moments(N, Hq, Hkv, q_samples, out, stream=stream)
+    ws = torch.empty(jssa.jssa_calib_query_workspace_size(Hkv), dtype=torch.uint8, device=q_samples.device)
+    jssa.jssa_calib_query_moments(N, Hq, Hkv, q_samples, out, ws, stream=stream)
     return out
 
 
