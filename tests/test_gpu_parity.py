@@ -604,11 +604,15 @@ def _screen_inputs(case):
         return inp, 512
     if case == "ragged_dup_seeds":
         return ragged_inputs(), 100
+    if case.startswith("clustered_r"):                        # ranks 16, 64, 128: other kernel shapes
+        r = int(case[len("clustered_r"):])
+        return synth.make_gqa(replace(synth.TINY, B=2, T=20000, r=r, key_model="clustered", seed=98 + r)), 128
     return synth.make_gqa(synth.TINY), 64                     # no_seeds
 
 
 @pytest.mark.parametrize("case", ["tiny", "llama_random_seeds", "clustered_32k", "clustered_paged_invalid",
-                                  "ragged_dup_seeds", "no_seeds"])
+                                  "ragged_dup_seeds", "no_seeds", "clustered_r16", "clustered_r64",
+                                  "clustered_r128"])
 def test_screened_topk_lossless(J, PL, case):
     inp, k = _screen_inputs(case)
     cfg = inp.cfg

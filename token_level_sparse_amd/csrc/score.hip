@@ -160,6 +160,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
 #pragma unroll
     for (int i = 0; i < 4; ++i) kw[i] = w0 + i < fo.keep_words ? kp[w0 + i] : 0u;
   }
+  if (SCREEN && (kw[0] | kw[1] | kw[2] | kw[3]) == 0u) {   // every tile dropped (block-uniform)
+    if (tid == 0) {
+      fo.segs.cnt[seg] = 0;
+      if (fo.pmax) fo.pmax[seg] = 0u;
+    }
+    return;
+  }
   auto dropped = [&](int tile) -> bool {            // wave-uniform
     const int ct = tile * kWaves + w;
     if (!SCREEN || ct >= 128) return false;
@@ -189,9 +196,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     return !paged || pid[(t - t_begin) >> 4] >= 0;
   };
 
+  // Screening: the wave streams only its kept tiles, in order. Lane r holds
+  // the r-th kept tile of the wave (pushed there by the lane of that tile),
+  // read back with a uniform readlane; past the last one the last is
+  // repeated (loads hit the cache, the stage write repeats the same scores).
+  int nkept = TPW, klist = 0;
+  uint32_t kmask = 0u;
+  if constexpr (SCREEN) {
+    const bool kb = lane < TPW && !dropped(lane);
+    kmask = uint32_t(__ballot(kb));
+    nkept = __builtin_popcount(kmask);
+    const int rank = __builtin_popcount(kmask & ((1u << (lane & 31)) - 1u));
+    klist = __builtin_amdgcn_ds_permute((kb ? rank : 63) * 4, lane);
+  }
+  auto kept_tile = [&](int i) -> int {
+    if constexpr (!SCREEN) return i;
+    return __builtin_amdgcn_readlane(klist, i < nkept ? i : nkept - 1);
+  };
+
   u32x4 bufs[kDepth][PP];
+  if (nkept > 0) {
 #pragma unroll
-  for (int u = 0; u < kDepth - 1; ++u) load_tile(u, bufs[u]);   // in flight during the prologue
+    for (int u = 0; u < kDepth - 1; ++u) load_tile(kept_tile(u), bufs[u]);   // in flight during the prologue
+  }
 
   // ---- prologue: qp = P_j^T qbar (fp32). The slice of P this thread needs
   // and the group's query rows are loaded together (one round trip, not two),
@@ -296,12 +323,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   // buffer whose loads are in flight would wait for them): while one tile's
   // scores are computed, the loads of the next kDepth - 1 tiles are in flight.
   static_assert(TPW % kDepth == 0, "tiles are streamed in groups of kDepth");
-  for (int tile = 0; tile < TPW; tile += kDepth) {
+  if constexpr (SCREEN) {
+    for (int tile = 0; tile < TPW; ++tile)             // dropped tiles: staged as such, nothing read
+      if (!((kmask >> tile) & 1u)) stage[sidx((tile * kWaves + w) * 64 + lane)] = __uint_as_float(kDroppedBits);
+  }
+  for (int i = 0; i < nkept; i += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      // past the chunk on the last group: clamped, unused
-      load_tile(tile + u + kDepth - 1, bufs[(u + kDepth - 1) % kDepth]);
-      stage_tile(tile + u, bufs[u]);
+      // past the chunk (or the last kept tile) on the last group: clamped, unused
+      load_tile(kept_tile(i + u + kDepth - 1), bufs[(u + kDepth - 1) % kDepth]);
+      stage_tile(kept_tile(i + u), bufs[u]);
     }
   }
   __syncthreads();

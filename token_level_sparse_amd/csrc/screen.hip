@@ -14,7 +14,8 @@
 //
 //  tile_bounds_kernel  lo/hi per (sequence, KV head, tile) from the
 //                      projected cache, once and after appends (setup work)
-//  screen_kernel       one block per (sequence, KV head): qp, the seeds'
+//  screen_kernel       one block (1024 threads; 512 for r >= 64) per (sequence, KV head):
+//                      qp, the distinct seeds (an LDS hash set) and their
 //                      scores, tau, then one keep bit per tile
 //
 // Both sides of the comparison carry fp32 rounding: the stream scores the
@@ -31,8 +32,11 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kMaxSeed = 4096;
-constexpr int kScreenNT = 256;
-constexpr int kScrBins = 256;
+constexpr int kSeedTableBits = 13;                  // 2 * kMaxSeed slots
+constexpr int kSeedTable = 1 << kSeedTableBits;
+// threads per block: 1024, or 512 for the wide ranks (register room for a
+// whole projected row per seed); one histogram bin per thread
+constexpr int screen_threads(int R) { return R >= 64 ? 512 : 1024; }
 constexpr float kScreenEps = 1.0f / 65536.0f;
 
 __global__ __launch_bounds__(64) void tile_bounds_kernel(GqaDev g, const uint16_t* __restrict__ Kp,
@@ -74,91 +78,119 @@ __global__ __launch_bounds__(64) void tile_bounds_kernel(GqaDev g, const uint16_
   }
 }
 
-__global__ __launch_bounds__(kScreenNT) void screen_kernel(GqaDev g, const uint16_t* __restrict__ q,
+template <int R>
+__global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, const uint16_t* __restrict__ q,
                                                            const float* __restrict__ P,
                                                            const uint16_t* __restrict__ Kp,
                                                            const uint16_t* __restrict__ bounds, int ntiles,
                                                            const int32_t* __restrict__ seeds, int n_seed, int k,
                                                            uint32_t* __restrict__ keep, int nwords,
                                                            int32_t* __restrict__ kept_tiles) {
-  constexpr int NT = kScreenNT, NW = NT / 64;
+  constexpr int NT = screen_threads(R), NW = NT / 64;
+  constexpr int kScrBins = NT, kScrBits = NT == 1024 ? 10 : 9;
+  constexpr int NS = NT / R, NI = (128 + NS - 1) / NS; // P row slices and rows per slice
   __shared__ float qbar[128];
   __shared__ float qp[128];
-  __shared__ int32_t sidx[kMaxSeed];
+  __shared__ float qpart[NS][R];
+  __shared__ int32_t table[kSeedTable];                 // distinct seed tokens (open addressing)
   __shared__ uint32_t hist[kScrBins];
   __shared__ ScanSmem<NT> scan;
   __shared__ int res[2];
   __shared__ uint32_t red[3][NW];
   const int row = blockIdx.x, b = row / g.Hkv, j = row % g.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int R = g.r, Tb = seq_len(g, b);
+  const int Tb = seq_len(g, b);
 
-  // qp = P_j^T (sum of the group's query rows), fp32
+  // qp = P_j^T (sum of the group's query rows), fp32: thread (slice sl,
+  // column c) holds rows sl, sl + NS, ... of P's column c; its loads go out
+  // with the query rows and the seed indices, in one round trip
+  const int pc = tid % R, sl = tid / R;                 // threads with sl >= NS take no part
+  float pv[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int i = sl + ii * NS;
+    pv[ii] = (sl < NS && i < 128) ? P[(int64_t(j) * 128 + i) * R + pc] : 0.f;
+  }
+  constexpr int SPT = kMaxSeed / NT;
+  int st[SPT];
+  bool mine[SPT];
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) {
+    const int i = tid + x * NT;
+    st[x] = i < n_seed ? seeds[int64_t(row) * n_seed + i] : -1;
+    mine[x] = false;
+  }
   if (tid < 128) {
     float s = 0.f;
     for (int h = 0; h < g.G; ++h) s += bf(q[(int64_t(b) * g.Hq + int64_t(j) * g.G + h) * 128 + tid]);
     qbar[tid] = s;
   }
-  // the seeds of this row, sorted ascending (bitonic, padded with INT_MAX) so
-  // that repeated entries can be counted once
-  int npow = 1;
-  while (npow < n_seed) npow <<= 1;
-  for (int i = tid; i < npow; i += NT) {
-    int t = i < n_seed ? seeds[int64_t(row) * n_seed + i] : 0x7fffffff;
-    sidx[i] = t;
-  }
+  for (int i = tid; i < kSeedTable; i += NT) table[i] = -1;
   __syncthreads();
-  if (tid < R) {
+  if (sl < NS) {
     float s = 0.f;
-    for (int i = 0; i < 128; ++i) s = __builtin_fmaf(P[(int64_t(j) * 128 + i) * R + tid], qbar[i], s);
-    qp[tid] = s;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int i = sl + ii * NS;
+      s = __builtin_fmaf(pv[ii], qbar[i < 128 ? i : 127], s);
+    }
+    qpart[sl][pc] = s;
   }
-  for (int size = 2; size <= npow; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < npow / 2; i += NT) {
-        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int a = sidx[lo], c = sidx[hi];
-        if ((a > c) == up) {
-          sidx[lo] = c;
-          sidx[hi] = a;
-        }
-      }
-      __syncthreads();
+  // seeds: each valid token enters the table once; the thread that inserts
+  // it scores it, so repeated entries count once
+#pragma unroll
+  for (int x = 0; x < SPT; ++x) {
+    const int t = st[x];
+    if (t < 0 || t >= Tb) continue;
+    uint32_t h = (uint32_t(t) * 2654435761u) >> (32 - kSeedTableBits);
+    for (;;) {                                          // at most kMaxSeed entries in 2 * kMaxSeed slots
+      const int old = atomicCAS(&table[h], -1, t);
+      if (old == -1) { mine[x] = true; break; }
+      if (old == t) break;
+      h = (h + 1) & (kSeedTable - 1);
     }
   }
-  __syncthreads();
-
-  // score each distinct valid seed (key 0: none); S = the largest sum |qp_c Kp_c|
-  constexpr int SPT = kMaxSeed / NT;
+  __syncthreads();                                      // qpart complete
+  if (tid < R) {
+    float s = 0.f;
+    for (int x = 0; x < NS; ++x) s += qpart[x][tid];
+    qp[tid] = s;
+  }
+  __syncthreads();                                      // qp complete
   uint32_t skey[SPT];
   uint32_t kmax = 0u, kmin = 0xffffffffu;
   float amax = 0.f;
   int nvalid = 0;
 #pragma unroll
   for (int x = 0; x < SPT; ++x) {
-    const int i = tid + x * NT;
     skey[x] = 0u;
-    if (i < n_seed) {
-      const int t = sidx[i];
-      const bool first = i == 0 || sidx[i - 1] != t;
-      if (first && t >= 0 && t < Tb) {
-        const int64_t off = row_off(g, b, j, t, R);
-        if (off >= 0) {
-          float s = 0.f, a = 0.f;
-          for (int c = 0; c < R; ++c) {
-            const float v = bf(Kp[off + c]);
-            s = __builtin_fmaf(qp[c], v, s);
-            a = __builtin_fmaf(__builtin_fabsf(qp[c]), __builtin_fabsf(v), a);
-          }
-          skey[x] = score_key(s);
-          amax = a > amax ? a : amax;
-          kmax = skey[x] > kmax ? skey[x] : kmax;
-          kmin = skey[x] < kmin ? skey[x] : kmin;
-          ++nvalid;
-        }
+    if (!mine[x]) continue;
+    const int64_t off = row_off(g, b, j, st[x], R);
+    if (off < 0) continue;                              // no valid page
+    const u32x4* rowp = reinterpret_cast<const u32x4*>(Kp + off);
+    u32x4 rv[R / 8];
+#pragma unroll
+    for (int c8 = 0; c8 < R / 8; ++c8) rv[c8] = rowp[c8];   // the row's loads all in flight
+    float s = 0.f, a = 0.f;
+#pragma unroll
+    for (int c8 = 0; c8 < R / 8; ++c8) {
+      const u32x4 v = rv[c8];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf_lo(wd[e]), x1 = bf_hi(wd[e]);
+        const float q0 = qp[c8 * 8 + 2 * e], q1 = qp[c8 * 8 + 2 * e + 1];
+        s = __builtin_fmaf(q0, x0, s);
+        s = __builtin_fmaf(q1, x1, s);
+        a = __builtin_fmaf(__builtin_fabsf(q0), __builtin_fabsf(x0), a);
+        a = __builtin_fmaf(__builtin_fabsf(q1), __builtin_fabsf(x1), a);
       }
     }
+    skey[x] = score_key(s);
+    amax = a > amax ? a : amax;
+    kmax = skey[x] > kmax ? skey[x] : kmax;
+    kmin = skey[x] < kmin ? skey[x] : kmin;
+    ++nvalid;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -184,17 +216,17 @@ __global__ __launch_bounds__(kScreenNT) void screen_kernel(GqaDev g, const uint1
   }
 
   // tau: the lower edge of the bin holding the k-th largest seed key, over
-  // two levels of 256 linear bins (at least k distinct seeds lie at or above
-  // it, so it is at or below the k-th largest score)
-  bool screen = nv_tot >= k && k > 0;                   // block-uniform
+  // two levels of linear bins (at least k distinct seeds lie at or above it,
+  // so it is at or below the k-th largest score)
+  const bool screen = nv_tot >= k && k > 0;             // block-uniform
   float tau_lo = -__builtin_inff();
   if (screen) {
     uint64_t lo = kmin, hi = kmax;
     int rem = k;
     for (int level = 0; level < 2; ++level) {
       const uint64_t range = hi - lo;
-      const int sh = range < uint64_t(kScrBins) ? 0 : (64 - __builtin_clzll(range)) - 8;
-      hist[tid] = 0u;
+      const int sh = range < uint64_t(kScrBins) ? 0 : (64 - __builtin_clzll(range)) - kScrBits;
+      for (int i = tid; i < kScrBins; i += NT) hist[i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int x = 0; x < SPT; ++x)
@@ -210,26 +242,45 @@ __global__ __launch_bounds__(kScreenNT) void screen_kernel(GqaDev g, const uint1
       __syncthreads();
       if (sh == 0) break;
     }
-    const float tau = key_score(uint32_t(lo));
-    tau_lo = tau - kScreenEps * amax;
+    tau_lo = key_score(uint32_t(lo)) - kScreenEps * amax;
   }
 
   // one keep bit per tile; tiles past the sequence or without a valid token
-  // are dropped
+  // are dropped. A tile's 2R bounds are read 16 bytes at a time, all loads
+  // issued before use.
   const int nt_row = (Tb + kTile - 1) / kTile;
   int kept = 0;
   for (int base = 0; base < nwords * 32; base += NT) {
     const int tile = base + tid;
     bool k_it = false;
     if (tile < nt_row && tile < ntiles) {
-      const uint16_t* bd = bounds + ((int64_t(b) * g.Hkv + j) * ntiles + tile) * 2 * R;
+      const u32x4* bd = reinterpret_cast<const u32x4*>(bounds + ((int64_t(b) * g.Hkv + j) * ntiles + tile) * 2 * R);
+      // the tile's bounds in groups of up to 8 vectors per half, each
+      // group's loads all in flight before use
+      constexpr int KC = R / 8 < 8 ? R / 8 : 8;
       float ub = 0.f, U = 0.f;
       bool empty = false;
-      for (int c = 0; c < R; ++c) {
-        const float l = bf(bd[c]), h = bf(bd[R + c]);
-        empty = empty || l > h;
-        ub += fmaxf(qp[c] * l, qp[c] * h);
-        U = __builtin_fmaf(__builtin_fabsf(qp[c]), fmaxf(__builtin_fabsf(l), __builtin_fabsf(h)), U);
+#pragma unroll
+      for (int c0 = 0; c0 < R / 8; c0 += KC) {
+        u32x4 lv[KC], hv[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          lv[c] = bd[c0 + c];
+          hv[c] = bd[R / 8 + c0 + c];
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const uint32_t lw[4] = {lv[c].x, lv[c].y, lv[c].z, lv[c].w}, hw[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float l = (e & 1) ? bf_hi(lw[e >> 1]) : bf_lo(lw[e >> 1]);
+            const float h = (e & 1) ? bf_hi(hw[e >> 1]) : bf_lo(hw[e >> 1]);
+            const float qc = qp[(c0 + c) * 8 + e];
+            empty = empty || l > h;
+            ub += fmaxf(qc * l, qc * h);
+            U = __builtin_fmaf(__builtin_fabsf(qc), fmaxf(__builtin_fabsf(l), __builtin_fabsf(h)), U);
+          }
+        }
       }
       k_it = !empty && (!screen || ub + kScreenEps * U >= tau_lo);
     }
@@ -263,8 +314,17 @@ hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bou
 hipError_t launch_screen(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
                          const uint16_t* bounds, const int32_t* seeds, int n_seed, int k, uint32_t* keep,
                          int32_t* kept_tiles, hipStream_t st) {
-  hipLaunchKernelGGL(screen_kernel, dim3(g.B * g.Hkv), dim3(kScreenNT), 0, st, g, q, P, Kp, bounds,
-                     screen_tiles(g.max_seq), seeds, n_seed, k, keep, screen_words(g.max_seq), kept_tiles);
+  switch (g.r) {
+#define JSSA_SCR(RR)                                                                                        \
+  case RR:                                                                                                  \
+    hipLaunchKernelGGL(screen_kernel<RR>, dim3(g.B * g.Hkv), dim3(screen_threads(RR)), 0, st, g, q, P, Kp, bounds, \
+                       screen_tiles(g.max_seq), seeds, n_seed, k, keep, screen_words(g.max_seq), kept_tiles); \
+    break;
+    JSSA_SCR(16) JSSA_SCR(32) JSSA_SCR(48) JSSA_SCR(64) JSSA_SCR(128)
+#undef JSSA_SCR
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
