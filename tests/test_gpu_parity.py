@@ -865,6 +865,65 @@ def test_full_size_128k_b16_sampled(J, PL):
         U.check_attention(inp, b, j, hs, K, V, idx[b, j], out, lse, c.scale)
 
 
+def test_full_size_128k_b16_extensions_sampled(J, PL):
+    """The 128K x B=16 workload through the scope's extension rows, in the
+    configurations the benchmark times: top-delta selection + attention
+    (delta 2, k_max 256), screening with the previous step's selection as
+    seeds, and the calibration moments; checked on sampled units (and one
+    KV head over all sequences) against the oracle."""
+    cfg = synth.BATCHED_128K
+    inp = synth.make_gqa(cfg)
+    c = PL.GqaCache(inp)
+    c.project()
+    k = cfg.k
+    units = [(0, 0), (5, 3), (11, 6), (15, 7)]
+    # top-delta + attention
+    td = PL.TopDeltaStep(c, k, 2.0, 4, 64)
+    td.run()
+    torch.cuda.synchronize()
+    idx, cnt, out, lse = _np(td.idx), _np(td.counts), _np(td.out), _np(td.lse)
+    assert np.all(np.isfinite(out[cnt.repeat(cfg.G, axis=1) > 0]))
+    oracle_units = {}
+    for b, j in units:
+        K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
+        oracle_units[(b, j)] = (K, V, Kp, s, hs)
+        valid = np.ones(s.shape[0], bool)
+        U.check_topdelta(idx[b, j], int(cnt[b, j]), s, valid, k, 2.0, 4, 64, c.scale, cfg.G)
+        U.check_attention(inp, b, j, hs, K, V, idx[b, j][:cnt[b, j]], out, lse, c.scale)
+    # screening with the previous step's selection as seeds
+    seeds = _prev_step_seeds(PL, c, inp, k)
+    sc = PL.ScreenedStep(c, k, seeds)
+    sc.build_bounds()
+    sc.chunks()
+    sc.final()
+    plain = PL.SparseStep(c, k=k, fused=True)
+    plain.score_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(sc.idx), _np(plain.idx))
+    sd = _np(seeds)
+    base = J.jssa_score_topk_workspace_size(c.desc, k)
+    off = (base + 255) // 256 * 256
+    nt = cfg.T // 64
+    kw = _np(sc.ws)[off:off + cfg.B * cfg.Hkv * (nt // 32) * 4].view(np.uint32).reshape(cfg.B, cfg.Hkv, nt // 32)
+    for b, j in units:
+        K, V, Kp, s, hs = oracle_units[(b, j)]
+        qp = O.project_query(inp.q[b, hs], inp.P[j])
+        _, keep_o = O.screened_topk(s, qp, Kp, sd[b, j], k)
+        bits = np.unpackbits(kw[b, j].view(np.uint8), bitorder="little")[:nt].astype(bool)
+        assert np.all(bits[keep_o])
+    # calibration moments: one KV head over all 16 sequences, and the queries
+    Sk = _np(PL.calib_key_moments(c))
+    ref = O.key_second_moment(inp.K[:, 2].reshape(-1, cfg.d))
+    npb = 512 // cfg.Hkv
+    n_chain = 32 * ((cfg.B * (cfg.T // 8192) + npb - 1) // npb) * 64 + npb * 4
+    assert np.all(np.abs(Sk[2] - ref) <= _moment_limit(ref, n_chain))
+    qs = synth.gen_calib_queries(cfg, 4096)
+    Sq = _np(PL.calib_query_moments(torch.from_numpy(qs.view(np.int16)).cuda(), cfg.Hkv))
+    for j in (0, 7):
+        refq = O.query_second_moment(qs, j, cfg.G)
+        assert np.all(np.abs(Sq[j] - refq) <= _moment_limit(refq, 4096 + cfg.G))
+
+
 def test_full_size_qwen_paged_k2048_sampled(J, PL):
     """Paged, ragged Qwen3-14B-shaped workload at full size with the largest
     budget of its sweep, in the benchmark's launch configuration (chunk pass,
