@@ -169,6 +169,22 @@ def test_topk_bit_exact(J, T, k):
     _topk_case(J, B, H, T, k, lens, s)
 
 
+@pytest.mark.parametrize("T,k", [(4096, 256), (40000, 256), (70000, 2048)])
+def test_topk_small_tied_bin(J, T, k):
+    """A few tokens tie exactly at the k-th score, with some of them taken:
+    the bin holding the k-th key is small, so the final pass ranks it within
+    one wave, and the tied tokens taken must be the lowest-indexed ones."""
+    rng = np.random.default_rng(T + 7 * k)
+    B, H = 2, 2
+    s = rng.standard_normal((B, H, T)).astype(np.float32)
+    for b in range(B):
+        for h in range(H):
+            order = np.argsort(-s[b, h], kind="stable")
+            lo = k - 3 if (b + h) % 2 == 0 else k - 1          # 3 of 5, or 1 of 5 tied tokens taken
+            s[b, h, order[lo:lo + 5]] = s[b, h, order[k - 1]]
+    _topk_case(J, B, H, T, k, [T, T - 5], s)
+
+
 def test_topk_long_row_multi_round(J):
     """A row long enough that the chunk lists need more than one merge."""
     rng = np.random.default_rng(5)

@@ -83,10 +83,14 @@ constexpr uint32_t kDroppedBits = 0xffffffffu;
 
 template <int R>
 struct ScoreSmem {
-  float qbar[kD];
-  float qpart[kWaves * 64];
+  union {
+    struct {
+      float qbar[kD];
+      float qpart[kWaves * 64];
+    } pro;                                                   // prologue only
+    float part[(R / 8) & (R / 8 - 1) ? kWaves * 4 * R : 1];  // stream: LDS reduction (r = 48 only)
+  } u;
   float qp[R];
-  float part[(R / 8) & (R / 8 - 1) ? kWaves * 8 * R : 1];   // LDS reduction (r = 48 only)
 };
 
 template <int R, int MODE, bool FUSED, bool SCREEN>
@@ -97,7 +101,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
                                                     float* __restrict__ scores, FusedOut fo) {
   constexpr int PP = R / 8;                   // lanes (16-byte pieces) per token
   constexpr bool kDpp = (PP & (PP - 1)) == 0; // power of two -> DPP groups
-  constexpr int NSL = kDpp ? 1 : PP;          // qp slices held per lane
+  // qp slices held per lane: load m of a tile gives lane l piece
+  // (64 m + l) % PP, which repeats with period PP / gcd(64, PP) in m
+  constexpr int kLow = PP & -PP;              // gcd(64, PP) for PP <= 64
+  constexpr int NSL = kDpp ? 1 : PP / kLow;
   constexpr int TPW = tiles_per_wave(MODE, FUSED);
   __shared__ ScoreSmem<R> sm;
   // Fused: token o of the chunk is staged at (o % TPW) * SS + o / TPW with
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
         s += a0; s += a1; s += a2; s += a3;
       }
       for (; h < g.G; ++h) s += bf(qg[h * kD]);
-      sm.qbar[tid] = s;
+      sm.u.pro.qbar[tid] = s;
     }
     __syncthreads();
     if (sl < NS) {
@@ -257,14 +264,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
         const int i = sl + ii * NS;
         const int ic = i < kD ? i : kD - 1;
         const float p = kPreP ? pv[kPreP ? ii : 0] : Pj[ic * R + c];
-        s = __builtin_fmaf(p, i < kD ? sm.qbar[ic] : 0.f, s);
+        s = __builtin_fmaf(p, i < kD ? sm.u.pro.qbar[ic] : 0.f, s);
       }
-      sm.qpart[sl * R + c] = s;
+      sm.u.pro.qpart[sl * R + c] = s;
     }
     __syncthreads();
     if (tid < R) {
       float s = 0.f;
-      for (int x = 0; x < NS; ++x) s += sm.qpart[x * R + tid];
+      for (int x = 0; x < NS; ++x) s += sm.u.pro.qpart[x * R + tid];
       sm.qp[tid] = s;
     }
     __syncthreads();
@@ -294,14 +301,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       }
       return mine;
     } else {
-      float* pw = sm.part + w * 64 * PP;
-#pragma unroll
-      for (int m = 0; m < PP; ++m) pw[m * 64 + lane] = dot8(qr[m], v[m]);
-      wave_lds_sync();
+      // Token t of the tile sits in lanes PP*t .. PP*t+PP-1 of the loads taken
+      // as one 64*PP-lane row; the first PP/2 loads hold tokens 0..31 and the
+      // rest tokens 32..63, so the partials go through LDS half at a time.
+      static_assert(PP % 2 == 0, "a tile's loads split into two halves of 32 tokens");
+      constexpr int HALF = PP / 2;
+      float* pw = sm.u.part + w * 32 * PP;
       float s = 0.f;
 #pragma unroll
-      for (int pc = 0; pc < PP; ++pc) s += pw[lane * PP + pc];
-      wave_lds_sync();
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int m = 0; m < HALF; ++m) pw[m * 64 + lane] = dot8(qr[(hh * HALF + m) % NSL], v[hh * HALF + m]);
+        wave_lds_sync();
+        if ((lane >> 5) == hh) {
+#pragma unroll
+          for (int pc = 0; pc < PP; ++pc) s += pw[(lane & 31) * PP + pc];
+        }
+        wave_lds_sync();
+      }
       return s;
     }
   };

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
 // ---------------------------------------------------------------------------
 // final pass
 // ---------------------------------------------------------------------------
+constexpr int kBinList = 64;   // a bin this small is finished by one wave
 template <int NT>
 struct FinalSmem {
   uint32_t hist[kFinBins];
@@ -80,6 +81,8 @@ struct FinalSmem {
   ScanSmem<NT> scan;
   uint32_t red[2][NT / 64];
   int res[2];
+  uint32_t bin[kBinList];
+  int nbin;
 };
 
 // One block per (row, group of gs consecutive segments). MERGE = false: the
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       const uint64_t range = hi - lo;
       const int sh = range < uint64_t(kFinBins) ? 0 : (64 - __builtin_clzll(range)) - kFinBits;
       for (int i = tid; i < kFinBins; i += NT) sm.hist[i] = 0u;
+      if (tid == 0) sm.nbin = 0;
       __syncthreads();
       for_each_key([&](uint32_t key) {
         if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> sh], 1u);
@@ -341,6 +345,31 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
         trem = rem;
         break;
       }
+      if (cnt <= kBinList) {             // few keys in the bin: one wave ranks them exactly
+        for_each_key([&](uint32_t key) {
+          if (key >= lo && key <= hi && ((key - lo) >> sh) == D) sm.bin[atomicAdd(&sm.nbin, 1)] = key;
+        });
+        __syncthreads();
+        if (wv == 0) {
+          const uint32_t mine = lane < cnt ? sm.bin[lane] : 0u;
+          int gt = 0, eq = 0;                      // keys of the bin above / equal to this lane's
+          for (int i = 0; i < cnt; ++i) {
+            const uint32_t x = uint32_t(__builtin_amdgcn_readlane(int(mine), i));
+            gt += x > mine ? 1 : 0;
+            eq += x == mine ? 1 : 0;
+          }
+          // the rem-th largest key v of the bin: gt < rem <= gt + eq; take
+          // the rem - gt first of the keys equal to v (all of them: no ranking)
+          if (lane < cnt && gt < rem && rem <= gt + eq) {
+            sm.res[0] = int(mine);
+            sm.res[1] = rem - gt == eq ? 0x7fffffff : rem - gt;
+          }
+        }
+        __syncthreads();
+        tkey = uint32_t(sm.res[0]);
+        trem = sm.res[1];
+        break;
+      }
       const uint64_t bhi = blo + (uint64_t(1) << sh) - 1;
       lo = blo;
       hi = bhi < hi ? bhi : hi;
@@ -356,11 +385,13 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   int tie_base = 0, out_base = 0;
   __shared__ int32_t sel[GT > 0 ? kAttendMaxK : 1];   // the selected tokens, for the attention
   auto emit = [&](const uint32_t (&ck)[EF], const int32_t (&ci)[EF]) {
-    int nt = 0;
+    int tt = 0, tr = 0;
+    if (trem != 0x7fffffff) {                         // tied candidates are ranked only when some are left out
+      int nt = 0;
 #pragma unroll
-    for (int e = 0; e < EF; ++e) nt += (ci[e] >= 0 && ck[e] == tkey) ? 1 : 0;
-    int tt;
-    int tr = block_scan<NT>(nt, sm.scan, &tt) - nt + tie_base;
+      for (int e = 0; e < EF; ++e) nt += (ci[e] >= 0 && ck[e] == tkey) ? 1 : 0;
+      tr = block_scan<NT>(nt, sm.scan, &tt) - nt + tie_base;
+    }
     static_assert(EF <= 32, "taken flags are one bit each");
     uint32_t take = 0u;
 #pragma unroll
