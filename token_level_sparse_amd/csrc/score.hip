@@ -120,16 +120,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
 
   const int b = blockIdx.z, j = blockIdx.y;
+  // Chunk of this block: launch position x holds chunk (x + row) mod nx.
+  // Blocks go to the XCDs round-robin by launch position, so without the
+  // rotation chunk c of every row lands on XCD c mod 8; with ragged lengths
+  // the late chunks are empty for short rows and the low XCDs would carry
+  // most of the work.
+  const int nx = int(gridDim.x);
+  const int cx = int((blockIdx.x + unsigned(b * g.Hkv + j) % 8u) % unsigned(nx));
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, kept scalar
   const int Tb = seq_len(g, b);
   const int chunk = kWaves * 64 * TPW;
-  const int t_begin = blockIdx.x * chunk;
+  const int t_begin = cx * chunk;
   float* srow = scores ? scores + (int64_t(b) * g.Hkv + j) * g.max_seq : nullptr;
   const bool paged = g.page_size != 0;
   const int64_t ubase = (int64_t(b) * g.Hkv + j) * int64_t(g.max_seq) * R;   // contiguous unit base
 
-  const int64_t seg = FUSED ? int64_t(b * g.Hkv + j) * fo.segs.nseg + blockIdx.x : 0;
+  const int64_t seg = FUSED ? int64_t(b * g.Hkv + j) * fo.segs.nseg + cx : 0;
   if (t_begin >= Tb) {                       // whole chunk past the sequence's end
     if (!FUSED || fo.write_scores) {
       const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;

@@ -44,7 +44,11 @@ __device__ __forceinline__ int row_len(int max_seq, const int32_t* seq_lens, int
 __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
                                                     const float* __restrict__ scores, int k, CandSegs segs) {
   __shared__ ChunkSmem<kCT, kCE> sm;
-  const int tid = threadIdx.x, row = blockIdx.y, chunk = blockIdx.x;
+  // launch position x holds chunk (x + row) mod gridDim.x, which spreads each
+  // chunk index over the XCDs (blocks go to them round-robin by position;
+  // with ragged rows the late chunks are the empty ones)
+  const int tid = threadIdx.x, row = blockIdx.y;
+  const int chunk = int((blockIdx.x + unsigned(row) % 8u) % gridDim.x);
   const int Tb = row_len(max_seq, seq_lens, row / H);
   const int start = chunk * kChunk;
   int n = Tb - start;
