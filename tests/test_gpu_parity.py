@@ -943,13 +943,13 @@ def test_full_size_128k_b16_extensions_sampled(J, PL):
 def test_full_size_qwen_paged_k2048_sampled(J, PL):
     """Paged, ragged Qwen3-14B-shaped workload at full size with the largest
     budget of its sweep, in the benchmark's launch configuration (chunk pass,
-    merge levels + final selection, eight-split attention, combine)."""
+    merge levels + final selection, four-split attention, combine)."""
     cfg = replace(synth.PAGED_QWEN14B, k=2048)
     inp = synth.make_gqa(cfg)
     c = PL.GqaCache(inp)
     c.project()
     st = PL.SparseStep(c, k=cfg.k, fused=True, keep_scores=False)
-    assert st.S == 8
+    assert st.S == 4
     st.run()
     torch.cuda.synchronize()
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
