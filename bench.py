@@ -132,9 +132,9 @@ def cpu_oracle_gqa(inp, k, units, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the per-(sequence, KV-head) work would shard over batch or KV heads with no "
-              "communication; see the design notes).", file=sys.stderr)
+              "communication).", file=sys.stderr)
         sys.exit(2)
     import torch
     from token_level_sparse_amd import jssa, pipeline, synth  # noqa: F401  (loads libjssa.so)

@@ -24,7 +24,7 @@ blocks. Sources (page title, section):
             and FAQ (the top-delta rule, the sink/local pseudo-max and its
             fail-safe property).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
 
 R1 group aggregation: a KV head's score is the raw sum over its GQA group of
    the query heads' subspace scores (by linearity: the projected group-summed
