@@ -8,8 +8,9 @@
 // atomics (same-address atomics serialise across the XCDs):
 //  chunk   one 256-thread block per 8192 scores of a row (32 per thread)
 //          keeps every token at or above a bound on the chunk's own k-th key
-//          (chunk_select: a token below that key cannot be in the row's
-//          top-k) and writes them to the chunk's workspace segment.
+//          (chunk_select_top2 for full chunks with k <= 256, else
+//          chunk_select: a token below that key cannot be in the row's top-k)
+//          and writes them to the chunk's workspace segment.
 //  final   one block per row loads the row's candidate list (its segments
 //          in order, which is ascending token order) into registers, finds
 //          the exact threshold key with adaptive LDS histogram levels (each
@@ -41,9 +42,22 @@ __device__ __forceinline__ int row_len(int max_seq, const int32_t* seq_lens, int
 // ---------------------------------------------------------------------------
 // chunk pass over a score buffer
 // ---------------------------------------------------------------------------
+// A token past the row's end is staged as this NaN, whose score_key is 0,
+// the key of no token.
+constexpr uint32_t kNoTokenBits = 0xffffffffu;
+
 __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
                                                     const float* __restrict__ scores, int k, CandSegs segs) {
-  __shared__ ChunkSmem<kCT, kCE> sm;
+  // The chunk's scores go through LDS: loaded 16 bytes per lane (coalesced),
+  // staged so that thread i then reads its kCE consecutive tokens
+  // o = i*kCE + e at e*SS + i (token o sits at (o % kCE)*SS + o / kCE; the
+  // pad makes the writes and those reads hit distinct banks).
+  constexpr int SS = kCT + (kCE <= 64 ? 64 / kCE : 1);
+  constexpr int kStageBytes = kCE * SS * 4;
+  constexpr int kBufBytes =
+      kStageBytes > int(sizeof(ChunkSmem<kCT, kCE>)) ? kStageBytes : int(sizeof(ChunkSmem<kCT, kCE>));
+  __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
+  __shared__ Top2Smem<kCT> tsm;
   // launch position x holds chunk (x + row) mod gridDim.x, which spreads each
   // chunk index over the XCDs (blocks go to them round-robin by position;
   // with ragged rows the late chunks are the empty ones)
@@ -54,24 +68,57 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
   int n = Tb - start;
   n = n < 0 ? 0 : (n > kChunk ? kChunk : n);
   const float* src = scores + int64_t(row) * max_seq + start;
+  const int64_t seg = int64_t(row) * segs.nseg + chunk;
   if (n == 0) {
-    if (tid == 0) segs.cnt[int64_t(row) * segs.nseg + chunk] = 0;
+    if (tid == 0) segs.cnt[seg] = 0;
     return;
   }
-  // Thread i takes the chunk's scores i*kCE .. i*kCE+kCE-1 (consecutive
-  // tokens per thread, as chunk_select expects). All loads are issued
-  // together; positions past the row's end re-read its last score and are
-  // masked out as keys.
-  float v[kCE];
+  float* stage = reinterpret_cast<float*>(sbuf);
+  auto sidx = [](int o) { return (o % kCE) * SS + o / kCE; };
+  const float none = __uint_as_float(kNoTokenBits);
+  // All loads are issued together; positions past the row's end read a
+  // readable position and are staged as no token.
+  if ((max_seq & 3) == 0) {                      // 16-byte aligned rows (block-uniform)
+    const int lim = max_seq - start < kChunk ? max_seq - start : kChunk;   // readable, a multiple of 4, >= 4
+    f32x4 v[kCE / 4];
 #pragma unroll
-  for (int e = 0; e < kCE; ++e) {
-    const int p = tid * kCE + e;
-    v[e] = src[p < n ? p : n - 1];
+    for (int i = 0; i < kCE / 4; ++i) {
+      const int o = (i * kCT + tid) * 4;
+      v[i] = *reinterpret_cast<const f32x4*>(src + (o < lim ? o : lim - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < kCE / 4; ++i) {
+      const int o = (i * kCT + tid) * 4;
+      stage[sidx(o)] = o < n ? v[i].x : none;
+      stage[sidx(o + 1)] = o + 1 < n ? v[i].y : none;
+      stage[sidx(o + 2)] = o + 2 < n ? v[i].z : none;
+      stage[sidx(o + 3)] = o + 3 < n ? v[i].w : none;
+    }
+  } else {
+    float v[kCE];
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+      const int o = i * kCT + tid;
+      v[i] = src[o < n ? o : n - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kCE; ++i) {
+      const int o = i * kCT + tid;
+      stage[sidx(o)] = o < n ? v[i] : none;
+    }
   }
+  __syncthreads();
   uint32_t key[kCE];
 #pragma unroll
-  for (int e = 0; e < kCE; ++e) key[e] = tid * kCE + e < n ? score_key(v[e]) : 0u;
-  chunk_select<kCT, kCE>(key, start, start + n, n, k, sm, segs, int64_t(row) * segs.nseg + chunk);
+  for (int e = 0; e < kCE; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*kCE + e
+  // the top-two bound first (block-uniform; it leaves the stage intact),
+  // the histogram select when it does not apply or keeps too many
+  const bool done = n == kChunk && k <= kCT && chunk_select_top2<kCT, kCE>(key, start, k, tsm, stage, SS, segs, seg);
+  if (!done) {
+    __syncthreads();                             // the stage is reused below
+    ChunkSmem<kCT, kCE>& csm = *reinterpret_cast<ChunkSmem<kCT, kCE>*>(sbuf);
+    chunk_select<kCT, kCE>(key, start, start + n, n, k, csm, segs, seg);
+  }
 }
 
 // ---------------------------------------------------------------------------
