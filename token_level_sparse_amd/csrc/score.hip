@@ -39,7 +39,8 @@ constexpr int kPlainTiles = 16;            // 4096-token chunks for the score-on
 constexpr int kMlaTiles = 4;               // 1024-token chunks: the latent cache has only B rows
 constexpr int kDepth = 2;                  // tiles per wave whose loads are in flight together
 
-// sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16)
+// sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16), left in every
+// lane of the group (a butterfly; the lanes' sums are bit-identical)
 template <int PP>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (PP >= 2) x += dpp_mov<0xb1>(x);     // quad_perm [1,0,3,2]
@@ -299,14 +300,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   auto tile_scores = [&](const u32x4 (&v)[PP]) -> float {
     if constexpr (kDpp) {
       constexpr int TPI = 64 / PP;            // tokens per load column
-      float mine = 0.f;
+      // Every lane of a group holds the group sum; lane g*PP + i keeps the
+      // sum of load i (token i*TPI + g), so one permute hands each lane its
+      // token: token t is in load t / TPI, group t % TPI.
+      float r = 0.f;
 #pragma unroll
       for (int m = 0; m < PP; ++m) {
         const float s = group_sum<PP>(dot8(qr[0], v[m]));
-        const float x = __shfl(s, (lane % TPI) * PP, 64);
-        if (lane / TPI == m) mine = x;
+        r = (lane % PP) == m ? s : r;
       }
-      return mine;
+      return __shfl(r, (lane % TPI) * PP + lane / TPI, 64);
     } else {
       // Token t of the tile sits in lanes PP*t .. PP*t+PP-1 of the loads taken
       // as one 64*PP-lane row; the first PP/2 loads hold tokens 0..31 and the
