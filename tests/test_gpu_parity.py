@@ -157,8 +157,10 @@ def _topk_case(J, B, H, T, k, lens, scores):
 @pytest.mark.parametrize("T,k", [(4096, 256), (32768, 256), (50000, 1), (20000, 1024), (70000, 2048),
                                  (40000, 4096), (3000, 3000), (1500, 700), (100, 7),
                                  # rows whose length is not a multiple of 4 (scalar score loads), one
-                                 # token past a chunk, exactly one chunk
-                                 (9999, 300), (8193, 256), (8192, 256), (17, 5)])
+                                 # token past a chunk, exactly one chunk; few rows with a budget whose
+                                 # 8192-token lists would need merging take 32768-token chunks
+                                 # (70000 and 40000 above, and 32769: odd, one past a wide chunk)
+                                 (9999, 300), (8193, 256), (8192, 256), (17, 5), (32769, 2048)])
 def test_topk_bit_exact(J, T, k):
     rng = np.random.default_rng(T + k)
     B, H = 3, 2

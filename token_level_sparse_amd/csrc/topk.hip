@@ -121,6 +121,55 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
   }
 }
 
+// Wide chunks, for rows too few to fill the GPU with 8192-token chunks and
+// budgets large enough that those chunks' lists would need a merge level
+// (e.g. one latent head per sequence, k = 2048): one 1024-thread block per
+// 32768 scores of a row, 32 consecutive scores per thread, the histogram
+// select. Four such chunks of a 128K row keep few enough candidates for the
+// final pass to read them directly.
+constexpr int kWT = 1024;
+constexpr int kWideChunk = kWT * kCE;   // 32768
+
+__global__ __launch_bounds__(kWT) void chunk_wide_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
+                                                         const float* __restrict__ scores, int k, CandSegs segs) {
+  __shared__ ChunkSmem<kWT, kCE> sm;
+  const int tid = threadIdx.x, row = blockIdx.y;
+  const int chunk = int((blockIdx.x + unsigned(row) % 8u) % gridDim.x);   // spread over the XCDs, as above
+  const int Tb = row_len(max_seq, seq_lens, row / H);
+  const int start = chunk * kWideChunk;
+  int n = Tb - start;
+  n = n < 0 ? 0 : (n > kWideChunk ? kWideChunk : n);
+  const float* src = scores + int64_t(row) * max_seq + start;
+  const int64_t seg = int64_t(row) * segs.nseg + chunk;
+  if (n == 0) {
+    if (tid == 0) segs.cnt[seg] = 0;
+    return;
+  }
+  // Thread i takes scores i*kCE .. i*kCE+kCE-1, all loads issued together;
+  // positions past the row's end read a readable position and are masked.
+  float v[kCE];
+  const int p0 = tid * kCE;
+  if ((max_seq & 3) == 0) {                      // 16-byte aligned rows (block-uniform)
+    const int lim = max_seq - start < kWideChunk ? max_seq - start : kWideChunk;   // a multiple of 4, >= 4
+#pragma unroll
+    for (int i = 0; i < kCE / 4; ++i) {
+      const int o = p0 + 4 * i;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + (o < lim ? o : lim - 4));
+      v[4 * i] = x.x;
+      v[4 * i + 1] = x.y;
+      v[4 * i + 2] = x.z;
+      v[4 * i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kCE; ++e) v[e] = src[p0 + e < n ? p0 + e : n - 1];
+  }
+  uint32_t key[kCE];
+#pragma unroll
+  for (int e = 0; e < kCE; ++e) key[e] = p0 + e < n ? score_key(v[e]) : 0u;
+  chunk_select<kWT, kCE>(key, start, start + n, n, k, sm, segs, seg);
+}
+
 // ---------------------------------------------------------------------------
 // final pass
 // ---------------------------------------------------------------------------
@@ -615,16 +664,43 @@ hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uin
   return hipGetLastError();
 }
 
+namespace {
+// Wide chunks when the 8192-token grid is small (fewer blocks than CUs) and
+// its lists would need merging, but the wide lists would not.
+bool use_wide(int rows, int max_seq, int k) {
+  const int nchunks = chunks_of(max_seq), nwide = (max_seq + kWideChunk - 1) / kWideChunk;
+  return int64_t(rows) * nchunks < 256 && needs_merge(nchunks, k) && !needs_merge(nwide, k);
+}
+}  // namespace
+
 size_t topk_workspace_bytes(int rows, int max_seq, int k) {
   size_t total = 0;
   carve_segs(nullptr, rows, chunks_of(max_seq), kChunk, &total);
-  return total + merge_workspace_bytes(rows, chunks_of(max_seq), k);
+  total += merge_workspace_bytes(rows, chunks_of(max_seq), k);
+  if (use_wide(rows, max_seq, k)) {
+    size_t wide = 0;
+    carve_segs(nullptr, rows, (max_seq + kWideChunk - 1) / kWideChunk, kWideChunk, &wide);
+    total = wide > total ? wide : total;
+  }
+  return total;
 }
 
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
                        int32_t* idx, void* wsp, hipStream_t st) {
   const int rows = B * H;
   const int nchunks = chunks_of(max_seq);
+  if (use_wide(rows, max_seq, k)) {               // (the workspace size covers this layout)
+    const int nwide = (max_seq + kWideChunk - 1) / kWideChunk;
+    CandSegs segs = carve_segs(wsp, rows, nwide, kWideChunk, nullptr);
+    hipLaunchKernelGGL(chunk_wide_kernel, dim3(nwide, rows), dim3(kWT), 0, st, H, max_seq, seq_lens, scores, k,
+                       segs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // about nwide * k candidates plus ties: the 12-per-thread final holds them
+    hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
+                       segs, segs.nseg, idx, CandSegs{}, AttendArgs{}, DeltaArgs{});
+    return hipGetLastError();
+  }
   size_t main_bytes = 0;
   CandSegs segs = carve_segs(wsp, rows, nchunks, kChunk, &main_bytes);
   hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
