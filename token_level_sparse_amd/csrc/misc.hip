@@ -11,43 +11,71 @@
 namespace jssa {
 namespace {
 
-// One row (b, h) per tpr = dv/4 threads, several rows per 256-thread block.
-// Loads of the partials are issued 8 splits at a time so their latencies
-// overlap.
-__global__ __launch_bounds__(256) void combine_kernel(int rows, int S, int dv,
+// A row (b, h) is handled by tpr = dv/4 threads (4 outputs each) times SG
+// split groups: group sg weights splits sg, sg + SG, ..., with up to 8 of
+// its loads in flight at a time, and the groups' sums are added in LDS in
+// group order (deterministic). Several rows share a 256-thread block when
+// tpr * SG < 256. Every thread first reads all S log-sum-exps of its row for
+// the maximum (the same addresses across the row's threads).
+__global__ __launch_bounds__(256) void combine_kernel(int rows, int S, int dv, int SG,
                                                       const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       void* __restrict__ out, int out_bf16,
                                                       float* __restrict__ lse_out) {
-  const int tpr = dv / 4;
-  const int rpb = 256 / tpr;
-  const int bh = blockIdx.x * rpb + threadIdx.x / tpr;
-  const int c4 = threadIdx.x % tpr;
-  if (bh >= rows || threadIdx.x >= rpb * tpr) return;
-  const float* pl = part_lse + int64_t(bh) * S;
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
+  __shared__ f32x4 red_o[256];
+  __shared__ float red_l[256];
+  const int tpr = dv / 4, tprow = tpr * SG;
+  const int rpb = 256 / tprow;
+  const int slot = threadIdx.x / tprow;                 // row of the block
+  const int sg = (threadIdx.x / tpr) % SG, c4 = threadIdx.x % tpr;
+  const int bh = blockIdx.x * rpb + slot;
+  const bool live = slot < rpb && bh < rows;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -__builtin_inff()) {
-    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + int64_t(bh) * S * dv) + c4;
+  float L = 0.f, M = -__builtin_inff();
+  if (live) {
+    const float* pl = part_lse + int64_t(bh) * S;
     for (int s0 = 0; s0 < S; s0 += 8) {
-      f32x4 v[8];
-      float wgt[8];
+      float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int s = s0 + i;
-        wgt[i] = s < S ? __expf(pl[s] - M) : 0.f;
-        v[i] = (s < S && wgt[i] != 0.f) ? po[int64_t(s) * tpr] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int i = 0; i < 8; ++i) x[i] = s0 + i < S ? pl[s0 + i] : -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        L += wgt[i];
-        acc += wgt[i] * v[i];
+      for (int i = 0; i < 8; ++i) M = fmaxf(M, x[i]);
+    }
+    if (M != -__builtin_inff()) {
+      const f32x4* po = reinterpret_cast<const f32x4*>(part_o + int64_t(bh) * S * dv) + c4;
+      for (int s0 = sg; s0 < S; s0 += 8 * SG) {
+        f32x4 v[8];
+        float wgt[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int s = s0 + i * SG;
+          wgt[i] = s < S ? __expf(pl[s] - M) : 0.f;
+          v[i] = (s < S && wgt[i] != 0.f) ? po[int64_t(s) * tpr] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          L += wgt[i];
+          acc += wgt[i] * v[i];
+        }
       }
     }
-    acc *= 1.f / L;
   }
+  if (SG > 1) {                                         // block-uniform
+    red_o[threadIdx.x] = acc;
+    red_l[threadIdx.x] = L;
+    __syncthreads();
+    if (!live || sg != 0) return;
+    const int r0 = slot * tprow;
+    acc = red_o[r0 + c4];
+    L = red_l[r0];
+    for (int x = 1; x < SG; ++x) {
+      acc += red_o[r0 + x * tpr + c4];
+      L += red_l[r0 + x * tpr];
+    }
+  } else if (!live) {
+    return;
+  }
+  if (L > 0.f) acc *= 1.f / L;
   if (out_bf16) {
     uint16_t* o = static_cast<uint16_t*>(out) + int64_t(bh) * dv + c4 * 4;
     u32x2 pk = {uint32_t(f32_to_bf16_rne(acc.x)) | (uint32_t(f32_to_bf16_rne(acc.y)) << 16),
@@ -91,9 +119,13 @@ hipError_t launch_combine(int B, int H, int S, int dv, const float* part_o, cons
                           void* out, bool out_bf16, float* lse, hipStream_t st) {
   const int rows = B * H;
   const int tpr = dv / 4;
-  const int rpb = tpr >= 256 ? 1 : 256 / tpr;
-  if (tpr > 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, rows, S, dv, part_o,
+  if (tpr > 256 || tpr < 1 || S < 1) return hipErrorInvalidValue;
+  // split groups per row: up to 8, as many as fit the block and the splits
+  int SG = 256 / tpr;
+  SG = SG < 8 ? SG : 8;
+  SG = SG < S ? SG : S;
+  const int rpb = 256 / (tpr * SG);
+  hipLaunchKernelGGL(combine_kernel, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, rows, S, dv, SG, part_o,
                      part_lse, out, out_bf16 ? 1 : 0, lse);
   return hipGetLastError();
 }
