@@ -31,42 +31,69 @@ __device__ __forceinline__ int mla_len(const MlaDev& m, int b) {
 
 // ---------------------------------------------------------------------------
 // Kp_lat = bf16_rne(c . P), fp64 accumulation (same rounding argument as the
-// GQA key projection). Block: 64 tokens x R columns; P read through L2.
+// GQA key projection), on fp64 MFMA: v_mfma_f64_16x16x4f64 takes A[m][k]
+// from lane 16k + m, B[k][n] from lane 16k + n, and leaves D[k' + 4i][n] in
+// register i of lane 16k' + n. Block: 64 tokens (16 per wave) x R columns.
+// The 576 dims go in 9 chunks of 64; in chunk c, step s, lane group kq
+// covers dim 64c + 16kq + s (the same order for A and B), so a lane's A
+// values are 16 consecutive dims of its token (32 bytes), and the chunk's
+// P rows sit in LDS. The next chunk's A loads are in flight during the
+// current chunk's products.
 // ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int R>
 __global__ __launch_bounds__(256) void mla_project_kernel(MlaDev m, const uint16_t* __restrict__ lat,
                                                           const float* __restrict__ P,
                                                           uint16_t* __restrict__ Kp) {
-  constexpr int TOK = 64;
-  constexpr int TG = 256 / R;            // token groups
-  constexpr int TPT = TOK / TG;          // tokens per thread
-  __shared__ uint16_t Cs[TOK * kDc];
+  static_assert(R % 16 == 0, "columns in tiles of 16");
+  constexpr int TOK = 64, CH = 64, NCH = kDc / CH;
+  static_assert(kDc % CH == 0, "whole chunks");
+  __shared__ __attribute__((aligned(16))) float Pc[CH * R];
   const int b = blockIdx.y, t0 = blockIdx.x * TOK;
   const int Tb = mla_len(m, b);
-  const int tid = threadIdx.x;
-  const uint16_t* src = lat + (int64_t(b) * m.max_seq + t0) * kDc;
-  const int nrows = min(TOK, max(0, Tb - t0));
-  for (int e = tid; e < TOK * kDc / 8; e += 256) {
-    const int row = e / (kDc / 8);
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (row < nrows) v = reinterpret_cast<const u32x4*>(src)[e];
-    reinterpret_cast<u32x4*>(Cs)[e] = v;
-  }
-  __syncthreads();
-  const int c = tid % R, tg = tid / R;
-  double acc[TPT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int mm = lane & 15, kq = lane >> 4;
+  const int tok = t0 + 16 * w + mm;                      // this lane's A row
+  const bool aval = tok < Tb;
+  const uint16_t* arow = lat + (int64_t(b) * m.max_seq + (aval ? tok : 0)) * kDc + 16 * kq;
+  auto load_a = [&](int c, u32x4 (&v)[2]) {
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) acc[i] = 0.0;
-  for (int i = 0; i < kDc; ++i) {
-    const double p = double(P[i * R + c]);
+    for (int q = 0; q < 2; ++q)
+      v[q] = aval ? reinterpret_cast<const u32x4*>(arow + c * CH)[q] : u32x4{0u, 0u, 0u, 0u};
+  };
+  f64x4 acc[R / 16];
 #pragma unroll
-    for (int x = 0; x < TPT; ++x) acc[x] = __builtin_fma(double(bf(Cs[(tg + x * TG) * kDc + i])), p, acc[x]);
+  for (int ct = 0; ct < R / 16; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+  u32x4 av[2], an[2];
+  load_a(0, av);
+#pragma unroll 1
+  for (int c = 0; c < NCH; ++c) {
+    load_a(c + 1 < NCH ? c + 1 : c, an);                // (the last chunk reloads itself, unused)
+    __syncthreads();                                    // the previous chunk's P rows are read
+    for (int e = tid * 4; e < CH * R; e += 256 * 4)
+      *reinterpret_cast<f32x4*>(Pc + e) = *reinterpret_cast<const f32x4*>(P + int64_t(c) * CH * R + e);
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < R / 16; ++ct) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t wd = av[s >> 3][(s >> 1) & 3];
+        const double x = double(__uint_as_float((s & 1) ? (wd & 0xffff0000u) : (wd << 16)));
+        const double y = double(Pc[(16 * kq + s) * R + 16 * ct + mm]);
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, y, acc[ct], 0, 0, 0);
+      }
+    }
+    av[0] = an[0];
+    av[1] = an[1];
   }
 #pragma unroll
-  for (int x = 0; x < TPT; ++x) {
-    const int t = t0 + tg + x * TG;
-    if (t < Tb) Kp[(int64_t(b) * m.max_seq + t) * R + c] = f64_to_bf16_rne(acc[x]);
-  }
+  for (int ct = 0; ct < R / 16; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * w + kq + 4 * i;
+      if (t < Tb) Kp[(int64_t(b) * m.max_seq + t) * R + 16 * ct + mm] = f64_to_bf16_rne(acc[ct][i]);
+    }
 }
 
 // ---------------------------------------------------------------------------
