@@ -313,6 +313,41 @@ def test_score_topk_fused_equals_split(J, PL, case):
     np.testing.assert_array_equal(_np(h.scores), _np(a.scores))
 
 
+@pytest.mark.parametrize("case", ["no_seq_lens", "b65_ragged", "b64_ragged"])
+def test_chunk_pass_launch_orders(J, PL, case):
+    """The chunk pass maps launch positions to (sequence, KV head, chunk)
+    two ways: with per-sequence lengths and up to 64 sequences the real
+    chunks come first (packed), otherwise each row's chunks are rotated.
+    Both must give the indices (and scores) of jssa_score + jssa_topk."""
+    if case == "no_seq_lens":
+        inp = synth.make_gqa(replace(synth.TINY, B=2, T=20000, seed=91))
+    else:
+        B = 65 if case == "b65_ragged" else 64
+        inp = synth.make_gqa(replace(synth.TINY, B=B, Hq=4, Hkv=1, T=17000, len_lo=1, len_hi=17000, seed=92))
+    c = PL.GqaCache(inp)
+    c.project()
+    if case == "no_seq_lens":                       # every row full: the lengths may be left out
+        assert np.all(inp.seq_lens == c.T)
+        c.desc = J.gqa_desc(c.B, c.Hq, c.Hkv, c.r, c.T, c.d, 0, 0, 0, None, None)
+    k = 256
+    a = PL.SparseStep(c, k=k, fused=False)
+    a.score()
+    a.topk()
+    b = PL.SparseStep(c, k=k, fused=True, keep_scores=True)
+    b.score_topk()
+    nb = PL.SparseStep(c, k=k, fused=True, keep_scores=False)
+    nb.score_topk()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(b.idx), _np(a.idx))
+    np.testing.assert_array_equal(_np(nb.idx), _np(a.idx))
+    np.testing.assert_array_equal(_np(b.scores), _np(a.scores))
+    # and against the oracle on a few rows
+    for bb in sorted({0, c.B // 2, c.B - 1}):
+        for j in range(c.Hkv):
+            _, _, _, s, _ = U.oracle_unit(inp, bb, j)
+            U.check_indices(_np(nb.idx)[bb, j], s, k)
+
+
 @pytest.mark.parametrize("case", ["llama_k256", "ragged_k100", "qwen_paged_k256_G5", "tiny_k512", "G8_k300", "k1024_split"])
 def test_final_attend_matches_separate(J, PL, case):
     """jssa_score_topk_final_attend writes the indices of the separate final

@@ -38,6 +38,7 @@ constexpr int kFusedTiles = 32;            // tiles of 64 tokens per wave: 8192-
 constexpr int kPlainTiles = 16;            // 4096-token chunks for the score-only stream
 constexpr int kMlaTiles = 4;               // 1024-token chunks: the latent cache has only B rows
 constexpr int kDepth = 2;                  // tiles per wave whose loads are in flight together
+constexpr int kPackMaxB = 64;              // sequences up to which blocks take packed work items
 
 // sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16), left in every
 // lane of the group (a butterfly; the lanes' sums are bit-identical)
@@ -120,14 +121,41 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   constexpr int kBufBytes = kStageBytes > int(sizeof(ChunkSmem<NT, TPW>)) ? kStageBytes : int(sizeof(ChunkSmem<NT, TPW>));
   __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
 
-  const int b = blockIdx.z, j = blockIdx.y;
-  // Chunk of this block: launch position x holds chunk (x + row) mod nx.
-  // Blocks go to the XCDs round-robin by launch position, so without the
-  // rotation chunk c of every row lands on XCD c mod 8; with ragged lengths
-  // the late chunks are empty for short rows and the low XCDs would carry
-  // most of the work.
+  // Work item of this block. Blocks go to the XCDs round-robin by launch
+  // position. With per-sequence lengths (up to kPackMaxB sequences), the first
+  // launch positions take the rows' real chunks in row-major order and the
+  // rest the chunks past their sequence's end, which only record an empty
+  // segment: the real work is dealt evenly over the XCDs and CUs instead of
+  // leaving the slots of empty chunks idle. Otherwise launch position x holds
+  // chunk (x + row) mod nx, so chunk c of every row does not land on one XCD.
   const int nx = int(gridDim.x);
-  const int cx = int((blockIdx.x + unsigned(b * g.Hkv + j) % 8u) % unsigned(nx));
+  int b, j, cx;
+  if (g.seq_lens && g.B <= kPackMaxB) {
+    const int chunk_len = kWaves * 64 * TPW;
+    const int lin = int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    auto nch = [&](int bb) { return (seq_len(g, bb) + chunk_len - 1) / chunk_len; };   // <= nx
+    int real = 0;
+    for (int bb = 0; bb < g.B; ++bb) real += g.Hkv * nch(bb);
+    b = 0;
+    j = 0;
+    cx = 0;
+    int acc = lin < real ? 0 : real;
+    for (int bb = 0; bb < g.B; ++bb) {
+      const int n = lin < real ? nch(bb) : nx - nch(bb), c = g.Hkv * n;   // chunks of each row of bb in this part
+      if (lin < acc + c) {
+        const int r = lin - acc;
+        b = bb;
+        j = r / n;
+        cx = (lin < real ? 0 : nx - n) + (r - j * n);
+        break;
+      }
+      acc += c;
+    }
+  } else {
+    b = int(blockIdx.z);
+    j = int(blockIdx.y);
+    cx = int((blockIdx.x + unsigned(b * g.Hkv + j) % 8u) % unsigned(nx));
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, kept scalar
   const int Tb = seq_len(g, b);
