@@ -122,20 +122,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   __shared__ __attribute__((aligned(16))) char sbuf[kBufBytes];   // staged scores, then selection scratch
 
   // Work item of this block. Blocks go to the XCDs round-robin by launch
-  // position. With per-sequence lengths (up to kPackMaxB sequences), the first
-  // launch positions take the rows' real chunks in row-major order and the
-  // rest the chunks past their sequence's end, which only record an empty
-  // segment: the real work is dealt evenly over the XCDs and CUs instead of
-  // leaving the slots of empty chunks idle. Otherwise launch position x holds
-  // chunk (x + row) mod nx, so chunk c of every row does not land on one XCD.
+  // position. When some chunks lie past their sequence's end (per-sequence
+  // lengths, up to kPackMaxB sequences), the first launch positions take the
+  // rows' real chunks in row-major order and the rest the empty ones, which
+  // only record an empty segment: the real work is dealt evenly over the
+  // XCDs and CUs instead of leaving the slots of empty chunks idle. Otherwise
+  // launch position x holds chunk (x + row) mod nx, so chunk c of every row
+  // does not land on one XCD.
   const int nx = int(gridDim.x);
   int b, j, cx;
+  const int chunk_len = kWaves * 64 * TPW;
+  auto nch = [&](int bb) { return (seq_len(g, bb) + chunk_len - 1) / chunk_len; };   // <= nx
+  int real = g.B * g.Hkv * nx;                          // chunks before the sequences' ends
   if (g.seq_lens && g.B <= kPackMaxB) {
-    const int chunk_len = kWaves * 64 * TPW;
-    const int lin = int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-    auto nch = [&](int bb) { return (seq_len(g, bb) + chunk_len - 1) / chunk_len; };   // <= nx
-    int real = 0;
+    real = 0;
+#pragma unroll 8
     for (int bb = 0; bb < g.B; ++bb) real += g.Hkv * nch(bb);
+  }
+  if (real < g.B * g.Hkv * nx) {                        // some chunk lies past its sequence's end
+    const int lin = int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
     b = 0;
     j = 0;
     cx = 0;
