@@ -384,8 +384,12 @@ JSSA_API jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const
  * valid seeds nothing is dropped.
  */
 
-/* Size of the tile bounds: device bf16 [B,Hkv,ceil(max_seq/64),2,r], per tile
- * the r minima then the r maxima (+inf / -inf for a tile with no valid token). */
+/* Size of the tile bounds: device bf16 [B,Hkv,ntg,2r/8,64,8] with
+ * ntg = ceil(ceil(max_seq/64)/64): tiles in groups of 64; per group, 8-dim
+ * vector v of each of its 64 tiles in turn, v < r/8 holding the minima of
+ * dims 8v..8v+7 and v >= r/8 the maxima of dims 8(v-r/8)..8(v-r/8)+7 (+inf /
+ * -inf for a tile with no valid token). Tiles past ceil(max_seq/64) are
+ * never written or read. */
 JSSA_API jssa_status jssa_tile_bounds_size(const jssa_gqa_desc* desc, size_t* bytes);
 
 /* Builds every tile's bounds from the projected cache Kp (layout of desc).

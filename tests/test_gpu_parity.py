@@ -660,6 +660,8 @@ def _screen_inputs(case):
         return inp, 512
     if case == "ragged_dup_seeds":
         return ragged_inputs(), 100
+    if case == "clustered_long":                              # tiles past the preloaded iterations
+        return synth.make_gqa(replace(synth.TINY, B=1, T=140000, key_model="clustered", seed=96)), 128
     if case.startswith("clustered_r"):                        # ranks 16, 64, 128: other kernel shapes
         r = int(case[len("clustered_r"):])
         return synth.make_gqa(replace(synth.TINY, B=2, T=20000, r=r, key_model="clustered", seed=98 + r)), 128
@@ -667,8 +669,8 @@ def _screen_inputs(case):
 
 
 @pytest.mark.parametrize("case", ["tiny", "llama_random_seeds", "clustered_32k", "clustered_paged_invalid",
-                                  "ragged_dup_seeds", "no_seeds", "clustered_r16", "clustered_r64",
-                                  "clustered_r128"])
+                                  "ragged_dup_seeds", "no_seeds", "clustered_long", "clustered_r16",
+                                  "clustered_r64", "clustered_r128"])
 def test_screened_topk_lossless(J, PL, case):
     inp, k = _screen_inputs(case)
     cfg = inp.cfg
@@ -693,7 +695,9 @@ def test_screened_topk_lossless(J, PL, case):
     np.testing.assert_array_equal(_np(sc.idx), _np(plain.idx))          # the selection is unchanged
     # bounds: exact bf16 min / max per tile
     nt = (cfg.T + 63) // 64
-    bd = _np(sc.bounds).reshape(cfg.B, cfg.Hkv, nt, 2, cfg.r)
+    ntg = (nt + 63) // 64                                     # groups of 64 tiles, vector-major inside
+    bd = _np(sc.bounds).reshape(cfg.B, cfg.Hkv, ntg, 2, cfg.r // 8, 64, 8).transpose(0, 1, 2, 5, 3, 4, 6)
+    bd = bd.reshape(cfg.B, cfg.Hkv, ntg * 64, 2, cfg.r)
     bdf = O.bf16_to_f64(bd)
     # keep bits written after the jssa_score_topk workspace
     base = J.jssa_score_topk_workspace_size(c.desc, k)

@@ -483,7 +483,8 @@ jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const void* q,
 jssa_status jssa_tile_bounds_size(const jssa_gqa_desc* desc, size_t* bytes) {
   if (jssa_status s = check_desc(__func__, desc, true)) return s;
   if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
-  *bytes = size_t(desc->B) * desc->Hkv * jssa::screen_tiles(desc->max_seq) * 2 * desc->r * sizeof(uint16_t);
+  *bytes = size_t(desc->B) * desc->Hkv * ((jssa::screen_tiles(desc->max_seq) + 63) / 64 * 64) * 2 * desc->r *
+           sizeof(uint16_t);
   return JSSA_OK;
 }
 

@@ -20,11 +20,17 @@
 //
 // Both sides of the comparison carry fp32 rounding: the stream scores the
 // same token in another order than the seed pass, and ub is an fp32 sum.
-// A tile is dropped only when ub + eps * U < tau - eps * S, with U the
-// tile's sum_c |qp_c| max(|lo_c|, |hi_c|) (a bound on every sum_c |qp_c
-// Kp_c| in the tile), S the largest such sum over the seeds and eps = 2^-16,
+// A tile is dropped only when ub + eps * U < tau - eps * S, with U a bound
+// on every sum_c |qp_c Kp_c| in the tile ((sum_c |qp_c|) max_c max(|lo_c|,
+// |hi_c|) for r <= 48, sum_c |qp_c| max(|lo_c|, |hi_c|) above), S the
+// largest such sum over the seeds and eps = 2^-16,
 // far above the error of a sum of r <= 128 fp32 terms: a tile that exact
 // arithmetic would keep is never dropped.
+//
+// Bounds layout: tiles in groups of 64; for each group, 16-byte vector v of
+// every tile of the group in turn (v < r/8: the minima of dims 8v .. 8v+7,
+// else the maxima of dims 8(v - r/8) .. 8(v - r/8)+7). A wave that reads
+// vector v of 64 consecutive tiles reads 1 KB of consecutive bytes.
 #include "internal.hpp"
 
 namespace jssa {
@@ -39,12 +45,16 @@ constexpr int kSeedTable = 1 << kSeedTableBits;
 constexpr int screen_threads(int R) { return R >= 64 ? 512 : 1024; }
 constexpr float kScreenEps = 1.0f / 65536.0f;
 
+// index (in 16-byte vectors) of vector v of a tile; row = b * Hkv + j
+__device__ __forceinline__ int64_t bound_vec(int64_t row, int ngroups, int nv2, int tile, int v) {
+  return ((row * ngroups + (tile >> 6)) * nv2 + v) * 64 + (tile & 63);
+}
+
 __global__ __launch_bounds__(64) void tile_bounds_kernel(GqaDev g, const uint16_t* __restrict__ Kp,
                                                           uint16_t* __restrict__ bounds, int ntiles) {
   const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int Tb = seq_len(g, b);
-  const int R = g.r;
-  uint16_t* dst = bounds + ((int64_t(b) * g.Hkv + j) * ntiles + tile) * 2 * R;
+  const int R = g.r, ngroups = (ntiles + 63) / 64, row = b * g.Hkv + j;
   for (int c0 = 0; c0 < R; c0 += 64) {
     const int c = c0 + lane;
     float lo = __builtin_inff(), hi = -__builtin_inff();
@@ -72,8 +82,8 @@ __global__ __launch_bounds__(64) void tile_bounds_kernel(GqaDev g, const uint16_
       }
       // min and max of bf16 values are bf16 values: the conversion is exact
       // (and +-inf for a tile without a valid token)
-      dst[c] = uint16_t(__float_as_uint(lo) >> 16);
-      dst[R + c] = uint16_t(__float_as_uint(hi) >> 16);
+      bounds[bound_vec(row, ngroups, R / 4, tile, c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(lo) >> 16);
+      bounds[bound_vec(row, ngroups, R / 4, tile, R / 8 + c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(hi) >> 16);
     }
   }
 }
@@ -91,6 +101,7 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
   constexpr int NS = NT / R, NI = (128 + NS - 1) / NS; // P row slices and rows per slice
   __shared__ float qbar[128];
   __shared__ float qp[128];
+  __shared__ uint32_t qsel[64];                         // per dim pair: 0xffff halves where qp_c > 0
   __shared__ float qpart[NS][R];
   __shared__ int32_t table[kSeedTable];                 // distinct seed tokens (open addressing)
   __shared__ uint32_t hist[kScrBins];
@@ -120,10 +131,20 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
     st[x] = i < n_seed ? seeds[int64_t(row) * n_seed + i] : -1;
     mine[x] = false;
   }
-  if (tid < 128) {
-    float s = 0.f;
-    for (int h = 0; h < g.G; ++h) s += bf(q[(int64_t(b) * g.Hq + int64_t(j) * g.G + h) * 128 + tid]);
-    qbar[tid] = s;
+  // the group's query rows, by the first two waves: up to 8 rows with all
+  // loads in flight (heads past G re-read the last one), the rest after
+  constexpr int NV = R / 8;
+  constexpr int kQh = 8;
+  if (__builtin_amdgcn_readfirstlane(wv) < 2) {         // wave-uniform: tid < 128
+    const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * 128 + tid;
+    uint16_t qv[kQh];
+#pragma unroll
+    for (int h = 0; h < kQh; ++h) qv[h] = qg[(h < g.G ? h : g.G - 1) * 128];
+    float qs = 0.f;
+#pragma unroll
+    for (int h = 0; h < kQh; ++h) qs += h < g.G ? bf(qv[h]) : 0.f;
+    for (int h = kQh; h < g.G; ++h) qs += bf(qg[h * 128]);
+    qbar[tid] = qs;
   }
   for (int i = tid; i < kSeedTable; i += NT) table[i] = -1;
   __syncthreads();
@@ -155,6 +176,8 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
     float s = 0.f;
     for (int x = 0; x < NS; ++x) s += qpart[x][tid];
     qp[tid] = s;
+    const float s1 = __shfl_down(s, 1, 64);
+    if ((tid & 1) == 0) qsel[tid >> 1] = (s > 0.f ? 0xffffu : 0u) | (s1 > 0.f ? 0xffff0000u : 0u);
   }
   __syncthreads();                                      // qp complete
   uint32_t skey[SPT];
@@ -168,9 +191,9 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
     const int64_t off = row_off(g, b, j, st[x], R);
     if (off < 0) continue;                              // no valid page
     const u32x4* rowp = reinterpret_cast<const u32x4*>(Kp + off);
-    u32x4 rv[R / 8];
+    u32x4 rv[NV];
 #pragma unroll
-    for (int c8 = 0; c8 < R / 8; ++c8) rv[c8] = rowp[c8];   // the row's loads all in flight
+    for (int c8 = 0; c8 < NV; ++c8) rv[c8] = rowp[c8];   // the row's loads all in flight
     float s = 0.f, a = 0.f;
 #pragma unroll
     for (int c8 = 0; c8 < R / 8; ++c8) {
@@ -220,7 +243,11 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
   // so it is at or below the k-th largest score)
   const bool screen = nv_tot >= k && k > 0;             // block-uniform
   float tau_lo = -__builtin_inff();
-  if (screen) {
+  if (screen && nv_tot == k) {
+    // exactly k distinct valid seeds (a previous selection of the same k):
+    // the k-th largest is the smallest
+    tau_lo = key_score(kmin) - kScreenEps * amax;
+  } else if (screen) {
     uint64_t lo = kmin, hi = kmax;
     int rem = k;
     for (int level = 0; level < 2; ++level) {
@@ -245,45 +272,68 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
     tau_lo = key_score(uint32_t(lo)) - kScreenEps * amax;
   }
 
+  const int nt_row = (Tb + kTile - 1) / kTile, ngroups = (ntiles + 63) / 64;
+  // vector v of a tile: the row's base plus v KB (uniform, scalar registers)
+  // plus the tile's 32-bit byte offset (one vector register for all v)
+  const char* bdr = reinterpret_cast<const char*>(bounds) + int64_t(row) * ngroups * 2 * NV * 64 * 16;
+  auto toff = [&](int tile) { return uint32_t(((tile >> 6) * 2 * NV * 64 + (tile & 63)) * 16); };
+  auto bvec = [&](uint32_t off, int v) { return *reinterpret_cast<const u32x4*>(bdr + v * 1024 + off); };
   // one keep bit per tile; tiles past the sequence or without a valid token
-  // are dropped. A tile's 2R bounds are read 16 bytes at a time, all loads
-  // issued before use.
-  const int nt_row = (Tb + kTile - 1) / kTile;
+  // (bounds +inf / -inf in every dim) are dropped.
+  //  ranks <= 48: for l <= h, max(q l, q h) is q h when q > 0, else q l: one
+  //    bit-select per pair of packed bf16 bounds, then one fma per dim;
+  //    max |bound| is tracked on the packed magnitudes (unsigned 16-bit order
+  //    is magnitude order for bf16) and the margin is eps (sum |qp|) max|b|.
+  //  ranks >= 64 (fewer registers per thread for the loaded bounds): ub as
+  //    sum max(q l, q h), the margin eps sum |q| max(|l|, |h|).
+  constexpr bool kPacked = R <= 48;
+  float qabs = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < R; ++c) qabs += __builtin_fabsf(qp[c]);
   int kept = 0;
-  for (int base = 0; base < nwords * 32; base += NT) {
-    const int tile = base + tid;
-    bool k_it = false;
-    if (tile < nt_row && tile < ntiles) {
-      const u32x4* bd = reinterpret_cast<const u32x4*>(bounds + ((int64_t(b) * g.Hkv + j) * ntiles + tile) * 2 * R);
-      // the tile's bounds in groups of up to 8 vectors per half, each
-      // group's loads all in flight before use
-      constexpr int KC = R / 8 < 8 ? R / 8 : 8;
-      float ub = 0.f, U = 0.f;
-      bool empty = false;
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  // qo: a zero the compiler cannot see through, so that the coefficient
+  // reads stay inside the loop over tiles instead of occupying registers
+  // for the whole loop
+  auto add_bounds = [&](const u32x4& lv, const u32x4& hv, int c8, int qo, float& ub, float& mag) {
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w};
+    if constexpr (kPacked) {
+      uint32_t mw = __float_as_uint(mag);
 #pragma unroll
-      for (int c0 = 0; c0 < R / 8; c0 += KC) {
-        u32x4 lv[KC], hv[KC];
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          lv[c] = bd[c0 + c];
-          hv[c] = bd[R / 8 + c0 + c];
-        }
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const uint32_t lw[4] = {lv[c].x, lv[c].y, lv[c].z, lv[c].w}, hw[4] = {hv[c].x, hv[c].y, hv[c].z, hv[c].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float l = (e & 1) ? bf_hi(lw[e >> 1]) : bf_lo(lw[e >> 1]);
-            const float h = (e & 1) ? bf_hi(hw[e >> 1]) : bf_lo(hw[e >> 1]);
-            const float qc = qp[(c0 + c) * 8 + e];
-            empty = empty || l > h;
-            ub += fmaxf(qc * l, qc * h);
-            U = __builtin_fmaf(__builtin_fabsf(qc), fmaxf(__builtin_fabsf(l), __builtin_fabsf(h)), U);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t qs = qsel[qo + c8 * 4 + e];
+        const uint32_t sel = (qs & hw[e]) | (~qs & lw[e]);
+        ub = __builtin_fmaf(qp[qo + c8 * 8 + 2 * e], bf_lo(sel), ub);
+        ub = __builtin_fmaf(qp[qo + c8 * 8 + 2 * e + 1], bf_hi(sel), ub);
+        u16x2 mm = __builtin_bit_cast(u16x2, mw);
+        mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, lw[e] & 0x7fff7fffu));
+        mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, hw[e] & 0x7fff7fffu));
+        mw = __builtin_bit_cast(uint32_t, mm);
       }
-      k_it = !empty && (!screen || ub + kScreenEps * U >= tau_lo);
+      mag = __uint_as_float(mw);                        // two packed magnitudes, not a float
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float l = (e & 1) ? bf_hi(lw[e >> 1]) : bf_lo(lw[e >> 1]);
+        const float h = (e & 1) ? bf_hi(hw[e >> 1]) : bf_lo(hw[e >> 1]);
+        const float qc = qp[c8 * 8 + e];
+        ub += fmaxf(qc * l, qc * h);
+        mag = __builtin_fmaf(__builtin_fabsf(qc), fmaxf(__builtin_fabsf(l), __builtin_fabsf(h)), mag);
+      }
     }
+  };
+  // the tile test without the empty check
+  auto keep_bound = [&](float ub, float mag) {
+    float margin;
+    if constexpr (kPacked) {
+      const uint32_t mw = __float_as_uint(mag);
+      margin = qabs * fmaxf(bf_lo(mw), bf_hi(mw));
+    } else {
+      margin = mag;
+    }
+    return !screen || ub + kScreenEps * margin >= tau_lo;
+  };
+  auto emit = [&](int base, bool k_it) {
     const uint64_t bits = __ballot(k_it);
     kept += k_it ? 1 : 0;
     if (lane == 0) {
@@ -291,6 +341,36 @@ __global__ __launch_bounds__(screen_threads(R)) void screen_kernel(GqaDev g, con
       if (wbase < nwords) keep[int64_t(row) * nwords + wbase] = uint32_t(bits);
       if (wbase + 1 < nwords) keep[int64_t(row) * nwords + wbase + 1] = uint32_t(bits >> 32);
     }
+  };
+  for (int base = 0; base < nwords * 32; base += NT) {
+    const int tile = base + tid;
+    bool k_it = false;
+    if (tile < nt_row && tile < ntiles) {
+      // in groups of vectors (all of them up to rank 48, 4 per half above),
+      // each group's loads all in flight before use
+      constexpr int KC = kPacked ? NV : 4, kGroupUnroll = kPacked ? 8 : 1;
+      const uint32_t to = toff(tile);
+      float ub = 0.f, mag = 0.f;
+      bool empty = false;
+      int qo = 0;
+      if constexpr (kPacked) asm volatile("s_mov_b32 %0, 0" : "=s"(qo));
+      // (ranks >= 64: a rolled loop over the groups keeps one group's
+      // bounds and coefficients in registers at a time)
+#pragma unroll kGroupUnroll
+      for (int c0 = 0; c0 < NV; c0 += KC) {
+        u32x4 lv[KC], hv[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          lv[c] = bvec(to, c0 + c);
+          hv[c] = bvec(to, NV + c0 + c);
+        }
+        if (c0 == 0) empty = bf_lo(lv[0].x) > bf_lo(hv[0].x);   // a valid token makes lo <= hi in dim 0
+#pragma unroll
+        for (int c = 0; c < KC; ++c) add_bounds(lv[c], hv[c], c0 + c, qo, ub, mag);
+      }
+      k_it = !empty && keep_bound(ub, mag);
+    }
+    emit(base, k_it);
   }
   if (kept_tiles) {
     int tot;
