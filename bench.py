@@ -344,6 +344,9 @@ def bench_screening(args, cfg, inp, c, torch, pipeline, synth, stream):
     seeds = prev.idx.clone()
     sc = pipeline.ScreenedStep(c, k, seeds)
     b_us = time_launches(sc.build_bounds, 3, torch, stream)
+    # one appended token per sequence (its last): only its tile is rebuilt
+    last_pos = (c.seq_lens - 1).clamp(min=0).to(torch.int32).contiguous()
+    u_us = time_launches(lambda: sc.update_bounds(last_pos, 1), 20, torch, stream)
     plain = pipeline.SparseStep(c, k=k, S=1, fused=True, keep_scores=False)
     steps = max(5, args.steps // 2)
     p_total, _ = time_loop(plain.stages(), steps, 2, torch, stream)
@@ -359,7 +362,8 @@ def bench_screening(args, cfg, inp, c, torch, pipeline, synth, stream):
             "screen_plus_chunks_us": round(s_us[0], 2), "final_attend_us": round(s_us[1], 2),
             "kept_tile_fraction": round(kept_frac, 4),
             "chunk_pass_bytes": {"plain": int(tiles * 64 * 2 * cfg.r), "screened": read_bytes},
-            "bounds_build_us": round(b_us, 1), "indices_equal_plain": same}
+            "bounds_build_us": round(b_us, 1), "bounds_update_one_token_us": round(u_us, 2),
+            "indices_equal_plain": same}
 
 
 def bench_calibration(args, cfg, inp, c, sp, torch, pipeline, synth, jssa, stream, n_queries=4096):

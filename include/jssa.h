@@ -397,6 +397,19 @@ JSSA_API jssa_status jssa_tile_bounds_size(const jssa_gqa_desc* desc, size_t* by
  * tiles holding new tokens change). */
 JSSA_API jssa_status jssa_build_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, void* bounds, void* stream);
 
+/* Rebuilds only the tiles that hold appended tokens pos[b] .. pos[b]+n_new-1
+ * (those in [0, max_seq)), with the arguments of jssa_append_kv: the bounds
+ * of a tile depend on its valid tokens alone. After jssa_append_kv, with
+ * desc->seq_lens grown by at most the appended run (pos[b] <= the previous
+ * T_b, new T_b <= max(previous T_b, pos[b] + n_new)), the result equals
+ * jssa_build_tile_bounds, at the cost of at most ceil(n_new/64) + 1 tiles
+ * per (sequence, KV head). Tokens made valid in any other way need a full
+ * build.
+ *  pos    device int32 [B]
+ *  1 <= n_new <= max_seq */
+JSSA_API jssa_status jssa_update_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, const int32_t* pos,
+                                             int32_t n_new, void* bounds, void* stream);
+
 /* Workspace of jssa_score_topk_screened_chunks: the jssa_score_topk workspace
  * (same layout, at the start) plus one keep bit per tile. */
 JSSA_API jssa_status jssa_score_topk_screened_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes);

@@ -729,6 +729,45 @@ def test_screened_topk_lossless(J, PL, case):
         assert dropped == 0
 
 
+@pytest.mark.parametrize("case", ["one_token", "span_and_clip", "paged_r48"])
+def test_update_tile_bounds_equals_rebuild(J, PL, case):
+    """After an append (and the matching seq_lens update), rebuilding only
+    the tiles that hold the new tokens gives the bounds of a full rebuild."""
+    if case == "paged_r48":
+        cfg = replace(synth.PAGED_QWEN14B, B=2, T=1024, len_lo=600, len_hi=900, seed=41)
+    else:
+        cfg = replace(synth.TINY, B=3, T=4096, len_lo=1000, len_hi=3000, seed=42)
+    inp = synth.make_gqa(cfg)
+    if case == "span_and_clip":
+        inp.seq_lens = np.array([2000, cfg.T - 30, 1500], np.int32)
+    c = PL.GqaCache(inp)
+    c.project()
+    sc = PL.ScreenedStep(c, 64, torch.zeros((cfg.B, cfg.Hkv, 0), dtype=torch.int32, device="cuda"))
+    sc.bounds.zero_()
+    sc.build_bounds()
+    lens = inp.seq_lens.astype(np.int64)
+    if case == "one_token":
+        n_new, pos = 1, lens.copy()
+    elif case == "span_and_clip":   # overwrite from a 64-aligned start, append past max_seq, a negative start
+        n_new, pos = 100, np.array([640, cfg.T - 30, -3])
+    else:
+        n_new, pos = 7, lens.copy()
+    rng = np.random.default_rng(5)
+    k_new = synth.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.Hkv, n_new, cfg.d)))
+    v_new = synth.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.Hkv, n_new, cfg.d)))
+    pos_d = PL.to_device(pos.astype(np.int32))
+    before = sc.bounds.clone()
+    J.jssa_append_kv(c.desc, c.K, c.V, c.Kp, PL.to_device(k_new), PL.to_device(v_new), c.P, pos_d, n_new)
+    new_lens = np.maximum(lens, np.minimum(pos + n_new, cfg.T)).astype(np.int32)
+    c.seq_lens.copy_(PL.to_device(new_lens))
+    sc.update_bounds(pos_d, n_new)
+    full = torch.zeros_like(sc.bounds)
+    J.jssa_build_tile_bounds(c.desc, c.Kp, full)
+    torch.cuda.synchronize()
+    assert torch.equal(sc.bounds, full)
+    assert not torch.equal(before, full)                      # the append did change some tiles
+
+
 def test_screened_final_attend_identical(J, PL):
     inp = synth.make_gqa(replace(synth.LLAMA8B_32K, key_model="clustered", seed=97))
     c = PL.GqaCache(inp)

@@ -492,7 +492,18 @@ jssa_status jssa_build_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, vo
   if (jssa_status s = check_desc(__func__, desc, true)) return s;
   REQUIRE_PTR(Kp); REQUIRE_PTR(bounds); REQUIRE_ALIGNED_OPT(desc->seq_lens);
   return hip_status(jssa::launch_tile_bounds(to_dev(desc), static_cast<const uint16_t*>(Kp),
-                                             static_cast<uint16_t*>(bounds), S(stream)),
+                                             static_cast<uint16_t*>(bounds), nullptr, 0, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_update_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, const int32_t* pos, int32_t n_new,
+                                    void* bounds, void* stream) {
+  if (jssa_status s = check_desc(__func__, desc, true)) return s;
+  REQUIRE_PTR(Kp); REQUIRE_PTR(pos); REQUIRE_PTR(bounds); REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  if (n_new < 1 || n_new > desc->max_seq)
+    return fail(JSSA_ERR_SHAPE, "%s: n_new %d outside [1, max_seq]", __func__, n_new);
+  return hip_status(jssa::launch_tile_bounds(to_dev(desc), static_cast<const uint16_t*>(Kp),
+                                             static_cast<uint16_t*>(bounds), pos, n_new, S(stream)),
                     __func__);
 }
 

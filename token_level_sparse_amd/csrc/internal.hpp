@@ -34,7 +34,8 @@ hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* 
 int screen_tiles(int max_seq);
 int screen_words(int max_seq);
 int screen_max_seeds();
-hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bounds, hipStream_t st);
+hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bounds, const int32_t* pos,
+                              int n_tok, hipStream_t st);
 hipError_t launch_screen(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp,
                          const uint16_t* bounds, const int32_t* seeds, int n_seed, int k, uint32_t* keep,
                          int32_t* kept_tiles, hipStream_t st);

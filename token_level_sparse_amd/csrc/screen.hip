@@ -13,7 +13,8 @@
 // top-k; the score stream then does not read it.
 //
 //  tile_bounds_kernel  lo/hi per (sequence, KV head, tile) from the
-//                      projected cache, once and after appends (setup work)
+//                      projected cache: every tile (set-up), or only the
+//                      tiles holding appended tokens (decode)
 //  screen_kernel       one block (1024 threads; 512 for r >= 64) per (sequence, KV head):
 //                      qp, the distinct seeds (an LDS hash set) and their
 //                      scores, tau, then one keep bit per tile
@@ -50,41 +51,78 @@ __device__ __forceinline__ int64_t bound_vec(int64_t row, int ngroups, int nv2, 
   return ((row * ngroups + (tile >> 6)) * nv2 + v) * 64 + (tile & 63);
 }
 
-__global__ __launch_bounds__(64) void tile_bounds_kernel(GqaDev g, const uint16_t* __restrict__ Kp,
-                                                          uint16_t* __restrict__ bounds, int ntiles) {
-  const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+// One wave per tile, four tiles per block. pos == nullptr: tile 4x + w of
+// block x (set-up, every tile). Otherwise the (4x + w)-th tile holding one
+// of the tokens pos[b] .. pos[b] + n_tok - 1 that lie in [0, max_seq) (an
+// append); waves past the last such tile only take part in the barrier.
+// Lane (row group rg, vector v) loads 16-byte vector v of rows rg, rg + RG,
+// ... of the tile, all loads in flight at once (rows past T_b or without a
+// valid page read row 0 of the cache and are left out); the row groups'
+// minima and maxima then meet in LDS.
+template <int R>
+__global__ __launch_bounds__(256) void tile_bounds_kernel(GqaDev g, const uint16_t* __restrict__ Kp,
+                                                           uint16_t* __restrict__ bounds, int ntiles,
+                                                           const int32_t* __restrict__ pos, int n_tok) {
+  constexpr int NV = R / 8, RG = 64 / NV, NI = (kTile + RG - 1) / RG;   // row groups, loads per lane
+  __shared__ float part[4][2][RG][R];
+  const int j = blockIdx.y, b = blockIdx.z, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Tb = seq_len(g, b);
-  const int R = g.r, ngroups = (ntiles + 63) / 64, row = b * g.Hkv + j;
-  for (int c0 = 0; c0 < R; c0 += 64) {
-    const int c = c0 + lane;
-    float lo = __builtin_inff(), hi = -__builtin_inff();
-    if (c < R) {
-      // 16 rows at a time, every load issued before any is used (rows past
-      // T_b or without a valid page read row 0 of the tile's sequence head
-      // and are left out)
-      for (int i0 = 0; i0 < kTile; i0 += 16) {
-        float v[16];
-        bool ok[16];
+  int tile = int(blockIdx.x) * 4 + w;
+  bool valid = tile < ntiles;
+  if (pos) {
+    const int64_t t0 = pos[b], t1 = t0 + n_tok - 1;    // first and last appended token
+    const int first = int((t0 > 0 ? t0 : 0) / kTile);
+    const int last = int((t1 < g.max_seq - 1 ? t1 : g.max_seq - 1) / kTile);
+    tile += first;
+    valid = t1 >= 0 && t0 < g.max_seq && tile <= last;
+  }
+  const int v = lane % NV, rg = lane / NV;
+  float lo[8], hi[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = tile * kTile + i0 + i;
-          int64_t off = t < Tb ? row_off(g, b, j, t, R) : -1;
-          ok[i] = off >= 0;
-          off = ok[i] ? off : row_off(g, b, j, 0, R);
-          v[i] = off >= 0 ? bf(Kp[off + c]) : 0.f;
-        }
+  for (int e = 0; e < 8; ++e) { lo[e] = __builtin_inff(); hi[e] = -__builtin_inff(); }
+  if (valid && rg < RG) {
+    u32x4 x[NI];
+    bool ok[NI];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (!ok[i]) continue;
-          lo = v[i] < lo ? v[i] : lo;
-          hi = v[i] > hi ? v[i] : hi;
-        }
-      }
-      // min and max of bf16 values are bf16 values: the conversion is exact
-      // (and +-inf for a tile without a valid token)
-      bounds[bound_vec(row, ngroups, R / 4, tile, c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(lo) >> 16);
-      bounds[bound_vec(row, ngroups, R / 4, tile, R / 8 + c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(hi) >> 16);
+    for (int i = 0; i < NI; ++i) {
+      const int r = rg + RG * i, t = tile * kTile + r;
+      const int64_t off = (r < kTile && t < Tb) ? row_off(g, b, j, t, R) : -1;
+      ok[i] = off >= 0;
+      x[i] = *reinterpret_cast<const u32x4*>(Kp + (ok[i] ? off : 0) + 8 * v);
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (!ok[i]) continue;
+      const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (e & 1) ? bf_hi(wd[e >> 1]) : bf_lo(wd[e >> 1]);
+        lo[e] = f < lo[e] ? f : lo[e];
+        hi[e] = f > hi[e] ? f : hi[e];
+      }
+    }
+  }
+  if (rg < RG) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      part[w][0][rg][8 * v + e] = lo[e];
+      part[w][1][rg][8 * v + e] = hi[e];
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const int ngroups = (ntiles + 63) / 64, row = b * g.Hkv + j;
+  for (int c = lane; c < R; c += 64) {
+    float l = __builtin_inff(), h = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      l = fminf(l, part[w][0][q][c]);
+      h = fmaxf(h, part[w][1][q][c]);
+    }
+    // min and max of bf16 values are bf16 values: the conversion is exact
+    // (and +-inf for a tile without a valid token)
+    bounds[bound_vec(row, ngroups, 2 * NV, tile, c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(l) >> 16);
+    bounds[bound_vec(row, ngroups, 2 * NV, tile, NV + c / 8) * 8 + c % 8] = uint16_t(__float_as_uint(h) >> 16);
   }
 }
 
@@ -385,9 +423,23 @@ int screen_tiles(int max_seq) { return (max_seq + kTile - 1) / kTile; }
 int screen_words(int max_seq) { return 2 * ((screen_tiles(max_seq) + 63) / 64); }
 int screen_max_seeds() { return kMaxSeed; }
 
-hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bounds, hipStream_t st) {
+hipError_t launch_tile_bounds(const GqaDev& g, const uint16_t* Kp, uint16_t* bounds, const int32_t* pos,
+                              int n_tok, hipStream_t st) {
   const int nt = screen_tiles(g.max_seq);
-  hipLaunchKernelGGL(tile_bounds_kernel, dim3(nt, g.Hkv, g.B), dim3(64), 0, st, g, Kp, bounds, nt);
+  // n_tok tokens from any start touch at most ceil(n_tok / 64) + 1 tiles
+  int n = pos ? (n_tok + kTile - 1) / kTile + 1 : nt;
+  n = n < nt ? n : nt;
+  const dim3 grid((n + 3) / 4, g.Hkv, g.B);
+  switch (g.r) {
+#define JSSA_TB(RR)                                                                                      \
+  case RR:                                                                                               \
+    hipLaunchKernelGGL(tile_bounds_kernel<RR>, grid, dim3(256), 0, st, g, Kp, bounds, nt, pos, n_tok); \
+    break;
+    JSSA_TB(16) JSSA_TB(32) JSSA_TB(48) JSSA_TB(64) JSSA_TB(128)
+#undef JSSA_TB
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ ENTRY_POINTS = (
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
-    "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_score_topk_screened_workspace_size",
+    "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_update_tile_bounds",
+    "jssa_score_topk_screened_workspace_size",
     "jssa_score_topk_screened_chunks", "jssa_calib_workspace_size", "jssa_calib_query_workspace_size", "jssa_calib_key_moments", "jssa_calib_query_moments",
     "jssa_calib_projection", "jssa_status_string", "jssa_last_error", "jssa_version",
 )
@@ -90,6 +91,7 @@ _SIGS = {
                                    _vp, _vp, _vp, _sz, _vp],
     "jssa_tile_bounds_size": [_P(GqaDesc), _P(_sz)],
     "jssa_build_tile_bounds": [_P(GqaDesc), _vp, _vp, _vp],
+    "jssa_update_tile_bounds": [_P(GqaDesc), _vp, _vp, _i32, _vp, _vp],
     "jssa_score_topk_screened_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
     "jssa_score_topk_screened_chunks": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp],
     "jssa_calib_workspace_size": [_P(GqaDesc), _P(_sz)],
@@ -342,6 +344,11 @@ def jssa_tile_bounds_size(desc) -> int:
 
 def jssa_build_tile_bounds(desc, Kp, bounds, stream=None):
     _check(_lib.jssa_build_tile_bounds(ctypes.byref(desc), _p(Kp), _p(bounds), _s(stream)), "jssa_build_tile_bounds")
+
+
+def jssa_update_tile_bounds(desc, Kp, pos, n_new, bounds, stream=None):
+    _check(_lib.jssa_update_tile_bounds(ctypes.byref(desc), _p(Kp), _p(pos), n_new, _p(bounds), _s(stream)),
+           "jssa_update_tile_bounds")
 
 
 def jssa_score_topk_screened_workspace_size(desc, k) -> int:

@@ -361,6 +361,11 @@ class ScreenedStep:
     def build_bounds(self, stream=None):
         jssa.jssa_build_tile_bounds(self.c.desc, self.c.Kp, self.bounds, stream)
 
+    def update_bounds(self, pos, n_new, stream=None):
+        """After an append of n_new tokens at pos (device int32 [B]) and the
+        matching seq_lens update: rebuild only the tiles holding them."""
+        jssa.jssa_update_tile_bounds(self.c.desc, self.c.Kp, pos, n_new, self.bounds, stream)
+
     def chunks(self, stream=None):
         c = self.c
         jssa.jssa_score_topk_screened_chunks(c.desc, c.q, c.P, c.Kp, self.bounds, self.seeds, self.n_seed, self.k,
