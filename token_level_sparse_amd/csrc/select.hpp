@@ -116,6 +116,10 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   auto real = [&](int e) { return base + tid * E + e < lim; };
+  // key 0 (no token: a dropped tile of a screened chunk) takes no part in
+  // the bounds or the histograms; thousands of them in one bin would
+  // serialize its atomics
+  auto cand = [&](int e) { return real(e) && key[e] != 0u; };
   const bool keep_all = n <= k;
   const bool full = n == NT * E;
   uint32_t thr = 0;                          // keep real keys >= thr
@@ -123,7 +127,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
     uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (real(e)) {
+      if (cand(e)) {
         const uint32_t x = key[e];
         m2 = x > m1 ? m1 : (x > m2 ? x : m2);
         m1 = x > m1 ? x : m1;
@@ -168,9 +172,15 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
     if (full && r <= 64) lo = lo2 > lo ? lo2 : lo;
     const uint32_t range = hi - lo;
     const int sh0 = range < uint32_t(kSelBins) ? 0 : (32 - __builtin_clz(range)) - 11;
+    // fewer than k candidates (a screened chunk): no bin reaches k, and the
+    // threshold stays lo, the smallest candidate key, so all of them stay
+    if (tid == 0) {
+      sm.res[0] = 0;
+      sm.res[1] = 0;
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (real(e) && key[e] >= lo) atomicAdd(&sm.hist[(key[e] - lo) >> sh0], 1u);
+      if (cand(e) && key[e] >= lo) atomicAdd(&sm.hist[(key[e] - lo) >> sh0], 1u);
     __syncthreads();
     pick_bin<NT, kSelBins / NT>(sm.hist, k, true, sm.scan, sm.res);
     const uint32_t d0 = uint32_t(sm.res[0]);
@@ -184,7 +194,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (real(e) && key[e] >= thr && ((key[e] - lo) >> sh0) == d0)
+        if (cand(e) && key[e] >= thr && ((key[e] - lo) >> sh0) == d0)
           atomicAdd(&sm.hist[(key[e] - thr) >> sh1], 1u);
       __syncthreads();
       pick_bin<NT, kSelBins / NT>(sm.hist, need, true, sm.scan, sm.res);
