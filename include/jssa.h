@@ -28,7 +28,8 @@
  *  - Device-side values (seq_lens, page tables, indices) are not read on the
  *    host. Kernels clamp seq_lens to [0, max_seq] and treat a page-table
  *    entry outside [0, num_pages) or an index outside [0, T_b) as an absent
- *    token: it is never read, never scored above -inf and never attended.
+ *    token: it is never read, scores -inf, is never selected and never
+ *    attended. In a score row, -inf marks such a position.
  *  - Inputs must be finite; results for NaN or Inf inputs are unspecified.
  *  - No entry point keeps state between calls; calls on different streams
  *    may run concurrently as long as they do not write the same memory.
@@ -105,7 +106,9 @@ JSSA_API jssa_status jssa_append_kv(const jssa_gqa_desc* desc, void* K, void* V,
 
 /*
  * Build the projected key cache for tokens [0, T_b) of an existing cache
- * (set-up, or after a basis change). Same arithmetic as jssa_append_kv.
+ * (set-up, or after a basis change). Source: digest Synopsis (tokens are
+ * scored in the shared low-dimensional subspace), as for jssa_append_kv, of
+ * which this is the bulk form with the same arithmetic.
  *  K   device bf16 cache (read); P device fp32 [Hkv,d,r]; Kp device bf16 (written)
  */
 JSSA_API jssa_status jssa_project_keys(const jssa_gqa_desc* desc, const void* K, const float* P,
@@ -127,7 +130,9 @@ JSSA_API jssa_status jssa_score(const jssa_gqa_desc* desc, const void* q, const 
 
 /*
  * Workspace bytes needed by jssa_topk for `rows` = B*H score rows of length
- * max_seq and budget k (host-only; no HIP call).
+ * max_seq and budget k (host-only; no HIP call). The selection it serves is
+ * the per-KV-head top-k of the JSSA abstract (Abstract); the workspace holds
+ * the per-chunk candidate lists of this library's two-level selection.
  */
 JSSA_API jssa_status jssa_topk_workspace_size(int32_t B, int32_t H, int32_t max_seq, int32_t k, size_t* bytes);
 
@@ -136,9 +141,11 @@ JSSA_API jssa_status jssa_topk_workspace_size(int32_t B, int32_t H, int32_t max_
  * per-KV-head selections; digest Synopsis).
  *  scores   device fp32 [B,H,max_seq]
  *  seq_lens device int32 [B] or NULL (= max_seq)
- *  idx      device int32 [B,H,k] (written): the first min(k,T_b) tokens of
+ *  idx      device int32 [B,H,k] (written): the first min(k,n) tokens of
  *           the order (score descending, index ascending; -0.0 == +0.0),
- *           listed ascending by token index, then -1 padding.
+ *           listed ascending by token index, then -1 padding; n counts the
+ *           positions t < T_b whose score is not -inf (a -inf score marks a
+ *           position without a token, which is never selected).
  *  ws       device workspace of at least jssa_topk_workspace_size bytes
  *  1 <= k <= 4096, k <= max_seq. Deterministic: identical inputs give
  *  identical outputs whatever the scheduling.
@@ -223,7 +230,10 @@ JSSA_API jssa_status jssa_indexed_decode(const jssa_gqa_desc* desc, const void* 
                                 float scale, float* part_o, float* part_lse, void* stream);
 
 /*
- * Log-sum-exp merge of split partials.
+ * Log-sum-exp merge of split partials. Source: the split-K indexed decode
+ * of the JSSA abstract (Abstract: attention runs on the selected tokens)
+ * evaluated in S parts; the merge weights part s by exp(lse_s), which makes
+ * the result equal to attention over the union of the parts.
  *  part_o [B,H,S,dv] fp32, part_lse [B,H,S] fp32 (device)
  *  out    device [B,H,dv] fp32 (out_bf16 = 0) or bf16 bits (out_bf16 = 1)
  *  lse    device fp32 [B,H] or NULL
@@ -259,8 +269,8 @@ JSSA_API jssa_status jssa_gather_kv(const jssa_gqa_desc* desc, const void* K, co
                            void* stream);
 
 /*
- * MLA shared latent cache (digest Perspective: for MLA models the selection
- * runs over the shared latent cache).
+ * MLA shared latent cache (digest Perspective: on MLA models the selection
+ * runs on the one latent cache all heads read).
  *  B, H (query heads), d_latent (512), d_rope (64), d_nope (128), d_v (128),
  *  r (scoring rank, 64), max_seq, seq_lens (device int32 [B] or NULL).
  *  The latent cache is [B,max_seq,d_latent+d_rope] bf16, its projected copy
@@ -318,9 +328,10 @@ JSSA_API jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat
 
 /*
  * Top-delta selection (Faster Than Flash review on evolve.pub, Summary, Key
- * claims and FAQ: keep what lies within delta, in log space, of a pseudo-max
- * estimated from sink and local tokens; the pseudo-max never exceeds the
- * true max, so an error only enlarges the kept set). Applied here per token
+ * claims and FAQ: a token stays when its log-weight is at most delta below a
+ * stand-in for the maximum taken over the first and most recent tokens;
+ * since the stand-in cannot exceed the true maximum, a poor stand-in can
+ * only keep more tokens). Applied here per token
  * and per KV head to the subspace score s_t: the approximate logit is the
  * group-mean scale * s_t / G; the pseudo-max m is the largest s_t over the
  * first n_sink and the last n_local positions of the sequence; token t is

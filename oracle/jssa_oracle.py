@@ -31,17 +31,28 @@ R1 group aggregation: a KV head's score is the raw sum over its GQA group of
    query dotted with the projected key).
 R2 the projected key cache stores bf16(K_j P_j), rounded to nearest-even
    from the exact (fp64) product.
-R3 selection: the first min(k, T_b) tokens of the total order (score
-   descending, token index ascending), returned ascending by index and padded
-   with -1. The decision is taken on scores rounded to fp32, the precision of
-   the GPU path's score buffer; -0.0 ranks equal to +0.0.
+R3 selection: among the tokens that exist, the first min(k, n) of the
+   total order (score descending, token index ascending), returned ascending
+   by index and padded with -1; n counts the existing tokens. A token past
+   T_b or behind an invalid page has the score -inf and does not exist: it
+   is never selected. Scores are compared after rounding to fp32 (-0.0 ranks
+   equal to +0.0, ties go to the lower index). The pages fix no precision
+   for the selection, and the GPU ranks fp32 scores; a comparison that turns
+   floats into an integer result is taken here in that precision. Rounding
+   to nearest is monotone, so it never reverses two exact scores; it only
+   merges exact scores that round to one fp32 value into a tie. The result
+   therefore differs from a selection on exact scores only among tokens
+   within one fp32 ulp (2^-23 relative) of the k-th score, far inside the
+   1e-4 tie band of the index comparison, and on fp32 score rows (the
+   top-k entry point's input) it is the exact selection.
 R4 attention over a selected set: softmax(scale * q K_S^T) V_S per query
    head, base e, with log-sum-exp lse = m + ln(sum exp(l - m)); an empty set
    gives o = 0, lse = -inf.
 R5 split partials merge by weights exp(lse_s) (log-sum-exp combine).
 R6 query head h reads KV head floor(h / G).
 R7 paged layout: token t of sequence b lives in page table[b][t // 16], slot
-   t % 16, of a pool laid out [pages, Hkv, 16, width].
+   t % 16, of a pool laid out [pages, Hkv, 16, width]. A table entry outside
+   [0, pages) holds no token: its 16 positions do not exist (score -inf).
 R8 MLA: keys are [W_uk[h] c[:512]; c[512:]], values c[:512], output
    W_uv[h] (sum_t p_t c_t[:512]); the selection score projects the summed
    absorbed query [W_uk[h]^T q_nope; q_rope] and the latent row through one
@@ -148,24 +159,30 @@ def subspace_scores(q_group_bits, P_j, Kp_bits) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Step 3: distinct top-k token set per KV head  [JSSA-S], [JSSA-A]
 # ---------------------------------------------------------------------------
-def select_topk(scores, k: int) -> np.ndarray:
-    """Indices of the first min(k, n) tokens in the order (score desc, index
-    asc), sorted ascending and padded with -1 to length k (R3)."""
+def selection_order(scores) -> np.ndarray:
+    """The existing tokens (score > -inf) in the order of R3: fp32-rounded
+    score descending, then token index ascending."""
     s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
-    n = s32.shape[0]
-    order = np.lexsort((np.arange(n), -s32))
-    keep = np.sort(order[:min(k, n)])
+    t = np.nonzero(s32 > -np.inf)[0]
+    return t[np.lexsort((t, -s32[t]))]
+
+
+def select_topk(scores, k: int) -> np.ndarray:
+    """Indices of the first min(k, n) existing tokens in the order (score
+    desc, index asc), sorted ascending and padded with -1 to length k (R3)."""
+    keep = np.sort(selection_order(scores)[:k])
     out = np.full(k, -1, np.int64)
     out[:keep.shape[0]] = keep
     return out
 
 
 def kth_score(scores, k: int) -> float:
-    """The score of the last token the selection keeps (fp64)."""
-    s = np.asarray(scores, np.float64)
-    s32 = s.astype(np.float32).astype(np.float64)
-    order = np.lexsort((np.arange(s.shape[0]), -s32))
-    return float(s[order[min(k, s.shape[0]) - 1]])
+    """The (fp64) score of the last token the selection keeps: the min(k, n)-th
+    existing token of R3's order. No token kept: ValueError."""
+    order = selection_order(scores)
+    if order.shape[0] == 0 or k < 1:
+        raise ValueError("the selection keeps no token")
+    return float(np.asarray(scores, np.float64)[order[min(k, order.shape[0]) - 1]])
 
 
 # ---------------------------------------------------------------------------
@@ -204,10 +221,22 @@ def combine(part_o, part_lse):
 # ---------------------------------------------------------------------------
 # Paged addressing (R7)
 # ---------------------------------------------------------------------------
+def page_valid(table_row, t, num_pages: int) -> np.ndarray:
+    """Whether logical positions t have a page (R7)."""
+    pg = np.asarray(table_row, np.int64)[np.asarray(t, np.int64) // PAGE]
+    return (pg >= 0) & (pg < num_pages)
+
+
 def paged_rows(pool, table_row, j: int, t) -> np.ndarray:
-    """Rows of KV head j at logical positions t from a pool [pages,Hkv,16,w]."""
+    """Rows of KV head j at logical positions t from a pool [pages,Hkv,16,w].
+    Every position must have a page (ValueError otherwise: such a position
+    holds no row, R7)."""
     t = np.asarray(t, np.int64)
-    return np.asarray(pool)[np.asarray(table_row)[t // PAGE], j, t % PAGE]
+    pool = np.asarray(pool)
+    pg = np.asarray(table_row, np.int64)[t // PAGE]
+    if np.any((pg < 0) | (pg >= pool.shape[0])):
+        raise ValueError("a position without a page holds no row")
+    return pool[pg, j, t % PAGE]
 
 
 def logical_rows(cache, b: int, j: int, t, page_table=None) -> np.ndarray:
@@ -281,8 +310,8 @@ def mla_attend_explicit(q_nope_bits, q_rope_bits, W_uk_bits, W_uv_bits, C_rows_b
 
 # ---------------------------------------------------------------------------
 # Subspace calibration (R12)  [JSSA-A]; [JSSA-I] (queries and keys kept
-# together; oracle top-k recall as the measure of ranking quality);
-# [JSSA-P] (the marginal bound controls the exact score error)
+# together; recall of the exact top-k measures the ranking); [JSSA-P]
+# (bounding the marginal objective bounds the error of the exact scores)
 # ---------------------------------------------------------------------------
 def key_second_moment(K_rows_bits) -> np.ndarray:
     """S_k = mean over the rows k of K [n, d] of k k^T (fp64); zeros if n = 0."""

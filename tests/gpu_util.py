@@ -23,37 +23,50 @@ OUT_TOL = 2e-3
 
 
 def unit_rows(inp: synth.GqaInputs, b: int, j: int):
-    """Logical K and V rows [T_b, d] of one unit, read out of the host arrays."""
+    """Logical K and V rows [T_b, d] of one unit, read out of the host arrays.
+    Positions without a page (reading R7) hold no row; they come back as
+    zero rows and are marked absent by unit_valid."""
     n = int(inp.seq_lens[b])
     t = np.arange(n)
     if inp.page_table is None:
         return inp.K[b, j, :n], inp.V[b, j, :n]
-    return (O.paged_rows(inp.K, inp.page_table[b], j, t), O.paged_rows(inp.V, inp.page_table[b], j, t))
+    ok = unit_valid(inp, b)
+    K = np.zeros((n, inp.K.shape[-1]), inp.K.dtype)
+    V = np.zeros((n, inp.V.shape[-1]), inp.V.dtype)
+    K[ok] = O.paged_rows(inp.K, inp.page_table[b], j, t[ok])
+    V[ok] = O.paged_rows(inp.V, inp.page_table[b], j, t[ok])
+    return K, V
 
 
 def oracle_unit(inp: synth.GqaInputs, b: int, j: int, rows=None):
+    """(K, V, Kp, s, hs) of one unit; absent positions score -inf (R3, R7)."""
     cfg = inp.cfg
     K, V = unit_rows(inp, b, j) if rows is None else rows
     hs = list(O.group_heads(j, cfg.G))
     Kp = O.project_keys(K, inp.P[j])
     s = O.subspace_scores(inp.q[b, hs], inp.P[j], Kp)
+    if rows is None:
+        s = np.where(unit_valid(inp, b), s, -np.inf)
     return K, V, Kp, s, hs
 
 
 def check_indices(gpu_idx: np.ndarray, s: np.ndarray, k: int) -> int:
-    """Returns the number of tolerated swaps; asserts the rule."""
+    """Returns the number of tolerated swaps; asserts the rule. s holds the
+    oracle scores of positions [0, T_b), -inf for absent positions."""
     Tb = s.shape[0]
-    n = min(k, Tb)
+    n = min(k, int(np.sum(s > -np.inf)))
     g = gpu_idx[:n].astype(np.int64)
-    assert np.all(gpu_idx[n:] == -1), "padding past min(k, T_b) must be -1"
+    assert np.all(gpu_idx[n:] == -1), "padding past min(k, existing tokens) must be -1"
     if n == 0:
         return 0
     assert np.all(g >= 0) and np.all(g < Tb), "indices outside [0, T_b)"
     assert np.all(np.diff(g) > 0), "indices must be strictly ascending"
+    assert np.all(s[g] > -np.inf), "an absent token was selected"
     o = O.select_topk(s, k)[:n]
     diff = np.setxor1d(g, o)
     if diff.size:
         sk = O.kth_score(s, k)
+        assert np.isfinite(sk), f"sets differ while the k-th score is {sk}"
         bad = diff[np.abs(s[diff] - sk) > IDX_REL * abs(sk)]
         assert bad.size == 0, f"swapped tokens {bad[:8]} outside the tie band (s_k={sk})"
     return int(diff.size // 2)

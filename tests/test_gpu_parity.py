@@ -198,6 +198,22 @@ def test_topk_long_row_multi_round(J):
     _topk_case(J, 1, 1, T, k, [T], s)
 
 
+def test_topk_absent_tokens(J):
+    """-inf marks a position without a token: never selected, so a row with
+    fewer than k existing tokens lists exactly those, then -1 (reading R3)."""
+    rng = np.random.default_rng(41)
+    B, H, T, k = 2, 2, 20000, 300
+    s = rng.standard_normal((B, H, T)).astype(np.float32)
+    s[0, 0, rng.random(T) < 0.3] = -np.inf              # scattered absent positions
+    s[0, 1, :] = -np.inf
+    s[0, 1, [5, 9000, 17000]] = [1.0, -2.0, 0.5]          # three tokens exist
+    s[1, 0, 8192:16384] = -np.inf                        # one whole chunk absent
+    s[1, 1, :] = -np.inf                                 # nothing exists
+    got = _topk_case(J, B, H, T, k, [T, T], s)
+    np.testing.assert_array_equal(got[0, 1, :4], [5, 9000, 17000, -1])
+    assert np.all(got[1, 1] == -1)
+
+
 def test_topk_empty_and_all_equal(J):
     T, k = 9000, 300
     s = np.zeros((2, 1, T), np.float32)
@@ -546,6 +562,34 @@ def test_invalid_page_entries_are_absent(J, PL):
     assert not np.any((idx[0] >= 48) & (idx[0] < 64))
     assert not np.any((idx[1] >= 160) & (idx[1] < 176))
     assert np.all(np.isfinite(_np(st.out)))
+
+
+@pytest.mark.parametrize("fused,S", [(True, 1), (True, 4), (False, 1), (False, 4)])
+def test_paged_fewer_existing_tokens_than_k(J, PL, fused, S):
+    """Positions behind invalid page-table entries hold no token (reading
+    R7). Sequence 0 keeps only three pages (48 tokens < k): its selection is
+    exactly those tokens, then -1, and the attention runs over them alone;
+    sequence 1 loses every other page; sequence 2 is whole. Compared with the
+    oracle's selection on the fused and the split paths."""
+    cfg = replace(synth.PAGED_QWEN14B, B=3, T=4096, len_lo=3000, len_hi=4096, seed=73)
+    inp = synth.make_gqa(cfg)
+    table = inp.page_table
+    n0 = (int(inp.seq_lens[0]) + 15) // 16
+    keep0 = {2, 5, n0 - 1}
+    for p in range(n0):
+        if p not in keep0:
+            table[0, p] = -1 if p % 2 else inp.num_pages + p
+    n1 = (int(inp.seq_lens[1]) + 15) // 16
+    table[1, 1:n1:2] = -7
+    k = 256
+    c, st, _ = _sparse_and_check(J, PL, inp, k, S, fused=fused)
+    idx = _np(st.idx)
+    exist0 = np.nonzero(U.unit_valid(inp, 0))[0]
+    assert exist0.size < k
+    for j in range(cfg.Hkv):
+        np.testing.assert_array_equal(idx[0, j, :exist0.size], exist0)
+        assert np.all(idx[0, j, exist0.size:] == -1)
+        assert np.all(U.unit_valid(inp, 1)[idx[1, j]])
 
 
 # ---------------------------------------------------------------------------

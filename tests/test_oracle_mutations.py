@@ -141,6 +141,28 @@ def _seed_threshold_kplus1(scores, seeds, k, valid=None):
     return _orig_seed_threshold(scores, seeds, k + 1, valid)
 
 
+def _kth_off_by_one(scores, k):
+    order = O.selection_order(scores)
+    return float(np.asarray(scores, np.float64)[order[min(k, order.shape[0] - 1)]])
+
+
+def _order_with_absent(scores):
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    t = np.arange(s32.shape[0])
+    return t[np.lexsort((t, -s32))]
+
+
+def _order_fp64(scores):
+    s = np.asarray(scores, np.float64)
+    t = np.nonzero(s > -np.inf)[0]
+    return t[np.lexsort((t, -s[t]))]
+
+
+def _paged_rows_unchecked(pool, table_row, j, t):
+    t = np.asarray(t, np.int64)
+    return np.asarray(pool)[np.asarray(table_row)[t // 16], j, t % 16]
+
+
 _orig_tile_bounds = O.tile_bounds
 _orig_seed_threshold = O.seed_threshold
 _orig_topdelta = O.select_topdelta
@@ -176,6 +198,10 @@ MUTATIONS = [
     ("seed_threshold", _seed_with_duplicates, [pins.test_screen_seed_closed_form]),
     ("tile_bounds", _tile_bounds_all_rows, [pins.test_screen_hand_values]),
     ("seed_threshold", _seed_threshold_kplus1, [pins.test_screen_seed_closed_form]),
+    ("kth_score", _kth_off_by_one, [pins.test_kth_score_and_absent_tokens_golden]),
+    ("selection_order", _order_with_absent, [pins.test_kth_score_and_absent_tokens_golden]),
+    ("selection_order", _order_fp64, [pins.test_kth_score_and_absent_tokens_golden]),
+    ("paged_rows", _paged_rows_unchecked, [pins.test_paged_rows_reject_positions_without_a_page]),
 ]
 
 
@@ -186,6 +212,6 @@ def test_planted_mistake_is_caught(monkeypatch, name, fn, checks):
     for check in checks:
         try:
             check()
-        except (AssertionError, ValueError, IndexError):
+        except (AssertionError, ValueError, IndexError, pytest.fail.Exception):
             caught += 1
     assert caught >= 1, f"mutation {name}/{fn.__name__} passed every pin"

@@ -211,6 +211,80 @@ def test_topk_special_cases():
     np.testing.assert_array_equal(O.select_topk(np.array([a, b]), 1), [0])
 
 
+def _val(x: str) -> float:
+    try:
+        return float(x)
+    except ValueError:
+        return _num(x)
+
+
+def test_kth_score_and_absent_tokens_golden():
+    """The k-th score (the anchor of the index tie band) and the selection
+    with absent (-inf) tokens against hand-derived values; it distinguishes
+    -0.0 from +0.0 by sign, so the returned token is pinned, not only its
+    magnitude."""
+    g = _golden("kth_score_hand.json")
+    s = np.array([_val(x) for x in g["scores"]])
+    for c in g["cases"]:
+        want = _val(c["kth"])
+        got = O.kth_score(s, c["k"])
+        assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (c, got)
+        np.testing.assert_array_equal(O.select_topk(s, c["k"]), c["idx"])
+    f = g["fp32_tie"]
+    s2 = np.array([_val(x) for x in f["scores"]])
+    assert s2[1] != s2[0]                              # distinct in fp64, equal in fp32
+    assert O.kth_score(s2, f["k"]) == _val(f["kth"])
+    np.testing.assert_array_equal(O.select_topk(s2, f["k"]), f["idx"])
+    e = g["none_exist"]
+    s3 = np.array([_val(x) for x in e["scores"]])
+    np.testing.assert_array_equal(O.select_topk(s3, e["k"]), e["idx"])
+    with pytest.raises(ValueError):
+        O.kth_score(s3, e["k"])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_kth_score_brute_force_small(seed):
+    """k-th score against a plain Python sort of (score, index) pairs on
+    small rows with many exact ties, absent tokens and signed zeros."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 40))
+    s = rng.integers(-3, 4, n).astype(np.float64) * 0.25
+    s[rng.random(n) < 0.2] = -np.inf
+    s[s == 0] = np.where(rng.random(int((s == 0).sum())) < 0.5, -0.0, 0.0)
+    alive = [t for t in range(n) if s[t] != -np.inf]
+    ranked = sorted(alive, key=lambda t: (-(s[t] + 0.0), t))
+    for k in range(1, n + 3):
+        if not ranked:
+            with pytest.raises(ValueError):
+                O.kth_score(s, k)
+            continue
+        assert O.kth_score(s, k) == s[ranked[min(k, len(ranked)) - 1]]
+        sel = sorted(ranked[:k])
+        assert list(O.select_topk(s, k)) == sel + [-1] * (k - len(sel))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp32_decision_differs_from_exact_only_within_one_ulp(seed):
+    """Reading R3 decides on fp32-rounded scores. Rounding to nearest is
+    monotone, so against a selection decided on the exact (fp64) scores the
+    two sets may differ only among tokens within one fp32 ulp (2^-23
+    relative) of the k-th score. Built with many exact scores that differ by
+    less than an fp32 ulp."""
+    rng = np.random.default_rng(500 + seed)
+    m = 1000
+    n, k = 3 * m, 3 * int(rng.integers(20, 200)) + 1   # the boundary splits one triple
+    base = np.abs(rng.standard_normal(m)) + 0.1
+    # three exact scores per value, all one fp32 value; the lowest index
+    # holds the smallest, so the two rules keep different members
+    s = np.concatenate([base * (1 - 2.0 ** -35), base, base * (1 + 2.0 ** -30)])
+    exact = sorted(range(n), key=lambda t: (-s[t], t))[:k]
+    got = O.select_topk(s, k)
+    diff = np.setxor1d(got, exact)
+    sk = O.kth_score(s, k)
+    assert np.all(np.abs(s[diff] - sk) <= 2.0 ** -23 * abs(sk)), diff
+    assert diff.size > 0                               # the test does reach the coarsening
+
+
 # ---------------------------------------------------------------------------
 # Attention over the selected set, combine
 # ---------------------------------------------------------------------------
@@ -341,6 +415,20 @@ def test_paged_matches_contiguous():
         np.testing.assert_array_equal(O.logical_rows(pool, b, 3, t, ident + b * (cfg.T // 16)), flat.K[b, 3, t])
 
 
+def test_paged_rows_reject_positions_without_a_page():
+    """Reading R7: a table entry outside [0, pages) holds no token; reading a
+    row there is an error, and page_valid marks exactly those positions."""
+    pool = np.arange(3 * 1 * 16 * 2, dtype=np.uint16).reshape(3, 1, 16, 2)
+    table = np.array([2, -1, 0, 3], np.int32)                   # pages 2, none, 0, none
+    t = np.arange(64)
+    np.testing.assert_array_equal(O.page_valid(table, t, 3), (t < 16) | ((t >= 32) & (t < 48)))
+    np.testing.assert_array_equal(O.paged_rows(pool, table, 0, [0, 17 + 16, 15]),
+                                  pool[[2, 0, 2], 0, [0, 1, 15]])
+    for bad in ([16], [63], [5, 20]):
+        with pytest.raises(ValueError):
+            O.paged_rows(pool, table, 0, bad)
+
+
 # ---------------------------------------------------------------------------
 # MLA
 # ---------------------------------------------------------------------------
@@ -382,6 +470,24 @@ def test_mla_brute_force_loops():
         for v in range(3):
             assert abs(o[h, v] - sum(Wv_[h, v, c] * olat[c] for c in range(8))) < 1e-12
         assert abs(lse[h] - (m + math.log(Z))) < 1e-12
+
+
+def test_mla_sparse_with_k_equal_T_is_dense():
+    """With k = T the selection keeps every latent row, so sparse MLA equals
+    dense MLA over the whole latent cache (the k = T fact of the decode step
+    on the shared-latent path)."""
+    qn, qr, Wk, Wv, C = _tiny_mla(n=37)
+    P = synth.gen_projection(7, 1, 40, 8)[0]
+    s = O.mla_scores(qn, qr, Wk, P, O.project_keys(C, P))
+    idx = O.select_topk(s, C.shape[0])
+    np.testing.assert_array_equal(idx, np.arange(C.shape[0]))
+    dense = O.mla_attend_explicit(qn, qr, Wk, Wv, C, 0.3)
+    sparse = O.mla_attend_explicit(qn, qr, Wk, Wv, C[idx], 0.3)
+    for a, b in zip(dense, sparse):
+        np.testing.assert_array_equal(a, b)
+    # and with k < T the output differs (the pin is not vacuous)
+    part = O.mla_attend_explicit(qn, qr, Wk, Wv, C[O.select_topk(s, 5)], 0.3)
+    assert not np.allclose(part[0], dense[0])
 
 
 def test_mla_score_is_summed_per_head_projection():

@@ -79,10 +79,15 @@ __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shf
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, kWave); }
 
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.
+// Key 0 means "no token": -inf (the score of a position past the sequence
+// or behind an invalid page) maps to it, as does the all-ones NaN that
+// staging uses for such positions, so neither is ever selected. Finite
+// scores map to keys >= 0x00800000.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u == 0xff800000u ? 0u : key;
 }
 
 // Ordering fence for data exchanged through LDS between lanes of one wave.

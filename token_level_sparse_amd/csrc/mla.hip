@@ -1,8 +1,8 @@
 // MLA shared-latent path: selection over the shared latent cache and
 // attention over the selected latent rows.
 //
-// For MLA models JSSA's selection operates over the shared latent cache
-// (ai4snews digest, Perspective). Per head h the key of token t is
+// On MLA models the selection runs on the one latent cache that every head
+// reads (ai4snews digest, Perspective). Per head h the key of token t is
 // [W_uk[h] c_t[:512]; c_t[512:]] and its value c_t[:512]; absorbing W_uk into
 // the query (q_abs = [W_uk[h]^T q_nope; q_rope]) turns the logits into one
 // 576-dim dot per (head, token) and the output into W_uv[h] (sum_t p_t c_t).

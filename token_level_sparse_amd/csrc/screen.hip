@@ -1,8 +1,8 @@
 // Lossless tile screening of the score stream ("DoSA Makes Sparse Attention
 // Selection Conditional Without Approximation", cctest.ai, How the method
-// works: a seed set gives a lower bound on the winning threshold, and
-// candidates whose upper bound falls below it are dropped before exact
-// scoring, leaving the top-k unchanged).
+// works). The scores of a few seed tokens bound the selection threshold from
+// below; a candidate whose score cannot reach that bound is never scored
+// exactly, and the selected set stays the same.
 //
 // The score is one r-dim dot product s_t = qp . Kp_t, so a tile of 64
 // consecutive tokens has the box bound ub = sum_c max(qp_c lo_c, qp_c hi_c),

@@ -339,8 +339,9 @@ __device__ bool chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
 }
 
 // Top-delta filter of a row's final selection (Faster Than Flash review on
-// evolve.pub, Summary and FAQ: keep what lies within delta, in log space, of
-// a pseudo-max estimated from sink and local tokens). pmax[row * nseg0 + s]
+// evolve.pub, Summary and FAQ: a token stays when its log-weight is no more
+// than delta below a stand-in for the maximum taken over the first and the
+// most recent tokens). pmax[row * nseg0 + s]
 // is the largest score key of the row's sink or local tokens in segment s
 // (0: none there); the row's pseudo-max m is their maximum, and a selected
 // token stays only if its score is >= m - thr_off (thr_off = delta * G /

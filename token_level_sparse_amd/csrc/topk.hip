@@ -1,8 +1,9 @@
 // Per-(sequence, head) top-k with lowest-index ties.
 //
-// JSSA keeps a distinct selected token set for each KV head (JSSA abstract;
-// ai4snews digest, Synopsis). The result is the first min(k, T_b) tokens of
-// the total order (score descending, index ascending), listed ascending.
+// Each KV head gets its own selection (JSSA abstract; ai4snews digest,
+// Synopsis). The result is the first min(k, n) existing tokens of the total
+// order (score descending, index ascending), listed ascending; a -inf score
+// marks a position without a token (past T_b, or behind an invalid page).
 //
 // Radix selection over order-preserving uint32 keys, two kernels, no global
 // atomics (same-address atomics serialise across the XCDs):
@@ -298,9 +299,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NW; ++i) pm = pred[i] > pm ? pred[i] : pm;
-      if (pm != 0u) thr_key = score_key(key_score(pm) - dl.thr_off);
-      const uint32_t neg_inf = score_key(-__builtin_inff());
-      thr_key = thr_key > neg_inf ? thr_key : neg_inf + 1u;      // -inf scores: no valid page
+      if (pm != 0u) thr_key = score_key(key_score(pm) - dl.thr_off);   // (-inf: key 0, no filter)
     }
   }
   int n;
