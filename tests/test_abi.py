@@ -94,6 +94,21 @@ def test_topk_workspace(J):
         assert J.jssa_topk_workspace_size(4, 2, T, k) > 0
 
 
+def test_workspace_is_bounded_by_the_budget(J):
+    """Each 8192-token chunk keeps at most max(2k, k + 64) candidates, so the
+    workspace grows with the budget, not with the chunk length: at 128K x
+    B = 16 x Hkv = 8 with k = 256 it stays under 64 MB (16 segments of 512
+    key/index slots per row, plus one 16-byte summary per segment)."""
+    d = J.gqa_desc(16, 32, 8, 32, 131072)
+    n = J.jssa_score_topk_workspace_size(d, 256)
+    rows, nseg = 16 * 8, 16
+    assert n <= 64 << 20
+    assert n >= rows * nseg * (512 * 8 + 16)
+    assert J.jssa_topk_workspace_size(16, 8, 131072, 256) <= 64 << 20
+    # and it grows with k (two candidate slots per budget unit per chunk)
+    assert J.jssa_score_topk_workspace_size(d, 1024) > 3 * n
+
+
 def test_combine_and_mla_validation(J):
     assert _status(J.jssa_combine, 1, 1, 0, 128, A, A, A) == J.ERR_SHAPE
     assert _status(J.jssa_combine, 1, 1, 4, 130, A, A, A) == J.ERR_UNSUPPORTED

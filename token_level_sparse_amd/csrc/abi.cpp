@@ -198,7 +198,7 @@ jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k,
   if (k < 1 || k > 4096 || k > desc->max_seq)
     return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
   const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
-  jssa::carve_segs(nullptr, rows, nseg, jssa::score_topk_segment_cap(), bytes);
+  jssa::carve_segs(nullptr, rows, nseg, jssa::score_topk_segment_cap(k), bytes);
   *bytes += jssa::merge_workspace_bytes(rows, nseg, k);
   return JSSA_OK;
 }
@@ -213,7 +213,7 @@ jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const floa
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
   size_t main_bytes = 0;
   jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), &main_bytes);
+                                         jssa::score_topk_segment_cap(k), &main_bytes);
   return hip_status(jssa::launch_score_topk(to_dev(desc), static_cast<const uint16_t*>(q), P,
                                             static_cast<const uint16_t*>(Kp), k, scores, idx, segs,
                                             static_cast<char*>(ws) + main_bytes, S(stream)),
@@ -229,7 +229,7 @@ jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, con
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
   jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), nullptr);
+                                         jssa::score_topk_segment_cap(k), nullptr);
   return hip_status(jssa::launch_score_chunks(to_dev(desc), static_cast<const uint16_t*>(q), P,
                                               static_cast<const uint16_t*>(Kp), k, scores, segs, S(stream)),
                     __func__);
@@ -245,7 +245,7 @@ jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const vo
   size_t main_bytes = 0;
   jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv,
                                          jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), &main_bytes);
+                                         jssa::score_topk_segment_cap(k), &main_bytes);
   return hip_status(jssa::launch_select_final(desc->B * desc->Hkv, desc->Hkv, desc->max_seq, desc->seq_lens, k,
                                               segs, idx, static_cast<char*>(const_cast<void*>(ws)) + main_bytes,
                                               S(stream)),
@@ -264,7 +264,7 @@ jssa_status jssa_score_topk_final_attend(const jssa_gqa_desc* desc, int32_t k, c
   size_t main_bytes = 0;
   const int nseg = jssa::score_topk_segments(desc->max_seq);
   jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv, nseg,
-                                         jssa::score_topk_segment_cap(), &main_bytes);
+                                         jssa::score_topk_segment_cap(k), &main_bytes);
   const jssa::GqaDev g = to_dev(desc);
   const auto* q16 = static_cast<const uint16_t*>(q);
   const auto* K16 = static_cast<const uint16_t*>(K);
@@ -429,7 +429,7 @@ jssa_status topdelta_setup(const char* fn, const jssa_gqa_desc* desc, int32_t k_
   jssa_score_topk_workspace_size(desc, k_max, &base);
   size_t main_bytes = 0;
   const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
-  td->segs = jssa::carve_segs(ws, rows, nseg, jssa::score_topk_segment_cap(), &main_bytes);
+  td->segs = jssa::carve_segs(ws, rows, nseg, jssa::score_topk_segment_cap(k_max), &main_bytes);
   td->merge_ws = static_cast<char*>(ws) + main_bytes;
   td->pmax = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + jssa::align256(base));
   td->dl = jssa::DeltaArgs{td->pmax, nseg, rule->delta * float(desc->Hq / desc->Hkv) / scale, counts};
@@ -530,7 +530,7 @@ jssa_status jssa_score_topk_screened_chunks(const jssa_gqa_desc* desc, const voi
   size_t base = 0;
   jssa_score_topk_workspace_size(desc, k, &base);
   jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(), nullptr);
+                                         jssa::score_topk_segment_cap(k), nullptr);
   auto* keep = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + jssa::align256(base));
   const jssa::GqaDev g = to_dev(desc);
   const auto* q16 = static_cast<const uint16_t*>(q);

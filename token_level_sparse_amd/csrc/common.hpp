@@ -75,6 +75,33 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Reductions over the 64 lanes of a wave (every lane active), returned
+// wave-uniform: DPP moves inside each 16-lane row, then the four rows'
+// results read out of lanes 0, 16, 32 and 48.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, 0xf, 0xf, false));
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, dpp_u32<0xb1>(x));
+  x = op(x, dpp_u32<0x4e>(x));
+  x = op(x, dpp_u32<0x141>(x));
+  x = op(x, dpp_u32<0x140>(x));
+  const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(x), 0)), b = uint32_t(__builtin_amdgcn_readlane(int(x), 16));
+  const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(x), 32)), d = uint32_t(__builtin_amdgcn_readlane(int(x), 48));
+  return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, kWave)); }
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, kWave); }
 

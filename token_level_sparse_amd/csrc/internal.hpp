@@ -21,7 +21,7 @@ hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, cons
 size_t topk_workspace_bytes(int rows, int max_seq, int k);
 CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total);
 int score_topk_segments(int max_seq);
-int score_topk_segment_cap();
+int score_topk_segment_cap(int k);
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                              float* scores, int32_t* idx, CandSegs segs, void* merge_ws, hipStream_t st);
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,

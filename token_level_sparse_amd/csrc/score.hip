@@ -37,7 +37,12 @@ constexpr int kWaves = 4;
 constexpr int kFusedTiles = 32;            // tiles of 64 tokens per wave: 8192-token chunks
 constexpr int kPlainTiles = 16;            // 4096-token chunks for the score-only stream
 constexpr int kMlaTiles = 4;               // 1024-token chunks: the latent cache has only B rows
-constexpr int kDepth = 2;                  // tiles per wave whose loads are in flight together
+// Tiles per wave whose loads are in flight together. The plain score stream
+// takes four for r <= 32 (measured: 199 -> 192 us at 128K x B = 16); the
+// fused stream keeps two (four measured no faster: its time beyond the pure
+// stream is the select and the XCD tail, not the loads in flight), as do
+// larger ranks, whose buffers would not fit beside the select's registers.
+constexpr int depth_of(int r, bool fused) { return r <= 32 && !fused ? 4 : 2; }
 constexpr int kPackMaxB = 64;              // sequences up to which blocks take packed work items
 
 // sum over aligned groups of PP lanes (PP = 1, 2, 4, 8 or 16), left in every
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       for (int i = tid; i < lim; i += NT) srow[t_begin + i] = -__builtin_inff();
     }
     if (FUSED && tid == 0) {
-      fo.segs.cnt[seg] = 0;
+      write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
       if (fo.pmax) fo.pmax[seg] = 0u;
     }
     return;
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   }
   if (SCREEN && (kw[0] | kw[1] | kw[2] | kw[3]) == 0u) {   // every tile dropped (block-uniform)
     if (tid == 0) {
-      fo.segs.cnt[seg] = 0;
+      write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
       if (fo.pmax) fo.pmax[seg] = 0u;
     }
     return;
@@ -262,11 +267,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     return __builtin_amdgcn_readlane(klist, i < nkept ? i : nkept - 1);
   };
 
+  constexpr int kDepth = depth_of(R, FUSED);
   u32x4 bufs[kDepth][PP];
-  if (nkept > 0) {
+  // the first tiles' loads: in flight during the prologue, issued after the
+  // prologue's own loads (a wave's loads complete in issue order, so the
+  // prologue then waits for its query and P values only, not for a tile)
+  auto first_tiles = [&]() {
+    if (nkept > 0) {
 #pragma unroll
-    for (int u = 0; u < kDepth - 1; ++u) load_tile(kept_tile(u), bufs[u]);   // in flight during the prologue
-  }
+      for (int u = 0; u < kDepth - 1; ++u) load_tile(kept_tile(u), bufs[u]);
+    }
+  };
 
   // ---- prologue: qp = P_j^T qbar (fp32). The slice of P this thread needs
   // and the group's query rows are loaded together (one round trip, not two),
@@ -275,6 +286,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     constexpr int NS = NT / R;                 // row slices of P
     constexpr int NI = (kD + NS - 1) / NS;     // rows per slice
     constexpr bool kPreP = NI <= 32;           // hold the slice in registers
+    constexpr int kMaxG = 16;                  // query heads per KV head (validated on the host)
     const int c = tid % R, sl = tid / R;
     const float* Pj = P + int64_t(j) * kD * R;
     float pv[kPreP ? NI : 1];
@@ -285,16 +297,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
         pv[ii] = Pj[(i < kD ? i : kD - 1) * R + c];   // unconditional load, zero weight past d
       }
     }
+    uint16_t qh[kMaxG];                        // column tid of the group's query rows
     if (tid < kD) {
       const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + tid;
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) qh[h] = qg[(h < g.G ? h : g.G - 1) * kD];   // clamped: a valid row
+    }
+    first_tiles();
+    if (tid < kD) {
       float s = 0.f;
-      int h = 0;
-      for (; h + 4 <= g.G; h += 4) {
-        const float a0 = bf(qg[h * kD]), a1 = bf(qg[(h + 1) * kD]);
-        const float a2 = bf(qg[(h + 2) * kD]), a3 = bf(qg[(h + 3) * kD]);
-        s += a0; s += a1; s += a2; s += a3;
-      }
-      for (; h < g.G; ++h) s += bf(qg[h * kD]);
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) s += h < g.G ? bf(qh[h]) : 0.f;
       sm.u.pro.qbar[tid] = s;
     }
     __syncthreads();
@@ -318,7 +331,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     __syncthreads();
   } else {
     // MLA: the selection query qp = P^T sum_h q_abs[b,h] comes precomputed
-    if (tid < R) sm.qp[tid] = qsel[int64_t(b) * R + tid];
+    const float qv = qsel[int64_t(b) * R + (tid < R ? tid : 0)];
+    first_tiles();
+    if (tid < R) sm.qp[tid] = qv;
     __syncthreads();
   }
   float qr[NSL][8];
@@ -498,7 +513,7 @@ int score_topk_segments(int max_seq) {
   return (max_seq + chunk - 1) / chunk;
 }
 
-int score_topk_segment_cap() { return kWaves * 64 * kFusedTiles; }
+int score_topk_segment_cap(int k) { return seg_cap(k, kWaves * 64 * kFusedTiles); }
 
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax, int n_sink,

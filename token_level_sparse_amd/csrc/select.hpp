@@ -15,14 +15,40 @@ namespace jssa {
 
 constexpr int kSelBins = 2048;
 
-// Segmented candidate lists: segment (row, s) holds cnt[row*nseg+s] entries
-// at key/idx + (row*nseg+s)*cap.
+// Summary of one candidate segment, written by its producer beside the list
+// (one 16-byte store) and read by the row's final pass together with the
+// candidates, so that the final pass needs no reduction over the candidates
+// to bracket the row's k-th key.
+struct SegInfo {
+  int32_t cnt;     // candidates in the segment (at most cap)
+  uint32_t floor;  // a key with at least k of the segment's candidates at or above it; 0: none known
+  uint32_t top;    // at or above every candidate key (0 when empty)
+  uint32_t bot;    // at or below every candidate key (0xffffffff when empty)
+};
+
+// Segmented candidate lists: segment (row, s) holds info[row*nseg+s].cnt
+// entries at key/idx + (row*nseg+s)*cap, in ascending token order.
 struct CandSegs {
-  int32_t* cnt;
+  SegInfo* info;
   uint32_t* key;
   int32_t* idx;
   int nseg, cap;
 };
+
+// Slots per segment for a budget k: a chunk keeps at most this many
+// candidates (at most 2k through the top-two bound, else k plus the slack of
+// the histogram select; a chunk whose kept set would exceed it resolves its
+// k-th key exactly and keeps exactly k). Never more than the chunk length.
+__host__ __device__ inline int seg_cap(int k, int chunk_len) {
+  int c = 2 * k > k + 64 ? 2 * k : k + 64;
+  c = (c + 3) & ~3;
+  return c < chunk_len ? c : chunk_len;
+}
+
+__device__ __forceinline__ void write_info(const CandSegs& out, int64_t seg, int cnt, uint32_t floor, uint32_t top,
+                                           uint32_t bot) {
+  *reinterpret_cast<u32x4*>(out.info + seg) = u32x4{uint32_t(cnt), floor, top, bot};
+}
 
 template <int NT>
 struct ScanSmem {
@@ -116,57 +142,59 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   auto real = [&](int e) { return base + tid * E + e < lim; };
-  // key 0 (no token: a dropped tile of a screened chunk) takes no part in
-  // the bounds or the histograms; thousands of them in one bin would
-  // serialize its atomics
+  // key 0 (no token: past the row, behind an invalid page, or a dropped
+  // tile of a screened chunk) takes no part in the bounds or the
+  // histograms; thousands of them in one bin would serialize its atomics.
+  // Every caller gives positions at or past lim the key 0 as well.
   auto cand = [&](int e) { return real(e) && key[e] != 0u; };
   const bool keep_all = n <= k;
   const bool full = n == NT * E;
   uint32_t thr = 0;                          // keep real keys >= thr
-  if (!keep_all) {
-    uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
+  uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (cand(e)) {
-        const uint32_t x = key[e];
-        m2 = x > m1 ? m1 : (x > m2 ? x : m2);
-        m1 = x > m1 ? x : m1;
-        tmin = x < tmin ? x : tmin;
-      }
-    uint32_t bound2 = 0u;                    // the wave's r-th largest m2 (0: not usable)
-    const int r = (k + 2 * NW - 1) / (2 * NW);
-    if (full && r <= 64) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = bound2 | (1u << bit);
-        if (__popcll(__ballot(m2 >= c)) >= r) bound2 = c;
-      }
+  for (int e = 0; e < E; ++e)
+    if (cand(e)) {
+      const uint32_t x = key[e];
+      m2 = x > m1 ? m1 : (x > m2 ? x : m2);
+      m1 = x > m1 ? x : m1;
+      tmin = x < tmin ? x : tmin;
     }
-    uint32_t mx = m1, mnmx = m1, mn = tmin;
+  uint32_t bound2 = 0u;                      // the wave's r-th largest m2 (0: not usable)
+  const int r = (k + 2 * NW - 1) / (2 * NW);
+  if (!keep_all && full && r <= 64) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = bound2 | (1u << bit);
+      if (__popcll(__ballot(m2 >= c)) >= r) bound2 = c;
+    }
+  }
+  uint32_t mx = m1, mnmx = m1, mn = tmin;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
-      const uint32_t c = uint32_t(__shfl_xor(int(mnmx), o, 64));
-      const uint32_t d = uint32_t(__shfl_xor(int(mn), o, 64));
-      mx = a > mx ? a : mx;
-      mnmx = c < mnmx ? c : mnmx;
-      mn = d < mn ? d : mn;
-    }
-    if (lane == 0) {
-      sm.red[0][wv] = mx;
-      sm.red[1][wv] = mnmx;
-      sm.red[2][wv] = mn;
-      sm.red[3][wv] = bound2;
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
+    const uint32_t c = uint32_t(__shfl_xor(int(mnmx), o, 64));
+    const uint32_t d = uint32_t(__shfl_xor(int(mn), o, 64));
+    mx = a > mx ? a : mx;
+    mnmx = c < mnmx ? c : mnmx;
+    mn = d < mn ? d : mn;
+  }
+  if (lane == 0) {
+    sm.red[0][wv] = mx;
+    sm.red[1][wv] = mnmx;
+    sm.red[2][wv] = mn;
+    sm.red[3][wv] = bound2;
+  }
+  if (!keep_all)
     for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
-    __syncthreads();
-    uint32_t hi = sm.red[0][0], lo_full = sm.red[1][0], lo_any = sm.red[2][0], lo2 = sm.red[3][0];
+  __syncthreads();
+  uint32_t hi = sm.red[0][0], lo_full = sm.red[1][0], lo_any = sm.red[2][0], lo2 = sm.red[3][0];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
-      lo_full = sm.red[1][i] < lo_full ? sm.red[1][i] : lo_full;
-      lo_any = sm.red[2][i] < lo_any ? sm.red[2][i] : lo_any;
-      lo2 = sm.red[3][i] < lo2 ? sm.red[3][i] : lo2;
-    }
+  for (int i = 1; i < NW; ++i) {
+    hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
+    lo_full = sm.red[1][i] < lo_full ? sm.red[1][i] : lo_full;
+    lo_any = sm.red[2][i] < lo_any ? sm.red[2][i] : lo_any;
+    lo2 = sm.red[3][i] < lo2 ? sm.red[3][i] : lo2;
+  }
+  if (!keep_all) {
     uint32_t lo = lo_any;
     if (full && k <= NT) lo = lo_full > lo ? lo_full : lo;
     if (full && r <= 64) lo = lo2 > lo ? lo2 : lo;
@@ -199,17 +227,69 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
       __syncthreads();
       pick_bin<NT, kSelBins / NT>(sm.hist, need, true, sm.scan, sm.res);
       thr += uint32_t(sm.res[0]) << sh1;
+      __syncthreads();                                 // (the histogram is reused below)
     }
+  }
+  // The kept set: every candidate at or above thr, one bit per key.
+  uint32_t take = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) take |= (cand(e) && key[e] >= thr) ? (1u << e) : 0u;
+  int tot;
+  int at = block_scan<NT>(__builtin_popcount(take), sm.scan, &tot) - __builtin_popcount(take);
+  uint32_t floor = 0u, bot = thr > lo_any ? thr : lo_any;
+  if (tot > out.cap) {
+    // More than the segment holds (long runs of equal or nearly equal keys):
+    // resolve the chunk's k-th key K exactly, by further histogram levels
+    // over the bracket [thr, hi] that holds it, and keep exactly k tokens:
+    // every key above K and the lowest-indexed tokens equal to K. Tokens of
+    // the chunk outside these are outranked by k of its own tokens and
+    // cannot be among the row's k best. (tot > cap >= k: K >= thr.)
+    uint32_t elo = thr, ehi = hi;                       // 32-bit bracket: keys compare as 32-bit
+    int rem = k, trem = 0x7fffffff;
+    uint32_t tkey = thr;
+    for (;;) {
+      const uint32_t range = ehi - elo;
+      const int sh = range < uint32_t(kSelBins) ? 0 : (32 - __builtin_clz(range)) - 11;
+      for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)                       // (elo >= 1: key 0, no token, is never counted)
+        if (key[e] >= elo && key[e] <= ehi) atomicAdd(&sm.hist[(key[e] - elo) >> sh], 1u);
+      __syncthreads();
+      pick_bin<NT, kSelBins / NT>(sm.hist, rem, true, sm.scan, sm.res);
+      const uint32_t D = uint32_t(sm.res[0]);
+      rem -= sm.res[1];
+      const int cnt = int(sm.hist[D]);
+      __syncthreads();
+      const uint32_t blo = elo + (D << sh);                  // D < 2^11, sh <= 21: no overflow
+      if (cnt == rem) { tkey = blo; break; }                 // the whole bin is taken
+      if (sh == 0) { tkey = blo; trem = rem; break; }        // one key value, tied
+      const uint32_t wid = (1u << sh) - 1u;
+      elo = blo;
+      ehi = ehi - blo > wid ? blo + wid : ehi;
+    }
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) nt += key[e] == tkey ? 1 : 0;   // (tkey >= 1)
+    int ttot;
+    int tr = block_scan<NT>(nt, sm.scan, &ttot) - nt;       // ties before this thread's, in token order
+    take = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      bool t = key[e] > tkey;
+      if (key[e] == tkey) t = tr++ < trem;
+      take |= t ? (1u << e) : 0u;
+    }
+    at = block_scan<NT>(__builtin_popcount(take), sm.scan, &tot) - __builtin_popcount(take);
+    floor = tkey;
+    bot = tkey;
+  } else if (tot >= k) {
+    floor = bot;                                        // >= k candidates at or above thr and lo_any
   }
   // Compaction in token order: a thread's tokens are consecutive, so one
   // block scan of the per-thread counts places every kept key. The kept
   // pairs are gathered in LDS (over the histogram, which is no longer read)
   // and leave as coalesced stores; more than fit go out directly.
-  int mine = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) mine += (real(e) && key[e] >= thr && key[e] != 0u) ? 1 : 0;   // key 0: no token
-  int tot;
-  int at = block_scan<NT>(mine, sm.scan, &tot) - mine;
   uint32_t* okey = out.key + seg * out.cap;
   int32_t* oidx = out.idx + seg * out.cap;
   constexpr int kStaged = kSelBins / 2;
@@ -218,7 +298,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
   int32_t* sidx = reinterpret_cast<int32_t*>(sm.hist + kStaged);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (real(e) && key[e] >= thr && key[e] != 0u) {
+    if ((take >> e) & 1u) {
       if (staged) {
         skey[at] = key[e];
         sidx[at] = base + tid * E + e;
@@ -236,7 +316,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
       oidx[i] = sidx[i];
     }
   }
-  if (tid == 0) out.cnt[seg] = tot;
+  if (tid == 0) write_info(out, seg, tot, floor, hi, tot > 0 ? bot : 0xffffffffu);
 }
 
 constexpr int kTop2Bins = 256;
@@ -334,7 +414,8 @@ __device__ bool chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
     oidx[at] = base + tid * E + e;
     ++at;
   }
-  if (tid == 0) out.cnt[seg] = tot;
+  // at least k keys of M (distinct tokens) are at or above c, and all are kept
+  if (tid == 0) write_info(out, seg, tot, c, hi, tot > 0 ? c : 0xffffffffu);
   return true;
 }
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
   const float* src = scores + int64_t(row) * max_seq + start;
   const int64_t seg = int64_t(row) * segs.nseg + chunk;
   if (n == 0) {
-    if (tid == 0) segs.cnt[seg] = 0;
+    if (tid == 0) write_info(segs, seg, 0, 0u, 0u, 0xffffffffu);
     return;
   }
   float* stage = reinterpret_cast<float*>(sbuf);
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kWT) void chunk_wide_kernel(int H, int max_seq, con
   const float* src = scores + int64_t(row) * max_seq + start;
   const int64_t seg = int64_t(row) * segs.nseg + chunk;
   if (n == 0) {
-    if (tid == 0) segs.cnt[seg] = 0;
+    if (tid == 0) write_info(segs, seg, 0, 0u, 0u, 0xffffffffu);
     return;
   }
   // Thread i takes scores i*kCE .. i*kCE+kCE-1, all loads issued together;
@@ -180,7 +180,7 @@ struct FinalSmem {
   uint32_t hist[kFinBins];
   int offs[kMaxSeg + 1];
   ScanSmem<NT> scan;
-  uint32_t red[2][NT / 64];
+  uint32_t red[6][NT / 64];
   int res[2];
   uint32_t bin[kBinList];
   int nbin;
@@ -241,89 +241,131 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   const int64_t seg0 = int64_t(row) * segs.nseg + s0;
   const uint32_t* gkey = segs.key + seg0 * segs.cap;
   const int32_t* gidx = segs.idx + seg0 * segs.cap;
+  const SegInfo* ginfo = segs.info + seg0;
 
-  // Direct layout: segment s is read by TPS = NT/nseg threads, EF slots each,
-  // at fixed positions, so these loads go out together with the segment
-  // counts instead of after them. Thread order is then list order. Used when
-  // every segment fits its TPS*EF slots; otherwise the list is re-read below
-  // by list position.
+  // Direct layout: segment s is read by TPS = NT/nseg threads, EF slots each
+  // (slots past the segment's capacity are not read), at fixed positions, so
+  // these loads go out together with the segment summaries instead of after
+  // them; thread order is then list order. Used when every segment's count
+  // fits its threads' slots (always when TPS*EF >= cap); otherwise the list
+  // is re-read below by list position.
   static_assert(EF % 4 == 0, "direct slots are read 16 bytes at a time");
   const int TPS = NT / nseg;
-  const bool try_direct = TPS > 0 && TPS * EF <= segs.cap && segs.cap % 4 == 0;   // block-uniform
+  const bool try_direct = TPS > 0 && segs.cap % 4 == 0;      // block-uniform
+  const int dslots = TPS > 0 ? min(TPS * EF, segs.cap) : 0;  // direct slots per segment
   const int dseg = TPS > 0 ? tid / TPS : nseg;
   const int dj = TPS > 0 ? (tid % TPS) * EF : 0;
   uint32_t rkey[EF];
   int32_t ridx[EF];
+  int dcnt = 0;                                         // candidates of this thread's direct segment
   if (try_direct) {
-    const int64_t o = int64_t(dseg < nseg ? dseg : 0) * segs.cap + dj;
+    const int ds = dseg < nseg ? dseg : 0;
+    dcnt = ginfo[ds].cnt;
+    const int64_t o = int64_t(ds) * segs.cap;
 #pragma unroll
     for (int e = 0; e < EF; e += 4) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(gkey + o + e);
-      const u32x4 iv = *reinterpret_cast<const u32x4*>(gidx + o + e);
+      const int j0 = dj + e < segs.cap ? dj + e : segs.cap - 4;   // in the segment's slots
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(gkey + o + j0);
+      const u32x4 iv = *reinterpret_cast<const u32x4*>(gidx + o + j0);
       rkey[e] = kv.x; rkey[e + 1] = kv.y; rkey[e + 2] = kv.z; rkey[e + 3] = kv.w;
       ridx[e] = int32_t(iv.x); ridx[e + 1] = int32_t(iv.y); ridx[e + 2] = int32_t(iv.z); ridx[e + 3] = int32_t(iv.w);
     }
   }
 
-  // segment offsets: each thread scans SPT consecutive segments
+  // Segment summaries: thread tid takes segments tid, tid + NT, ... (one
+  // load when nseg <= NT). The row's candidate count, the largest
+  // per-segment count, and the bracket of the k-th key come out of wave
+  // reductions and one barrier: every candidate is at or below hi, and lo
+  // (the largest segment floor, or the smallest candidate) is at or below
+  // the need_all-th largest candidate key.
   constexpr int SPT = kMaxSeg / NT;
-  int c[SPT];
-  int mine = 0;
-#pragma unroll
-  for (int x = 0; x < SPT; ++x) {
-    const int s = tid * SPT + x;
-    c[x] = segs.cnt[seg0 + (s < nseg ? s : nseg - 1)];
+  uint32_t fl = 0u, tp = 0u, bt = 0xffffffffu, cmx = 0u, mine = 0u;
+  for (int s = tid; s < nseg; s += NT) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ginfo + s);
+    mine += v.x;
+    fl = v.y > fl ? v.y : fl;
+    tp = v.z > tp ? v.z : tp;
+    bt = v.w < bt ? v.w : bt;
+    cmx = v.x > cmx ? v.x : cmx;
   }
-#pragma unroll
-  for (int x = 0; x < SPT; ++x) {
-    c[x] = tid * SPT + x < nseg ? c[x] : 0;
-    mine += c[x];
+  for (int i = tid; i < kFinBins; i += NT) sm.hist[i] = 0u;   // the first histogram level
+  if (tid == 0) sm.nbin = 0;
+  {
+    const uint32_t a = wave_sum_u32(mine), f = wave_max_u32(fl), t = wave_max_u32(tp);
+    const uint32_t u = wave_min_u32(bt), m = wave_max_u32(cmx);
+    if (lane == 0) {
+      sm.red[0][wv] = a;
+      sm.red[1][wv] = f;
+      sm.red[2][wv] = t;
+      sm.red[3][wv] = u;
+      sm.red[4][wv] = m;
+    }
   }
   // top-delta (final level only): the row's pseudo-max and the key a kept
-  // token must reach (0: no filter)
-  uint32_t thr_key = 0u;
+  // token must reach (0: no filter); its slots are read with the summaries
+  uint32_t pm = 0u;
   if constexpr (!MERGE) {
     if (dl.pmax) {                                      // block-uniform
-      __shared__ uint32_t pred[NW];
-      uint32_t pm = 0u;
       for (int s = tid; s < dl.nseg0; s += NT) {
         const uint32_t v = dl.pmax[int64_t(row) * dl.nseg0 + s];
         pm = v > pm ? v : pm;
       }
+      pm = wave_max_u32(pm);
+      if (lane == 0) sm.red[5][wv] = pm;
+    }
+  }
+  __syncthreads();
+  int n = 0;
+  uint32_t lo = 0u, hi = 0u, lbot = 0xffffffffu, cmax = 0u;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = uint32_t(__shfl_xor(int(pm), o, 64));
-        pm = y > pm ? y : pm;
-      }
-      if (lane == 0) pred[wv] = pm;
-      __syncthreads();
+  for (int i = 0; i < NW; ++i) {
+    n += int(sm.red[0][i]);
+    lo = sm.red[1][i] > lo ? sm.red[1][i] : lo;
+    hi = sm.red[2][i] > hi ? sm.red[2][i] : hi;
+    lbot = sm.red[3][i] < lbot ? sm.red[3][i] : lbot;
+    cmax = sm.red[4][i] > cmax ? sm.red[4][i] : cmax;
+  }
+  lo = lbot > lo ? lbot : lo;
+  uint32_t thr_key = 0u;
+  if constexpr (!MERGE) {
+    if (dl.pmax) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) pm = pred[i] > pm ? pred[i] : pm;
+      for (int i = 0; i < NW; ++i) pm = sm.red[5][i] > pm ? sm.red[5][i] : pm;
       if (pm != 0u) thr_key = score_key(key_score(pm) - dl.thr_off);   // (-inf: key 0, no filter)
     }
   }
-  int n;
-  int run = block_scan<NT>(mine, sm.scan, &n) - mine;
+  const bool direct = try_direct && int(cmax) <= dslots;       // block-uniform
+  // Offsets of the segments in the row's list: needed only when the list is
+  // read by position (not direct).
+  if (!direct) {                                       // (thread tid: SPT consecutive segments)
+    int c[SPT];
+    int mc = 0;
 #pragma unroll
-  for (int x = 0; x < SPT; ++x) {
-    const int s = tid * SPT + x;
-    if (s < nseg) sm.offs[s] = run;
-    run += c[x];
+    for (int x = 0; x < SPT; ++x) {
+      const int s = tid * SPT + x;
+      c[x] = s < nseg ? ginfo[s].cnt : 0;
+      mc += c[x];
+    }
+    int tot;
+    int run = block_scan<NT>(mc, sm.scan, &tot) - mc;
+#pragma unroll
+    for (int x = 0; x < SPT; ++x) {
+      const int s = tid * SPT + x;
+      if (s < nseg) sm.offs[s] = run;
+      run += c[x];
+    }
+    if (tid == 0) sm.offs[nseg] = n;
+    __syncthreads();
   }
-  if (tid == 0) sm.offs[nseg] = n;
-  bool over = false;
-#pragma unroll
-  for (int x = 0; x < SPT; ++x) over = over || c[x] > TPS * EF;
-  const bool direct = !__syncthreads_or(over) && try_direct;   // (the barrier also orders the offs writes)
   // The row's candidate list is its segments one after the other: ascending
   // token order (segments cover ascending token ranges, each in token order).
   auto locate = [&](int i) -> int {      // segment holding list position i < n
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
+    int lo_s = 0, hi_s = nseg - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (sm.offs[mid] <= i) lo_s = mid; else hi_s = mid - 1;
     }
-    return lo;
+    return lo_s;
   };
   // list positions i0 .. i0+EF-1 (idx -1 past the end). Addresses first,
   // then every load at once; positions past the end re-read entry n - 1.
@@ -355,7 +397,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   constexpr int kRegCap = NT * EF;
   const bool reg = direct || n <= kRegCap;
   if (direct) {
-    const int cnt = dseg < nseg ? sm.offs[dseg + 1] - sm.offs[dseg] : 0;
+    const int cnt = dseg < nseg ? dcnt : 0;
 #pragma unroll
     for (int e = 0; e < EF; ++e)
       if (dj + e >= cnt) ridx[e] = -1;
@@ -391,42 +433,24 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   // order, i.e. lowest token indices) whose key equals tkey.
   uint32_t tkey = 0u;
   int trem = 0x7fffffff;
-  if (n > need_all && need_all > 0) {
-    uint32_t mx = 0u, mn = 0xffffffffu;
-    for_each_key([&](uint32_t key) {
-      mx = key > mx ? key : mx;
-      mn = key < mn ? key : mn;
-    });
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
-      const uint32_t c = uint32_t(__shfl_xor(int(mn), o, 64));
-      mx = a > mx ? a : mx;
-      mn = c < mn ? c : mn;
-    }
-    if (lane == 0) {
-      sm.red[0][wv] = mx;
-      sm.red[1][wv] = mn;
-    }
-    __syncthreads();
-    uint64_t hi = 0, lo = 0xffffffffull;
-    for (int i = 0; i < NW; ++i) {
-      hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
-      lo = sm.red[1][i] < lo ? sm.red[1][i] : lo;
-    }
+  const bool search = n > need_all && need_all > 0;   // block-uniform
+  if (search) {
     // Adaptive levels: kFinBins linear bins over the current bracket
     // [lo, hi] of keys; the bin holding the rem-th largest key becomes the
     // next bracket. Every level narrows the bracket by 2^12, so at most three
     // levels reach a single key value.
+    uint64_t blo_ = lo, bhi_ = hi;
     int rem = need_all;
-    for (;;) {
-      const uint64_t range = hi - lo;
+    for (int level = 0;; ++level) {
+      const uint64_t range = bhi_ - blo_;
       const int sh = range < uint64_t(kFinBins) ? 0 : (64 - __builtin_clzll(range)) - kFinBits;
-      for (int i = tid; i < kFinBins; i += NT) sm.hist[i] = 0u;
-      if (tid == 0) sm.nbin = 0;
-      __syncthreads();
+      if (level > 0) {
+        for (int i = tid; i < kFinBins; i += NT) sm.hist[i] = 0u;
+        if (tid == 0) sm.nbin = 0;
+        __syncthreads();
+      }
       for_each_key([&](uint32_t key) {
-        if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> sh], 1u);
+        if (key >= blo_ && key <= bhi_) atomicAdd(&sm.hist[(key - blo_) >> sh], 1u);
       });
       __syncthreads();
       pick_bin<NT, kFinBins / NT>(sm.hist, rem, true, sm.scan, sm.res);
@@ -434,7 +458,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       rem -= sm.res[1];
       const int cnt = int(sm.hist[D]);
       __syncthreads();
-      const uint64_t blo = lo + (D << sh);
+      const uint64_t blo = blo_ + (D << sh);
       if (cnt == rem) {                  // the whole bin is taken
         tkey = uint32_t(blo);
         break;
@@ -446,21 +470,21 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
       }
       if (cnt <= kBinList) {             // few keys in the bin: one wave ranks them exactly
         for_each_key([&](uint32_t key) {
-          if (key >= lo && key <= hi && ((key - lo) >> sh) == D) sm.bin[atomicAdd(&sm.nbin, 1)] = key;
+          if (key >= blo_ && key <= bhi_ && ((key - blo_) >> sh) == D) sm.bin[atomicAdd(&sm.nbin, 1)] = key;
         });
         __syncthreads();
         if (wv == 0) {
-          const uint32_t mine = lane < cnt ? sm.bin[lane] : 0u;
+          const uint32_t mk = lane < cnt ? sm.bin[lane] : 0u;
           int gt = 0, eq = 0;                      // keys of the bin above / equal to this lane's
           for (int i = 0; i < cnt; ++i) {
-            const uint32_t x = uint32_t(__builtin_amdgcn_readlane(int(mine), i));
-            gt += x > mine ? 1 : 0;
-            eq += x == mine ? 1 : 0;
+            const uint32_t x = uint32_t(__builtin_amdgcn_readlane(int(mk), i));
+            gt += x > mk ? 1 : 0;
+            eq += x == mk ? 1 : 0;
           }
           // the rem-th largest key v of the bin: gt < rem <= gt + eq; take
           // the rem - gt first of the keys equal to v (all of them: no ranking)
           if (lane < cnt && gt < rem && rem <= gt + eq) {
-            sm.res[0] = int(mine);
+            sm.res[0] = int(mk);
             sm.res[1] = rem - gt == eq ? 0x7fffffff : rem - gt;
           }
         }
@@ -470,8 +494,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
         break;
       }
       const uint64_t bhi = blo + (uint64_t(1) << sh) - 1;
-      lo = blo;
-      hi = bhi < hi ? bhi : hi;
+      blo_ = blo;
+      bhi_ = bhi < bhi_ ? bhi : bhi_;
     }
   }
 
@@ -505,14 +529,14 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     }
     const int ns = __popc(take);
     int st;
-    int at = block_scan<NT>(ns, sm.scan, &st) - ns + out_base;
+    int at2 = block_scan<NT>(ns, sm.scan, &st) - ns + out_base;
 #pragma unroll
     for (int e = 0; e < EF; ++e)
       if (take >> e & 1u) {
-        if constexpr (MERGE) dkey[at] = ck[e];
-        if constexpr (GT > 0) sel[at] = ci[e];
-        if (write_idx) dst[at] = ci[e];
-        ++at;
+        if constexpr (MERGE) dkey[at2] = ck[e];
+        if constexpr (GT > 0) sel[at2] = ci[e];
+        if (write_idx) dst[at2] = ci[e];
+        ++at2;
       }
     tie_base += tt;
     out_base += st;
@@ -527,7 +551,11 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     }
   }
   if constexpr (MERGE) {
-    if (tid == 0) outs.cnt[int64_t(row) * ng + grp] = out_base;
+    // the group's first min(k, n) candidates: all at or above tkey (searched)
+    // or lo (all of them taken)
+    const uint32_t b = search ? tkey : lo;
+    if (tid == 0)
+      write_info(outs, int64_t(row) * ng + grp, out_base, out_base >= k ? b : 0u, hi, out_base > 0 ? b : 0xffffffffu);
   } else {
     if (write_idx)
       for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
@@ -571,7 +599,7 @@ CandSegs carve_segs(void* base, int rows, int nseg, int cap, size_t* total) {
   size_t off = 0;
   auto take = [&](size_t bytes) { char* q = p ? p + off : nullptr; off += align256(bytes); return q; };
   CandSegs w;
-  w.cnt = reinterpret_cast<int32_t*>(take(size_t(rows) * nseg * 4));
+  w.info = reinterpret_cast<SegInfo*>(take(size_t(rows) * nseg * sizeof(SegInfo)));
   w.key = reinterpret_cast<uint32_t*>(take(size_t(rows) * nseg * cap * 4));
   w.idx = reinterpret_cast<int32_t*>(take(size_t(rows) * nseg * cap * 4));
   w.nseg = nseg;
@@ -674,11 +702,11 @@ bool use_wide(int rows, int max_seq, int k) {
 
 size_t topk_workspace_bytes(int rows, int max_seq, int k) {
   size_t total = 0;
-  carve_segs(nullptr, rows, chunks_of(max_seq), kChunk, &total);
+  carve_segs(nullptr, rows, chunks_of(max_seq), seg_cap(k, kChunk), &total);
   total += merge_workspace_bytes(rows, chunks_of(max_seq), k);
   if (use_wide(rows, max_seq, k)) {
     size_t wide = 0;
-    carve_segs(nullptr, rows, (max_seq + kWideChunk - 1) / kWideChunk, kWideChunk, &wide);
+    carve_segs(nullptr, rows, (max_seq + kWideChunk - 1) / kWideChunk, seg_cap(k, kWideChunk), &wide);
     total = wide > total ? wide : total;
   }
   return total;
@@ -690,7 +718,7 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
   const int nchunks = chunks_of(max_seq);
   if (use_wide(rows, max_seq, k)) {               // (the workspace size covers this layout)
     const int nwide = (max_seq + kWideChunk - 1) / kWideChunk;
-    CandSegs segs = carve_segs(wsp, rows, nwide, kWideChunk, nullptr);
+    CandSegs segs = carve_segs(wsp, rows, nwide, seg_cap(k, kWideChunk), nullptr);
     hipLaunchKernelGGL(chunk_wide_kernel, dim3(nwide, rows), dim3(kWT), 0, st, H, max_seq, seq_lens, scores, k,
                        segs);
     const hipError_t e = hipGetLastError();
@@ -701,7 +729,7 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
     return hipGetLastError();
   }
   size_t main_bytes = 0;
-  CandSegs segs = carve_segs(wsp, rows, nchunks, kChunk, &main_bytes);
+  CandSegs segs = carve_segs(wsp, rows, nchunks, seg_cap(k, kChunk), &main_bytes);
   hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
