@@ -269,7 +269,7 @@ jssa_status jssa_score_topk_final_attend(const jssa_gqa_desc* desc, int32_t k, c
   const auto* q16 = static_cast<const uint16_t*>(q);
   const auto* K16 = static_cast<const uint16_t*>(K);
   const auto* V16 = static_cast<const uint16_t*>(V);
-  if (jssa::select_attend_fused(nseg, k, g.G))
+  if (jssa::select_attend_fused(segs, k, g.G))
     return hip_status(jssa::launch_select_attend(g, k, segs, q16, K16, V16, scale, idx, out, lse, S(stream)),
                       __func__);
   hipError_t e = jssa::launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx,
@@ -470,7 +470,7 @@ jssa_status jssa_score_topdelta_attend(const jssa_gqa_desc* desc, const void* q,
   hipError_t e = jssa::launch_score_chunks(g, q16, P, static_cast<const uint16_t*>(Kp), k_max, nullptr, td.segs,
                                            S(stream), td.pmax, rule->n_sink, rule->n_local);
   if (e != hipSuccess) return hip_status(e, __func__);
-  if (jssa::select_attend_fused(td.segs.nseg, k_max, g.G))
+  if (jssa::select_attend_fused(td.segs, k_max, g.G))
     return hip_status(jssa::launch_select_attend(g, k_max, td.segs, q16, K16, V16, scale, idx, out, lse,
                                                  S(stream), td.dl),
                       __func__);

@@ -21,7 +21,7 @@
 namespace jssa {
 namespace {
 
-template <int GT, int STEPS, int NW, bool DENSE>
+template <int GT, int STEPS, int NW, bool DENSE, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
@@ -58,9 +58,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
   constexpr int RB = STEPS * 4;                 // rows per wave batch
   for (int base = r0 + w * RB; base < r1; base += NW * RB) {
     if constexpr (DENSE)
-      attn_batch<GT, STEPS>(g, b, j, Tb, K, V, qv, qs, base, r1, [](int rr) { return rr; }, A);
+      attn_batch<GT, STEPS, PAGED>(g, b, j, Tb, K, V, qv, qs, base, r1, [](int rr) { return rr; }, A);
     else
-      attn_batch<GT, STEPS>(g, b, j, Tb, K, V, qv, qs, base, r1, [&](int rr) { return irow[rr]; }, A);
+      attn_batch<GT, STEPS, PAGED>(g, b, j, Tb, K, V, qv, qs, base, r1, [&](int rr) { return irow[rr]; }, A);
   }
   attn_wave_reduce(A);
   if constexpr (NW > 1) {
@@ -78,8 +78,12 @@ hipError_t launch_attn_t(const GqaDev& g, const uint16_t* q, const uint16_t* K, 
                          hipStream_t st) {
   const int ngroups = (g.G + GT - 1) / GT;
   dim3 grid(S, g.Hkv * ngroups, g.B);
-  hipLaunchKernelGGL((attn_kernel<GT, STEPS, NW, DENSE>), grid, dim3(NW * 64), 0, st, g, q, K, V,
-                     idx, k, S, scale, po, pl);
+  if (g.page_size)
+    hipLaunchKernelGGL((attn_kernel<GT, STEPS, NW, DENSE, true>), grid, dim3(NW * 64), 0, st, g, q, K, V,
+                       idx, k, S, scale, po, pl);
+  else
+    hipLaunchKernelGGL((attn_kernel<GT, STEPS, NW, DENSE, false>), grid, dim3(NW * 64), 0, st, g, q, K, V,
+                       idx, k, S, scale, po, pl);
   return hipGetLastError();
 }
 

@@ -39,19 +39,24 @@ __device__ __forceinline__ void attn_init(AttnAcc<GT>& A) {
 }
 
 // Query slice (dims sub*8..+8) of heads qrow0 .. qrow0+nh-1 (rows of q
-// [.,128]) as bf16 pairs; heads past nh are zero. Logits use
-// v_dot2_f32_bf16 (exact bf16 products, fp32 sums).
+// [.,128]) as bf16 pairs; heads past nh (>= 1) are zero. Logits use
+// v_dot2_f32_bf16 (exact bf16 products, fp32 sums). The loads are
+// unconditional (heads past nh re-read row qrow0 and are zeroed after), so
+// none of them sits under a branch: a value merged from a branch would make
+// the compiler wait for every load in flight at that point.
 template <int GT>
 __device__ __forceinline__ void attn_load_q(bf16x2 (&qv)[GT][4], const uint16_t* q, int64_t qrow0, int nh,
                                             int sub) {
+  u32x4 v[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) v[h] = *reinterpret_cast<const u32x4*>(q + (qrow0 + (h < nh ? h : 0)) * kAttnD + sub * 8);
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (h < nh) v = *reinterpret_cast<const u32x4*>(q + (qrow0 + h) * kAttnD + sub * 8);
-    qv[h][0] = as_pair(v.x);
-    qv[h][1] = as_pair(v.y);
-    qv[h][2] = as_pair(v.z);
-    qv[h][3] = as_pair(v.w);
+    const u32x4 x = h < nh ? v[h] : u32x4{0u, 0u, 0u, 0u};
+    qv[h][0] = as_pair(x.x);
+    qv[h][1] = as_pair(x.y);
+    qv[h][2] = as_pair(x.z);
+    qv[h][3] = as_pair(x.w);
   }
 }
 
@@ -61,9 +66,10 @@ __device__ __forceinline__ void attn_load_q(bf16x2 (&qv)[GT][4], const uint16_t*
 //
 // Every load of the batch is issued without a data-dependent branch (a load
 // under one would be waited for before the next is issued): the batch's
-// tokens, then (paged) their page ids, then the K and V rows. Skipped rows
-// read a valid row (token 0, or page 0) and are masked out.
-template <int GT, int STEPS, class TokFn>
+// tokens, then (PAGED: a paged cache, page_size 16) their page ids, then the
+// K and V rows. Skipped rows read a valid row (token 0, or page 0) and are
+// masked out.
+template <int GT, int STEPS, bool PAGED, class TokFn>
 __device__ __forceinline__ void attn_batch(const GqaDev& g, int b, int j, int Tb, const uint16_t* __restrict__ K,
                                            const uint16_t* __restrict__ V, const bf16x2 (&qv)[GT][4], float qs,
                                            int base, int r1, TokFn tok, AttnAcc<GT>& A) {
@@ -82,12 +88,12 @@ __device__ __forceinline__ void attn_batch(const GqaDev& g, int b, int j, int Tb
     const int rr = base + st * 4 + gi;
     ok[st] = rr < r1 && tt[st] >= 0 && tt[st] < Tb;
     tt[st] = ok[st] ? tt[st] : 0;
-    pg[st] = g.page_size ? g.page_table[int64_t(b) * g.max_pages + (tt[st] >> 4)] : 0;
+    if constexpr (PAGED) pg[st] = g.page_table[int64_t(b) * g.max_pages + (tt[st] >> 4)];
   }
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     int64_t off;
-    if (g.page_size) {
+    if constexpr (PAGED) {
       ok[st] = ok[st] && pg[st] >= 0 && pg[st] < g.num_pages;
       off = ((int64_t(ok[st] ? pg[st] : 0) * g.Hkv + j) * kPage + (tt[st] & (kPage - 1))) * kAttnD;
     } else {

@@ -450,8 +450,10 @@ size_t merge_workspace_bytes(int rows, int nseg, int k);
 hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_lens, int k, CandSegs segs,
                                int32_t* idx, void* merge_ws, hipStream_t st, DeltaArgs dl = DeltaArgs{});
 // Final selection fused with the attention of each row's query heads over the
-// selected tokens (one split), when select_attend_fused(nseg, k, G) holds.
-bool select_attend_fused(int nseg, int k, int G);
+// selected tokens (one split; final_attend.hip), when select_attend_fused
+// holds: every segment fits the fused kernel's direct layout, k <= 512 and
+// G <= 16.
+bool select_attend_fused(const CandSegs& segs, int k, int G);
 hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
                                 const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
                                 hipStream_t st, DeltaArgs dl = DeltaArgs{});

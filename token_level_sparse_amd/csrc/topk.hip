@@ -23,7 +23,6 @@
 // capacity re-read their segments at each level (slower, same result).
 #include "internal.hpp"
 #include "select.hpp"
-#include "attn_core.hpp"
 
 namespace jssa {
 namespace {
@@ -192,48 +191,15 @@ struct FinalSmem {
 // candidates of the (key desc, index asc) order, as (key, index) pairs in
 // token order, to segment (row, group) of `outs`: a smaller candidate list
 // for the next level that still holds the row's top k.
-// With GT > 0 (final mode only) the block then runs the attention of the
-// row's query heads over the selected tokens, read in place, and writes the
-// normalised outputs and log-sum-exps (split-K with one split): the indices
-// never make a round trip through memory before the attention reads them.
-// hs blocks share a row: each makes the same (deterministic) selection and
-// attends for its own heads hpb*h .. hpb*h+hpb-1 of the row's group; only
-// the first writes the indices. A row's blocks are 8 launch positions apart,
-// so they land on one XCD and share its L2 for the candidates and K/V rows.
-struct AttendArgs {
-  GqaDev g;
-  const uint16_t* q;
-  const uint16_t* K;
-  const uint16_t* V;
-  float scale;
-  float* out;
-  float* lse;
-  int hs, hpb;                                          // blocks per row, heads per block
-};
-constexpr int kAttendMaxK = 512;
-
-template <int NT, int EF, bool MERGE, int GT = 0>
+template <int NT, int EF, bool MERGE>
 __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
                                                    CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs,
-                                                   AttendArgs at = AttendArgs{}, DeltaArgs dl = DeltaArgs{}) {
-  static_assert(GT == 0 || !MERGE, "attention follows the row's final selection only");
+                                                   DeltaArgs dl = DeltaArgs{}) {
   constexpr int NW = NT / 64;
   __shared__ FinalSmem<NT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ng = (segs.nseg + gs - 1) / gs;
-  int row = blockIdx.x / ng, grp = blockIdx.x % ng;
-  int hsplit = 0;                                       // this block's head share (GT > 0)
-  if constexpr (GT > 0) {
-    const int hs = at.hs, lin = blockIdx.x;
-    if (hs > 1 && (gridDim.x / hs) % 8 == 0) {          // lin = (q*hs + hsplit)*8 + row % 8
-      row = (lin / (8 * hs)) * 8 + lin % 8;
-      hsplit = (lin / 8) % hs;
-    } else {
-      row = lin / hs;
-      hsplit = lin % hs;
-    }
-    grp = 0;
-  }
+  const int row = blockIdx.x / ng, grp = blockIdx.x % ng;
   const int Tb = row_len(max_seq, seq_lens, row / H);
   const int need_all = MERGE ? k : min(k, Tb);
   const int s0 = grp * gs;
@@ -503,10 +469,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
   // per page of candidates, one ranking the tied candidates and one placing
   // the taken ones.
   int32_t* dst = MERGE ? outs.idx + (int64_t(row) * ng + grp) * outs.cap : out + int64_t(row) * k;
-  const bool write_idx = MERGE || hsplit == 0;
   uint32_t* dkey = MERGE ? outs.key + (int64_t(row) * ng + grp) * outs.cap : nullptr;
   int tie_base = 0, out_base = 0;
-  __shared__ int32_t sel[GT > 0 ? kAttendMaxK : 1];   // the selected tokens, for the attention
   auto emit = [&](const uint32_t (&ck)[EF], const int32_t (&ci)[EF]) {
     int tt = 0, tr = 0;
     if (trem != 0x7fffffff) {                         // tied candidates are ranked only when some are left out
@@ -534,8 +498,7 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     for (int e = 0; e < EF; ++e)
       if (take >> e & 1u) {
         if constexpr (MERGE) dkey[at2] = ck[e];
-        if constexpr (GT > 0) sel[at2] = ci[e];
-        if (write_idx) dst[at2] = ci[e];
+        dst[at2] = ci[e];
         ++at2;
       }
     tie_base += tt;
@@ -557,34 +520,8 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     if (tid == 0)
       write_info(outs, int64_t(row) * ng + grp, out_base, out_base >= k ? b : 0u, hi, out_base > 0 ? b : 0xffffffffu);
   } else {
-    if (write_idx)
-      for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
-    if (dl.counts && write_idx && tid == 0) dl.counts[row] = out_base;
-  }
-  if constexpr (GT > 0) {
-    constexpr int STEPS = 8, RB = STEPS * 4;
-    const GqaDev& g = at.g;
-    const int b = row / H, j = row % H, w = tid >> 6;
-    const int cnt = out_base;                           // selected tokens (<= kAttendMaxK)
-    const float qs = at.scale * kAttnLog2e;
-    __shared__ AttnMergeSmem<GT, NW> msm;
-    __syncthreads();                                    // sel complete
-    const int hb0 = hsplit * at.hpb, hb1 = min(g.G, hb0 + at.hpb);   // heads of this block
-    for (int hl = hb0; hl < hb1; hl += GT) {
-      const int h0 = j * g.G + hl, nh = min(GT, hb1 - hl);
-      bf16x2 qv[GT][4];
-      attn_load_q<GT>(qv, at.q, int64_t(b) * g.Hq + h0, nh, lane & 15);
-      AttnAcc<GT> A;
-      attn_init(A);
-      for (int base = w * RB; base < cnt; base += NW * RB)
-        attn_batch<GT, STEPS>(g, b, j, Tb, at.K, at.V, qv, qs, base, cnt, [&](int rr) { return sel[rr]; }, A);
-      attn_wave_reduce(A);
-      attn_block_merge(A, msm);
-      if (w == 0)
-        attn_store(A, nh, [&](int h) { return at.out + (int64_t(b) * g.Hq + h0 + h) * kAttnD; },
-                   [&](int h) { return at.lse + int64_t(b) * g.Hq + h0 + h; });
-      __syncthreads();                                  // msm is reused by the next head group
-    }
+    for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+    if (dl.counts && tid == 0) dl.counts[row] = out_base;
   }
 }
 
@@ -651,43 +588,10 @@ hipError_t launch_select_final(int rows, int H, int max_seq, const int32_t* seq_
   // are streamed from memory page by page
   if (int64_t(cur.nseg) * k <= kFinalDirect)
     hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
-                       cur, cur.nseg, idx, CandSegs{}, AttendArgs{}, dl);
+                       cur, cur.nseg, idx, CandSegs{}, dl);
   else
     hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
-                       cur, cur.nseg, idx, CandSegs{}, AttendArgs{}, dl);
-  return hipGetLastError();
-}
-
-bool select_attend_fused(int nseg, int k, int G) {
-  return !needs_merge(nseg, k) && k <= kAttendMaxK && G <= 16;
-}
-
-hipError_t launch_select_attend(const GqaDev& g, int k, CandSegs segs, const uint16_t* q, const uint16_t* K,
-                                const uint16_t* V, float scale, int32_t* idx, float* out, float* lse,
-                                hipStream_t st, DeltaArgs dl) {
-  if (segs.nseg > kMaxSeg || !select_attend_fused(segs.nseg, k, g.G)) return hipErrorInvalidValue;
-  const int rows = g.B * g.Hkv;
-  // Spread the row's query heads over hs blocks until the launch covers the
-  // CUs (256 blocks); the selection is repeated per block, the attention
-  // (the larger part) is split.
-  int hs = 1;
-  while (rows * hs < 256 && hs < g.G) ++hs;
-  const int hpb = (g.G + hs - 1) / hs;
-  hs = (g.G + hpb - 1) / hpb;
-  const AttendArgs aa{g, q, K, V, scale, out, lse, hs, hpb};
-  // query heads per pass over the selected rows: all of the block's heads
-  // when they are 1, 2 or 5 (or 10, 15), else 4 at a time
-  const int gt = hpb <= 2 ? hpb : (hpb % 5 == 0 ? 5 : 4);
-#define JSSA_FA(GT)                                                                                      \
-  hipLaunchKernelGGL((final_kernel<512, 16, false, GT>), dim3(rows * hs), dim3(512), 0, st, g.Hkv,         \
-                     g.max_seq, g.seq_lens, k, segs, segs.nseg, idx, CandSegs{}, aa, dl)
-  switch (gt) {
-    case 1: JSSA_FA(1); break;
-    case 2: JSSA_FA(2); break;
-    case 5: JSSA_FA(5); break;
-    default: JSSA_FA(4); break;
-  }
-#undef JSSA_FA
+                       cur, cur.nseg, idx, CandSegs{}, dl);
   return hipGetLastError();
 }
 
@@ -725,7 +629,7 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
     if (e != hipSuccess) return e;
     // about nwide * k candidates plus ties: the 12-per-thread final holds them
     hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
-                       segs, segs.nseg, idx, CandSegs{}, AttendArgs{}, DeltaArgs{});
+                       segs, segs.nseg, idx, CandSegs{}, DeltaArgs{});
     return hipGetLastError();
   }
   size_t main_bytes = 0;
