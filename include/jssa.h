@@ -175,6 +175,26 @@ JSSA_API jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, c
                                      void* stream);
 
 /*
+ * jssa_score_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, with the candidate lists in a static
+ * scratch array of the library instead of a caller workspace.
+ *  Arguments as jssa_score_topk without ws / ws_bytes.
+ *  Limit: shapes whose jssa_score_topk_workspace_size exceeds 16 MiB
+ *  (16 << 20 bytes) are rejected with JSSA_ERR_WORKSPACE, launching nothing;
+ *  128K tokens x B = 16 x Hkv = 8 at k = 256 needs about 8 MiB.
+ *  The call allocates nothing; the scratch array (16 MiB per GPU) exists from
+ *  library load to process exit, and its device address is looked up once
+ *  per GPU, on the first call made with that GPU current.
+ *  Every call on one GPU uses that GPU's one array: calls that overlap in
+ *  time on one GPU (different streams, or threads) race and give undefined
+ *  results. The array needs no clearing: each call writes every part of it
+ *  that it reads.
+ */
+JSSA_API jssa_status jssa_score_topk_noalloc(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                             int32_t k, float* scores, int32_t* idx, void* stream);
+
+/*
  * The two halves of jssa_score_topk, for callers that schedule or time them
  * separately. jssa_score_topk_chunks streams Kp once and leaves, per 8192-
  * token chunk of each (sequence, KV head) row, that chunk's candidates in

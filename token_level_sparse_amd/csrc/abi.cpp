@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "internal.hpp"
@@ -218,6 +219,62 @@ jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const floa
                                             static_cast<const uint16_t*>(Kp), k, scores, idx, segs,
                                             static_cast<char*>(ws) + main_bytes, S(stream)),
                     __func__);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// jssa_score_topk without a caller workspace: the candidate lists live in a
+// file-scope device array of this library (each GPU the library runs on
+// holds its own copy until the process ends). Host code never passes the
+// array's name to a kernel: its device address is taken once per device
+// with hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device.
+jssa_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(JSSA_ERR_UNSUPPORTED, "%s: device ordinal %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(JSSA_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return JSSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+jssa_status jssa_score_topk_noalloc(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
+                                   int32_t k, float* scores, int32_t* idx, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(idx);
+  REQUIRE_ALIGNED_OPT(scores);
+  if (need > kScratchBytes)
+    return fail(JSSA_ERR_WORKSPACE,
+                "%s: this shape needs %zu bytes of candidate lists, more than the %zu-byte static scratch; "
+                "use jssa_score_topk with a workspace",
+                __func__, need, kScratchBytes);
+  void* ws = nullptr;
+  if (jssa_status s = scratch_address(__func__, &ws)) return s;
+  return jssa_score_topk(desc, q, P, Kp, k, scores, idx, ws, kScratchBytes, stream);
 }
 
 jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,

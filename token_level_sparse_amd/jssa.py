@@ -27,7 +27,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR
 
 ENTRY_POINTS = (
     "jssa_append_kv", "jssa_project_keys", "jssa_score", "jssa_topk_workspace_size", "jssa_topk",
-    "jssa_score_topk_workspace_size", "jssa_score_topk", "jssa_score_topk_chunks", "jssa_score_topk_final",
+    "jssa_score_topk_workspace_size", "jssa_score_topk", "jssa_score_topk_noalloc", "jssa_score_topk_chunks",
+    "jssa_score_topk_final",
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
@@ -73,6 +74,7 @@ _SIGS = {
     "jssa_topk": [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
     "jssa_score_topk_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
     "jssa_score_topk": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
+    "jssa_score_topk_noalloc": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp],
     "jssa_score_topk_chunks": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
     "jssa_score_topk_final": [_P(GqaDesc), _i32, _vp, _sz, _vp, _vp],
     "jssa_score_topk_final_attend": [_P(GqaDesc), _i32, _vp, _sz, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp],
@@ -197,6 +199,11 @@ def jssa_score_topk(desc, q, P, Kp, k, scores, idx, ws, ws_bytes=None, stream=No
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.jssa_score_topk(ctypes.byref(desc), _p(q), _p(P), _p(Kp), k, _p(scores), _p(idx), _p(ws),
                                 ws_bytes, _s(stream)), "jssa_score_topk")
+
+
+def jssa_score_topk_noalloc(desc, q, P, Kp, k, scores, idx, stream=None):
+    _check(_lib.jssa_score_topk_noalloc(ctypes.byref(desc), _p(q), _p(P), _p(Kp), k, _p(scores), _p(idx),
+                                        _s(stream)), "jssa_score_topk_noalloc")
 
 
 def jssa_score_topk_chunks(desc, q, P, Kp, k, scores, ws, ws_bytes=None, stream=None):
