@@ -947,10 +947,13 @@ def test_calib_end_to_end_recall(J, PL):
 # ---------------------------------------------------------------------------
 # MLA
 # ---------------------------------------------------------------------------
-def test_mla_parity(J, PL):
-    cfg = replace(synth.MLA_DSV3, B=2, T=6000, k=512)
+@pytest.mark.parametrize("seed,B,T,k,S", [(5, 2, 6000, 512, 4), (1, 4, 4096, 2048, 16), (2, 4, 4096, 2048, 16),
+                                          (3, 4, 4096, 2048, 8), (7, 4, 4096, 2048, 16), (11, 4, 4096, 2048, 16),
+                                          (13, 4, 4096, 2048, 16)])
+def test_mla_parity(J, PL, seed, B, T, k, S):
+    cfg = replace(synth.MLA_DSV3, B=B, T=T, k=k, seed=seed)
     inp = synth.make_mla(cfg)
-    st = PL.MlaStep(inp, S=4)
+    st = PL.MlaStep(inp, S=S)
     st.project()
     torch.cuda.synchronize()
     Kp = _np(st.Kp)

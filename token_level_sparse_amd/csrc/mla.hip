@@ -8,8 +8,9 @@
 // 576-dim dot per (head, token) and the output into W_uv[h] (sum_t p_t c_t).
 // All heads share the latent rows, so with 128 heads the per-token work is a
 // genuine dense contraction: QK^T and PV run on bf16 MFMA (gfx950
-// v_mfma_f32_16x16x32_bf16). The query enters QK^T as a hi + lo pair of bf16
-// (two MFMAs) so the logits keep ~fp32 accuracy.
+// v_mfma_f32_16x16x32_bf16). The query enters QK^T, and the softmax weights
+// enter PV, as hi + lo pairs of bf16 (two MFMAs each), so logits and weighted
+// sums keep ~fp32 accuracy.
 #include "internal.hpp"
 
 namespace jssa {
@@ -377,14 +378,24 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
     for (int t = 0; t < 32; ++t) {
       O[t][0] *= ar[0]; O[t][1] *= ar[1]; O[t][2] *= ar[2]; O[t][3] *= ar[3];
     }
-    bf16x8 pa;
+    // The weights enter PV as a hi + lo pair of bf16 (two MFMAs), like the
+    // query in QK^T: p = hi + lo to about 2^-16 relative, so the weighted sum
+    // matches the fp32 denominator lrun instead of carrying bf16 rounding
+    // (2^-9 relative per weight).
+    bf16x8 pa, pl;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pa[i] = __bf16(p[i]);
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = __bf16(p[i]);
+      pa[i] = h;
+      pl[i] = __bf16(p[i] - float(h));
+    }
     wave_lds_sync();
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const u32x4 vraw = *reinterpret_cast<const u32x4*>(&Vt[(t * 16 + n) * kVtStride + 8 * g]);
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vraw), O[t], 0, 0, 0);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, vraw);
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[t], 0, 0, 0);
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, O[t], 0, 0, 0);
     }
     wave_lds_sync();
   }
