@@ -327,6 +327,24 @@ def test_score_topk_fused_equals_split(J, PL, case):
     np.testing.assert_array_equal(_np(h.idx), _np(a.idx))
     np.testing.assert_array_equal(_np(b.scores), _np(a.scores))
     np.testing.assert_array_equal(_np(h.scores), _np(a.scores))
+    # the tie-heavy and full-chunk cases also against the oracle's own
+    # selection, computed from its own (identically edited) projected keys
+    if case in ("full_k256_ties", "full_all_equal", "paged_full_invalid", "clustered_full_k256", "full_k64"):
+        if case == "paged_full_invalid":
+            inp.page_table = table
+        idx = _np(a.idx)
+        for bb in range(inp.cfg.B):
+            for j in range(inp.cfg.Hkv):
+                K, V, Kp, s_, hs = U.oracle_unit(inp, bb, j)
+                if case == "full_k256_ties":
+                    Kp = Kp[np.arange(Kp.shape[0]) % 37]
+                elif case == "full_all_equal":
+                    Kp = np.zeros_like(Kp)
+                if case in ("full_k256_ties", "full_all_equal"):
+                    s_ = O.subspace_scores(inp.q[bb, hs], inp.P[j], Kp)
+                U.check_indices(idx[bb, j], s_, k)
+                if case == "full_all_equal":          # all scores tie: the k lowest indices
+                    np.testing.assert_array_equal(idx[bb, j], np.arange(k))
 
 
 @pytest.mark.parametrize("case", ["no_seq_lens", "b65_ragged", "b64_ragged"])
@@ -985,9 +1003,10 @@ def test_mla_parity(J, PL, seed, B, T, k, S):
 def test_full_size_128k_b16_sampled(J, PL):
     """The 128K x B=16 workload in the launch configuration the benchmark
     times (fused chunk pass, then final selection + attention at one split),
-    checked on sampled units against the oracle and everywhere for the
-    properties that hold at any size; the separate entry points must give
-    the same indices."""
+    checked on all 128 (sequence, KV head) units against the oracle
+    (indices, outputs, log-sum-exps, sampled projected-key rows) and
+    everywhere for the properties that hold at any size; the separate entry
+    points must give the same indices."""
     cfg = synth.BATCHED_128K
     inp = synth.make_gqa(cfg)
     c = PL.GqaCache(inp)
@@ -1004,11 +1023,19 @@ def test_full_size_128k_b16_sampled(J, PL):
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     rng = np.random.default_rng(0)
     rows = rng.choice(cfg.T, 2048, replace=False)
-    for b, j in [(0, 0), (3, 5), (7, 2), (12, 7), (15, 1)]:
+    kp_rows = _np(c.Kp[:, :, torch.from_numpy(rows).cuda()])
+
+    def unit(bj):
+        b, j = bj
         K, V, Kp, s, hs = U.oracle_unit(inp, b, j)
-        np.testing.assert_array_equal(_np(c.Kp[b, j, torch.from_numpy(rows).cuda()]), Kp[rows])
-        U.check_indices(idx[b, j], s, cfg.k)
+        np.testing.assert_array_equal(kp_rows[b, j], Kp[rows])
+        swaps = U.check_indices(idx[b, j], s, cfg.k)
         U.check_attention(inp, b, j, hs, K, V, idx[b, j], out, lse, c.scale)
+        return swaps
+    # every (sequence, KV head) unit of the step against the oracle
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(unit, [(b, j) for b in range(cfg.B) for j in range(cfg.Hkv)]))
 
 
 def test_full_size_128k_b16_extensions_sampled(J, PL):

@@ -17,7 +17,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libjssa.so")
+# JSSA_LIBRARY names another build of the same library (the host-sanitizer
+# build of the test suite); by default the in-tree libjssa.so
+LIB_PATH = os.environ.get("JSSA_LIBRARY") or os.path.join(_HERE, "libjssa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m token_level_sparse_amd.build`")
