@@ -203,9 +203,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   }
   // Screening (SCREEN, a separate instantiation: the plain stream carries
   // none of this): the chunk's 128 tiles of 64 tokens have one keep bit
-  // each. A dropped tile's loads still go out (no branch) but read the
-  // chunk's first tile again, a cache hit, so the tile costs no HBM bytes;
-  // its tokens are staged as dropped.
+  // each. A wave streams only its kept tiles; its dropped tiles are staged
+  // as dropped and cost no HBM bytes.
   uint32_t kw[4] = {~0u, ~0u, ~0u, ~0u};
   if (SCREEN) {
     const uint32_t* kp = fo.keep + int64_t(b * g.Hkv + j) * fo.keep_words;
@@ -220,14 +219,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
     return;
   }
-  auto dropped = [&](int tile) -> bool {            // wave-uniform
-    const int ct = tile * kWaves + w;
-    if (!SCREEN || ct >= 128) return false;
-    const uint32_t word = ct < 32 ? kw[0] : (ct < 64 ? kw[1] : (ct < 96 ? kw[2] : kw[3]));
-    return ((word >> (ct & 31)) & 1u) == 0u;
-  };
   auto load_tile = [&](int tile, u32x4 (&buf)[PP]) {
-    const int t0 = t_begin + (dropped(tile) ? 0 : (tile * kWaves + w) * 64);
+    const int t0 = t_begin + (tile * kWaves + w) * 64;
 #pragma unroll
     for (int m = 0; m < PP; ++m) {
       const int p = m * 64 + lane;
@@ -256,7 +249,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   int nkept = TPW, klist = 0;
   uint32_t kmask = 0u;
   if constexpr (SCREEN) {
-    const bool kb = lane < TPW && !dropped(lane);
+    // lane l < TPW: is tile l of this wave (chunk tile l * kWaves + w) kept?
+    const int ct = lane * kWaves + w;
+    const uint32_t word = ct < 32 ? kw[0] : (ct < 64 ? kw[1] : (ct < 96 ? kw[2] : kw[3]));
+    const bool kb = lane < TPW && ((word >> (ct & 31)) & 1u) != 0u;
     kmask = uint32_t(__ballot(kb));
     nkept = __builtin_popcount(kmask);
     const int rank = __builtin_popcount(kmask & ((1u << (lane & 31)) - 1u));
@@ -277,6 +273,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
 #pragma unroll
       for (int u = 0; u < kDepth - 1; ++u) load_tile(kept_tile(u), bufs[u]);
     }
+    // keep the scheduler from moving the prologue's arithmetic (which waits
+    // for the query values) above these loads
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- prologue: qp = P_j^T qbar (fp32). The slice of P this thread needs
@@ -297,9 +296,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
         pv[ii] = Pj[(i < kD ? i : kD - 1) * R + c];   // unconditional load, zero weight past d
       }
     }
-    uint16_t qh[kMaxG];                        // column tid of the group's query rows
-    if (tid < kD) {
-      const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + tid;
+    // column tid of the group's query rows, loaded by every thread (column 0
+    // past d, unused): loads under a branch would make the compiler wait for
+    // them before issuing the tiles' loads
+    uint16_t qh[kMaxG];
+    {
+      const uint16_t* qg = q + (int64_t(b) * g.Hq + int64_t(j) * g.G) * kD + (tid < kD ? tid : 0);
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) qh[h] = qg[(h < g.G ? h : g.G - 1) * kD];   // clamped: a valid row
     }
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     const int off = (tile * kWaves + w) * 64;
     const float x = tile_scores(buf);
     const float v = token_ok(t_begin + off + lane) ? x : -__builtin_inff();
-    stage[sidx(off + lane)] = (SCREEN && dropped(tile)) ? __uint_as_float(kDroppedBits) : v;
+    stage[sidx(off + lane)] = v;
   };
   // kDepth register buffers rotate with no copies between them (a copy of a
   // buffer whose loads are in flight would wait for them): while one tile's
