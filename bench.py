@@ -628,11 +628,8 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
     def absorb():
         jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.P, st.q_abs, st.q_sel, stream)
 
-    def score():
-        jssa.jssa_mla_score(st.desc, st.q_sel, st.Kp, st.scores, stream)
-
-    def topk():
-        jssa.jssa_topk(c.B, 1, c.T, st.seq_lens, st.scores, st.k, st.idx, st.ws, None, stream)
+    def score_topk():
+        jssa.jssa_mla_score_topk(st.desc, st.q_sel, st.Kp, st.k, st.scores, st.idx, st.ws, None, stream)
 
     def attend():
         jssa.jssa_mla_indexed_decode(st.desc, st.q_abs, st.latent, st.idx, st.k, st.S, st.scale, st.part_o,
@@ -645,10 +642,10 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
         jssa.jssa_mla_up_v(st.desc, st.o_lat, st.W_uv, st.out, stream)
 
     flush = Flush(torch)
-    fns = [absorb, score, topk, attend, combine, up]
+    fns = [absorb, score_topk, attend, combine, up]
     step_us, _ = time_steps(fns, args.steps, args.warmup, torch, stream, flush=flush)
     us = [float(np.median(x)) for x in time_stages(fns, args.steps, torch, stream, flush=flush)]
-    names = ["absorb", "score", "topk", "indexed_mfma", "combine", "up_v"]
+    names = ["absorb", "score_topk", "indexed_mfma", "combine", "up_v"]
     total = float(np.median(step_us)) * 1e-6 * args.steps
     steps_s = args.steps / total
     core_flops = 2 * c.B * c.H * c.k * (2 * c.d_c + c.d_latent)       # QK^T (hi+lo) + PV
@@ -659,7 +656,7 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
            "config": {"workload": c.name, "B": c.B, "H": c.H, "T": c.T, "r": c.r, "k": c.k, "S": S},
            "step_us": summary(step_us), "timed_as": "median of flushed per-step HIP event times",
            "stages_us": {n: round(u, 2) for n, u in zip(names, us)},
-           "indexed_mfma_TFLOP_s": round(core_flops / (us[3] * 1e-6) / 1e12, 2)}
+           "indexed_mfma_TFLOP_s": round(core_flops / (us[2] * 1e-6) / 1e12, 2)}
     print(json.dumps(res), flush=True)
 
 

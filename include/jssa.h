@@ -328,6 +328,24 @@ JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_se
                            float* scores, void* stream);
 
 /*
+ * jssa_mla_score followed by the latent top-k (jssa_topk with H = 1): the same
+ * scores and the same idx [B,k], in fewer and cheaper passes (per sequence
+ * one selection over the shared latent cache, digest Perspective; ties and
+ * absent tokens as jssa_topk). The score stream also records, per
+ * 1024-token chunk, a key that a known number of the chunk's tokens reach;
+ * when the chunks of a sequence together guarantee k tokens at or above the
+ * smallest such key, no token below it can be selected and the top-k pass
+ * keeps only the tokens above it. The selection is exact either way.
+ *  k in [1, min(4096, max_seq)]; scores device fp32 [B,max_seq] (written),
+ *  idx device int32 [B,k] (written); ws device, at least
+ *  jssa_mla_score_topk_workspace_size bytes, its contents scratch.
+ */
+JSSA_API jssa_status jssa_mla_score_topk_workspace_size(const jssa_mla_desc* desc, int32_t k, size_t* bytes);
+JSSA_API jssa_status jssa_mla_score_topk(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat,
+                                int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * MLA attention over the selected latent rows, read in place (bf16 MFMA):
  * logits = scale * q_abs[b,h] . latent[b,t] (all d_c dims), values are
  * latent[b,t,:d_latent]. idx device int32 [B,k] (jssa_topk with H = 1).

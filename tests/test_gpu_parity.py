@@ -996,6 +996,61 @@ def test_mla_parity(J, PL, seed, B, T, k, S):
         U.check_close(lse[b], l, what=f"mla lse b={b}")
 
 
+_MLA_TOPK_CASES = [
+    # name, B, max_seq, k, lengths (None: all max_seq), kind
+    ("full_128k", 4, 131072, 2048, None, "random"),
+    ("ragged", 4, 131072, 2048, [131072, 100003, 5000, 1], "random"),
+    ("unaligned_rows", 3, 70001, 1000, [70001, 69999, 40000], "random"),
+    ("clustered", 2, 65536, 1024, None, "clustered"),
+    ("all_tied", 2, 32768, 512, None, "tied"),
+    ("small_k", 2, 131072, 64, None, "random"),
+    ("k_4096", 1, 131072, 4096, None, "random"),
+    ("no_bound_path", 2, 4096, 2048, None, "random"),
+]
+
+
+@pytest.mark.parametrize("case", _MLA_TOPK_CASES, ids=[c[0] for c in _MLA_TOPK_CASES])
+def test_mla_score_topk_matches_separate_passes(J, case):
+    """jssa_mla_score_topk (score stream with chunk bounds, floored top-k)
+    against jssa_mla_score + jssa_topk on the same inputs: identical scores
+    and identical indices, and the indices equal the oracle's selection on
+    those scores. Covers the bounded path (full, ragged, unaligned rows,
+    clustered top tokens, every score tied, k = 64 and 4096) and the plain
+    path (too few chunks for a bound)."""
+    name, B, T, k, lens, kind = case
+    r, H = 64, 128
+    rng = np.random.default_rng(sum(map(ord, name)))
+    qsel = rng.standard_normal((B, r)).astype(np.float32)
+    if kind == "tied":
+        kp = np.zeros((B, T, r), np.float32)            # every score 0: the lowest indices win
+    else:
+        kp = rng.standard_normal((B, T, r)).astype(np.float32)
+        if kind == "clustered":                         # 600 near-identical top tokens in two chunks
+            kp[:, 3000:3600] = 4.0 * qsel[:, None, :] + 0.01 * rng.standard_normal((B, 600, r))
+    kp_bits = synth.f32_to_bf16_bits(kp).view(np.int16)
+    lens_np = np.full(B, T, np.int32) if lens is None else np.asarray(lens, np.int32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q_t, kp_t, sl = dev(qsel), dev(kp_bits), dev(lens_np)
+    desc = J.mla_desc(B, H, r, T, seq_lens=sl)
+    s1 = torch.empty((B, T), dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    i1 = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    i2 = torch.empty_like(i1)
+    ws1 = torch.empty(max(J.jssa_mla_score_topk_workspace_size(desc, k), 16), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(max(J.jssa_topk_workspace_size(B, 1, T, k), 16), dtype=torch.uint8, device="cuda")
+    print(f"[case] mla score_topk {name} B={B} T={T} k={k}", flush=True)
+    J.jssa_mla_score_topk(desc, q_t, kp_t, k, s1, i1, ws1)
+    J.jssa_mla_score(desc, q_t, kp_t, s2)
+    J.jssa_topk(B, 1, T, sl, s2, k, i2, ws2)
+    torch.cuda.synchronize()
+    sc1, sc2 = _np(s1), _np(s2)
+    np.testing.assert_array_equal(sc1.view(np.uint32), sc2.view(np.uint32))
+    np.testing.assert_array_equal(_np(i1), _np(i2))
+    for b in range(B):
+        n = int(lens_np[b])
+        np.testing.assert_array_equal(_np(i1)[b], O.select_topk(sc1[b, :n].astype(np.float64), k))
+
+
 # ---------------------------------------------------------------------------
 # full size: the 128K x B=16 workload in the launch configuration the
 # benchmark times; sampled units against the oracle, properties everywhere

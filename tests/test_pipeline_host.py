@@ -13,6 +13,19 @@ def test_one_split_up_to_512(k):
 
 
 @pytest.mark.parametrize("k,units,want", [
+    (256, 128, 2),     # 128K, B = 16, attention launched on its own: 256 blocks
+    (256, 64, 4),
+    (512, 16, 8),
+    (64, 128, 1),      # 64 rows cannot be split further
+    (100, 512, 1),     # the pairs alone fill the CUs
+])
+def test_unfused_attention_up_to_512_fills_the_cus(k, units, want):
+    s = default_splits(k, units, attend_fused=False)
+    assert s == want
+    assert s == 1 or (s * units <= 256 and k // s >= 64)
+
+
+@pytest.mark.parametrize("k,units,want", [
     (2048, 64, 4),     # paged Qwen: 8 sequences x 8 KV heads
     (1024, 64, 4),
     (2048, 32, 8),     # 128K, B = 4

@@ -424,6 +424,59 @@ jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const 
                     __func__);
 }
 
+namespace {
+// Selection over the latent rows with chunk bounds: each stream chunk of a
+// row reports a key that 4 * cw of its tokens reach (cw per wave), and the
+// chunks of a row together must cover k for that key to bound the row's
+// k-th key from below. Used while that needs at most 16 per wave.
+int mla_bound_cw(int max_seq, int k) {
+  const int nb = jssa::mla_score_chunks(max_seq);
+  const int c = (k + nb - 1) / nb;               // tokens per chunk
+  const int cw = (c + 3) / 4;                    // per wave
+  return cw <= 16 ? cw : 0;
+}
+}  // namespace
+
+jssa_status jssa_mla_score_topk_workspace_size(const jssa_mla_desc* desc, int32_t k, size_t* bytes) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  size_t plain = 0;
+  if (jssa_status s = jssa_topk_workspace_size(desc->B, 1, desc->max_seq, k, &plain)) return s;
+  const size_t nb = size_t(jssa::mla_score_chunks(desc->max_seq));
+  const size_t floored = jssa::align256(size_t(desc->B) * nb * sizeof(uint32_t)) +
+                         jssa::topk_floor_workspace_bytes(desc->B, desc->max_seq, k);
+  *bytes = mla_bound_cw(desc->max_seq, k) ? floored : plain;
+  return JSSA_OK;
+}
+
+jssa_status jssa_mla_score_topk(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat, int32_t k,
+                                float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  if (jssa_status s = jssa_mla_score_topk_workspace_size(desc, k, &need)) return s;
+  REQUIRE_PTR(q_sel); REQUIRE_PTR(Kp_lat); REQUIRE_PTR(scores); REQUIRE_PTR(idx);
+  REQUIRE_ALIGNED_OPT(desc->seq_lens);
+  if (need > 0) REQUIRE_PTR(ws);
+  if (ws_bytes < need)
+    return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  const jssa::MlaDev m = to_mla(desc);
+  const auto* Kp = static_cast<const uint16_t*>(Kp_lat);
+  const hipStream_t st = S(stream);
+  const int cw = mla_bound_cw(desc->max_seq, k);
+  hipError_t e;
+  if (cw == 0) {
+    e = jssa::launch_mla_score(m, q_sel, Kp, scores, st);
+    if (e == hipSuccess) e = jssa::launch_topk(desc->B, 1, desc->max_seq, desc->seq_lens, scores, k, idx, ws, st);
+  } else {
+    const int nb = jssa::mla_score_chunks(desc->max_seq);
+    auto* bounds = static_cast<uint32_t*>(ws);
+    void* rest = static_cast<char*>(ws) + jssa::align256(size_t(desc->B) * nb * sizeof(uint32_t));
+    e = jssa::launch_mla_score(m, q_sel, Kp, scores, st, bounds, cw);
+    if (e == hipSuccess)
+      e = jssa::launch_topk_floor(desc->B, 1, desc->max_seq, desc->seq_lens, scores, k, idx, rest, bounds, nb,
+                                  4 * cw, st);
+  }
+  return hip_status(e, __func__);
+}
+
 jssa_status jssa_mla_indexed_decode(const jssa_mla_desc* desc, const float* q_abs,
                                     const void* latent, const int32_t* idx, int32_t k, int32_t S_,
                                     float scale, float* part_o, float* part_lse, void* stream) {

@@ -41,6 +41,11 @@ hipError_t launch_screen(const GqaDev& g, const uint16_t* q, const float* P, con
                          int32_t* kept_tiles, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
+// Top-k of rows whose stream also wrote per-chunk bounds ([rows, nb], keys
+// reached by at least bound_c tokens of the chunk, or 0xffffffff).
+size_t topk_floor_workspace_bytes(int rows, int max_seq, int k);
+hipError_t launch_topk_floor(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+                             int32_t* idx, void* ws, const uint32_t* bounds, int nb, int bound_c, hipStream_t st);
 
 hipError_t launch_indexed(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                           const int32_t* idx, int k, int S, float scale, float* part_o,
@@ -75,8 +80,11 @@ hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const flo
                               uint16_t* Kp, hipStream_t st);
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
                              const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st);
+// bound (optional, [B, mla_score_chunks(max_seq)]): per chunk of the stream
+// a key reached by at least 4 * bound_cw of its tokens, or 0xffffffff
 hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
-                            hipStream_t st);
+                            hipStream_t st, uint32_t* bound = nullptr, int bound_cw = 0);
+int mla_score_chunks(int max_seq);
 hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_t* latent,
                               const int32_t* idx, int k, int S, float scale, float* part_o,
                               float* part_lse, hipStream_t st);

@@ -83,10 +83,17 @@ struct FusedOut {
   int n_sink, n_local;      // sink tokens: t < n_sink; local tokens: t >= T_b - n_local
   const uint32_t* keep;     // screening: one bit per 64-token tile ([rows, keep_words]); nullptr: all kept
   int keep_words;
+  // score-only stream: per chunk a key that at least 4 * bound_cw of the
+  // chunk's tokens reach ([rows, chunks]; kNoBound: no such guarantee), or
+  // nullptr
+  uint32_t* bound;
+  int bound_cw;
 };
 // A token of a dropped tile is staged with this value: a NaN whose score_key
 // is 0, the key of no token (finite scores map to keys above 0).
 constexpr uint32_t kDroppedBits = 0xffffffffu;
+// A chunk bound that guarantees nothing (no token key reaches it).
+constexpr uint32_t kNoBound = 0xffffffffu;
 
 template <int R>
 struct ScoreSmem {
@@ -185,6 +192,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
       if (fo.pmax) fo.pmax[seg] = 0u;
     }
+    if (!FUSED && fo.bound && tid == 0) fo.bound[int64_t(b * g.Hkv + j) * gridDim.x + cx] = kNoBound;
     return;
   }
   // Tokens of this block are [t_begin, tend); loads of later positions are
@@ -424,6 +432,42 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       for (int i = tid; i < chunk && i < lim; i += NT) dst[i] = stage[sidx(i)];
     }
   }
+  if constexpr (!FUSED) {
+    if (fo.bound) {                                      // block-uniform
+      // Lower bound for the row's top-k threshold: thread i's largest key
+      // over its tokens i + NT e; each wave's bound_cw-th largest of those
+      // (distinct threads, so distinct tokens: bound_cw tokens reach it);
+      // the block's bound is the smallest over the waves, reached by
+      // kWaves * bound_cw tokens. A wave with fewer threads holding a token
+      // gives no guarantee (kNoBound).
+      __shared__ uint32_t wb[kWaves];
+      uint32_t v = 0u;
+#pragma unroll
+      for (int e = 0; e < TPW; ++e) {
+        const uint32_t x = score_key(stage[sidx(tid + NT * e)]);
+        v = x > v ? x : v;
+      }
+      uint32_t kth = 0u;
+      for (int i = 0; i < fo.bound_cw; ++i) {
+        const uint32_t mx = wave_max_u32(v);
+        kth = mx;
+        const uint64_t at = __ballot(v == mx);            // one lane holding it drops out
+        if (lane == int(__builtin_ctzll(at))) v = 0u;
+      }
+      if (lane == 0) wb[w] = kth;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t bd = 0xffffffffu;
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          ok = ok && wb[i] != 0u;
+          bd = wb[i] < bd ? wb[i] : bd;
+        }
+        fo.bound[int64_t(b * g.Hkv + j) * gridDim.x + cx] = ok ? bd : kNoBound;
+      }
+    }
+  }
   if constexpr (FUSED) {
     if (fo.pmax) {                                       // top-delta pseudo-max contribution of this chunk
       const int e1 = fo.n_sink < tend ? fo.n_sink : tend;
@@ -497,7 +541,7 @@ hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, cons
 }
 
 hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
-                            hipStream_t st) {
+                            hipStream_t st, uint32_t* bound, int bound_cw) {
   GqaDev g{};
   g.B = m.B;
   g.Hq = 1;
@@ -507,7 +551,15 @@ hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t*
   g.r = m.r;
   g.max_seq = m.max_seq;
   g.seq_lens = m.seq_lens;
-  return launch_score_t<kMla, false>(g, nullptr, q_sel, nullptr, Kp, scores, st, FusedOut{});
+  FusedOut fo{};
+  fo.bound = bound;
+  fo.bound_cw = bound_cw;
+  return launch_score_t<kMla, false>(g, nullptr, q_sel, nullptr, Kp, scores, st, fo);
+}
+
+int mla_score_chunks(int max_seq) {
+  const int chunk = kWaves * 64 * kMlaTiles;
+  return (max_seq + chunk - 1) / chunk;
 }
 
 int score_topk_segments(int max_seq) {

@@ -113,7 +113,7 @@ template <int NT, int E>
 struct ChunkSmem {
   uint32_t hist[kSelBins];
   ScanSmem<NT> scan;
-  uint32_t red[4][NT / 64];
+  uint32_t red[5][NT / 64];
   int res[2];
 };
 
@@ -139,26 +139,33 @@ constexpr int kSelSlack = 32;
 template <int NT, int E>
 __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n, int k, ChunkSmem<NT, E>& sm,
                              CandSegs out, int64_t seg) {
+  static_assert(E <= 32, "one mask bit per key");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  auto real = [&](int e) { return base + tid * E + e < lim; };
   // key 0 (no token: past the row, behind an invalid page, or a dropped
   // tile of a screened chunk) takes no part in the bounds or the
   // histograms; thousands of them in one bin would serialize its atomics.
-  // Every caller gives positions at or past lim the key 0 as well.
-  auto cand = [&](int e) { return real(e) && key[e] != 0u; };
+  // Every caller gives positions at or past lim the key 0 as well. The
+  // candidates (real tokens with a key) are one bit each of cmask, built
+  // without branches: per-key branches would cost exec-mask changes and
+  // spilled lane masks for every key.
+  const int nreal = lim - (base + tid * E);      // keys e < nreal are real tokens
+  uint32_t cmask = 0u;
+  uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool c = e < nreal && key[e] != 0u;
+    cmask |= c ? (1u << e) : 0u;
+    const uint32_t x = c ? key[e] : 0u;          // (0: no effect on m1, m2)
+    m2 = x > m1 ? m1 : (x > m2 ? x : m2);
+    m1 = x > m1 ? x : m1;
+    tmin = c && x < tmin ? x : tmin;
+  }
+  auto cand = [&](int e) { return ((cmask >> e) & 1u) != 0u; };
+  uint32_t nc = uint32_t(__builtin_popcount(cmask));
   const bool keep_all = n <= k;
   const bool full = n == NT * E;
   uint32_t thr = 0;                          // keep real keys >= thr
-  uint32_t m1 = 0u, m2 = 0u, tmin = 0xffffffffu;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (cand(e)) {
-      const uint32_t x = key[e];
-      m2 = x > m1 ? m1 : (x > m2 ? x : m2);
-      m1 = x > m1 ? x : m1;
-      tmin = x < tmin ? x : tmin;
-    }
   uint32_t bound2 = 0u;                      // the wave's r-th largest m2 (0: not usable)
   const int r = (k + 2 * NW - 1) / (2 * NW);
   if (!keep_all && full && r <= 64) {
@@ -177,24 +184,30 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
     mnmx = c < mnmx ? c : mnmx;
     mn = d < mn ? d : mn;
   }
+  nc = wave_sum_u32(nc);
   if (lane == 0) {
     sm.red[0][wv] = mx;
     sm.red[1][wv] = mnmx;
     sm.red[2][wv] = mn;
     sm.red[3][wv] = bound2;
+    sm.red[4][wv] = nc;
   }
   if (!keep_all)
     for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
   __syncthreads();
   uint32_t hi = sm.red[0][0], lo_full = sm.red[1][0], lo_any = sm.red[2][0], lo2 = sm.red[3][0];
+  uint32_t ncand = sm.red[4][0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) {
     hi = sm.red[0][i] > hi ? sm.red[0][i] : hi;
     lo_full = sm.red[1][i] < lo_full ? sm.red[1][i] : lo_full;
     lo_any = sm.red[2][i] < lo_any ? sm.red[2][i] : lo_any;
     lo2 = sm.red[3][i] < lo2 ? sm.red[3][i] : lo2;
+    ncand += sm.red[4][i];
   }
-  if (!keep_all) {
+  // at most k candidates (absent tokens and keys under a row floor do not
+  // count): every one of them is kept, no threshold to find
+  if (!keep_all && int(ncand) > k) {
     uint32_t lo = lo_any;
     if (full && k <= NT) lo = lo_full > lo ? lo_full : lo;
     if (full && r <= 64) lo = lo2 > lo ? lo2 : lo;

@@ -46,8 +46,16 @@ __device__ __forceinline__ int row_len(int max_seq, const int32_t* seq_lens, int
 // the key of no token.
 constexpr uint32_t kNoTokenBits = 0xffffffffu;
 
+// bounds (optional, [rows, nb]): per chunk of the score stream a key that at
+// least bound_c of its tokens reach, or kNoBound. With P chunks of a row
+// giving a bound and P * bound_c >= k, the row's k-th largest key is at or
+// above the smallest of those bounds, so every key below it is dropped here
+// (taken as no token): the row keeps few candidates however large k is.
+constexpr uint32_t kNoBound = 0xffffffffu;
+
 __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
-                                                    const float* __restrict__ scores, int k, CandSegs segs) {
+                                                    const float* __restrict__ scores, int k, CandSegs segs,
+                                                    const uint32_t* __restrict__ bounds, int nb, int bound_c) {
   // The chunk's scores go through LDS: loaded 16 bytes per lane (coalesced),
   // staged so that thread i then reads its kCE consecutive tokens
   // o = i*kCE + e at e*SS + i (token o sits at (o % kCE)*SS + o / kCE; the
@@ -73,6 +81,36 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
     if (tid == 0) write_info(segs, seg, 0, 0u, 0u, 0xffffffffu);
     return;
   }
+  // the row's floor from the stream's chunk bounds (computed while the
+  // chunk's score loads are in flight)
+  uint32_t floor = 0u;                           // keys below it cannot be in the row's top k
+  auto row_floor = [&]() {
+    if (!bounds) return;                         // kernel-uniform
+    __shared__ uint32_t fr[2][kCT / 64];
+    const int lane = tid & 63, wv = tid >> 6;
+    uint32_t mn = kNoBound, cnt = 0u;
+    for (int i = tid; i < nb; i += kCT) {
+      const uint32_t v = bounds[int64_t(row) * nb + i];
+      if (v != kNoBound) {
+        mn = v < mn ? v : mn;
+        ++cnt;
+      }
+    }
+    mn = wave_min_u32(mn);
+    cnt = wave_sum_u32(cnt);
+    if (lane == 0) {
+      fr[0][wv] = mn;
+      fr[1][wv] = cnt;
+    }
+    __syncthreads();
+    uint32_t m2 = kNoBound, c2 = 0u;
+#pragma unroll
+    for (int i = 0; i < kCT / 64; ++i) {
+      m2 = fr[0][i] < m2 ? fr[0][i] : m2;
+      c2 += fr[1][i];
+    }
+    floor = int64_t(c2) * bound_c >= k ? m2 : 0u;
+  };
   float* stage = reinterpret_cast<float*>(sbuf);
   auto sidx = [](int o) { return (o % kCE) * SS + o / kCE; };
   const float none = __uint_as_float(kNoTokenBits);
@@ -86,6 +124,7 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
       const int o = (i * kCT + tid) * 4;
       v[i] = *reinterpret_cast<const f32x4*>(src + (o < lim ? o : lim - 4));
     }
+    row_floor();
 #pragma unroll
     for (int i = 0; i < kCE / 4; ++i) {
       const int o = (i * kCT + tid) * 4;
@@ -101,6 +140,7 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
       const int o = i * kCT + tid;
       v[i] = src[o < n ? o : n - 1];
     }
+    row_floor();
 #pragma unroll
     for (int i = 0; i < kCE; ++i) {
       const int o = i * kCT + tid;
@@ -110,10 +150,15 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
   __syncthreads();
   uint32_t key[kCE];
 #pragma unroll
-  for (int e = 0; e < kCE; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*kCE + e
-  // the top-two bound first (block-uniform; it leaves the stage intact),
-  // the histogram select when it does not apply or keeps too many
-  const bool done = n == kChunk && k <= kCT && chunk_select_top2<kCT, kCE>(key, start, k, tsm, stage, SS, segs, seg);
+  for (int e = 0; e < kCE; ++e) {                // token tid*kCE + e
+    const uint32_t x = score_key(stage[e * SS + tid]);
+    key[e] = x >= floor ? x : 0u;
+  }
+  // the top-two bound first (block-uniform; it leaves the stage intact and
+  // reads it, so not with a floor), the histogram select when it does not
+  // apply or keeps too many
+  const bool done = n == kChunk && k <= kCT && floor == 0u &&
+                    chunk_select_top2<kCT, kCE>(key, start, k, tsm, stage, SS, segs, seg);
   if (!done) {
     __syncthreads();                             // the stage is reused below
     ChunkSmem<kCT, kCE>& csm = *reinterpret_cast<ChunkSmem<kCT, kCE>*>(sbuf);
@@ -634,10 +679,39 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
   }
   size_t main_bytes = 0;
   CandSegs segs = carve_segs(wsp, rows, nchunks, seg_cap(k, kChunk), &main_bytes);
-  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
+  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs,
+                     nullptr, 0, 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, static_cast<char*>(wsp) + main_bytes, st);
+}
+
+size_t topk_floor_workspace_bytes(int rows, int max_seq, int k) {
+  size_t total = 0;
+  carve_segs(nullptr, rows, chunks_of(max_seq), seg_cap(k, kChunk), &total);
+  return total;
+}
+
+// Top-k of score rows with per-chunk bounds of the stream that wrote them
+// (see chunk_kernel): the chunk pass keeps only keys at or above the row's
+// floor, and the final pass reads the lists directly, however many segments
+// (a list longer than its registers is read from memory level by level:
+// slower, same result).
+hipError_t launch_topk_floor(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+                             int32_t* idx, void* wsp, const uint32_t* bounds, int nb, int bound_c, hipStream_t st) {
+  const int rows = B * H;
+  const int nchunks = chunks_of(max_seq);
+  if (nchunks > kMaxSeg) return hipErrorInvalidValue;
+  CandSegs segs = carve_segs(wsp, rows, nchunks, seg_cap(k, kChunk), nullptr);
+  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs,
+                     bounds, nb, bound_c);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // (a floored row keeps about 2k candidates: 512 direct slots per segment of
+  // a 16-segment row hold them; a longer list is read from memory)
+  hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs,
+                     segs.nseg, idx, CandSegs{}, DeltaArgs{});
+  return hipGetLastError();
 }
 
 }  // namespace jssa

@@ -33,7 +33,8 @@ ENTRY_POINTS = (
     "jssa_score_topk_final",
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
-    "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_indexed_decode",
+    "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_score_topk_workspace_size",
+    "jssa_mla_score_topk", "jssa_mla_indexed_decode",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
     "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_update_tile_bounds",
     "jssa_score_topk_screened_workspace_size",
@@ -87,6 +88,8 @@ _SIGS = {
     "jssa_mla_project_latent": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_mla_absorb_q": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp],
+    "jssa_mla_score_topk_workspace_size": [_P(MlaDesc), _i32, _P(_sz)],
+    "jssa_mla_score_topk": [_P(MlaDesc), _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "jssa_mla_indexed_decode": [_P(MlaDesc), _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_mla_up_v": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_score_topdelta_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
@@ -262,6 +265,20 @@ def jssa_mla_absorb_q(desc, q_nope, q_rope, W_uk, P, q_abs, q_sel, stream=None):
 def jssa_mla_score(desc, q_sel, Kp_lat, scores, stream=None):
     _check(_lib.jssa_mla_score(ctypes.byref(desc), _p(q_sel), _p(Kp_lat), _p(scores), _s(stream)),
            "jssa_mla_score")
+
+
+def jssa_mla_score_topk_workspace_size(desc, k) -> int:
+    n = _sz(0)
+    _check(_lib.jssa_mla_score_topk_workspace_size(ctypes.byref(desc), k, ctypes.byref(n)),
+           "jssa_mla_score_topk_workspace_size")
+    return n.value
+
+
+def jssa_mla_score_topk(desc, q_sel, Kp_lat, k, scores, idx, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.jssa_mla_score_topk(ctypes.byref(desc), _p(q_sel), _p(Kp_lat), k, _p(scores), _p(idx), _p(ws),
+                                    ws_bytes, _s(stream)), "jssa_mla_score_topk")
 
 
 def jssa_mla_indexed_decode(desc, q_abs, latent, idx, k, S, scale, part_o, part_lse, stream=None):

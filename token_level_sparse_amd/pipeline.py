@@ -56,20 +56,22 @@ class GqaCache:
         jssa.jssa_project_keys(self.desc, self.K, self.P, self.Kp, stream)
 
 
-def default_splits(k: int, units: int = 1, blocks: int = 256) -> int:
-    """Splits of the selected set. Up to 512 selected tokens: one (the final
-    selection and the attention then share a kernel). Beyond that, the power
-    of two (2 to 64) that brings the attention launch closest to one block per
-    compute unit from below (`units` = B * Hkv (sequence, KV head) pairs, one
-    block per pair and split), keeping at least 128 rows per split. Measured:
-    paged Qwen at k = 2048 (64 pairs) 22.7 us of attention at 4 splits, 32.5 us
-    at 8; 128K B = 4 at k = 2048 (32 pairs) best at 8."""
-    if k <= 512:
+def default_splits(k: int, units: int = 1, blocks: int = 256, attend_fused: bool = True) -> int:
+    """Splits of the selected set. Up to 512 selected tokens with the final
+    selection and the attention sharing a kernel (attend_fused): one.
+    Otherwise the power of two (up to 64) that brings the attention launch
+    closest to one block per compute unit from below (`units` = B * Hkv
+    (sequence, KV head) pairs, one block per pair and split), keeping at
+    least 128 rows per split beyond 512 selected tokens and 64 up to it.
+    Measured: paged Qwen at k = 2048 (64 pairs) 22.7 us of attention at 4
+    splits, 32.5 us at 8; 128K B = 4 at k = 2048 (32 pairs) best at 8."""
+    if k <= 512 and attend_fused:
         return 1
-    s = 2
-    while s < 64 and 2 * s * units <= blocks and 2 * s <= k // 128:
+    rows = 128 if k > 512 else 64
+    s = 1
+    while s < 64 and 2 * s * units <= blocks and 2 * s <= k // rows:
         s *= 2
-    return s
+    return max(s, 2) if k > 512 else s
 
 
 class SparseStep:
@@ -85,7 +87,7 @@ class SparseStep:
     def __init__(self, c: GqaCache, k: int, S: int | None = None, fused: bool = False,
                  keep_scores: bool = True):
         dev = c.q.device
-        S = default_splits(k, c.B * c.Hkv) if S is None else S
+        S = default_splits(k, c.B * c.Hkv, attend_fused=fused) if S is None else S
         self.c, self.k, self.S, self.fused = c, k, S, fused
         self.scores = torch.empty((c.B, c.Hkv, c.T), dtype=torch.float32, device=dev) \
             if (keep_scores or not fused) else None
@@ -232,7 +234,7 @@ class GatherStep:
 
 
 class MlaStep:
-    """MLA: absorb -> score -> top-k (one set per sequence) -> indexed MFMA
+    """MLA: absorb -> score + top-k (one set per sequence) -> indexed MFMA
     attention over the latent rows -> combine -> value up-projection."""
 
     def __init__(self, inp: MlaInputs, S: int = 16, device="cuda"):
@@ -253,7 +255,8 @@ class MlaStep:
         self.q_abs = torch.empty((B, H, cfg.d_c), dtype=torch.float32, device=device)
         self.q_sel = torch.empty((B, cfg.r), dtype=torch.float32, device=device)
         self.scores = torch.empty((B, cfg.T), dtype=torch.float32, device=device)
-        nbytes = jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k)
+        nbytes = max(jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k),
+                     jssa.jssa_mla_score_topk_workspace_size(self.desc, cfg.k))
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.idx = torch.empty((B, cfg.k), dtype=torch.int32, device=device)
         self.part_o = torch.empty((B, H, S, cfg.d_latent), dtype=torch.float32, device=device)
@@ -269,8 +272,8 @@ class MlaStep:
         cfg = self.cfg
         jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.P, self.q_abs, self.q_sel,
                                stream)
-        jssa.jssa_mla_score(self.desc, self.q_sel, self.Kp, self.scores, stream)
-        jssa.jssa_topk(cfg.B, 1, cfg.T, self.seq_lens, self.scores, self.k, self.idx, self.ws, None, stream)
+        jssa.jssa_mla_score_topk(self.desc, self.q_sel, self.Kp, self.k, self.scores, self.idx, self.ws, None,
+                                 stream)
         jssa.jssa_mla_indexed_decode(self.desc, self.q_abs, self.latent, self.idx, self.k, self.S,
                                      self.scale, self.part_o, self.part_lse, stream)
         jssa.jssa_combine(cfg.B, cfg.H, self.S, cfg.d_latent, self.part_o, self.part_lse, self.o_lat, 0,
