@@ -707,9 +707,9 @@ hipError_t launch_topk_floor(int B, int H, int max_seq, const int32_t* seq_lens,
                      bounds, nb, bound_c);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // (a floored row keeps about 2k candidates: 512 direct slots per segment of
-  // a 16-segment row hold them; a longer list is read from memory)
-  hipLaunchKernelGGL((final_kernel<1024, 8, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs,
+  // (a floored row keeps a few k candidates: the 12-per-thread final holds
+  // them directly; a longer list is read from memory)
+  hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs,
                      segs.nseg, idx, CandSegs{}, DeltaArgs{});
   return hipGetLastError();
 }

@@ -11,6 +11,10 @@ lookup bench.py uses to report measured HBM traffic.
     python -m token_level_sparse_amd.prof_summary traffic FETCH_CSV WRITE_CSV \\
         COPY_FETCH_CSV COPY_WRITE_CSV --copy-mib 1024 --cmd "..." --kernel score_kernel
 
+    # L2 (TCC) hit rate per kernel from one `rocprofv3 --pmc TCC_HIT_sum
+    # TCC_MISS_sum` run
+    python -m token_level_sparse_amd.prof_summary l2 PMC_CSV --cmd "..."
+
 The traffic summary records a hash of the kernel sources it was measured
 with; read_traffic returns nothing once those sources have changed, so a
 stale measurement is never reported for a changed kernel.
@@ -86,6 +90,19 @@ def traffic_text(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_mib, cmd, co
     return "\n".join(out) + "\n"
 
 
+def l2_text(path: str, cmd: str) -> str:
+    hit = _per_kernel(path, "TCC_HIT_sum")
+    miss = _per_kernel(path, "TCC_MISS_sum")
+    out = ["# L2 (TCC) requests per launch from rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum",
+           f"# command: {cmd}", "",
+           f"{'kernel':60s} {'hits':>12s} {'misses':>12s} {'hit_rate':>9s}"]
+    for name in sorted(set(hit) | set(miss), key=lambda n: -(hit.get(n, 0.0) + miss.get(n, 0.0))):
+        h, m = hit.get(name, 0.0), miss.get(name, 0.0)
+        rate = h / (h + m) if h + m > 0 else float("nan")
+        out.append(f"{name[:60]:60s} {h:12.0f} {m:12.0f} {rate:9.3f}")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str, kernel: str):
     """HBM bytes per launch of `kernel` (fetch + write) from a traffic summary,
     or None when the file is missing or the kernel sources changed since."""
@@ -124,9 +141,14 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--copy-cmd", required=True)
     t.add_argument("--kernel", required=True)
+    l2 = sub.add_parser("l2")
+    l2.add_argument("csv")
+    l2.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         print(stats_text(a.csv, a.cmd), end="")
+    elif a.what == "l2":
+        print(l2_text(a.csv, a.cmd), end="")
     else:
         print(traffic_text(a.fetch_csv, a.write_csv, a.copy_fetch_csv, a.copy_write_csv, a.copy_mib, a.cmd,
                            a.copy_cmd, a.kernel), end="")
