@@ -220,57 +220,112 @@ __global__ __launch_bounds__(1024) void mla_selq_kernel(MlaDev m, const float* _
 }
 
 // ---------------------------------------------------------------------------
-// Indexed MLA attention on MFMA. Block = 1 wave = 16 heads x one split of the
-// selected slots, processed 32 tokens at a time.
+// Indexed MLA attention on MFMA. Block = 2 waves = 16 heads x one split of
+// the selected slots; wave w takes the w-th half of the split's slots, in
+// steps of 16 tokens, and the two halves meet in LDS at the end.
 //  QK^T: S^T[16 tok x 16 heads] += C[16 tok x 32 dims] . Qt[32 dims x 16 heads]
-//        over 18 dim blocks, twice (q hi and q lo), for two 16-token halves.
-//        Row m of half hf is token 8*(m/4) + 4*hf + m%4 of the 32-token block,
-//        so that lane group g (= lane/16) ends up with the logits of tokens
-//        8g..8g+7 for head lane%16: exactly the A operand of the PV MFMA.
-//  PV:   O[16 heads x 16 dims] += P[16 heads x 32 tok] . V[32 tok x 16 dims],
-//        32 dim tiles; V is staged transposed in LDS ([dim][token]) from the
-//        same loads that fed QK^T, so each lane reads its 8 tokens with one
-//        ds_read_b128.
+//        over 18 dim blocks (v_mfma_f32_16x16x32_bf16), twice (q hi and q
+//        lo). Lane (n, g) (n = lane % 16, g = lane / 16) supplies dims
+//        32 kb + 8g .. +7 of token n of the step, and receives the logits of
+//        tokens 4g .. 4g+3 for head n: the A operand of PV below as it is.
+//  PV:   O[16 heads x 16 dims] += P[16 heads x 16 tok] . V[16 tok x 16 dims],
+//        32 dim tiles (v_mfma_f32_16x16x16_bf16), the weights as hi + lo
+//        bf16 pairs. The step's value rows go to the wave's LDS as loaded
+//        (row-major, one 16-byte store per piece); the B operand of dim tile
+//        t, tokens 4g .. 4g+3 of dim 16 t + n in lane (n, g), comes back with
+//        one transposing LDS read (ds_read_b64_tr_b16: within a group of 16
+//        lanes, lane 4a + c receives element c of the 8 bytes that lanes 4j + a
+//        address, j = 0..3; so lane s of group g addresses token 4g + s / 4,
+//        dims 16 t + 4 (s % 4) .. +3).
+// Two waves per block and 69 KB of LDS per block keep two blocks, one wave
+// per SIMD, on every CU; the query's hi and lo parts sit in LDS once per
+// block (both waves serve the same heads), the registers holding the
+// accumulators and two steps of row loads.
 // ---------------------------------------------------------------------------
-constexpr int kVtStride = 40;   // u16 per transposed row (32 tokens + pad)
+constexpr int kVRS = kDl + 8;   // u16 per staged value row (16-byte aligned rows, banks staggered)
+constexpr float kLazy = 8.f;    // log2 headroom of the running softmax base
 
-__global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* __restrict__ qa,
-                                                         const uint16_t* __restrict__ lat,
-                                                         const int32_t* __restrict__ idx, int k,
-                                                         int S, float scale,
-                                                         float* __restrict__ part_o,
-                                                         float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDl * kVtStride];
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+__device__ __forceinline__ s16x4 pack_bf16x4(__bf16 a, __bf16 b, __bf16 c, __bf16 d) {
+  s16x4 r;
+  r[0] = __builtin_bit_cast(short, a);
+  r[1] = __builtin_bit_cast(short, b);
+  r[2] = __builtin_bit_cast(short, c);
+  r[3] = __builtin_bit_cast(short, d);
+  return r;
+}
+
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_indexed_kernel(
+    MlaDev m, const float* __restrict__ qa, const uint16_t* __restrict__ lat, const int32_t* __restrict__ idx, int k,
+    int S, float scale, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][16 * kVRS];
+  __shared__ bf16x8 qhi_s[18][64], qlo_s[18][64];
+  __shared__ float xm[2][16], xl[2][16];
   const int s = blockIdx.x, ht = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Tb = mla_len(m, b);
   const int cs = (k + S - 1) / S;
   const int r0 = min(s * cs, k), r1 = min(r0 + cs, k);
-  const int h = ht * 16 + n;                       // this lane's head in the QK B operand
+  const int hl = ((r1 - r0 + 1) / 2 + 15) / 16 * 16;   // slots per wave, whole steps
+  const int w0 = min(r0 + wv * hl, r1), w1 = min(w0 + hl, r1);
+  const int h = ht * 16 + n;                            // this lane's head in the QK B operand
+  uint16_t* vs = Vs[wv];
 
-  // B operand of QK^T (Q^T): lane holds Q[head n][dims kb*32 + 8g .. +8], as hi and lo bf16;
-  // the lo parts wait in LDS (registers go to the accumulators and loads in flight).
-  __shared__ bf16x8 qlo_s[18][64];
-  bf16x8 qhi[18];
+  // Row loads are pipelined by steps: while one step's 18 pieces per lane
+  // are multiplied, the next step's are in flight, and the slot indices are
+  // read a step further ahead, so no wait for an index stands between two
+  // steps. No load sits under a data-dependent branch: slots past the wave's
+  // range or with an invalid index read token 0 of the sequence (finite
+  // data) and are masked out of the softmax.
+  const int32_t* irow = idx + int64_t(b) * k;
+  const uint16_t* lrow = lat + int64_t(b) * m.max_seq * kDc;
+  auto tok_of = [&](int base) -> int {                 // token of row n of the step at slot base
+    const int sl = base + n;                            // (only called when w0 < w1)
+    return irow[sl < w1 ? sl : w1 - 1];
+  };
+  auto rows = [&](int base, int t, bool& ok, u32x4 (&A)[18]) {
+    ok = base + n < w1 && t >= 0 && t < Tb;
+    const uint16_t* crow = lrow + int64_t(ok ? t : 0) * kDc + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 18; ++kb) A[kb] = *reinterpret_cast<const u32x4*>(crow + kb * 32);
+  };
+  u32x4 A0[18], A1[18];
+  bool ok0 = false, ok1 = false;
+  int tb = 0;                                           // token of the step after the current one
+  if (w0 < w1) {                                        // the first step's rows go out before the query
+    const int ta = tok_of(w0);
+    tb = tok_of(w0 + 16);
+    rows(w0, ta, ok0, A0);
+  }
+
+  // B operand of QK^T (Q^T): lane holds Q[head n][dims kb*32 + 8g .. +8] as
+  // hi and lo bf16, kept in LDS (registers go to the accumulators and the
+  // loads in flight); wave w converts dim blocks 9w .. 9w+8.
   {
     const float* qrow = qa + (int64_t(b) * m.H + h) * kDc;
     const float qs = scale * kLog2e;
 #pragma unroll
-    for (int kb = 0; kb < 18; ++kb) {
+    for (int j = 0; j < 9; ++j) {
+      const int kb = 9 * wv + j;
       const f32x4v* p = reinterpret_cast<const f32x4v*>(qrow + kb * 32 + 8 * g);
       const f32x4v a = p[0], c = p[1];
       float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-      bf16x8 lo;
+      bf16x8 hv, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = x[e] * qs;
         const __bf16 hi = __bf16(v);
-        qhi[kb][e] = hi;
+        hv[e] = hi;
         lo[e] = __bf16(v - float(hi));
       }
+      qhi_s[kb][lane] = hv;
       qlo_s[kb][lane] = lo;
     }
   }
+  __syncthreads();
 
   f32x4v O[32];
 #pragma unroll
@@ -278,146 +333,149 @@ __global__ __launch_bounds__(64) void mla_indexed_kernel(MlaDev m, const float* 
   float mrun = -__builtin_inff();    // running max for head n (log2 domain), uniform over g
   float lrun = 0.f;                  // partial sum over this lane group's tokens
 
-  // Loads are pipelined by half tiles: while one half's 18 pieces per lane
-  // are multiplied, the other half's (or the next tile's first half's) are
-  // in flight. No load sits under a data-dependent branch: rows past the
-  // split or with an invalid index read token 0 of the sequence (finite
-  // data) and are masked out of the softmax.
-  const int32_t* irow = idx + int64_t(b) * k;
-  const uint16_t* lrow = lat + int64_t(b) * m.max_seq * kDc;
-  auto tile_index = [&](int base) -> int {           // lane l < 32: index of slot base + l
-    const int sl = base + (lane & 31);
-    return irow[sl < r1 ? sl : r1 - 1];
-  };
-  auto row_of = [&](int base, int tv, int hf, bool& ok) -> const uint16_t* {
-    const int tl = 8 * (n >> 2) + 4 * hf + (n & 3);  // token of MFMA row n in half hf
-    const int t = __shfl(tv, tl, 64);
-    ok = base + tl < r1 && t >= 0 && t < Tb;
-    return lrow + int64_t(ok ? t : 0) * kDc + 8 * g;
-  };
-  auto load_half = [&](const uint16_t* crow, u32x4 (&A)[18]) {
-#pragma unroll
-    for (int kb = 0; kb < 18; ++kb) A[kb] = *reinterpret_cast<const u32x4*>(crow + kb * 32);
-  };
-  // QK^T of one half tile; stashes the value part transposed in LDS. Four
-  // independent accumulator chains (hi/lo x even/odd dim blocks) keep the
-  // MFMA pipe busy instead of waiting on one chain's previous result.
-  auto qk_half = [&](const u32x4 (&A)[18], int hf) -> f32x4v {
-    const int tl = 8 * (n >> 2) + 4 * hf + (n & 3);
+  // one step: QK^T (stashing the value part transposed), the online softmax
+  // update and PV. Four independent accumulator chains (hi/lo x even/odd dim
+  // blocks) keep the MFMA pipe busy.
+  auto step = [&](const u32x4 (&A)[18], bool ok) {
     f32x4v acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    wave_lds_sync();                                    // the previous step's PV has read vs
 #pragma unroll
     for (int kb = 0; kb < 18; ++kb) {
-      if (kb < 16) {
-        const u32x4 raw = A[kb];
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&raw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(kb * 32 + 8 * g + e) * kVtStride + tl] = e16[e];
-      }
+      if (kb < 16) *reinterpret_cast<u32x4*>(&vs[n * kVRS + kb * 32 + 8 * g]) = A[kb];   // value dims
       const bf16x8 a = __builtin_bit_cast(bf16x8, A[kb]);
-      acc[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[kb], acc[kb & 1], 0, 0, 0);
+      acc[kb & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi_s[kb][lane], acc[kb & 1], 0, 0, 0);
       acc[2 + (kb & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo_s[kb][lane], acc[2 + (kb & 1)], 0, 0, 0);
     }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  };
-
-  u32x4 A0[18], A1[18];
-  int tv = r0 < r1 ? tile_index(r0) : 0;
-  bool ok0 = false, ok1 = false;
-  if (r0 < r1) load_half(row_of(r0, tv, 0, ok0), A0);
-  for (int base = r0; base < r1; base += 32) {
-    load_half(row_of(base, tv, 1, ok1), A1);
-    const int nb = base + 32 < r1 ? base + 32 : base;    // next tile (or this one again: unused)
-    const int tvn = tile_index(nb);
-    f32x4v St[2];
-    bool okrow[2];
-    St[0] = qk_half(A0, 0);
-    okrow[0] = ok0;
-    load_half(row_of(nb, tvn, 0, ok0), A0);            // next tile's first half
-    St[1] = qk_half(A1, 1);
-    okrow[1] = ok1;
-    tv = tvn;
-    // St[hf][i] = logit (log2 domain) of head n, token 8g + 4hf + i.
-    // validity of those tokens: rows 4g+i of each half belong to lanes n' = 4g+i
-    float lg[8];
+    const f32x4v St = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    // St[i] = logit (log2 domain) of head n, token 4g + i; that token's
+    // validity sits in lanes n' = 4g + i
+    float lg[4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int src = (lane & 48) | (4 * g + i);    // any lane whose n == 4g+i; same group
-        const int okv = __shfl(okrow[hf] ? 1 : 0, src, 64);
-        lg[hf * 4 + i] = okv ? St[hf][i] : -__builtin_inff();
-      }
-    float bm = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) bm = fmaxf(bm, lg[i]);
+    for (int i = 0; i < 4; ++i) {
+      const int okv = __shfl(ok ? 1 : 0, (lane & 48) | (4 * g + i), 64);
+      lg[i] = okv ? St[i] : -__builtin_inff();
+    }
+    float bm = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     bm = xor_max(bm, 16);
     bm = xor_max(bm, 32);
-    const float mnew = fmaxf(mrun, bm);
+    // Lazy rescaling: the exponent base mrun moves only when a logit exceeds
+    // it by more than kLazy (so every weight stays below 2^kLazy, exact in
+    // the hi + lo pair and harmless to the fp32 sums), and the 128
+    // accumulators are rescaled only on such a move of a head that already
+    // holds weight. The base cancels in O / l and enters the lse exactly.
+    const bool grow = bm > mrun + kLazy;                // (mrun = -inf: any finite bm)
+    const float mnew = grow ? bm : mrun;
     float alpha = 1.f;
-    float p[8];
+    float p[4];
     if (mnew == -__builtin_inff()) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
+      for (int i = 0; i < 4; ++i) p[i] = 0.f;
     } else {
-      alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      alpha = grow ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - mnew);
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - mnew);
     }
+    const bool held = mrun != -__builtin_inff();         // O of this head is not all zero
     mrun = mnew;
-    float ps = 0.f;
+    lrun = lrun * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    if (__ballot(grow && held) != 0) {                  // wave-uniform
+      // rescale O: accumulator rows are heads 4g+i; their alpha sits in lane n = 4g+i
+      float ar[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ps += p[i];
-    lrun = lrun * alpha + ps;
-    // rescale O: accumulator rows are heads 4g+i; their alpha sits in lane n = 4g+i
-    float ar[4];
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      O[t][0] *= ar[0]; O[t][1] *= ar[1]; O[t][2] *= ar[2]; O[t][3] *= ar[3];
+      for (int t = 0; t < 32; ++t) {
+        O[t][0] *= ar[0]; O[t][1] *= ar[1]; O[t][2] *= ar[2]; O[t][3] *= ar[3];
+      }
     }
     // The weights enter PV as a hi + lo pair of bf16 (two MFMAs), like the
     // query in QK^T: p = hi + lo to about 2^-16 relative, so the weighted sum
     // matches the fp32 denominator lrun instead of carrying bf16 rounding
     // (2^-9 relative per weight).
-    bf16x8 pa, pl;
+    __bf16 ph[4], pl[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = __bf16(p[i]);
-      pa[i] = h;
-      pl[i] = __bf16(p[i] - float(h));
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = __bf16(p[i]);
+      pl[i] = __bf16(p[i] - float(ph[i]));
     }
-    wave_lds_sync();
+    const s16x4 pa = pack_bf16x4(ph[0], ph[1], ph[2], ph[3]);
+    const s16x4 pb = pack_bf16x4(pl[0], pl[1], pl[2], pl[3]);
+    wave_lds_sync();                                    // this step's vs is written
+    const uint16_t* vrd = vs + (4 * g + (n >> 2)) * kVRS + 4 * (n & 3);
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
-      const u32x4 vraw = *reinterpret_cast<const u32x4*>(&Vt[(t * 16 + n) * kVtStride + 8 * g]);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vraw);
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[t], 0, 0, 0);
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, O[t], 0, 0, 0);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vrd + 16 * t));
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[t], 0, 0, 0);
+      O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, O[t], 0, 0, 0);
     }
-    wave_lds_sync();
+  };
+
+  for (int base = w0; base < w1; base += 32) {
+    const int tc = tok_of(base + 32);                   // (past the range: clamped, masked)
+    rows(base + 16, tb, ok1, A1);
+    step(A0, ok0);
+    const int td = tok_of(base + 48);
+    rows(base + 32, tc, ok0, A0);
+    step(A1, ok1);
+    tb = td;
   }
-  // total softmax denominator of head n: sum over the 4 lane groups
+  // total softmax denominator of head n over this wave's tokens
   lrun = xor_sum(xor_sum(lrun, 16), 32);
+
+  // The halves meet: wave 0 keeps dims 0..255 (tiles 0..15), wave 1 dims
+  // 256..511 (tiles 16..31); each hands the other tiles to the other wave
+  // through its own (now free) transposed-value buffer.
+  __syncthreads();                                      // both waves are done with their vs
+  float* xo = reinterpret_cast<float*>(vs);             // 16 tiles x 64 lanes x 4 = 16 KB
+  // (constant indexes into O in both branches: a wave-dependent index would
+  // put the accumulators in scratch memory)
+  if (wv == 0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4v*>(xo + (t * 64 + lane) * 4) = O[16 + t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4v*>(xo + (t * 64 + lane) * 4) = O[t];
+  }
+  if (g == 0) {
+    xm[wv][n] = mrun;
+    xl[wv][n] = lrun;
+  }
+  __syncthreads();
+  const float* yo = reinterpret_cast<const float*>(Vs[1 - wv]);
   // O[t][i] is head 4g+i, dim t*16+n
-  float lh[4], mh[4];
+  float fa[4], fb[4], inv[4], lse[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lh[i] = __shfl(lrun, 4 * g + i, 64);
-    mh[i] = __shfl(mrun, 4 * g + i, 64);
+    const int hh = 4 * g + i;
+    const float ma = xm[wv][hh], mb = xm[1 - wv][hh];
+    const float la = xl[wv][hh], lb = xl[1 - wv][hh];
+    const float M = fmaxf(ma, mb);
+    fa[i] = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ma - M);
+    fb[i] = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mb - M);
+    const float L = la * fa[i] + lb * fb[i];
+    inv[i] = L > 0.f ? 1.f / L : 0.f;
+    lse[i] = L > 0.f ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
   }
+  auto finish = [&](const f32x4v* mine, int keep) {    // mine: this wave's tiles keep .. keep+15
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = ht * 16 + 4 * g + i;
-    const int64_t ob = (int64_t(b) * m.H + hh) * S + s;
-    const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
-    float* dst = part_o + ob * kDl;
+    for (int i = 0; i < 4; ++i) {
+      const int hh = ht * 16 + 4 * g + i;
+      const int64_t ob = (int64_t(b) * m.H + hh) * S + s;
+      float* dst = part_o + ob * kDl;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) dst[t * 16 + n] = O[t][i] * inv;
-    if (n == 0) part_lse[ob] = lh[i] > 0.f ? (mh[i] + __builtin_log2f(lh[i])) * kLn2 : -__builtin_inff();
-  }
+      for (int t = 0; t < 16; ++t) {
+        const float other = yo[(t * 64 + lane) * 4 + i];
+        dst[(keep + t) * 16 + n] = (mine[t][i] * fa[i] + other * fb[i]) * inv[i];
+      }
+      if (wv == 0 && n == 0) part_lse[ob] = lse[i];
+    }
+  };
+  if (wv == 0)
+    finish(O, 0);
+  else
+    finish(O + 16, 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -498,7 +556,7 @@ hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_
                               const int32_t* idx, int k, int S, float scale, float* part_o,
                               float* part_lse, hipStream_t st) {
   dim3 grid(S, m.H / 16, m.B);
-  hipLaunchKernelGGL(mla_indexed_kernel, grid, dim3(64), 0, st, m, q_abs, latent, idx, k, S, scale,
+  hipLaunchKernelGGL(mla_indexed_kernel, grid, dim3(128), 0, st, m, q_abs, latent, idx, k, S, scale,
                      part_o, part_lse);
   return hipGetLastError();
 }
