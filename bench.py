@@ -320,8 +320,10 @@ def main():
     print(f"[bench] sparse step (flushed caches) median {med_us:.1f} us", file=sys.stderr, flush=True)
     st_us = time_stages(sp.stages(), args.steps, torch, stream, flush=flush)
     warm_s = time_warm(sp.stages(), args.steps, torch)
-    # the same step through the separate jssa_score / jssa_topk entry points
-    sp2 = pipeline.SparseStep(c, k=k, S=S, fused=False)
+    # the same step through the separate jssa_score / jssa_topk / jssa_indexed_decode entry points,
+    # with the split count that fills the CUs when the attention runs as its own launch
+    sp2 = pipeline.SparseStep(c, k=k, S=args.splits or None, fused=False)
+    S2 = sp2.S
     sep_step, _ = time_steps(sp2.stages(), args.steps, args.warmup, torch, stream, flush=flush)
     st2_us = time_stages(sp2.stages(), args.steps, torch, stream, flush=flush)
     print(f"[bench] sparse (separate score, top-k) median {np.median(sep_step):.1f} us", file=sys.stderr,
@@ -335,6 +337,8 @@ def main():
     topk_bytes = B * Hkv * T * 4 + B * Hkv * k * 4
     idx_bytes = nsel * 4 * d + B * Hkv * k * 4 + q_bytes + B * Hq * S * (d + 1) * 4
     comb_bytes = B * Hq * S * (d + 1) * 4 + B * Hq * (d + 1) * 4 if S > 1 else 0
+    idx_bytes2 = idx_bytes + B * Hq * (S2 - S) * (d + 1) * 4
+    comb_bytes2 = B * Hq * S2 * (d + 1) * 4 + B * Hq * (d + 1) * 4 if S2 > 1 else 0
     cand_bytes = B * Hkv * -(-T // 8192) * 8 * (k + 1)     # about k kept (key, index) pairs per 8192-token chunk
 
     def stage(us_list, nbytes):
@@ -352,9 +356,9 @@ def main():
         stages = {"score_topk_chunks": stage(st_us[0], fused_bytes),
                   "select_final": stage(st_us[1], cand_bytes + B * Hkv * k * 4),
                   "indexed": stage(st_us[2], idx_bytes), "combine": stage(st_us[3], comb_bytes)}
-    stages_split = {"score": stage(st2_us[0], score_bytes), "topk": stage(st2_us[1], topk_bytes),
-                    "indexed": stage(st2_us[2], idx_bytes),
-                    "combine": stage(st2_us[3] if S > 1 else [0.0], comb_bytes),
+    stages_split = {"S": S2, "score": stage(st2_us[0], score_bytes), "topk": stage(st2_us[1], topk_bytes),
+                    "indexed": stage(st2_us[2], idx_bytes2),
+                    "combine": stage(st2_us[3] if S2 > 1 else [0.0], comb_bytes2),
                     "step": summary(sep_step), "steps_per_s": round(1e6 / float(np.median(sep_step)), 2)}
     # the final stage warm (back-to-back launches over the same candidates), beside its cold time above
     if S == 1:
@@ -437,7 +441,7 @@ def main():
                                flush=flush)
         gst_us = [float(np.median(x)) for x in
                   time_stages([sp.score_topk, ga.gather, ga.attend, ga.combine], gsteps, torch, stream, flush)]
-        sparse_attn_us = float(np.median(st2_us[2])) + (float(np.median(st2_us[3])) if S > 1 else 0.0)
+        sparse_attn_us = float(np.median(st2_us[2])) + (float(np.median(st2_us[3])) if S2 > 1 else 0.0)
         gather_attn_us = gst_us[1] + gst_us[2] + gst_us[3]
         dense_attn_us = dst_us[0] + dst_us[1]
         result["gather_ablation"] = {
