@@ -639,17 +639,14 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
         jssa.jssa_mla_indexed_decode(st.desc, st.q_abs, st.latent, st.idx, st.k, st.S, st.scale, st.part_o,
                                      st.part_lse, stream)
 
-    def combine():
-        jssa.jssa_combine(c.B, c.H, st.S, c.d_latent, st.part_o, st.part_lse, st.o_lat, 0, st.lse, stream)
-
-    def up():
-        jssa.jssa_mla_up_v(st.desc, st.o_lat, st.W_uv, st.out, stream)
+    def combine_up():
+        jssa.jssa_mla_combine_up_v(st.desc, st.S, st.part_o, st.part_lse, st.W_uv, st.out, st.lse, stream)
 
     flush = Flush(torch)
-    fns = [absorb, score_topk, attend, combine, up]
+    fns = [absorb, score_topk, attend, combine_up]
     step_us, _ = time_steps(fns, args.steps, args.warmup, torch, stream, flush=flush)
     us = [float(np.median(x)) for x in time_stages(fns, args.steps, torch, stream, flush=flush)]
-    names = ["absorb", "score_topk", "indexed_mfma", "combine", "up_v"]
+    names = ["absorb", "score_topk", "indexed_mfma", "combine_up_v"]
     total = float(np.median(step_us)) * 1e-6 * args.steps
     steps_s = args.steps / total
     core_flops = 2 * c.B * c.H * c.k * (2 * c.d_c + c.d_latent)       # QK^T (hi+lo) + PV

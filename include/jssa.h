@@ -365,6 +365,22 @@ JSSA_API jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat
                           float* out, void* stream);
 
 /*
+ * jssa_combine of the S partials of jssa_mla_indexed_decode followed by
+ * jssa_mla_up_v, in one pass (the log-sum-exp merge of split partials, then
+ * the value up-projection of the absorbed attention, digest Perspective):
+ *  o_lat[b,h] = sum_s exp(lse_s - M) part_o[b,h,s] / sum_s exp(lse_s - M),
+ *  out[b,h]   = W_uv[h] . o_lat[b,h];   lse[b,h] = M + log(sum_s exp(lse_s - M)).
+ *  part_o device fp32 [B,H,S,d_latent], part_lse device fp32 [B,H,S],
+ *  W_uv device bf16 [H,d_v,d_latent], out device fp32 [B,H,d_v] (written),
+ *  lse device fp32 [B,H] (written; NULL: not written). 1 <= S <= 64.
+ *  o_lat stays on chip. Same results as the two calls up to fp32 summation
+ *  order.
+ */
+JSSA_API jssa_status jssa_mla_combine_up_v(const jssa_mla_desc* desc, int32_t S, const float* part_o,
+                                  const float* part_lse, const void* W_uv, float* out, float* lse,
+                                  void* stream);
+
+/*
  * Top-delta selection (Faster Than Flash review on evolve.pub, Summary, Key
  * claims and FAQ: a token stays when its log-weight is at most delta below a
  * stand-in for the maximum taken over the first and most recent tokens;

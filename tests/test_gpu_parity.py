@@ -1051,6 +1051,37 @@ def test_mla_score_topk_matches_separate_passes(J, case):
         np.testing.assert_array_equal(_np(i1)[b], O.select_topk(sc1[b, :n].astype(np.float64), k))
 
 
+@pytest.mark.parametrize("S", [1, 5, 16, 64])
+def test_mla_combine_up_matches_two_calls(J, S):
+    """jssa_mla_combine_up_v against jssa_combine + jssa_mla_up_v on random
+    partials (some splits empty: lse -inf) and random W_uv: same lse and
+    output up to fp32 summation order."""
+    B, H = 3, 32
+    rng = np.random.default_rng(100 + S)
+    po = rng.standard_normal((B, H, S, 512)).astype(np.float32)
+    pl = (3.0 * rng.standard_normal((B, H, S))).astype(np.float32)
+    pl[0, 0, :] = -np.inf                                 # a row with no weight at all
+    if S > 1:
+        pl[1, :, ::2] = -np.inf                           # rows with empty splits
+    wuv = synth.f32_to_bf16_bits(rng.standard_normal((H, 128, 512)) / np.sqrt(512)).view(np.int16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    po_t, pl_t, w_t = dev(po), dev(pl), dev(wuv)
+    desc = J.mla_desc(B, H, 64, 1024)
+    out1 = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse1 = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    olat = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out1)
+    lse2 = torch.empty_like(lse1)
+    print(f"[case] mla combine_up S={S}", flush=True)
+    J.jssa_mla_combine_up_v(desc, S, po_t, pl_t, w_t, out1, lse1)
+    J.jssa_combine(B, H, S, 512, po_t, pl_t, olat, 0, lse2)
+    J.jssa_mla_up_v(desc, olat, w_t, out2)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(_np(lse1), _np(lse2), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(_np(out1), _np(out2), rtol=1e-5, atol=1e-6)
+    assert np.all(_np(out1)[0, 0] == 0.0) and _np(lse1)[0, 0] == -np.inf
+
+
 # ---------------------------------------------------------------------------
 # full size: the 128K x B=16 workload in the launch configuration the
 # benchmark times; sampled units against the oracle, properties everywhere

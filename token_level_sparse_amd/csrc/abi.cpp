@@ -501,6 +501,16 @@ jssa_status jssa_mla_up_v(const jssa_mla_desc* desc, const float* o_lat, const v
                     __func__);
 }
 
+jssa_status jssa_mla_combine_up_v(const jssa_mla_desc* desc, int32_t n_split, const float* part_o, const float* part_lse,
+                                  const void* W_uv, float* out, float* lse, void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  if (n_split < 1 || n_split > 64) return fail(JSSA_ERR_SHAPE, "%s: S %d outside [1, 64]", __func__, n_split);
+  REQUIRE_PTR(part_o); REQUIRE_PTR(part_lse); REQUIRE_PTR(W_uv); REQUIRE_PTR(out);
+  return hip_status(jssa::launch_mla_combine_up(to_mla(desc), n_split, part_o, part_lse,
+                                                static_cast<const uint16_t*>(W_uv), out, lse, S(stream)),
+                    __func__);
+}
+
 jssa_status jssa_score_topdelta_workspace_size(const jssa_gqa_desc* desc, int32_t k_max, size_t* bytes) {
   size_t base = 0;
   if (jssa_status s = jssa_score_topk_workspace_size(desc, k_max, &base)) return s;

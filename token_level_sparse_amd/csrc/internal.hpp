@@ -90,5 +90,7 @@ hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_
                               float* part_lse, hipStream_t st);
 hipError_t launch_mla_up_v(const MlaDev& m, const float* o_lat, const uint16_t* W_uv, float* out,
                            hipStream_t st);
+hipError_t launch_mla_combine_up(const MlaDev& m, int S, const float* part_o, const float* part_lse,
+                                 const uint16_t* W_uv, float* out, float* lse, hipStream_t st);
 
 }  // namespace jssa

@@ -524,6 +524,106 @@ __global__ __launch_bounds__(256) void mla_up_v_kernel(MlaDev m, const float* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split merge and value up-projection in one pass (A6 + the W_uv step): one
+// block per head h merges the S partials of rows (b, h), with weights
+// exp(lse_s - M) over their sum L as jssa_combine does, into the latent
+// outputs in LDS (kCB sequences at a time), then applies W_uv[h]:
+// out[b,h,v] = W_uv[h,v,:] . o_lat[b,h]. Each W_uv row is read once for all
+// sequences (wave w holds rows 16w .. 16w+15, lane l dims 8l..8l+7, loaded
+// first), and each partial once; thread c holds column c. The partials of a
+// group of sequences are loaded before their weights are known, so the two
+// round trips overlap.
+// ---------------------------------------------------------------------------
+constexpr int kCB = 4;          // sequences merged per pass
+
+__global__ __launch_bounds__(512) void mla_combine_up_kernel(MlaDev m, int S, const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_lse,
+                                                             const uint16_t* __restrict__ Wuv,
+                                                             float* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ __attribute__((aligned(16))) float ol[kCB][kDl];
+  __shared__ float wts[kCB][64];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave's first 8 W_uv rows in registers from the start; the other 8
+  // are loaded when the merged outputs are ready
+  u32x4 wr[8];
+  const uint16_t* W = Wuv + (int64_t(h) * 128 + 16 * w) * kDl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wr[j] = reinterpret_cast<const u32x4*>(W + int64_t(j) * kDl)[lane];
+  for (int b0 = 0; b0 < m.B; b0 += kCB) {
+    const int nb = m.B - b0 < kCB ? m.B - b0 : kCB;
+    // this thread's column of the group's partials, 16 splits at a time
+    // (rows past B: row B-1, unused); the first 16 are loaded before the
+    // weights are known
+    constexpr int kSP = 16;
+    float pv[kCB][kSP];
+    auto load = [&](int s0) {
+#pragma unroll
+      for (int q = 0; q < kCB; ++q) {
+        const int64_t row = int64_t(b0 + (q < nb ? q : nb - 1)) * m.H + h;
+        const float* po = part_o + (row * S + s0) * kDl + tid;
+#pragma unroll
+        for (int i = 0; i < kSP; ++i) pv[q][i] = po[int64_t(s0 + i < S ? i : S - 1 - s0) * kDl];
+      }
+    };
+    load(0);
+    // weights: wave q < nb takes row b0 + q, lane s its split
+    if (w < nb) {
+      const int64_t row = int64_t(b0 + w) * m.H + h;
+      const float x = part_lse[row * S + (lane < S ? lane : 0)];
+      float M = lane < S ? x : -__builtin_inff();
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+      const float wgt = lane < S && M != -__builtin_inff() ? __expf(x - M) : 0.f;
+      float L = wgt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o, 64);
+      wts[w][lane] = L > 0.f ? wgt / L : 0.f;
+      if (lse_out && lane == 0) lse_out[row] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+    }
+    __syncthreads();
+    float acc[kCB];
+#pragma unroll
+    for (int q = 0; q < kCB; ++q) acc[q] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kSP) {
+      if (s0 > 0) load(s0);
+#pragma unroll
+      for (int q = 0; q < kCB; ++q)
+#pragma unroll
+        for (int i = 0; i < kSP; ++i)
+          acc[q] = __builtin_fmaf(s0 + i < S ? wts[q][s0 + i] : 0.f, pv[q][i], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kCB; ++q) ol[q][tid] = acc[q];
+    __syncthreads();
+    u32x4 wr2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wr2[j] = reinterpret_cast<const u32x4*>(W + int64_t(8 + j) * kDl)[lane];
+    for (int q = 0; q < nb; ++q) {
+      const f32x4v o0 = reinterpret_cast<const f32x4v*>(ol[q])[2 * lane];
+      const f32x4v o1 = reinterpret_cast<const f32x4v*>(ol[q])[2 * lane + 1];
+      const int64_t row = int64_t(b0 + q) * m.H + h;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const u32x4 r = j < 8 ? wr[j] : wr2[j - 8];
+        float a = 0.f;
+        a = __builtin_fmaf(o0.x, bf_lo(r.x), a);
+        a = __builtin_fmaf(o0.y, bf_hi(r.x), a);
+        a = __builtin_fmaf(o0.z, bf_lo(r.y), a);
+        a = __builtin_fmaf(o0.w, bf_hi(r.y), a);
+        a = __builtin_fmaf(o1.x, bf_lo(r.z), a);
+        a = __builtin_fmaf(o1.y, bf_hi(r.z), a);
+        a = __builtin_fmaf(o1.z, bf_lo(r.w), a);
+        a = __builtin_fmaf(o1.w, bf_hi(r.w), a);
+        a = row16_sum(a);
+        a = xor_sum(xor_sum(a, 16), 32);
+        if (lane == 0) out[row * 128 + 16 * w + j] = a;
+      }
+    }
+    __syncthreads();                                    // ol and wts are reused by the next group
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const float* P, uint16_t* Kp,
@@ -558,6 +658,12 @@ hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_
   dim3 grid(S, m.H / 16, m.B);
   hipLaunchKernelGGL(mla_indexed_kernel, grid, dim3(128), 0, st, m, q_abs, latent, idx, k, S, scale,
                      part_o, part_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_combine_up(const MlaDev& m, int S, const float* part_o, const float* part_lse,
+                                 const uint16_t* W_uv, float* out, float* lse, hipStream_t st) {
+  hipLaunchKernelGGL(mla_combine_up_kernel, dim3(m.H), dim3(512), 0, st, m, S, part_o, part_lse, W_uv, out, lse);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ ENTRY_POINTS = (
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
     "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_score_topk_workspace_size",
-    "jssa_mla_score_topk", "jssa_mla_indexed_decode",
+    "jssa_mla_score_topk", "jssa_mla_indexed_decode", "jssa_mla_combine_up_v",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
     "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_update_tile_bounds",
     "jssa_score_topk_screened_workspace_size",
@@ -92,6 +92,7 @@ _SIGS = {
     "jssa_mla_score_topk": [_P(MlaDesc), _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "jssa_mla_indexed_decode": [_P(MlaDesc), _vp, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp],
     "jssa_mla_up_v": [_P(MlaDesc), _vp, _vp, _vp, _vp],
+    "jssa_mla_combine_up_v": [_P(MlaDesc), _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "jssa_score_topdelta_workspace_size": [_P(GqaDesc), _i32, _P(_sz)],
     "jssa_score_topdelta": [_P(GqaDesc), _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp, _vp, _sz, _vp],
     "jssa_score_topdelta_attend": [_P(GqaDesc), _vp, _vp, _vp, _vp, _vp, _i32, _P(TopDeltaRule), _f32, _vp, _vp,
@@ -289,6 +290,11 @@ def jssa_mla_indexed_decode(desc, q_abs, latent, idx, k, S, scale, part_o, part_
 def jssa_mla_up_v(desc, o_lat, W_uv, out, stream=None):
     _check(_lib.jssa_mla_up_v(ctypes.byref(desc), _p(o_lat), _p(W_uv), _p(out), _s(stream)),
            "jssa_mla_up_v")
+
+
+def jssa_mla_combine_up_v(desc, S, part_o, part_lse, W_uv, out, lse=None, stream=None):
+    _check(_lib.jssa_mla_combine_up_v(ctypes.byref(desc), S, _p(part_o), _p(part_lse), _p(W_uv), _p(out), _p(lse),
+                                      _s(stream)), "jssa_mla_combine_up_v")
 
 
 def jssa_calib_workspace_size(desc) -> int:

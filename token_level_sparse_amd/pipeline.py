@@ -235,7 +235,7 @@ class GatherStep:
 
 class MlaStep:
     """MLA: absorb -> score + top-k (one set per sequence) -> indexed MFMA
-    attention over the latent rows -> combine -> value up-projection."""
+    attention over the latent rows -> combine + value up-projection."""
 
     def __init__(self, inp: MlaInputs, S: int = 16, device="cuda"):
         cfg = inp.cfg
@@ -276,9 +276,8 @@ class MlaStep:
                                  stream)
         jssa.jssa_mla_indexed_decode(self.desc, self.q_abs, self.latent, self.idx, self.k, self.S,
                                      self.scale, self.part_o, self.part_lse, stream)
-        jssa.jssa_combine(cfg.B, cfg.H, self.S, cfg.d_latent, self.part_o, self.part_lse, self.o_lat, 0,
-                          self.lse, stream)
-        jssa.jssa_mla_up_v(self.desc, self.o_lat, self.W_uv, self.out, stream)
+        jssa.jssa_mla_combine_up_v(self.desc, self.S, self.part_o, self.part_lse, self.W_uv, self.out, self.lse,
+                                   stream)
 
 
 # ---------------------------------------------------------------------------
