@@ -967,7 +967,11 @@ def test_calib_end_to_end_recall(J, PL):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("seed,B,T,k,S", [(5, 2, 6000, 512, 4), (1, 4, 4096, 2048, 16), (2, 4, 4096, 2048, 16),
                                           (3, 4, 4096, 2048, 8), (7, 4, 4096, 2048, 16), (11, 4, 4096, 2048, 16),
-                                          (13, 4, 4096, 2048, 16)])
+                                          (13, 4, 4096, 2048, 16),
+                                          # ragged splits and steps: k / S not a multiple of 16, a split
+                                          # smaller than a step, one slot, and the chunk-bound selection
+                                          # with a partial last chunk
+                                          (17, 2, 3000, 100, 3), (19, 1, 2048, 1, 1), (23, 3, 5000, 333, 7)])
 def test_mla_parity(J, PL, seed, B, T, k, S):
     cfg = replace(synth.MLA_DSV3, B=B, T=T, k=k, seed=seed)
     inp = synth.make_mla(cfg)
