@@ -282,9 +282,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // data) and are masked out of the softmax.
   const int32_t* irow = idx + int64_t(b) * k;
   const uint16_t* lrow = lat + int64_t(b) * m.max_seq * kDc;
+  const int smax = w1 > w0 ? w1 - 1 : 0;               // (a wave without slots reads slot 0, unused)
   auto tok_of = [&](int base) -> int {                 // token of row n of the step at slot base
-    const int sl = base + n;                            // (only called when w0 < w1)
-    return irow[sl < w1 ? sl : w1 - 1];
+    const int sl = base + n;
+    return irow[sl < w1 ? sl : smax];
   };
   auto rows = [&](int base, int t, bool& ok, u32x4 (&A)[18]) {
     ok = base + n < w1 && t >= 0 && t < Tb;
@@ -295,23 +296,34 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   u32x4 A0[18], A1[18];
   bool ok0 = false, ok1 = false;
   int tb = 0;                                           // token of the step after the current one
-  if (w0 < w1) {                                        // the first step's rows go out before the query
-    const int ta = tok_of(w0);
-    tb = tok_of(w0 + 16);
-    rows(w0, ta, ok0, A0);
+  // Prologue loads, all issued unconditionally (clamped and masked: a load
+  // under a branch would make the waits after the join count conservatively):
+  // the slot indices, the first step's rows, then the query. (An L2 prefetch
+  // of the next steps' rows here was measured: the steps did not get faster,
+  // they wait on LDS and MFMA latency, not on the rows.)
+  const int ta = tok_of(w0);
+  tb = tok_of(w0 + 16);
+  __builtin_amdgcn_sched_barrier(0);
+  rows(w0, ta, ok0, A0);
+  const float* qrow = qa + (int64_t(b) * m.H + h) * kDc;
+  f32x4v qv[9][2];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const f32x4v* p = reinterpret_cast<const f32x4v*>(qrow + (9 * wv + j) * 32 + 8 * g);
+    qv[j][0] = p[0];
+    qv[j][1] = p[1];
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // B operand of QK^T (Q^T): lane holds Q[head n][dims kb*32 + 8g .. +8] as
   // hi and lo bf16, kept in LDS (registers go to the accumulators and the
   // loads in flight); wave w converts dim blocks 9w .. 9w+8.
   {
-    const float* qrow = qa + (int64_t(b) * m.H + h) * kDc;
     const float qs = scale * kLog2e;
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
       const int kb = 9 * wv + j;
-      const f32x4v* p = reinterpret_cast<const f32x4v*>(qrow + kb * 32 + 8 * g);
-      const f32x4v a = p[0], c = p[1];
+      const f32x4v a = qv[j][0], c = qv[j][1];
       float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
       bf16x8 hv, lo;
 #pragma unroll
@@ -526,101 +538,108 @@ __global__ __launch_bounds__(256) void mla_up_v_kernel(MlaDev m, const float* __
 
 // ---------------------------------------------------------------------------
 // Split merge and value up-projection in one pass (A6 + the W_uv step): one
-// block per head h merges the S partials of rows (b, h), with weights
+// block per head h. The S partials of rows (b, h) are merged, with weights
 // exp(lse_s - M) over their sum L as jssa_combine does, into the latent
-// outputs in LDS (kCB sequences at a time), then applies W_uv[h]:
-// out[b,h,v] = W_uv[h,v,:] . o_lat[b,h]. Each W_uv row is read once for all
-// sequences (wave w holds rows 16w .. 16w+15, lane l dims 8l..8l+7, loaded
-// first), and each partial once; thread c holds column c. The partials of a
-// group of sequences are loaded before their weights are known, so the two
-// round trips overlap.
+// outputs (kCB sequences at a time); then out[b,h,:] = W_uv[h] o_lat[b] runs
+// on MFMA: D[b][v] += A[b][32 dims] . B[32 dims][v] over 16 dim blocks
+// (v_mfma_f32_16x16x32_bf16), B = W_uv[h] rows as stored (bf16), A = o_lat
+// split exactly into three bf16 terms (8 significant bits each; three
+// MFMAs into three accumulators), so the products are exact, the sums fp32,
+// and no dot needs a cross-lane reduction.
+//  Wave w owns outputs v = 16w .. 16w+15: lane (n, g) holds
+//  W_uv[h][16w + n][32kb + 8g .. +7] for every kb, loaded at the start with
+//  the split weights' and the partials' loads.
+//  Merge: thread (q, c4) = (tid / 128, tid % 128) takes sequence b0 + q,
+//  columns 4c4 .. +3, 16 splits per batch of 16-byte loads; each wave
+//  computes its sequence's split weights itself (lane s: split s), so no
+//  barrier stands before the merge. The thread splits its merged values into
+//  the three bf16 terms once and stores them to LDS, where every wave reads
+//  its A operands (A rows past the group's sequences read a valid row; the
+//  D rows they produce are not stored).
 // ---------------------------------------------------------------------------
-constexpr int kCB = 4;          // sequences merged per pass
+constexpr int kCB = 4;          // sequences merged per pass (one per pair of waves)
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(512) void mla_combine_up_kernel(MlaDev m, int S, const float* __restrict__ part_o,
                                                              const float* __restrict__ part_lse,
                                                              const uint16_t* __restrict__ Wuv,
                                                              float* __restrict__ out, float* __restrict__ lse_out) {
-  __shared__ __attribute__((aligned(16))) float ol[kCB][kDl];
-  __shared__ float wts[kCB][64];
+  __shared__ __attribute__((aligned(16))) __bf16 ol3[3][kCB][kDl];   // o_lat = hi + mid + lo
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // the wave's first 8 W_uv rows in registers from the start; the other 8
-  // are loaded when the merged outputs are ready
-  u32x4 wr[8];
-  const uint16_t* W = Wuv + (int64_t(h) * 128 + 16 * w) * kDl;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) wr[j] = reinterpret_cast<const u32x4*>(W + int64_t(j) * kDl)[lane];
+  const int n = lane & 15, g = lane >> 4;
+  const int q = tid >> 7, c4 = tid & 127;
+  constexpr int kSP = 16;
   for (int b0 = 0; b0 < m.B; b0 += kCB) {
     const int nb = m.B - b0 < kCB ? m.B - b0 : kCB;
-    // this thread's column of the group's partials, 16 splits at a time
-    // (rows past B: row B-1, unused); the first 16 are loaded before the
-    // weights are known
-    constexpr int kSP = 16;
-    float pv[kCB][kSP];
+    const int64_t row = int64_t(b0 + (q < nb ? q : nb - 1)) * m.H + h;   // past B: row B-1, unused
+    // split weights of this wave's sequence: lane s holds split s
+    const float x = part_lse[row * S + (lane < S ? lane : 0)];
+    f32x4v pv[kSP];
     auto load = [&](int s0) {
+      const f32x4v* po = reinterpret_cast<const f32x4v*>(part_o + (row * S + s0) * kDl) + c4;
 #pragma unroll
-      for (int q = 0; q < kCB; ++q) {
-        const int64_t row = int64_t(b0 + (q < nb ? q : nb - 1)) * m.H + h;
-        const float* po = part_o + (row * S + s0) * kDl + tid;
-#pragma unroll
-        for (int i = 0; i < kSP; ++i) pv[q][i] = po[int64_t(s0 + i < S ? i : S - 1 - s0) * kDl];
-      }
+      for (int i = 0; i < kSP; ++i) pv[i] = po[int64_t(s0 + i < S ? i : S - 1 - s0) * (kDl / 4)];
     };
     load(0);
-    // weights: wave q < nb takes row b0 + q, lane s its split
-    if (w < nb) {
-      const int64_t row = int64_t(b0 + w) * m.H + h;
-      const float x = part_lse[row * S + (lane < S ? lane : 0)];
-      float M = lane < S ? x : -__builtin_inff();
+    u32x4 wb[16];                                       // (re-read per group: cache hits after the first)
+    {
+      const uint16_t* W = Wuv + (int64_t(h) * 128 + 16 * w + n) * kDl + 8 * g;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-      const float wgt = lane < S && M != -__builtin_inff() ? __expf(x - M) : 0.f;
-      float L = wgt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o, 64);
-      wts[w][lane] = L > 0.f ? wgt / L : 0.f;
-      if (lse_out && lane == 0) lse_out[row] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+      for (int kb = 0; kb < 16; ++kb) wb[kb] = *reinterpret_cast<const u32x4*>(W + kb * 32);
     }
-    __syncthreads();
-    float acc[kCB];
+    float M = lane < S ? x : -__builtin_inff();
 #pragma unroll
-    for (int q = 0; q < kCB; ++q) acc[q] = 0.f;
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float wgt = lane < S && M != -__builtin_inff() ? __expf(x - M) : 0.f;
+    float L = wgt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o, 64);
+    const float wt = L > 0.f ? wgt / L : 0.f;
+    if (lse_out && (w & 1) == 0 && lane == 0 && q < nb) lse_out[row] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+    f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += kSP) {
       if (s0 > 0) load(s0);
 #pragma unroll
-      for (int q = 0; q < kCB; ++q)
-#pragma unroll
-        for (int i = 0; i < kSP; ++i)
-          acc[q] = __builtin_fmaf(s0 + i < S ? wts[q][s0 + i] : 0.f, pv[q][i], acc[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < kCB; ++q) ol[q][tid] = acc[q];
-    __syncthreads();
-    u32x4 wr2[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wr2[j] = reinterpret_cast<const u32x4*>(W + int64_t(8 + j) * kDl)[lane];
-    for (int q = 0; q < nb; ++q) {
-      const f32x4v o0 = reinterpret_cast<const f32x4v*>(ol[q])[2 * lane];
-      const f32x4v o1 = reinterpret_cast<const f32x4v*>(ol[q])[2 * lane + 1];
-      const int64_t row = int64_t(b0 + q) * m.H + h;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const u32x4 r = j < 8 ? wr[j] : wr2[j - 8];
-        float a = 0.f;
-        a = __builtin_fmaf(o0.x, bf_lo(r.x), a);
-        a = __builtin_fmaf(o0.y, bf_hi(r.x), a);
-        a = __builtin_fmaf(o0.z, bf_lo(r.y), a);
-        a = __builtin_fmaf(o0.w, bf_hi(r.y), a);
-        a = __builtin_fmaf(o1.x, bf_lo(r.z), a);
-        a = __builtin_fmaf(o1.y, bf_hi(r.z), a);
-        a = __builtin_fmaf(o1.z, bf_lo(r.w), a);
-        a = __builtin_fmaf(o1.w, bf_hi(r.w), a);
-        a = row16_sum(a);
-        a = xor_sum(xor_sum(a, 16), 32);
-        if (lane == 0) out[row * 128 + 16 * w + j] = a;
+      for (int i = 0; i < kSP; ++i) {
+        // lanes >= S hold weight 0, so splits past S (clamped loads) add nothing
+        const float ws = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), s0 + i < 64 ? s0 + i : 63));
+        acc += ws * pv[i];
       }
     }
-    __syncthreads();                                    // ol and wts are reused by the next group
+    bf16x4 t0, t1, t2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 hb = __bf16(acc[e]);
+      const float r1 = acc[e] - float(hb);              // exact
+      const __bf16 mb = __bf16(r1);
+      t0[e] = hb;
+      t1[e] = mb;
+      t2[e] = __bf16(r1 - float(mb));                   // exact: acc = hi + mid + lo
+    }
+    __syncthreads();                                    // the previous group's ol3 is read
+    *reinterpret_cast<bf16x4*>(&ol3[0][q][4 * c4]) = t0;
+    *reinterpret_cast<bf16x4*>(&ol3[1][q][4 * c4]) = t1;
+    *reinterpret_cast<bf16x4*>(&ol3[2][q][4 * c4]) = t2;
+    __syncthreads();
+    f32x4v D[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) D[j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    const int r = n & (kCB - 1);                        // A row n: sequence b0 + n for n < nb
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, wb[kb]);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ol3[j][r][32 * kb + 8 * g]);
+        D[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw, D[j], 0, 0, 0);
+      }
+    }
+    // D of lane (n, g), register i: sequence b0 + 4g + i, output v = 16w + n
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i < nb) out[(int64_t(b0 + 4 * g + i) * m.H + h) * 128 + 16 * w + n] = (D[0][i] + D[1][i]) + D[2][i];
   }
 }
 
