@@ -310,19 +310,24 @@ JSSA_API jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const vo
  * shared latent cache).
  *  q_abs[b,h] = [W_uk[h]^T q_nope[b,h] ; q_rope[b,h]] (fp32): the attention
  *               query of head h against latent rows;
- *  q_sel[b]   = P^T sum_h q_abs[b,h] (fp32, fixed summation order): the one
- *               subspace query of sequence b that jssa_mla_score streams with.
+ *  q_sel[b,j] = P[64j .. 64j+63]^T sum_h q_abs[b,h][64j .. 64j+63], j < 9
+ *               (fp32, fixed summation order): the one subspace query of
+ *               sequence b, P^T sum_h q_abs[b,h], in 9 parts over 64-dim
+ *               blocks of the latent + rope dims; the MLA score passes add
+ *               the parts themselves, in order.
  *  q_nope device bf16 [B,H,d_nope], q_rope device bf16 [B,H,d_rope],
  *  W_uk device bf16 [H,d_nope,d_latent], P device fp32 [d_c,r],
- *  q_abs device fp32 [B,H,d_c] (written), q_sel device fp32 [B,r] (written)
+ *  q_abs device fp32 [B,H,d_c] (written), q_sel device fp32 [B,9,r] (written)
  */
 JSSA_API jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
                               const void* W_uk, const float* P, float* q_abs, float* q_sel, void* stream);
 
 /*
- * MLA selection scores: scores[b,t] = q_sel[b] . Kp_lat[b,t] for t < T_b,
- * -inf beyond. q_sel device fp32 [B,r] (from jssa_mla_absorb_q), scores
- * device fp32 [B,max_seq].
+ * MLA selection scores: scores[b,t] = (sum_j q_sel[b,j]) . Kp_lat[b,t] for
+ * t < T_b, -inf beyond; the 9 parts are added in order (the same query in
+ * every pass and every block). q_sel device fp32 [B,9,r] (from
+ * jssa_mla_absorb_q, or any split of the query into 9 rows), scores device
+ * fp32 [B,max_seq].
  */
 JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat,
                            float* scores, void* stream);

@@ -987,8 +987,12 @@ def test_mla_parity(J, PL, seed, B, T, k, S):
     for b in range(cfg.B):
         qa = O.mla_absorbed_query(inp.q_nope[b], inp.q_rope[b], inp.W_uk)
         U.check_close(_np(st.q_abs)[b], qa, tol=1e-4, what="absorbed query")
-        # the selection query is the projected head sum of the absorbed query
-        U.check_close(qsel[b], inp.P.astype(np.float64).T @ qa.sum(0), tol=1e-4, what="selection query")
+        # part j of the selection query: P rows 64j .. 64j+63 against the
+        # head sum of those absorbed dims; the parts add up to P^T sum_h qa
+        P64, qbar = inp.P.astype(np.float64), qa.sum(0)
+        parts = np.stack([P64[64 * j:64 * j + 64].T @ qbar[64 * j:64 * j + 64] for j in range(9)])
+        U.check_close(qsel[b], parts, tol=1e-4, what="selection query parts")
+        U.check_close(qsel[b].astype(np.float64).sum(0), P64.T @ qbar, tol=1e-4, what="selection query")
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
     for b in range(cfg.B):
         s = O.mla_scores(inp.q_nope[b], inp.q_rope[b], inp.W_uk, inp.P, O.project_keys(inp.latent[b], inp.P))
@@ -1024,7 +1028,10 @@ def test_mla_score_topk_matches_separate_passes(J, case):
     name, B, T, k, lens, kind = case
     r, H = 64, 128
     rng = np.random.default_rng(sum(map(ord, name)))
-    qsel = rng.standard_normal((B, r)).astype(np.float32)
+    # the query in 9 parts (as jssa_mla_absorb_q writes it); qsel is their
+    # sum, for building keys near it
+    qshare = (rng.standard_normal((B, 9, r)) / 3.0).astype(np.float32)
+    qsel = qshare.astype(np.float64).sum(1)
     if kind == "tied":
         kp = np.zeros((B, T, r), np.float32)            # every score 0: the lowest indices win
     else:
@@ -1034,7 +1041,7 @@ def test_mla_score_topk_matches_separate_passes(J, case):
     kp_bits = synth.f32_to_bf16_bits(kp).view(np.int16)
     lens_np = np.full(B, T, np.int32) if lens is None else np.asarray(lens, np.int32)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    q_t, kp_t, sl = dev(qsel), dev(kp_bits), dev(lens_np)
+    q_t, kp_t, sl = dev(qshare), dev(kp_bits), dev(lens_np)
     desc = J.mla_desc(B, H, r, T, seq_lens=sl)
     s1 = torch.empty((B, T), dtype=torch.float32, device="cuda")
     s2 = torch.empty_like(s1)

@@ -78,6 +78,10 @@ struct MlaDev {
 };
 hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const float* P,
                               uint16_t* Kp, hipStream_t st);
+// The MLA selection query P^T sum_h q_abs[b,h] is passed as kMlaSelParts
+// partial sums [B, kMlaSelParts, r]: part j over the latent + rope dims
+// 64j .. 64j+63. The score stream adds the parts in order.
+constexpr int kMlaSelParts = 9;
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
                              const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st);
 // bound (optional, [B, mla_score_chunks(max_seq)]): per chunk of the stream

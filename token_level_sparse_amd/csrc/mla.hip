@@ -158,64 +158,66 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// Selection query of a sequence: q_sel[b,:] = P^T (sum_h q_abs[b,h,:]), the
-// subspace query the latent score stream dots with every projected row
-// (fixed summation order: deterministic). Block per sequence, 1024 threads:
-// the head sum is split over 4 head quarters (unrolled loads) and merged in
-// LDS, then R columns x 1024/R row slices of P.
+// Selection query of a sequence, in parts: q_sel[b,j,:] = P[64j .. 64j+63]^T
+// (sum_h q_abs[b,h,64j .. 64j+63]) for the 9 blocks j of 64 latent + rope
+// dims. The query P^T sum_h q_abs[b,h] is their sum, which the score passes
+// form themselves (parts added in order), so the cross-head sum is spread
+// over B x 9 blocks instead of one block per sequence. Block (b, j), 256
+// threads: thread (c, hq) = (tid % 64, tid / 64) adds heads hq, hq + 4, ...
+// of dim 64j + c (fixed order; the four head classes meet in LDS in order),
+// then thread (rq, sl) projects: columns 4rq .. 4rq+3 of P over the block's
+// rows sl, sl + NS, ... (the slices meet in LDS in order).
 // ---------------------------------------------------------------------------
+static_assert(kMlaSelParts * 64 == kDc, "selection query parts: 64 dims each");
+
 template <int R>
-__global__ __launch_bounds__(1024) void mla_selq_kernel(MlaDev m, const float* __restrict__ qa,
-                                                        const float* __restrict__ P,
-                                                        float* __restrict__ qsel) {
-  __shared__ float part[4][kDc];
-  __shared__ float qbar[kDc];
-  __shared__ float ppart[1024];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int hq = tid >> 8, ct = tid & 255;              // head quarter, column thread
-  const int hpq = (m.H + 3) / 4;
-  const int h0 = hq * hpq, h1 = min(m.H, h0 + hpq);
-  // up to 32 heads per quarter: all loads of a column issued at once
-  // (clamped to a valid head, zero weight past the quarter)
-  for (int c = ct; c < kDc; c += 256) {
-    const float* qc = qa + int64_t(b) * m.H * kDc + c;
-    float s = 0.f;
-    for (int hb = h0; hb < h1; hb += 32) {
-      float a[32];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int h = hb + u < h1 ? hb + u : h1 - 1;
-        a[u] = qc[int64_t(h) * kDc];
-      }
-#pragma unroll
-      for (int u = 0; u < 32; ++u) s += hb + u < h1 ? a[u] : 0.f;
-    }
-    part[hq][c] = s;
-  }
-  __syncthreads();
-  for (int c = tid; c < kDc; c += 1024) qbar[c] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
-  __syncthreads();
-  constexpr int NS = 1024 / R;                          // row slices
-  constexpr int NI = (kDc + NS - 1) / NS;
-  const int c = tid % R, sl = tid / R;
-  float s = 0.f;
-  float pv[NI];
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {                   // every P load in flight at once
-    const int i = sl + ii * NS;
-    pv[ii] = P[(i < kDc ? i : kDc - 1) * R + c];
-  }
+__global__ __launch_bounds__(256) void mla_selq_kernel(MlaDev m, const float* __restrict__ qa,
+                                                       const float* __restrict__ P,
+                                                       float* __restrict__ qsel) {
+  constexpr int NQ = R / 4;               // 16-byte column groups of P
+  constexpr int NS = 256 / NQ;            // row slices
+  constexpr int NI = (64 + NS - 1) / NS;  // rows per slice
+  __shared__ float part[4][64];
+  __shared__ float qbar[64];
+  __shared__ __attribute__((aligned(16))) float pp[NS][R];
+  const int b = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+  const int c = tid & 63, hq = tid >> 6;
+  const int rq = tid % NQ, sl = tid / NQ;
+  // this slice's P rows (issued first: they do not depend on the sum)
+  f32x4v pv[NI];
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int i = sl + ii * NS;
-    s = __builtin_fmaf(pv[ii], i < kDc ? qbar[i < kDc ? i : kDc - 1] : 0.f, s);
+    pv[ii] = reinterpret_cast<const f32x4v*>(P + int64_t(64 * j + (i < 64 ? i : 63)) * R)[rq];
   }
-  ppart[sl * R + c] = s;
+  const float* qc = qa + int64_t(b) * m.H * kDc + 64 * j + c;
+  float s = 0.f;
+  for (int h0 = hq; h0 < m.H; h0 += 4 * 32) {            // 32 heads of the class in flight at once
+    float a[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int h = h0 + 4 * u;
+      a[u] = qc[int64_t(h < m.H ? h : hq) * kDc];         // clamped: a valid row, not added
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s += h0 + 4 * u < m.H ? a[u] : 0.f;
+  }
+  part[hq][c] = s;
+  __syncthreads();
+  if (tid < 64) qbar[tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+  __syncthreads();
+  f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int i = sl + ii * NS;
+    acc += (i < 64 ? qbar[i < 64 ? i : 63] : 0.f) * pv[ii];
+  }
+  *reinterpret_cast<f32x4v*>(&pp[sl][4 * rq]) = acc;
   __syncthreads();
   if (tid < R) {
     float t = 0.f;
-    for (int x = 0; x < NS; ++x) t += ppart[x * R + tid];
-    qsel[int64_t(b) * R + tid] = t;
+    for (int x = 0; x < NS; ++x) t += pp[x][tid];
+    qsel[(int64_t(b) * kMlaSelParts + j) * R + tid] = t;
   }
 }
 
@@ -662,10 +664,11 @@ hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(m.H, kDl / 128), dim3(256), 0, st, m, q_nope, q_rope, W_uk, q_abs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 grid(m.B, kMlaSelParts);
   switch (m.r) {
-    case 16: hipLaunchKernelGGL(mla_selq_kernel<16>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
-    case 32: hipLaunchKernelGGL(mla_selq_kernel<32>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
-    case 64: hipLaunchKernelGGL(mla_selq_kernel<64>, dim3(m.B), dim3(1024), 0, st, m, q_abs, P, q_sel); break;
+    case 16: hipLaunchKernelGGL(mla_selq_kernel<16>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
+    case 32: hipLaunchKernelGGL(mla_selq_kernel<32>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
+    case 64: hipLaunchKernelGGL(mla_selq_kernel<64>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -7,7 +7,9 @@
 // qp = P_j^T (sum_h q_h) with the stored projected key, so the stream reads
 // 2r bytes per token and does r FMAs. For the MLA latent cache the same
 // stream runs with the selection query qp = P^T (sum over all heads of the
-// absorbed query), which the absorb step computes once per sequence.
+// absorbed query), which the absorb step writes as kMlaSelParts partial
+// sums (one per 64-dim block of the latent + rope dims); every block adds
+// them in the same fixed order in its prologue.
 //
 // HBM-bound streaming kernel. Each wave reads a tile of 64 tokens' projected
 // keys as 64*r/8 contiguous 16-byte pieces, one coalesced dwordx4 load per
@@ -340,10 +342,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
     __syncthreads();
   } else {
-    // MLA: the selection query qp = P^T sum_h q_abs[b,h] comes precomputed
-    const float qv = qsel[int64_t(b) * R + (tid < R ? tid : 0)];
+    // MLA: the selection query qp = sum of its kMlaSelParts rows qsel[b,x,:]
+    // (written by the absorb step). Thread (c, part) adds rows part, part +
+    // NP, ... of column c, in order; the NP partial sums then meet in LDS,
+    // in order (a fixed summation order: every block of the sequence gets
+    // the same qp). The rows are loaded before the first tiles go out.
+    constexpr int NP = NT / R;
+    constexpr int kRows = (kMlaSelParts + NP - 1) / NP;   // rows per thread
+    const int c = tid % R, part = tid / R;
+    const float* qb = qsel + int64_t(b) * kMlaSelParts * R + c;
+    float hv[kRows];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int x = part + u * NP;
+      hv[u] = qb[int64_t(x < kMlaSelParts ? x : 0) * R];   // clamped: a valid row, not added
+    }
     first_tiles();
-    if (tid < R) sm.qp[tid] = qv;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) acc += part + u * NP < kMlaSelParts ? hv[u] : 0.f;
+    sm.u.pro.qpart[part * R + c] = acc;
+    __syncthreads();
+    if (tid < R) {
+      float t = 0.f;
+      for (int x = 0; x < NP; ++x) t += sm.u.pro.qpart[x * R + tid];
+      sm.qp[tid] = t;
+    }
     __syncthreads();
   }
   float qr[NSL][8];

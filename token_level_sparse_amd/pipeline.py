@@ -253,7 +253,7 @@ class MlaStep:
         B, H = cfg.B, cfg.H
         self.Kp = torch.zeros((B, cfg.T, cfg.r), dtype=torch.int16, device=device)
         self.q_abs = torch.empty((B, H, cfg.d_c), dtype=torch.float32, device=device)
-        self.q_sel = torch.empty((B, cfg.r), dtype=torch.float32, device=device)
+        self.q_sel = torch.empty((B, 9, cfg.r), dtype=torch.float32, device=device)   # the query in 9 parts
         self.scores = torch.empty((B, cfg.T), dtype=torch.float32, device=device)
         nbytes = max(jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k),
                      jssa.jssa_mla_score_topk_workspace_size(self.desc, cfg.k))
