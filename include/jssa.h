@@ -336,11 +336,12 @@ JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_se
  * jssa_mla_score followed by the latent top-k (jssa_topk with H = 1): the same
  * scores and the same idx [B,k], in fewer and cheaper passes (per sequence
  * one selection over the shared latent cache, digest Perspective; ties and
- * absent tokens as jssa_topk). The score stream also records, per
- * 1024-token chunk, a key that a known number of the chunk's tokens reach;
- * when the chunks of a sequence together guarantee k tokens at or above the
- * smallest such key, no token below it can be selected and the top-k pass
- * keeps only the tokens above it. The selection is exact either way.
+ * absent tokens as jssa_topk). The score stream also keeps each 1024-token
+ * chunk's own best tokens (about 4x its share of k, at least 64), and one
+ * final pass per sequence selects from the union of those lists. The union
+ * holds the sequence's top k unless a chunk held more of them than its list
+ * (checked on the device once the k-th key is known); such a sequence is
+ * selected again from its scores. The selection is exact either way.
  *  k in [1, min(4096, max_seq)]; scores device fp32 [B,max_seq] (written),
  *  idx device int32 [B,k] (written); ws device, at least
  *  jssa_mla_score_topk_workspace_size bytes, its contents scratch.

@@ -1019,12 +1019,16 @@ _MLA_TOPK_CASES = [
 
 @pytest.mark.parametrize("case", _MLA_TOPK_CASES, ids=[c[0] for c in _MLA_TOPK_CASES])
 def test_mla_score_topk_matches_separate_passes(J, case):
-    """jssa_mla_score_topk (score stream with chunk bounds, floored top-k)
+    """jssa_mla_score_topk (score stream with per-chunk lists, one final
+    pass over their union with the on-device check and the per-row
+    selection from scores when a chunk held more of the top k than its list)
     against jssa_mla_score + jssa_topk on the same inputs: identical scores
     and identical indices, and the indices equal the oracle's selection on
-    those scores. Covers the bounded path (full, ragged, unaligned rows,
-    clustered top tokens, every score tied, k = 64 and 4096) and the plain
-    path (too few chunks for a bound)."""
+    those scores. Covers the list path where the lists suffice (full 128K,
+    unaligned rows, k = 64 and 4096), rows they do not suffice for (a short
+    ragged row with k near its length, 600 clustered top tokens in two
+    chunks, every score tied) and the plain path (too few chunks for
+    lists)."""
     name, B, T, k, lens, kind = case
     r, H = 64, 128
     rng = np.random.default_rng(sum(map(ord, name)))

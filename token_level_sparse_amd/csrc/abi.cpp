@@ -425,26 +425,37 @@ jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const 
 }
 
 namespace {
-// Selection over the latent rows with chunk bounds: each stream chunk of a
-// row reports a key that 4 * cw of its tokens reach (cw per wave), and the
-// chunks of a row together must cover k for that key to bound the row's
-// k-th key from below. Used while that needs at most 16 per wave.
-int mla_bound_cw(int max_seq, int k) {
+// Per-chunk list length for the latent top-k: the score stream keeps each
+// 1024-token chunk's own top kc, and the final pass selects from the union
+// of those lists; the union holds the row's top k unless some chunk holds
+// more than about kc of them (checked on the device; such a row is selected
+// from its scores instead, so the result is exact either way). kc is 4x the
+// average per-chunk share of k, at least 64; 0 (no lists: score, then the
+// plain top-k) when that exceeds 256 or a row has more chunks than one final
+// block takes.
+int mla_list_k(int max_seq, int k) {
   const int nb = jssa::mla_score_chunks(max_seq);
-  const int c = (k + nb - 1) / nb;               // tokens per chunk
-  const int cw = (c + 3) / 4;                    // per wave
-  return cw <= 16 ? cw : 0;
+  if (nb > 4096) return 0;
+  int kc = 4 * ((k + nb - 1) / nb);
+  kc = kc < 64 ? 64 : kc;
+  kc = (kc + 3) & ~3;
+  return kc <= 256 ? kc : 0;
 }
+constexpr int kMlaChunk = 1024;
 }  // namespace
 
 jssa_status jssa_mla_score_topk_workspace_size(const jssa_mla_desc* desc, int32_t k, size_t* bytes) {
   if (jssa_status s = check_mla(__func__, desc)) return s;
   size_t plain = 0;
   if (jssa_status s = jssa_topk_workspace_size(desc->B, 1, desc->max_seq, k, &plain)) return s;
-  const size_t nb = size_t(jssa::mla_score_chunks(desc->max_seq));
-  const size_t floored = jssa::align256(size_t(desc->B) * nb * sizeof(uint32_t)) +
-                         jssa::topk_floor_workspace_bytes(desc->B, desc->max_seq, k);
-  *bytes = mla_bound_cw(desc->max_seq, k) ? floored : plain;
+  const int kc = mla_list_k(desc->max_seq, k);
+  if (kc == 0) {
+    *bytes = plain;
+    return JSSA_OK;
+  }
+  size_t lists = 0;
+  jssa::carve_segs(nullptr, desc->B, jssa::mla_score_chunks(desc->max_seq), jssa::seg_cap(kc, kMlaChunk), &lists);
+  *bytes = lists;
   return JSSA_OK;
 }
 
@@ -460,19 +471,17 @@ jssa_status jssa_mla_score_topk(const jssa_mla_desc* desc, const float* q_sel, c
   const jssa::MlaDev m = to_mla(desc);
   const auto* Kp = static_cast<const uint16_t*>(Kp_lat);
   const hipStream_t st = S(stream);
-  const int cw = mla_bound_cw(desc->max_seq, k);
+  const int kc = mla_list_k(desc->max_seq, k);
   hipError_t e;
-  if (cw == 0) {
+  if (kc == 0) {
     e = jssa::launch_mla_score(m, q_sel, Kp, scores, st);
     if (e == hipSuccess) e = jssa::launch_topk(desc->B, 1, desc->max_seq, desc->seq_lens, scores, k, idx, ws, st);
   } else {
-    const int nb = jssa::mla_score_chunks(desc->max_seq);
-    auto* bounds = static_cast<uint32_t*>(ws);
-    void* rest = static_cast<char*>(ws) + jssa::align256(size_t(desc->B) * nb * sizeof(uint32_t));
-    e = jssa::launch_mla_score(m, q_sel, Kp, scores, st, bounds, cw);
+    const jssa::CandSegs lists = jssa::carve_segs(ws, desc->B, jssa::mla_score_chunks(desc->max_seq),
+                                                  jssa::seg_cap(kc, kMlaChunk), nullptr);
+    e = jssa::launch_mla_score_lists(m, q_sel, Kp, scores, lists, kc, st);
     if (e == hipSuccess)
-      e = jssa::launch_topk_floor(desc->B, 1, desc->max_seq, desc->seq_lens, scores, k, idx, rest, bounds, nb,
-                                  4 * cw, st);
+      e = jssa::launch_topk_lists(desc->B, desc->max_seq, desc->seq_lens, scores, k, idx, lists, kMlaChunk, st);
   }
   return hip_status(e, __func__);
 }

@@ -41,11 +41,6 @@ hipError_t launch_screen(const GqaDev& g, const uint16_t* q, const float* P, con
                          int32_t* kept_tiles, hipStream_t st);
 hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores,
                        int k, int32_t* idx, void* ws, hipStream_t st);
-// Top-k of rows whose stream also wrote per-chunk bounds ([rows, nb], keys
-// reached by at least bound_c tokens of the chunk, or 0xffffffff).
-size_t topk_floor_workspace_bytes(int rows, int max_seq, int k);
-hipError_t launch_topk_floor(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
-                             int32_t* idx, void* ws, const uint32_t* bounds, int nb, int bound_c, hipStream_t st);
 
 hipError_t launch_indexed(const GqaDev& g, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                           const int32_t* idx, int k, int S, float scale, float* part_o,
@@ -84,11 +79,17 @@ hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const flo
 constexpr int kMlaSelParts = 9;
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
                              const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st);
-// bound (optional, [B, mla_score_chunks(max_seq)]): per chunk of the stream
-// a key reached by at least 4 * bound_cw of its tokens, or 0xffffffff
 hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
-                            hipStream_t st, uint32_t* bound = nullptr, int bound_cw = 0);
+                            hipStream_t st);
 int mla_score_chunks(int max_seq);
+// The MLA score stream writing, per 1024-token chunk, the chunk's own top
+// list_k (chunk_select; segment floor 0) to segment (b, chunk) of `lists`.
+hipError_t launch_mla_score_lists(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
+                                  CandSegs lists, int list_k, hipStream_t st);
+// Exact top-k of B score rows from their chunk lists (final select with the
+// list check; rows whose lists fall short are selected from their scores).
+hipError_t launch_topk_lists(int B, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+                             int32_t* idx, CandSegs lists, int chunk_len, hipStream_t st);
 hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_t* latent,
                               const int32_t* idx, int k, int S, float scale, float* part_o,
                               float* part_lse, hipStream_t st);

@@ -85,17 +85,10 @@ struct FusedOut {
   int n_sink, n_local;      // sink tokens: t < n_sink; local tokens: t >= T_b - n_local
   const uint32_t* keep;     // screening: one bit per 64-token tile ([rows, keep_words]); nullptr: all kept
   int keep_words;
-  // score-only stream: per chunk a key that at least 4 * bound_cw of the
-  // chunk's tokens reach ([rows, chunks]; kNoBound: no such guarantee), or
-  // nullptr
-  uint32_t* bound;
-  int bound_cw;
 };
 // A token of a dropped tile is staged with this value: a NaN whose score_key
 // is 0, the key of no token (finite scores map to keys above 0).
 constexpr uint32_t kDroppedBits = 0xffffffffu;
-// A chunk bound that guarantees nothing (no token key reaches it).
-constexpr uint32_t kNoBound = 0xffffffffu;
 
 template <int R>
 struct ScoreSmem {
@@ -184,7 +177,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   const bool paged = g.page_size != 0;
   const int64_t ubase = (int64_t(b) * g.Hkv + j) * int64_t(g.max_seq) * R;   // contiguous unit base
 
-  const int64_t seg = FUSED ? int64_t(b * g.Hkv + j) * fo.segs.nseg + cx : 0;
+  const bool lists = !FUSED && fo.segs.info != nullptr;   // score-only stream writing chunk lists (kernel-uniform)
+  const int64_t seg = FUSED || lists ? int64_t(b * g.Hkv + j) * fo.segs.nseg + cx : 0;
   if (t_begin >= Tb) {                       // whole chunk past the sequence's end
     if (!FUSED || fo.write_scores) {
       const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
@@ -194,7 +188,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
       if (fo.pmax) fo.pmax[seg] = 0u;
     }
-    if (!FUSED && fo.bound && tid == 0) fo.bound[int64_t(b * g.Hkv + j) * gridDim.x + cx] = kNoBound;
+    if (lists && tid == 0) write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
     return;
   }
   // Tokens of this block are [t_begin, tend); loads of later positions are
@@ -457,39 +451,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     }
   }
   if constexpr (!FUSED) {
-    if (fo.bound) {                                      // block-uniform
-      // Lower bound for the row's top-k threshold: thread i's largest key
-      // over its tokens i + NT e; each wave's bound_cw-th largest of those
-      // (distinct threads, so distinct tokens: bound_cw tokens reach it);
-      // the block's bound is the smallest over the waves, reached by
-      // kWaves * bound_cw tokens. A wave with fewer threads holding a token
-      // gives no guarantee (kNoBound).
-      __shared__ uint32_t wb[kWaves];
-      uint32_t v = 0u;
+    if (lists) {
+      // The chunk's own top fo.k (every real token at or above its fo.k-th
+      // key, chunk_select), written as the chunk's candidate segment in
+      // token order; thread tid takes tokens tid*TPW .. tid*TPW+TPW-1 (the
+      // stage is in token order, and positions past the end hold -inf: key 0).
+      uint32_t key[TPW];
 #pragma unroll
-      for (int e = 0; e < TPW; ++e) {
-        const uint32_t x = score_key(stage[sidx(tid + NT * e)]);
-        v = x > v ? x : v;
-      }
-      uint32_t kth = 0u;
-      for (int i = 0; i < fo.bound_cw; ++i) {
-        const uint32_t mx = wave_max_u32(v);
-        kth = mx;
-        const uint64_t at = __ballot(v == mx);            // one lane holding it drops out
-        if (lane == int(__builtin_ctzll(at))) v = 0u;
-      }
-      if (lane == 0) wb[w] = kth;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t bd = 0xffffffffu;
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-          ok = ok && wb[i] != 0u;
-          bd = wb[i] < bd ? wb[i] : bd;
-        }
-        fo.bound[int64_t(b * g.Hkv + j) * gridDim.x + cx] = ok ? bd : kNoBound;
-      }
+      for (int e = 0; e < TPW; ++e) key[e] = score_key(stage[tid * TPW + e]);
+      int n = Tb - t_begin;
+      n = n > chunk ? chunk : n;
+      __syncthreads();                                   // the stage is reused below
+      ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
+      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+      // a list of one chunk bounds nothing about the row's k-th key: no floor
+      if (tid == 0) fo.segs.info[seg].floor = 0u;
     }
   }
   if constexpr (FUSED) {
@@ -565,7 +541,21 @@ hipError_t launch_score(const GqaDev& g, const uint16_t* q, const float* P, cons
 }
 
 hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
-                            hipStream_t st, uint32_t* bound, int bound_cw) {
+                            hipStream_t st) {
+  GqaDev g{};
+  g.B = m.B;
+  g.Hq = 1;
+  g.Hkv = 1;
+  g.G = 1;
+  g.d = kDc;
+  g.r = m.r;
+  g.max_seq = m.max_seq;
+  g.seq_lens = m.seq_lens;
+  return launch_score_t<kMla, false>(g, nullptr, q_sel, nullptr, Kp, scores, st, FusedOut{});
+}
+
+hipError_t launch_mla_score_lists(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
+                                  CandSegs lists, int list_k, hipStream_t st) {
   GqaDev g{};
   g.B = m.B;
   g.Hq = 1;
@@ -576,8 +566,8 @@ hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t*
   g.max_seq = m.max_seq;
   g.seq_lens = m.seq_lens;
   FusedOut fo{};
-  fo.bound = bound;
-  fo.bound_cw = bound_cw;
+  fo.segs = lists;
+  fo.k = list_k;
   return launch_score_t<kMla, false>(g, nullptr, q_sel, nullptr, Kp, scores, st, fo);
 }
 

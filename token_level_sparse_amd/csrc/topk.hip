@@ -46,16 +46,8 @@ __device__ __forceinline__ int row_len(int max_seq, const int32_t* seq_lens, int
 // the key of no token.
 constexpr uint32_t kNoTokenBits = 0xffffffffu;
 
-// bounds (optional, [rows, nb]): per chunk of the score stream a key that at
-// least bound_c of its tokens reach, or kNoBound. With P chunks of a row
-// giving a bound and P * bound_c >= k, the row's k-th largest key is at or
-// above the smallest of those bounds, so every key below it is dropped here
-// (taken as no token): the row keeps few candidates however large k is.
-constexpr uint32_t kNoBound = 0xffffffffu;
-
 __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens,
-                                                    const float* __restrict__ scores, int k, CandSegs segs,
-                                                    const uint32_t* __restrict__ bounds, int nb, int bound_c) {
+                                                    const float* __restrict__ scores, int k, CandSegs segs) {
   // The chunk's scores go through LDS: loaded 16 bytes per lane (coalesced),
   // staged so that thread i then reads its kCE consecutive tokens
   // o = i*kCE + e at e*SS + i (token o sits at (o % kCE)*SS + o / kCE; the
@@ -81,36 +73,6 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
     if (tid == 0) write_info(segs, seg, 0, 0u, 0u, 0xffffffffu);
     return;
   }
-  // the row's floor from the stream's chunk bounds (computed while the
-  // chunk's score loads are in flight)
-  uint32_t floor = 0u;                           // keys below it cannot be in the row's top k
-  auto row_floor = [&]() {
-    if (!bounds) return;                         // kernel-uniform
-    __shared__ uint32_t fr[2][kCT / 64];
-    const int lane = tid & 63, wv = tid >> 6;
-    uint32_t mn = kNoBound, cnt = 0u;
-    for (int i = tid; i < nb; i += kCT) {
-      const uint32_t v = bounds[int64_t(row) * nb + i];
-      if (v != kNoBound) {
-        mn = v < mn ? v : mn;
-        ++cnt;
-      }
-    }
-    mn = wave_min_u32(mn);
-    cnt = wave_sum_u32(cnt);
-    if (lane == 0) {
-      fr[0][wv] = mn;
-      fr[1][wv] = cnt;
-    }
-    __syncthreads();
-    uint32_t m2 = kNoBound, c2 = 0u;
-#pragma unroll
-    for (int i = 0; i < kCT / 64; ++i) {
-      m2 = fr[0][i] < m2 ? fr[0][i] : m2;
-      c2 += fr[1][i];
-    }
-    floor = int64_t(c2) * bound_c >= k ? m2 : 0u;
-  };
   float* stage = reinterpret_cast<float*>(sbuf);
   auto sidx = [](int o) { return (o % kCE) * SS + o / kCE; };
   const float none = __uint_as_float(kNoTokenBits);
@@ -124,7 +86,6 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
       const int o = (i * kCT + tid) * 4;
       v[i] = *reinterpret_cast<const f32x4*>(src + (o < lim ? o : lim - 4));
     }
-    row_floor();
 #pragma unroll
     for (int i = 0; i < kCE / 4; ++i) {
       const int o = (i * kCT + tid) * 4;
@@ -140,7 +101,6 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
       const int o = i * kCT + tid;
       v[i] = src[o < n ? o : n - 1];
     }
-    row_floor();
 #pragma unroll
     for (int i = 0; i < kCE; ++i) {
       const int o = i * kCT + tid;
@@ -150,15 +110,10 @@ __global__ __launch_bounds__(kCT) void chunk_kernel(int H, int max_seq, const in
   __syncthreads();
   uint32_t key[kCE];
 #pragma unroll
-  for (int e = 0; e < kCE; ++e) {                // token tid*kCE + e
-    const uint32_t x = score_key(stage[e * SS + tid]);
-    key[e] = x >= floor ? x : 0u;
-  }
-  // the top-two bound first (block-uniform; it leaves the stage intact and
-  // reads it, so not with a floor), the histogram select when it does not
-  // apply or keeps too many
-  const bool done = n == kChunk && k <= kCT && floor == 0u &&
-                    chunk_select_top2<kCT, kCE>(key, start, k, tsm, stage, SS, segs, seg);
+  for (int e = 0; e < kCE; ++e) key[e] = score_key(stage[e * SS + tid]);   // token tid*kCE + e
+  // the top-two bound first (block-uniform; it leaves the stage intact),
+  // the histogram select when it does not apply or keeps too many
+  const bool done = n == kChunk && k <= kCT && chunk_select_top2<kCT, kCE>(key, start, k, tsm, stage, SS, segs, seg);
   if (!done) {
     __syncthreads();                             // the stage is reused below
     ChunkSmem<kCT, kCE>& csm = *reinterpret_cast<ChunkSmem<kCT, kCE>*>(sbuf);
@@ -230,16 +185,86 @@ struct FinalSmem {
   int nbin;
 };
 
+// Exact top-k of one score row straight from its scores, for rows whose
+// candidate lists were not enough: three radix levels over the order-
+// preserving keys (bits 31..20, 19..8, 7..0; each a histogram of the keys
+// that match the levels above), then the taken tokens in token order, tiles
+// of NT with block scans (ties, lowest index first). Slow (the row is read
+// four times), and only run when a row's lists do not hold its top k.
+template <int NT>
+__device__ void lists_fallback(const float* __restrict__ srow, int Tb, int k, int32_t* __restrict__ dst,
+                               uint32_t* hist, ScanSmem<NT>& scan, int* res) {
+  const int tid = threadIdx.x;
+  const int need = min(k, Tb);
+  uint32_t tkey = 0u, prefix = 0u, pmask = 0u;
+  int trem = 0x7fffffff;
+  if (need < Tb) {
+    int rem = need;
+    constexpr int kShift[3] = {20, 8, 0};
+    constexpr uint32_t kMask[3] = {0xfffu, 0xfffu, 0xffu};
+    for (int lv = 0; lv < 3; ++lv) {
+      const int sh = kShift[lv];
+      for (int i = tid; i < kFinBins; i += NT) hist[i] = 0u;
+      __syncthreads();
+      for (int t = tid; t < Tb; t += NT) {
+        const uint32_t key = score_key(srow[t]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & kMask[lv]], 1u);
+      }
+      __syncthreads();
+      pick_bin<NT, kFinBins / NT>(hist, rem, true, scan, res);
+      const uint32_t D = uint32_t(res[0]);
+      rem -= res[1];
+      const int cnt = int(hist[D]);
+      __syncthreads();
+      prefix |= D << sh;
+      pmask |= kMask[lv] << sh;
+      tkey = prefix;                   // the lowest key of the bin
+      if (cnt == rem) break;           // the whole bin is taken: every key >= tkey
+      if (lv == 2) trem = rem;         // one key value, tied
+    }
+  }
+  int tie_base = 0, out_base = 0;
+  for (int t0 = 0; t0 < Tb; t0 += NT) {
+    const int t = t0 + tid;
+    const uint32_t key = t < Tb ? score_key(srow[t]) : 0u;
+    const bool real = t < Tb;
+    int tt = 0, tr = 0;
+    if (trem != 0x7fffffff) {
+      const int nt = real && key == tkey ? 1 : 0;
+      tr = block_scan<NT>(nt, scan, &tt) - nt + tie_base;
+    }
+    const bool take = real && (key > tkey || (key == tkey && tr < trem));
+    int st;
+    const int at = block_scan<NT>(take ? 1 : 0, scan, &st) - (take ? 1 : 0) + out_base;
+    if (take) dst[at] = t;
+    tie_base += tt;
+    out_base += st;
+  }
+  for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
+}
+
 // One block per (row, group of gs consecutive segments). MERGE = false: the
 // group is the whole row (gs = nseg) and the block writes the row's selected
 // indices. MERGE = true: the block writes its group's first min(k, n)
 // candidates of the (key desc, index asc) order, as (key, index) pairs in
 // token order, to segment (row, group) of `outs`: a smaller candidate list
 // for the next level that still holds the row's top k.
-template <int NT, int EF, bool MERGE>
+// LISTS (final level only): each segment holds the top candidates of one
+// chunk of `lists.chunk_len` tokens of the score row `lists.scores`, a list
+// that need not contain the row's top k. A chunk that dropped real tokens
+// keeps every key above its segment's bot, so the union holds the row's top
+// k when every such chunk's bot is below the row's k-th key; the block checks
+// that once the k-th key is known, and otherwise selects the row again from
+// its scores (lists_fallback). Either way the result is exact.
+struct ListArgs {
+  const float* scores;
+  int chunk_len;
+};
+
+template <int NT, int EF, bool MERGE, bool LISTS = false>
 __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int32_t* __restrict__ seq_lens, int k,
                                                    CandSegs segs, int gs, int32_t* __restrict__ out, CandSegs outs,
-                                                   DeltaArgs dl = DeltaArgs{}) {
+                                                   DeltaArgs dl = DeltaArgs{}, ListArgs lists = ListArgs{}) {
   constexpr int NW = NT / 64;
   __shared__ FinalSmem<NT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -510,6 +535,23 @@ __global__ __launch_bounds__(NT) void final_kernel(int H, int max_seq, const int
     }
   }
 
+  if constexpr (LISTS) {
+    // (!search: every candidate is taken, so a chunk that dropped any real
+    // token leaves it out: the F = 0 test below then fails for it)
+    const uint32_t F = search ? tkey : 0u;
+    bool bad = false;
+    for (int s = tid; s < nseg; s += NT) {
+      const int real = min(lists.chunk_len, max(0, Tb - (s0 + s) * lists.chunk_len));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ginfo + s);
+      bad = bad || (int(v.x) < real && v.w >= F);
+    }
+    if (__syncthreads_or(bad)) {                       // block-uniform
+      lists_fallback<NT>(lists.scores + int64_t(row) * max_seq, Tb, k, out + int64_t(row) * k, sm.hist, sm.scan,
+                         sm.res);
+      return;
+    }
+  }
+
   // Output in list order, which is ascending token order: two block scans
   // per page of candidates, one ranking the tied candidates and one placing
   // the taken ones.
@@ -679,38 +721,17 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
   }
   size_t main_bytes = 0;
   CandSegs segs = carve_segs(wsp, rows, nchunks, seg_cap(k, kChunk), &main_bytes);
-  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs,
-                     nullptr, 0, 0);
+  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, static_cast<char*>(wsp) + main_bytes, st);
 }
 
-size_t topk_floor_workspace_bytes(int rows, int max_seq, int k) {
-  size_t total = 0;
-  carve_segs(nullptr, rows, chunks_of(max_seq), seg_cap(k, kChunk), &total);
-  return total;
-}
-
-// Top-k of score rows with per-chunk bounds of the stream that wrote them
-// (see chunk_kernel): the chunk pass keeps only keys at or above the row's
-// floor, and the final pass reads the lists directly, however many segments
-// (a list longer than its registers is read from memory level by level:
-// slower, same result).
-hipError_t launch_topk_floor(int B, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
-                             int32_t* idx, void* wsp, const uint32_t* bounds, int nb, int bound_c, hipStream_t st) {
-  const int rows = B * H;
-  const int nchunks = chunks_of(max_seq);
-  if (nchunks > kMaxSeg) return hipErrorInvalidValue;
-  CandSegs segs = carve_segs(wsp, rows, nchunks, seg_cap(k, kChunk), nullptr);
-  hipLaunchKernelGGL(chunk_kernel, dim3(nchunks, rows), dim3(kCT), 0, st, H, max_seq, seq_lens, scores, k, segs,
-                     bounds, nb, bound_c);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // (a floored row keeps a few k candidates: the 12-per-thread final holds
-  // them directly; a longer list is read from memory)
-  hipLaunchKernelGGL((final_kernel<1024, 12, false>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k, segs,
-                     segs.nseg, idx, CandSegs{}, DeltaArgs{});
+hipError_t launch_topk_lists(int B, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+                             int32_t* idx, CandSegs lists, int chunk_len, hipStream_t st) {
+  if (lists.nseg > kMaxSeg) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((final_kernel<1024, 12, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
+                     lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
   return hipGetLastError();
 }
 
