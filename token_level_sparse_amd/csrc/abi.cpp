@@ -429,15 +429,15 @@ namespace {
 // 1024-token chunk's own top kc, and the final pass selects from the union
 // of those lists; the union holds the row's top k unless some chunk holds
 // more than about kc of them (checked on the device; such a row is selected
-// from its scores instead, so the result is exact either way). kc is 4x the
-// average per-chunk share of k, at least 64; 0 (no lists: score, then the
+// from its scores instead, so the result is exact either way). kc is 3x the
+// average per-chunk share of k, at least 48; 0 (no lists: score, then the
 // plain top-k) when that exceeds 256 or a row has more chunks than one final
 // block takes.
 int mla_list_k(int max_seq, int k) {
   const int nb = jssa::mla_score_chunks(max_seq);
   if (nb > 4096) return 0;
-  int kc = 4 * ((k + nb - 1) / nb);
-  kc = kc < 64 ? 64 : kc;
+  int kc = 3 * ((k + nb - 1) / nb);
+  kc = kc < 48 ? 48 : kc;
   kc = (kc + 3) & ~3;
   return kc <= 256 ? kc : 0;
 }

@@ -463,7 +463,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       n = n > chunk ? chunk : n;
       __syncthreads();                                   // the stage is reused below
       ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
-      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+      // (no slack: the union of these lists is what the final pass selects from)
+      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg, 0);
       // a list of one chunk bounds nothing about the row's k-th key: no floor
       if (tid == 0) fo.segs.info[seg].floor = 0u;
     }

@@ -118,7 +118,8 @@ struct ChunkSmem {
 };
 
 // Extra candidates a chunk may keep in its threshold bin before a second,
-// finer histogram level pays for itself (they only cost the final pass work).
+// finer histogram level pays for itself (they only cost the final pass work;
+// callers whose final pass is the bottleneck pass a smaller slack).
 constexpr int kSelSlack = 32;
 
 // Chunk-local selection. Each thread holds E keys; key e of thread tid is
@@ -138,7 +139,7 @@ constexpr int kSelSlack = 32;
 //  - otherwise the smallest real key.
 template <int NT, int E>
 __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n, int k, ChunkSmem<NT, E>& sm,
-                             CandSegs out, int64_t seg) {
+                             CandSegs out, int64_t seg, int slack = kSelSlack) {
   static_assert(E <= 32, "one mask bit per key");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -229,7 +230,7 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
     const int cnt0 = int(sm.hist[d0]);
     thr = lo + (d0 << sh0);
     __syncthreads();
-    if (sh0 > 0 && cnt0 - need > kSelSlack) {          // block-uniform
+    if (sh0 > 0 && cnt0 - need > slack) {              // block-uniform
       const int sh1 = sh0 > 11 ? sh0 - 11 : 0;
       for (int i = tid; i < kSelBins; i += NT) sm.hist[i] = 0u;
       __syncthreads();

@@ -730,8 +730,15 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
 hipError_t launch_topk_lists(int B, int max_seq, const int32_t* seq_lens, const float* scores, int k,
                              int32_t* idx, CandSegs lists, int chunk_len, hipStream_t st) {
   if (lists.nseg > kMaxSeg) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((final_kernel<1024, 12, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
-                     lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
+  // lists of up to 56 per chunk (segment capacity 120) are held 8 per thread
+  // (a segment of up to 64 read directly by its 8 threads when the row has
+  // 128 chunks), longer ones 12 per thread
+  if (lists.cap <= 120)
+    hipLaunchKernelGGL((final_kernel<1024, 8, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
+                       lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
+  else
+    hipLaunchKernelGGL((final_kernel<1024, 12, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
+                       lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
   return hipGetLastError();
 }
 
