@@ -131,7 +131,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   // Work item of this block. Blocks go to the XCDs round-robin by launch
   // position. When some chunks lie past their sequence's end (per-sequence
   // lengths, up to kPackMaxB sequences), the first launch positions take the
-  // rows' real chunks in row-major order and the rest the empty ones, which
+  // sequences' real chunks in order, the KV head varying fastest (the heads
+  // of one token range, which share the cache pages, are read together:
+  // 1-2% on a paged cache), and the rest the empty ones, which
   // only record an empty segment: the real work is dealt evenly over the
   // XCDs and CUs instead of leaving the slots of empty chunks idle. Otherwise
   // launch position x holds chunk (x + row) mod nx, so chunk c of every row
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
       if (lin < acc + c) {
         const int r = lin - acc;
         b = bb;
-        j = r / n;
-        cx = (lin < real ? 0 : nx - n) + (r - j * n);
+        j = r % g.Hkv;
+        cx = (lin < real ? 0 : nx - n) + r / g.Hkv;
         break;
       }
       acc += c;
