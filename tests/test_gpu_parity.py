@@ -267,16 +267,35 @@ FULL16K = replace(synth.LLAMA8B_32K, B=1, T=16384, seed=84)
 
 @pytest.mark.parametrize("case", ["ragged32", "r48_paged_k2048", "r128_k4096", "tiny_k1", "r16_T100",
                                   "full_k64", "full_k256_ties", "full_all_equal", "full_k257",
-                                  "paged_full_invalid", "clustered_full_k256"])
+                                  "paged_full_invalid", "clustered_full_k256",
+                                  "lists_k2048", "lists_paged_ragged_k2048", "lists_clustered_k2048",
+                                  "lists_all_equal_k2048"])
 def test_score_topk_fused_equals_split(J, PL, case):
     """The fused score + top-k pass returns exactly the indices (and, when
     asked, the scores) of jssa_score followed by jssa_topk. The full_* and
     paged_full_* cases fill every 8192-token chunk, which takes the fused
     kernel's top-two bound path for k <= 256 (ties, all-equal scores, -inf
     tokens behind invalid pages), its fallback to the histogram select on
-    clustered keys, and the general path for k = 257."""
+    clustered keys, and the general path for k = 257. The lists_* cases
+    (8 chunks, k = 2048) take the chunk-list path: lists of 1024 per chunk,
+    one final pass over their union, where the lists hold each row's top k
+    (low-rank keys, contiguous and paged with ragged lengths) and where some
+    row needs the selection from its scores (clustered keys, all scores
+    equal)."""
     edit = None
-    if case.startswith("full_"):
+    if case.startswith("lists_"):
+        T64 = replace(synth.LLAMA8B_32K, B=1, T=65536, seed=87)
+        k = 2048
+        if case == "lists_k2048":
+            inp = synth.make_gqa(T64)
+        elif case == "lists_paged_ragged_k2048":
+            inp = synth.make_gqa(replace(synth.PAGED_QWEN14B, B=2, T=65536, len_lo=30000, len_hi=65536, seed=88))
+        elif case == "lists_clustered_k2048":
+            inp = synth.make_gqa(replace(T64, key_model="clustered", cluster_len=4096, seed=89))
+        else:
+            inp = synth.make_gqa(T64)
+            edit = lambda c: c.Kp.zero_()
+    elif case.startswith("full_"):
         inp = synth.make_gqa(FULL16K)
         k = {"full_k64": 64, "full_k256_ties": 256, "full_all_equal": 200, "full_k257": 257}[case]
         if case == "full_k256_ties":      # 37 distinct projected keys per (b, j): long runs of equal scores
@@ -329,7 +348,8 @@ def test_score_topk_fused_equals_split(J, PL, case):
     np.testing.assert_array_equal(_np(h.scores), _np(a.scores))
     # the tie-heavy and full-chunk cases also against the oracle's own
     # selection, computed from its own (identically edited) projected keys
-    if case in ("full_k256_ties", "full_all_equal", "paged_full_invalid", "clustered_full_k256", "full_k64"):
+    if case in ("full_k256_ties", "full_all_equal", "paged_full_invalid", "clustered_full_k256", "full_k64",
+                "lists_clustered_k2048", "lists_all_equal_k2048"):
         if case == "paged_full_invalid":
             inp.page_table = table
         idx = _np(a.idx)
@@ -338,12 +358,12 @@ def test_score_topk_fused_equals_split(J, PL, case):
                 K, V, Kp, s_, hs = U.oracle_unit(inp, bb, j)
                 if case == "full_k256_ties":
                     Kp = Kp[np.arange(Kp.shape[0]) % 37]
-                elif case == "full_all_equal":
+                elif case in ("full_all_equal", "lists_all_equal_k2048"):
                     Kp = np.zeros_like(Kp)
-                if case in ("full_k256_ties", "full_all_equal"):
+                if case in ("full_k256_ties", "full_all_equal", "lists_all_equal_k2048"):
                     s_ = O.subspace_scores(inp.q[bb, hs], inp.P[j], Kp)
                 U.check_indices(idx[bb, j], s_, k)
-                if case == "full_all_equal":          # all scores tie: the k lowest indices
+                if case in ("full_all_equal", "lists_all_equal_k2048"):   # all scores tie: the k lowest indices
                     np.testing.assert_array_equal(idx[bb, j], np.arange(k))
 
 

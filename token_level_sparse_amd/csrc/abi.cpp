@@ -113,6 +113,78 @@ jssa::MlaDev to_mla(const jssa_mla_desc* m) {
 
 }  // namespace
 
+namespace {
+// Workspace of the fused score -> top-k selection (jssa_score_topk and the
+// split _chunks / _final calls). Classic: each 8192-token chunk keeps every
+// token that can be among its row's top k (candidate segments of
+// score_topk_segment_cap(k)), merged level by level when a row's lists are
+// too long for one final pass. Lists (budgets whose candidates would need a
+// merge level): each chunk keeps only its own top kc, kc = 4x the chunk's
+// share of k; one final pass selects from their union and checks that the
+// union held the row's top k, selecting the row again from its scores when
+// it did not (so the stream also writes the scores, into the workspace).
+struct TopkWs {
+  jssa::CandSegs segs;
+  void* merge_ws;   // classic: merge levels
+  float* scores;    // lists: the rows' scores [rows, max_seq]; classic: nullptr
+  int kc;           // lists: per-chunk list length; classic: 0
+  size_t bytes;
+};
+
+int gqa_list_k(int max_seq, int k) {
+  const int nseg = jssa::score_topk_segments(max_seq);
+  if (nseg <= 1 || int64_t(nseg) * k <= 8192) return 0;          // one final pass already
+  int kc = 4 * ((k + nseg - 1) / nseg);
+  kc = kc < 64 ? 64 : kc;
+  kc = (kc + 3) & ~3;
+  return 2 * kc <= k ? kc : 0;
+}
+
+TopkWs topk_ws(const jssa_gqa_desc* d, int k, void* ws, bool allow_lists) {
+  TopkWs w{};
+  const int rows = d->B * d->Hkv, nseg = jssa::score_topk_segments(d->max_seq);
+  w.kc = allow_lists ? gqa_list_k(d->max_seq, k) : 0;
+  size_t main_bytes = 0;
+  if (w.kc) {
+    w.segs = jssa::carve_segs(ws, rows, nseg, jssa::seg_cap(w.kc, jssa::score_topk_chunk_len()), &main_bytes);
+    w.scores = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + main_bytes) : nullptr;
+    w.merge_ws = nullptr;
+    w.bytes = main_bytes + jssa::align256(size_t(rows) * d->max_seq * sizeof(float));
+  } else {
+    w.segs = jssa::carve_segs(ws, rows, nseg, jssa::score_topk_segment_cap(k), &main_bytes);
+    w.merge_ws = ws ? static_cast<char*>(ws) + main_bytes : nullptr;
+    w.scores = nullptr;
+    w.bytes = main_bytes + jssa::merge_workspace_bytes(rows, nseg, k);
+  }
+  return w;
+}
+
+// the final pass of either layout
+hipError_t topk_ws_final(const jssa_gqa_desc* d, int k, const TopkWs& w, int32_t* idx, hipStream_t st) {
+  if (w.kc)
+    return jssa::launch_topk_lists(d->B * d->Hkv, d->Hkv, d->max_seq, d->seq_lens, w.scores, k, idx, w.segs,
+                                   jssa::score_topk_chunk_len(), st);
+  return jssa::launch_select_final(d->B * d->Hkv, d->Hkv, d->max_seq, d->seq_lens, k, w.segs, idx, w.merge_ws, st);
+}
+
+// the fused stream of either layout (scores: the caller's optional buffer)
+hipError_t topk_ws_chunks(const jssa_gqa_desc* d, const void* q, const float* P, const void* Kp, int k,
+                          float* scores, const TopkWs& w, hipStream_t st) {
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* Kp16 = static_cast<const uint16_t*>(Kp);
+  if (w.kc) return jssa::launch_score_chunks_lists(to_dev(d), q16, P, Kp16, w.kc, w.scores, scores, w.segs, st);
+  return jssa::launch_score_chunks(to_dev(d), q16, P, Kp16, k, scores, w.segs, st);
+}
+
+hipError_t score_topk_impl(const jssa_gqa_desc* d, const void* q, const float* P, const void* Kp, int k,
+                           float* scores, int32_t* idx, void* ws, bool allow_lists, hipStream_t st) {
+  const TopkWs w = topk_ws(d, k, ws, allow_lists);
+  hipError_t e = topk_ws_chunks(d, q, P, Kp, k, scores, w, st);
+  if (e == hipSuccess) e = topk_ws_final(d, k, w, idx, st);
+  return e;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t jssa_version(void) { return 100; }
@@ -198,9 +270,7 @@ jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k,
   if (!bytes) return fail(JSSA_ERR_NULL, "%s: bytes is NULL", __func__);
   if (k < 1 || k > 4096 || k > desc->max_seq)
     return fail(JSSA_ERR_SHAPE, "%s: k %d outside [1, min(4096, max_seq)]", __func__, k);
-  const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
-  jssa::carve_segs(nullptr, rows, nseg, jssa::score_topk_segment_cap(k), bytes);
-  *bytes += jssa::merge_workspace_bytes(rows, nseg, k);
+  *bytes = topk_ws(desc, k, nullptr, true).bytes;
   return JSSA_OK;
 }
 
@@ -212,13 +282,7 @@ jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const floa
   REQUIRE_ALIGNED_OPT(scores);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  size_t main_bytes = 0;
-  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(k), &main_bytes);
-  return hip_status(jssa::launch_score_topk(to_dev(desc), static_cast<const uint16_t*>(q), P,
-                                            static_cast<const uint16_t*>(Kp), k, scores, idx, segs,
-                                            static_cast<char*>(ws) + main_bytes, S(stream)),
-                    __func__);
+  return hip_status(score_topk_impl(desc, q, P, Kp, k, scores, idx, ws, true, S(stream)), __func__);
 }
 
 }  // extern "C"
@@ -264,9 +328,10 @@ extern "C" {
 jssa_status jssa_score_topk_noalloc(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
                                    int32_t k, float* scores, int32_t* idx, void* stream) {
   size_t need = 0;
-  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &need)) return s;   // (validation)
   REQUIRE_PTR(q); REQUIRE_PTR(P); REQUIRE_PTR(Kp); REQUIRE_PTR(idx);
   REQUIRE_ALIGNED_OPT(scores);
+  need = topk_ws(desc, k, nullptr, false).bytes;        // the candidate-list layout: no score rows
   if (need > kScratchBytes)
     return fail(JSSA_ERR_WORKSPACE,
                 "%s: this shape needs %zu bytes of candidate lists, more than the %zu-byte static scratch; "
@@ -274,7 +339,7 @@ jssa_status jssa_score_topk_noalloc(const jssa_gqa_desc* desc, const void* q, co
                 __func__, need, kScratchBytes);
   void* ws = nullptr;
   if (jssa_status s = scratch_address(__func__, &ws)) return s;
-  return jssa_score_topk(desc, q, P, Kp, k, scores, idx, ws, kScratchBytes, stream);
+  return hip_status(score_topk_impl(desc, q, P, Kp, k, scores, idx, ws, false, S(stream)), __func__);
 }
 
 jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
@@ -285,11 +350,7 @@ jssa_status jssa_score_topk_chunks(const jssa_gqa_desc* desc, const void* q, con
   REQUIRE_ALIGNED_OPT(scores);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(k), nullptr);
-  return hip_status(jssa::launch_score_chunks(to_dev(desc), static_cast<const uint16_t*>(q), P,
-                                              static_cast<const uint16_t*>(Kp), k, scores, segs, S(stream)),
-                    __func__);
+  return hip_status(topk_ws_chunks(desc, q, P, Kp, k, scores, topk_ws(desc, k, ws, true), S(stream)), __func__);
 }
 
 jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const void* ws, size_t ws_bytes,
@@ -299,13 +360,7 @@ jssa_status jssa_score_topk_final(const jssa_gqa_desc* desc, int32_t k, const vo
   REQUIRE_PTR(idx); REQUIRE_PTR(ws);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  size_t main_bytes = 0;
-  jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv,
-                                         jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(k), &main_bytes);
-  return hip_status(jssa::launch_select_final(desc->B * desc->Hkv, desc->Hkv, desc->max_seq, desc->seq_lens, k,
-                                              segs, idx, static_cast<char*>(const_cast<void*>(ws)) + main_bytes,
-                                              S(stream)),
+  return hip_status(topk_ws_final(desc, k, topk_ws(desc, k, const_cast<void*>(ws), true), idx, S(stream)),
                     __func__);
 }
 
@@ -318,19 +373,15 @@ jssa_status jssa_score_topk_final_attend(const jssa_gqa_desc* desc, int32_t k, c
   REQUIRE_PTR(lse);
   if (ws_bytes < need)
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  size_t main_bytes = 0;
-  const int nseg = jssa::score_topk_segments(desc->max_seq);
-  jssa::CandSegs segs = jssa::carve_segs(const_cast<void*>(ws), desc->B * desc->Hkv, nseg,
-                                         jssa::score_topk_segment_cap(k), &main_bytes);
+  const TopkWs w = topk_ws(desc, k, const_cast<void*>(ws), true);
   const jssa::GqaDev g = to_dev(desc);
   const auto* q16 = static_cast<const uint16_t*>(q);
   const auto* K16 = static_cast<const uint16_t*>(K);
   const auto* V16 = static_cast<const uint16_t*>(V);
-  if (jssa::select_attend_fused(segs, k, g.G))
-    return hip_status(jssa::launch_select_attend(g, k, segs, q16, K16, V16, scale, idx, out, lse, S(stream)),
+  if (!w.kc && jssa::select_attend_fused(w.segs, k, g.G))
+    return hip_status(jssa::launch_select_attend(g, k, w.segs, q16, K16, V16, scale, idx, out, lse, S(stream)),
                       __func__);
-  hipError_t e = jssa::launch_select_final(g.B * g.Hkv, g.Hkv, g.max_seq, g.seq_lens, k, segs, idx,
-                                           static_cast<char*>(const_cast<void*>(ws)) + main_bytes, S(stream));
+  hipError_t e = topk_ws_final(desc, k, w, idx, S(stream));
   if (e == hipSuccess) e = jssa::launch_indexed(g, q16, K16, V16, idx, k, 1, scale, out, lse, S(stream));
   return hip_status(e, __func__);
 }
@@ -481,7 +532,7 @@ jssa_status jssa_mla_score_topk(const jssa_mla_desc* desc, const float* q_sel, c
                                                   jssa::seg_cap(kc, kMlaChunk), nullptr);
     e = jssa::launch_mla_score_lists(m, q_sel, Kp, scores, lists, kc, st);
     if (e == hipSuccess)
-      e = jssa::launch_topk_lists(desc->B, desc->max_seq, desc->seq_lens, scores, k, idx, lists, kMlaChunk, st);
+      e = jssa::launch_topk_lists(desc->B, 1, desc->max_seq, desc->seq_lens, scores, k, idx, lists, kMlaChunk, st);
   }
   return hip_status(e, __func__);
 }
@@ -522,7 +573,8 @@ jssa_status jssa_mla_combine_up_v(const jssa_mla_desc* desc, int32_t n_split, co
 
 jssa_status jssa_score_topdelta_workspace_size(const jssa_gqa_desc* desc, int32_t k_max, size_t* bytes) {
   size_t base = 0;
-  if (jssa_status s = jssa_score_topk_workspace_size(desc, k_max, &base)) return s;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k_max, &base)) return s;   // (validation)
+  base = topk_ws(desc, k_max, nullptr, false).bytes;   // the candidate-list layout
   const size_t rows = size_t(desc->B) * desc->Hkv, nseg = size_t(jssa::score_topk_segments(desc->max_seq));
   *bytes = jssa::align256(base) + jssa::align256(rows * nseg * sizeof(uint32_t));
   return JSSA_OK;
@@ -555,7 +607,7 @@ jssa_status topdelta_setup(const char* fn, const jssa_gqa_desc* desc, int32_t k_
   if (counts && !aligned(counts)) return fail(JSSA_ERR_ALIGN, "%s: counts is not 16-byte aligned", fn);
   if (ws_bytes < need) return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   size_t base = 0;
-  jssa_score_topk_workspace_size(desc, k_max, &base);
+  base = topk_ws(desc, k_max, nullptr, false).bytes;
   size_t main_bytes = 0;
   const int rows = desc->B * desc->Hkv, nseg = jssa::score_topk_segments(desc->max_seq);
   td->segs = jssa::carve_segs(ws, rows, nseg, jssa::score_topk_segment_cap(k_max), &main_bytes);
@@ -638,7 +690,7 @@ jssa_status jssa_update_tile_bounds(const jssa_gqa_desc* desc, const void* Kp, c
 
 jssa_status jssa_score_topk_screened_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes) {
   size_t base = 0;
-  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &base)) return s;
+  if (jssa_status s = jssa_score_topk_workspace_size(desc, k, &base)) return s;   // (the jssa_score_topk layout)
   const size_t rows = size_t(desc->B) * desc->Hkv;
   *bytes = jssa::align256(base) + jssa::align256(rows * jssa::screen_words(desc->max_seq) * sizeof(uint32_t));
   return JSSA_OK;
@@ -658,17 +710,21 @@ jssa_status jssa_score_topk_screened_chunks(const jssa_gqa_desc* desc, const voi
     return fail(JSSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
   size_t base = 0;
   jssa_score_topk_workspace_size(desc, k, &base);
-  jssa::CandSegs segs = jssa::carve_segs(ws, desc->B * desc->Hkv, jssa::score_topk_segments(desc->max_seq),
-                                         jssa::score_topk_segment_cap(k), nullptr);
+  const TopkWs w = topk_ws(desc, k, ws, true);      // the jssa_score_topk layout: its final pass follows
   auto* keep = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + jssa::align256(base));
   const jssa::GqaDev g = to_dev(desc);
   const auto* q16 = static_cast<const uint16_t*>(q);
   const auto* Kp16 = static_cast<const uint16_t*>(Kp);
   hipError_t e = jssa::launch_screen(g, q16, P, Kp16, static_cast<const uint16_t*>(bounds), seeds, n_seed, k, keep,
                                      kept_tiles, S(stream));
-  if (e == hipSuccess)
-    e = jssa::launch_score_chunks(g, q16, P, Kp16, k, nullptr, segs, S(stream), nullptr, 0, 0, keep,
-                                  jssa::screen_words(desc->max_seq));
+  if (e == hipSuccess) {
+    if (w.kc)
+      e = jssa::launch_score_chunks_lists(g, q16, P, Kp16, w.kc, w.scores, nullptr, w.segs, S(stream), keep,
+                                          jssa::screen_words(desc->max_seq));
+    else
+      e = jssa::launch_score_chunks(g, q16, P, Kp16, k, nullptr, w.segs, S(stream), nullptr, 0, 0, keep,
+                                    jssa::screen_words(desc->max_seq));
+  }
   return hip_status(e, __func__);
 }
 

@@ -29,6 +29,15 @@ hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* 
                                int n_sink = 0, int n_local = 0, const uint32_t* keep = nullptr,
                                int keep_words = 0);
 
+// The fused stream keeping per-chunk lists of kc (not necessarily the row's
+// top k; segment floor 0), writing the scores to scores_ws (and to
+// scores_user too when non-null) for the final pass's per-row fallback;
+// keep: screening bits as in launch_score_chunks (dropped tiles are written
+// as no token).
+hipError_t launch_score_chunks_lists(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int kc,
+                                     float* scores_ws, float* scores_user, CandSegs lists, hipStream_t st,
+                                     const uint32_t* keep = nullptr, int keep_words = 0);
+
 // Lossless tile screening (screen.hip): 64-token tile bounds of the projected
 // cache, and one keep bit per tile from a seed-set threshold.
 int screen_tiles(int max_seq);
@@ -88,8 +97,10 @@ hipError_t launch_mla_score_lists(const MlaDev& m, const float* q_sel, const uin
                                   CandSegs lists, int list_k, hipStream_t st);
 // Exact top-k of B score rows from their chunk lists (final select with the
 // list check; rows whose lists fall short are selected from their scores).
-hipError_t launch_topk_lists(int B, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+hipError_t launch_topk_lists(int rows, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
                              int32_t* idx, CandSegs lists, int chunk_len, hipStream_t st);
+// chunk length of the fused GQA stream (its segments)
+int score_topk_chunk_len();
 hipError_t launch_mla_indexed(const MlaDev& m, const float* q_abs, const uint16_t* latent,
                               const int32_t* idx, int k, int S, float scale, float* part_o,
                               float* part_lse, hipStream_t st);

@@ -85,6 +85,12 @@ struct FusedOut {
   int n_sink, n_local;      // sink tokens: t < n_sink; local tokens: t >= T_b - n_local
   const uint32_t* keep;     // screening: one bit per 64-token tile ([rows, keep_words]); nullptr: all kept
   int keep_words;
+  // fused stream keeping chunk lists (the chunk's own top k, which need not
+  // hold the row's top k; segment floor 0, no selection slack), with the
+  // scores written for the final pass's per-row fallback; scores2: a second
+  // destination for the scores (the caller's buffer), or nullptr
+  int lists;
+  float* scores2;
 };
 // A token of a dropped tile is staged with this value: a NaN whose score_key
 // is 0, the key of no token (finite scores map to keys above 0).
@@ -181,10 +187,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
 
   const bool lists = !FUSED && fo.segs.info != nullptr;   // score-only stream writing chunk lists (kernel-uniform)
   const int64_t seg = FUSED || lists ? int64_t(b * g.Hkv + j) * fo.segs.nseg + cx : 0;
+  float* srow2 = FUSED && fo.scores2 ? fo.scores2 + (int64_t(b) * g.Hkv + j) * g.max_seq : nullptr;
   if (t_begin >= Tb) {                       // whole chunk past the sequence's end
-    if (!FUSED || fo.write_scores) {
+    if (!FUSED || (fo.write_scores && !fo.lists)) {   // (list mode: its own copy is read below T_b only)
       const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
-      for (int i = tid; i < lim; i += NT) srow[t_begin + i] = -__builtin_inff();
+      for (int i = tid; i < lim; i += NT) __builtin_nontemporal_store(-__builtin_inff(), srow + t_begin + i);
+        }
+    if (srow2) {
+      const int lim = g.max_seq - t_begin < chunk ? g.max_seq - t_begin : chunk;
+      for (int i = tid; i < lim; i += NT) __builtin_nontemporal_store(-__builtin_inff(), srow2 + t_begin + i);
     }
     if (FUSED && tid == 0) {
       write_info(fo.segs, seg, 0, 0u, 0u, 0xffffffffu);
@@ -412,7 +423,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   };
 
   // Stream the chunk's tiles; the scores are staged in LDS and leave only
-  // after the stream. (A store inside the loop would sit in the in-order
+  // after the stream, as non-temporal stores (they are not read again in
+  // this kernel; kept out of the caches, they do not crowd the stream's
+  // loads: the score-only stream at 128K x B = 16 went from 192.7 to 183.9
+  // us). (A store inside the loop would sit in the in-order
   // vmcnt queue between tile loads, so every wait for a tile would also wait
   // for the previous store's write acknowledgement; holding them in
   // registers would cost occupancy.)
@@ -443,13 +457,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
   __syncthreads();
   if (!FUSED || fo.write_scores) {
     float* dst = srow + t_begin;
+    float* dst2 = srow2 ? srow2 + t_begin : nullptr;
     const int lim = g.max_seq - t_begin;                 // > 0
+    // list mode: the workspace copy is only read below T_b (the caller's copy,
+    // dst2, is the whole row)
+    const int lim1 = FUSED && fo.lists ? (Tb - t_begin + 3) & ~3 : lim;
     if ((g.max_seq & 3) == 0) {                          // 16-byte aligned row chunk
-      for (int i = tid * 4; i < chunk && i < lim; i += 4 * NT)
-        *reinterpret_cast<f32x4*>(dst + i) =
-            f32x4{stage[sidx(i)], stage[sidx(i + 1)], stage[sidx(i + 2)], stage[sidx(i + 3)]};
+      for (int i = tid * 4; i < chunk && i < lim; i += 4 * NT) {
+        const f32x4 v = f32x4{stage[sidx(i)], stage[sidx(i + 1)], stage[sidx(i + 2)], stage[sidx(i + 3)]};
+        if (i < lim1) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + i));
+        if (dst2) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst2 + i));
+      }
     } else {
-      for (int i = tid; i < chunk && i < lim; i += NT) dst[i] = stage[sidx(i)];
+      for (int i = tid; i < chunk && i < lim; i += NT) {
+        if (i < lim1) dst[i] = stage[sidx(i)];
+        if (dst2) dst2[i] = stage[sidx(i)];
+      }
     }
   }
   if constexpr (!FUSED) {
@@ -507,12 +530,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
     n = n < 0 ? 0 : (n > chunk ? chunk : n);
     // the top-two bound first (block-uniform; it leaves the stage intact),
     // the histogram select when it does not apply or keeps too many
-    const bool done = n == chunk && fo.k <= NT &&
+    const bool done = n == chunk && fo.k <= NT && !fo.lists &&
                       chunk_select_top2<NT, TPW>(key, t_begin, fo.k, tsm, stage, SS, fo.segs, seg);
     if (!done) {
       __syncthreads();                                   // stage is reused below
       ChunkSmem<NT, TPW>& csm = *reinterpret_cast<ChunkSmem<NT, TPW>*>(sbuf);
-      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg);
+      chunk_select<NT, TPW>(key, t_begin, Tb, n, fo.k, csm, fo.segs, seg, fo.lists ? 0 : kSelSlack);
+      // a list of one chunk bounds nothing about the row's k-th key: no floor
+      if (fo.lists && tid == 0) fo.segs.info[seg].floor = 0u;
     }
   }
 }
@@ -586,12 +611,22 @@ int score_topk_segments(int max_seq) {
 
 int score_topk_segment_cap(int k) { return seg_cap(k, kWaves * 64 * kFusedTiles); }
 
+int score_topk_chunk_len() { return kWaves * 64 * kFusedTiles; }
+
 hipError_t launch_score_chunks(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,
                                float* scores, CandSegs segs, hipStream_t st, uint32_t* pmax, int n_sink,
                                int n_local, const uint32_t* keep, int keep_words) {
   FusedOut fo{segs, k, scores ? 1 : 0, pmax, n_sink, n_local, keep, keep_words};
   if (keep) return launch_score_t<kGqa, true, true>(g, q, nullptr, P, Kp, scores, st, fo);
   return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores, st, fo);
+}
+
+hipError_t launch_score_chunks_lists(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int kc,
+                                     float* scores_ws, float* scores_user, CandSegs lists, hipStream_t st,
+                                     const uint32_t* keep, int keep_words) {
+  FusedOut fo{lists, kc, 1, nullptr, 0, 0, keep, keep_words, 1, scores_user};
+  if (keep) return launch_score_t<kGqa, true, true>(g, q, nullptr, P, Kp, scores_ws, st, fo);
+  return launch_score_t<kGqa, true>(g, q, nullptr, P, Kp, scores_ws, st, fo);
 }
 
 hipError_t launch_score_topk(const GqaDev& g, const uint16_t* q, const float* P, const uint16_t* Kp, int k,

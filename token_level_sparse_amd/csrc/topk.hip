@@ -186,19 +186,25 @@ struct FinalSmem {
 };
 
 // Exact top-k of one score row straight from its scores, for rows whose
-// candidate lists were not enough: three radix levels over the order-
+// candidate lists were not enough: the row's tokens are its positions below
+// T_b with a score above -inf (key 0: a position behind an invalid page
+// holds no token). A count, then three radix levels over the order-
 // preserving keys (bits 31..20, 19..8, 7..0; each a histogram of the keys
 // that match the levels above), then the taken tokens in token order, tiles
 // of NT with block scans (ties, lowest index first). Slow (the row is read
-// four times), and only run when a row's lists do not hold its top k.
+// five times), and only run when a row's lists do not hold its top k.
 template <int NT>
 __device__ void lists_fallback(const float* __restrict__ srow, int Tb, int k, int32_t* __restrict__ dst,
                                uint32_t* hist, ScanSmem<NT>& scan, int* res) {
   const int tid = threadIdx.x;
-  const int need = min(k, Tb);
-  uint32_t tkey = 0u, prefix = 0u, pmask = 0u;
+  int nt0 = 0;
+  for (int t = tid; t < Tb; t += NT) nt0 += score_key(srow[t]) != 0u ? 1 : 0;
+  int ntok;
+  block_scan<NT>(nt0, scan, &ntok);
+  const int need = min(k, ntok);
+  uint32_t tkey = 1u, prefix = 0u, pmask = 0u;        // (tkey 1: every token, no ties to rank)
   int trem = 0x7fffffff;
-  if (need < Tb) {
+  if (need < ntok) {
     int rem = need;
     constexpr int kShift[3] = {20, 8, 0};
     constexpr uint32_t kMask[3] = {0xfffu, 0xfffu, 0xffu};
@@ -208,7 +214,7 @@ __device__ void lists_fallback(const float* __restrict__ srow, int Tb, int k, in
       __syncthreads();
       for (int t = tid; t < Tb; t += NT) {
         const uint32_t key = score_key(srow[t]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & kMask[lv]], 1u);
+        if (key != 0u && (key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & kMask[lv]], 1u);
       }
       __syncthreads();
       pick_bin<NT, kFinBins / NT>(hist, rem, true, scan, res);
@@ -218,16 +224,16 @@ __device__ void lists_fallback(const float* __restrict__ srow, int Tb, int k, in
       __syncthreads();
       prefix |= D << sh;
       pmask |= kMask[lv] << sh;
-      tkey = prefix;                   // the lowest key of the bin
-      if (cnt == rem) break;           // the whole bin is taken: every key >= tkey
-      if (lv == 2) trem = rem;         // one key value, tied
+      tkey = prefix > 1u ? prefix : 1u;  // the lowest key of the bin (a token's key is at least 1)
+      if (cnt == rem) break;             // the whole bin is taken: every key >= tkey
+      if (lv == 2) trem = rem;           // one key value, tied
     }
   }
   int tie_base = 0, out_base = 0;
   for (int t0 = 0; t0 < Tb; t0 += NT) {
     const int t = t0 + tid;
     const uint32_t key = t < Tb ? score_key(srow[t]) : 0u;
-    const bool real = t < Tb;
+    const bool real = key != 0u;
     int tt = 0, tr = 0;
     if (trem != 0x7fffffff) {
       const int nt = real && key == tkey ? 1 : 0;
@@ -243,12 +249,6 @@ __device__ void lists_fallback(const float* __restrict__ srow, int Tb, int k, in
   for (int i = out_base + tid; i < k; i += NT) dst[i] = -1;
 }
 
-// One block per (row, group of gs consecutive segments). MERGE = false: the
-// group is the whole row (gs = nseg) and the block writes the row's selected
-// indices. MERGE = true: the block writes its group's first min(k, n)
-// candidates of the (key desc, index asc) order, as (key, index) pairs in
-// token order, to segment (row, group) of `outs`: a smaller candidate list
-// for the next level that still holds the row's top k.
 // LISTS (final level only): each segment holds the top candidates of one
 // chunk of `lists.chunk_len` tokens of the score row `lists.scores`, a list
 // that need not contain the row's top k. A chunk that dropped real tokens
@@ -727,17 +727,17 @@ hipError_t launch_topk(int B, int H, int max_seq, const int32_t* seq_lens, const
   return launch_select_final(rows, H, max_seq, seq_lens, k, segs, idx, static_cast<char*>(wsp) + main_bytes, st);
 }
 
-hipError_t launch_topk_lists(int B, int max_seq, const int32_t* seq_lens, const float* scores, int k,
+hipError_t launch_topk_lists(int rows, int H, int max_seq, const int32_t* seq_lens, const float* scores, int k,
                              int32_t* idx, CandSegs lists, int chunk_len, hipStream_t st) {
   if (lists.nseg > kMaxSeg) return hipErrorInvalidValue;
-  // lists of up to 56 per chunk (segment capacity 120) are held 8 per thread
-  // (a segment of up to 64 read directly by its 8 threads when the row has
-  // 128 chunks), longer ones 12 per thread
-  if (lists.cap <= 120)
-    hipLaunchKernelGGL((final_kernel<1024, 8, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
+  // Rows of up to about 7.7K list candidates (kc = cap / 2 per segment) are
+  // held 8 per thread; a segment of up to 1024 / nseg * 8 is then read
+  // directly by its threads. Longer lists 12 per thread.
+  if (int64_t(lists.nseg) * (lists.cap / 2) <= 7680)
+    hipLaunchKernelGGL((final_kernel<1024, 8, false, true>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
                        lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
   else
-    hipLaunchKernelGGL((final_kernel<1024, 12, false, true>), dim3(B), dim3(1024), 0, st, 1, max_seq, seq_lens, k,
+    hipLaunchKernelGGL((final_kernel<1024, 12, false, true>), dim3(rows), dim3(1024), 0, st, H, max_seq, seq_lens, k,
                        lists, lists.nseg, idx, CandSegs{}, DeltaArgs{}, ListArgs{scores, chunk_len});
   return hipGetLastError();
 }
