@@ -162,12 +162,21 @@ JSSA_API jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int3
  * written and read back (unless `scores` is given). Two launches: the chunk
  * pass (jssa_score_topk_chunks) and the per-row final pass
  * (jssa_score_topk_final); jssa_score_topk issues both.
+ * For budgets whose per-chunk candidates would need more than one final
+ * pass (chunks x k > 8192), each chunk instead keeps only its own best
+ * (about 4x its share of k) and writes its scores below T_b to the
+ * workspace; the final pass checks, once the row's k-th key is known, that
+ * every chunk that dropped tokens dropped only keys below it, and selects a
+ * row that fails that check again from its scores. The indices are the same
+ * either way.
  *  q, P, Kp  as jssa_score; k as jssa_topk (1 <= k <= min(4096, max_seq))
  *  scores    device fp32 [B,Hkv,max_seq] or NULL: if given, written exactly
  *            as by jssa_score
  *  idx       device int32 [B,Hkv,k]: exactly what jssa_topk returns for the
  *            scores jssa_score computes
  *  ws        device workspace of at least jssa_score_topk_workspace_size bytes
+ *            (candidate lists, plus the score rows [B*Hkv, max_seq] fp32 in
+ *            the list mode above); its contents are scratch
  */
 JSSA_API jssa_status jssa_score_topk_workspace_size(const jssa_gqa_desc* desc, int32_t k, size_t* bytes);
 JSSA_API jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, const float* P, const void* Kp,
@@ -180,9 +189,10 @@ JSSA_API jssa_status jssa_score_topk(const jssa_gqa_desc* desc, const void* q, c
  * the same computation and results, with the candidate lists in a static
  * scratch array of the library instead of a caller workspace.
  *  Arguments as jssa_score_topk without ws / ws_bytes.
- *  Limit: shapes whose jssa_score_topk_workspace_size exceeds 16 MiB
- *  (16 << 20 bytes) are rejected with JSSA_ERR_WORKSPACE, launching nothing;
- *  128K tokens x B = 16 x Hkv = 8 at k = 256 needs about 8 MiB.
+ *  Always the candidate-list layout (no list mode, no score rows in the
+ *  scratch). Limit: shapes whose candidate lists exceed 16 MiB (16 << 20
+ *  bytes) are rejected with JSSA_ERR_WORKSPACE, launching nothing; 128K
+ *  tokens x B = 16 x Hkv = 8 at k = 256 needs about 8 MiB.
  *  The call allocates nothing; the scratch array (16 MiB per GPU) exists from
  *  library load to process exit, and its device address is looked up once
  *  per GPU, on the first call made with that GPU current.
