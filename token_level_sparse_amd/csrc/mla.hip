@@ -250,6 +250,26 @@ constexpr float kLazy = 8.f;    // log2 headroom of the running softmax base
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// x combined with its partner in lane ^ 16 (permlane16_swap: odd 16-lane
+// rows of the first register trade places with even rows of the second) or
+// lane ^ 32 (permlane32_swap: upper half of the first with lower half of the
+// second). Both registers start as x, so afterwards each lane holds {x,
+// partner} in some order and max of the pair is the same in both lanes.
+// (The pair's elements are copied out by value: bit-casting a vector-element
+// lvalue reads element 0.)
+__device__ __forceinline__ float max_x16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
 __device__ __forceinline__ s16x4 pack_bf16x4(__bf16 a, __bf16 b, __bf16 c, __bf16 d) {
   s16x4 r;
   r[0] = __builtin_bit_cast(short, a);
@@ -363,17 +383,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       acc[2 + (kb & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo_s[kb][lane], acc[2 + (kb & 1)], 0, 0, 0);
     }
     const f32x4v St = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    // St[i] = logit (log2 domain) of head n, token 4g + i; that token's
-    // validity sits in lanes n' = 4g + i
+    // St[i] = logit (log2 domain) of head n, token 4g + i; row r's validity
+    // is bit r of one ballot (lanes 0..15 hold rows 0..15)
+    const uint64_t vm = __ballot(ok);
     float lg[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int okv = __shfl(ok ? 1 : 0, (lane & 48) | (4 * g + i), 64);
-      lg[i] = okv ? St[i] : -__builtin_inff();
-    }
+    for (int i = 0; i < 4; ++i) lg[i] = ((vm >> (4 * g + i)) & 1ull) ? St[i] : -__builtin_inff();
     float bm = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    bm = xor_max(bm, 16);
-    bm = xor_max(bm, 32);
+    bm = max_x16(bm);                                   // (permlane swaps: no LDS round trip)
+    bm = max_x32(bm);
     // Lazy rescaling: the exponent base mrun moves only when a logit exceeds
     // it by more than kLazy (so every weight stays below 2^kLazy, exact in
     // the hi + lo pair and harmless to the fp32 sums), and the 128
