@@ -247,7 +247,12 @@ def _sparse_and_check(J, PL, inp, k, S, units=None, fused=False):
 
 
 @pytest.mark.parametrize("cfg,k,S", [(synth.TINY, 256, 8), (synth.LLAMA8B_32K, 256, 8),
-                                     (synth.LLAMA8B_32K, 256, 1), (synth.LLAMA8B_32K, 1, 4)])
+                                     (synth.LLAMA8B_32K, 256, 1), (synth.LLAMA8B_32K, 1, 4),
+                                     # several 32-row batches per wave (the next batch's tokens
+                                     # load while this one is multiplied), a partial last one
+                                     (synth.LLAMA8B_32K, 1024, 1), (synth.TINY, 1000, 2),
+                                     # splits past the list's end (k = 3 over 8 splits)
+                                     (synth.TINY, 3, 8)])
 def test_sparse_step_parity(J, PL, cfg, k, S):
     _sparse_and_check(J, PL, synth.make_gqa(cfg), k, S)
 
