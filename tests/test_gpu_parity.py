@@ -1092,12 +1092,13 @@ def test_mla_score_topk_matches_separate_passes(J, case):
 
 
 @pytest.mark.parametrize("S", [1, 5, 16, 64])
-def test_mla_combine_up_matches_two_calls(J, S):
+@pytest.mark.parametrize("B,H", [(3, 32), (5, 16)])
+def test_mla_combine_up_matches_two_calls(J, S, B, H):
     """jssa_mla_combine_up_v against jssa_combine + jssa_mla_up_v on random
     partials (some splits empty: lse -inf) and random W_uv: same lse and
-    output up to fp32 summation order."""
-    B, H = 3, 32
-    rng = np.random.default_rng(100 + S)
+    output up to fp32 summation order; sequence counts that leave the last
+    pass of 4 partial (3, 5)."""
+    rng = np.random.default_rng(100 + S + 7 * B)
     po = rng.standard_normal((B, H, S, 512)).astype(np.float32)
     pl = (3.0 * rng.standard_normal((B, H, S))).astype(np.float32)
     pl[0, 0, :] = -np.inf                                 # a row with no weight at all
