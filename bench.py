@@ -630,7 +630,7 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
     c = cfg
 
     def absorb():
-        jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.P, st.q_abs, st.q_sel, stream)
+        jssa.jssa_mla_absorb_q(st.desc, st.q_nope, st.q_rope, st.W_uk, st.P, st.U, st.q_abs, st.q_sel, stream)
 
     def score_topk():
         jssa.jssa_mla_score_topk(st.desc, st.q_sel, st.Kp, st.k, st.scores, st.idx, st.ws, None, stream)

@@ -316,27 +316,43 @@ JSSA_API jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const vo
                                     void* Kp_lat, void* stream);
 
 /*
- * Absorbed query and selection query (digest Perspective: selection over the
- * shared latent cache).
+ * Folded selection weights, computed once per layer (set-up, like the latent
+ * projection): U[h] = W_uk[h] . P[0 .. d_latent) (fp32 [H,d_nope,r]; fp64
+ * sums rounded once to fp32). The selection query is linear in the absorbed
+ * query (digest Perspective: selection over the shared latent cache), so
+ * P_lat^T sum_h W_uk[h]^T q_nope[b,h] = sum_h U[h]^T q_nope[b,h]: with U the
+ * per-step selection query needs q_nope, not the absorbed query.
+ *  W_uk device bf16 [H,d_nope,d_latent], P device fp32 [d_c,r], U device
+ *  fp32 [H,d_nope,r] (written).
+ */
+JSSA_API jssa_status jssa_mla_fold_selection(const jssa_mla_desc* desc, const void* W_uk, const float* P,
+                                             float* U, void* stream);
+
+/*
+ * Absorbed query and selection query, in one launch (digest Perspective:
+ * selection over the shared latent cache).
  *  q_abs[b,h] = [W_uk[h]^T q_nope[b,h] ; q_rope[b,h]] (fp32): the attention
  *               query of head h against latent rows;
- *  q_sel[b,j] = P[64j .. 64j+63]^T sum_h q_abs[b,h][64j .. 64j+63], j < 9
- *               (fp32, fixed summation order): the one subspace query of
- *               sequence b, P^T sum_h q_abs[b,h], in 9 parts over 64-dim
- *               blocks of the latent + rope dims; the MLA score passes add
- *               the parts themselves, in order.
+ *  q_sel[b,g] = sum over the heads h = g, g + 64, ... (< H) of
+ *               U[h]^T q_nope[b,h] + P[d_latent .. d_c)^T q_rope[b,h],
+ *               g < 64 (fp32, fixed summation order): the one subspace
+ *               query of sequence b, P^T sum_h q_abs[b,h], in 64 parts by
+ *               class of heads; the MLA score passes add the parts
+ *               themselves, in order. Parts of classes with no head are 0.
  *  q_nope device bf16 [B,H,d_nope], q_rope device bf16 [B,H,d_rope],
- *  W_uk device bf16 [H,d_nope,d_latent], P device fp32 [d_c,r],
- *  q_abs device fp32 [B,H,d_c] (written), q_sel device fp32 [B,9,r] (written)
+ *  W_uk device bf16 [H,d_nope,d_latent], P device fp32 [d_c,r], U from
+ *  jssa_mla_fold_selection (same W_uk and P), q_abs device fp32 [B,H,d_c]
+ *  (written), q_sel device fp32 [B,64,r] (written).
  */
 JSSA_API jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
-                              const void* W_uk, const float* P, float* q_abs, float* q_sel, void* stream);
+                              const void* W_uk, const float* P, const float* U, float* q_abs, float* q_sel,
+                              void* stream);
 
 /*
  * MLA selection scores: scores[b,t] = (sum_j q_sel[b,j]) . Kp_lat[b,t] for
- * t < T_b, -inf beyond; the 9 parts are added in order (the same query in
- * every pass and every block). q_sel device fp32 [B,9,r] (from
- * jssa_mla_absorb_q, or any split of the query into 9 rows), scores device
+ * t < T_b, -inf beyond; the 64 parts are added in order (the same query in
+ * every pass and every block). q_sel device fp32 [B,64,r] (from
+ * jssa_mla_absorb_q, or any split of the query into 64 rows), scores device
  * fp32 [B,max_seq].
  */
 JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_sel, const void* Kp_lat,

@@ -118,7 +118,10 @@ def test_combine_and_mla_validation(J):
     m_badr = J.mla_desc(4, 128, 48, 131072)
     assert _status(J.jssa_mla_score, m_badh, A, A, A) == J.ERR_UNSUPPORTED
     assert _status(J.jssa_mla_score, m_badr, A, A, A) == J.ERR_UNSUPPORTED
-    assert _status(J.jssa_mla_absorb_q, m_ok, A, A, A, None, A, A) == J.ERR_NULL
+    assert _status(J.jssa_mla_absorb_q, m_ok, A, A, A, None, A, A, A) == J.ERR_NULL
+    assert _status(J.jssa_mla_absorb_q, m_ok, A, A, A, A, None, A, A) == J.ERR_NULL   # no folded weights
+    assert _status(J.jssa_mla_fold_selection, m_ok, A, None, A) == J.ERR_NULL
+    assert _status(J.jssa_mla_fold_selection, m_badr, A, A, A) == J.ERR_UNSUPPORTED
     assert _status(J.jssa_mla_indexed_decode, m_ok, A, A, A, 2048, 0, 0.1, A, A) == J.ERR_SHAPE
     assert _status(J.jssa_mla_up_v, m_ok, A, None, A) == J.ERR_NULL
 

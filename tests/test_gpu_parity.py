@@ -998,7 +998,18 @@ def test_calib_end_to_end_recall(J, PL):
                                           # with a partial last chunk
                                           (17, 2, 3000, 100, 3), (19, 1, 2048, 1, 1), (23, 3, 5000, 333, 7)])
 def test_mla_parity(J, PL, seed, B, T, k, S):
-    cfg = replace(synth.MLA_DSV3, B=B, T=T, k=k, seed=seed)
+    _mla_parity(PL, replace(synth.MLA_DSV3, B=B, T=T, k=k, seed=seed), S)
+
+
+@pytest.mark.parametrize("H", [48, 192])
+def test_mla_parity_head_counts(J, PL, H):
+    """Head counts other than 128: with 48 heads, 16 of the 64 selection
+    query classes hold no head (their parts are 0); with 192, each class
+    holds 3 heads, so its second chunk of 2 is partial."""
+    _mla_parity(PL, replace(synth.MLA_DSV3, B=3, H=H, T=3000, k=300, seed=29 + H), 4)
+
+
+def _mla_parity(PL, cfg, S):
     inp = synth.make_mla(cfg)
     st = PL.MlaStep(inp, S=S)
     st.project()
@@ -1006,16 +1017,25 @@ def test_mla_parity(J, PL, seed, B, T, k, S):
     Kp = _np(st.Kp)
     for b in range(cfg.B):
         np.testing.assert_array_equal(Kp[b], O.project_keys(inp.latent[b], inp.P))
+    # folded selection weights U[h] = W_uk[h] . P_lat: fp64 sums rounded once
+    # to fp32, so within 2^-24 relative of the fp64 product (plus fp64 noise)
+    P64 = inp.P.astype(np.float64)
+    W64 = O.bf16_to_f64(inp.W_uk)
+    Uref = W64 @ P64[:512]
+    mag = np.abs(W64) @ np.abs(P64[:512])
+    Ug = _np(st.U).astype(np.float64)
+    assert np.all(np.abs(Ug - Uref) <= 2.0 ** -24 * np.abs(Uref) + 1e-12 * mag), np.abs(Ug - Uref).max()
     st.run()
     torch.cuda.synchronize()
     qsel = _np(st.q_sel)
     for b in range(cfg.B):
         qa = O.mla_absorbed_query(inp.q_nope[b], inp.q_rope[b], inp.W_uk)
         U.check_close(_np(st.q_abs)[b], qa, tol=1e-4, what="absorbed query")
-        # part j of the selection query: P rows 64j .. 64j+63 against the
-        # head sum of those absorbed dims; the parts add up to P^T sum_h qa
-        P64, qbar = inp.P.astype(np.float64), qa.sum(0)
-        parts = np.stack([P64[64 * j:64 * j + 64].T @ qbar[64 * j:64 * j + 64] for j in range(9)])
+        # part g of the selection query: the heads h = g, g + 64, ... each
+        # contribute P^T qa_h = (W_uk[h] P_lat)^T q_nope_h + P_rope^T q_rope_h;
+        # the parts add up to P^T sum_h qa
+        qbar = qa.sum(0)
+        parts = np.stack([sum((P64.T @ qa[h] for h in range(g, cfg.H, 64)), np.zeros(cfg.r)) for g in range(64)])
         U.check_close(qsel[b], parts, tol=1e-4, what="selection query parts")
         U.check_close(qsel[b].astype(np.float64).sum(0), P64.T @ qbar, tol=1e-4, what="selection query")
     idx, out, lse = _np(st.idx), _np(st.out), _np(st.lse)
@@ -1057,9 +1077,9 @@ def test_mla_score_topk_matches_separate_passes(J, case):
     name, B, T, k, lens, kind = case
     r, H = 64, 128
     rng = np.random.default_rng(sum(map(ord, name)))
-    # the query in 9 parts (as jssa_mla_absorb_q writes it); qsel is their
+    # the query in 64 parts (as jssa_mla_absorb_q writes it); qsel is their
     # sum, for building keys near it
-    qshare = (rng.standard_normal((B, 9, r)) / 3.0).astype(np.float32)
+    qshare = (rng.standard_normal((B, 64, r)) / 8.0).astype(np.float32)
     qsel = qshare.astype(np.float64).sum(1)
     if kind == "tied":
         kp = np.zeros((B, T, r), np.float32)            # every score 0: the lowest indices win

@@ -454,14 +454,23 @@ jssa_status jssa_mla_project_latent(const jssa_mla_desc* desc, const void* laten
                     __func__);
 }
 
-jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
-                              const void* W_uk, const float* P, float* q_abs, float* q_sel, void* stream) {
+jssa_status jssa_mla_fold_selection(const jssa_mla_desc* desc, const void* W_uk, const float* P, float* U,
+                                    void* stream) {
   if (jssa_status s = check_mla(__func__, desc)) return s;
-  REQUIRE_PTR(q_nope); REQUIRE_PTR(q_rope); REQUIRE_PTR(W_uk); REQUIRE_PTR(P); REQUIRE_PTR(q_abs);
-  REQUIRE_PTR(q_sel);
+  REQUIRE_PTR(W_uk); REQUIRE_PTR(P); REQUIRE_PTR(U);
+  return hip_status(jssa::launch_mla_fold(to_mla(desc), static_cast<const uint16_t*>(W_uk), P, U, S(stream)),
+                    __func__);
+}
+
+jssa_status jssa_mla_absorb_q(const jssa_mla_desc* desc, const void* q_nope, const void* q_rope,
+                              const void* W_uk, const float* P, const float* U, float* q_abs, float* q_sel,
+                              void* stream) {
+  if (jssa_status s = check_mla(__func__, desc)) return s;
+  REQUIRE_PTR(q_nope); REQUIRE_PTR(q_rope); REQUIRE_PTR(W_uk); REQUIRE_PTR(P); REQUIRE_PTR(U);
+  REQUIRE_PTR(q_abs); REQUIRE_PTR(q_sel);
   return hip_status(jssa::launch_mla_absorb(to_mla(desc), static_cast<const uint16_t*>(q_nope),
                                             static_cast<const uint16_t*>(q_rope),
-                                            static_cast<const uint16_t*>(W_uk), P, q_abs, q_sel, S(stream)),
+                                            static_cast<const uint16_t*>(W_uk), P, U, q_abs, q_sel, S(stream)),
                     __func__);
 }
 

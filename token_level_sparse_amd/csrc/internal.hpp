@@ -83,11 +83,15 @@ struct MlaDev {
 hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const float* P,
                               uint16_t* Kp, hipStream_t st);
 // The MLA selection query P^T sum_h q_abs[b,h] is passed as kMlaSelParts
-// partial sums [B, kMlaSelParts, r]: part j over the latent + rope dims
-// 64j .. 64j+63. The score stream adds the parts in order.
-constexpr int kMlaSelParts = 9;
+// partial sums [B, kMlaSelParts, r]: part g over the heads h = g, g + 64,
+// ... The score stream adds the parts in order.
+constexpr int kMlaSelParts = 64;
+// U[h] = W_uk[h] . P[0 .. 512) (set-up; fp32 [H, 128, r], fp64 sums).
+hipError_t launch_mla_fold(const MlaDev& m, const uint16_t* W_uk, const float* P, float* U, hipStream_t st);
+// The absorbed query and the selection query parts, in one launch.
 hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
-                             const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st);
+                             const uint16_t* W_uk, const float* P, const float* U, float* q_abs, float* q_sel,
+                             hipStream_t st);
 hipError_t launch_mla_score(const MlaDev& m, const float* q_sel, const uint16_t* Kp, float* scores,
                             hipStream_t st);
 int mla_score_chunks(int max_seq);

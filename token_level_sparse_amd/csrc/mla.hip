@@ -98,48 +98,171 @@ __global__ __launch_bounds__(256) void mla_project_kernel(MlaDev m, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Absorbed query: q_abs[b,h,c] = sum_i q_nope[b,h,i] W_uk[h,i,c] for c < 512
-// (fp32), then the rope part copied. Block (h, column quarter): 128 columns
-// as 64 bf16 pairs; wave w sums rows i = 32w .. 32w+31, whose 32 pair loads
-// per lane are all issued before any is used; the four partial sums meet in
-// LDS. Each W_uk element is read once and serves every sequence.
+// Folded selection weights (set-up): U[h][n][c] = sum_d W_uk[h][n][d] P[d][c]
+// over the 512 latent dims, in fp64 (bf16 x fp32 products are exact in
+// fp64), rounded once to fp32. Since the selection query is linear in the
+// absorbed query, P_lat^T sum_h W_uk[h]^T q_nope[b,h] = sum_h U[h]^T
+// q_nope[b,h], so the per-step selection query needs U and q_nope only, not
+// the absorbed query. Block (h, n), one thread per column c.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_t* __restrict__ qn,
-                                                         const uint16_t* __restrict__ qr,
-                                                         const uint16_t* __restrict__ Wuk,
-                                                         float* __restrict__ qa) {
-  constexpr int BT = 8;                  // sequences per pass
-  __shared__ float qs[BT][128];
-  __shared__ float part[4][BT][128];
-  const int h = blockIdx.x, cq = blockIdx.y, tid = threadIdx.x;
+template <int R>
+__global__ __launch_bounds__(R) void mla_fold_kernel(const uint16_t* __restrict__ Wuk, const float* __restrict__ P,
+                                                     float* __restrict__ U) {
+  const int h = blockIdx.x, n = blockIdx.y, c = threadIdx.x;
+  const uint16_t* w = Wuk + (int64_t(h) * 128 + n) * kDl;
+  double s = 0.0;
+  for (int d = 0; d < kDl; ++d) s = __builtin_fma(double(bf(w[d])), double(P[int64_t(d) * R + c]), s);
+  U[(int64_t(h) * 128 + n) * R + c] = float(s);
+}
+
+// ---------------------------------------------------------------------------
+// One launch forms both per-step queries; its two kinds of blocks are
+// independent, so the selection query does not wait for the absorbed one.
+//
+// Selection query, in kMlaSelParts parts (blocks 0 .. kMlaSelParts-1):
+// part g covers the heads of class g (h = g, g + 64, ...), q_sel[b,g,:] =
+// sum over those heads of (U[h]^T q_nope[b,h] + P_rope^T q_rope[b,h]); the
+// score passes add the parts in order, which gives P^T sum_h q_abs[b,h].
+// A class's heads go in chunks of 2: 320 reduction rows per chunk (256 rows
+// U[h][n] against q_nope[b,h,n], 64 rows P[512 + e] against the chunk's
+// rope values summed over its heads in head order). Thread (rq, sl) owns columns 4rq .. 4rq+3 and
+// rows sl, sl + NS, ... (all its row loads in flight at once, after the
+// query loads); the NS slices meet in LDS in order. Fixed summation orders
+// throughout: every call gives the same query.
+//
+// Absorbed query (the other blocks, one per (h, column quarter)):
+// q_abs[b,h,c] = sum_i q_nope[b,h,i] W_uk[h,i,c] for c < 512 (fp32), then
+// the rope part copied. 128 columns as 64 bf16 pairs; wave w sums rows
+// i = 32w .. 32w+31, whose 32 pair loads per lane are issued before any is
+// used; the four partial sums meet in LDS. Each W_uk element is read once
+// and serves every sequence.
+// ---------------------------------------------------------------------------
+constexpr int kSelBT = 4;                 // sequences per pass of a selection block
+constexpr int kSelHC = 2;                 // heads per chunk
+constexpr int kSelRows = kSelHC * 128 + 64;   // reduction rows per chunk
+constexpr int kAbsBT = 8;                 // sequences per pass of an absorb block
+static_assert(kMlaSelParts == 64, "selection query parts: one per head class h % 64");
+
+template <int R>
+__device__ __forceinline__ void mla_sel_part(const MlaDev& m, int g, const uint16_t* __restrict__ qn,
+                                             const uint16_t* __restrict__ qr, const float* __restrict__ U,
+                                             const float* __restrict__ P, float* __restrict__ qsel) {
+  constexpr int NQ = R / 4, NS = 256 / NQ, NU = kSelRows / NS;
+  static_assert(kSelRows % NS == 0, "whole rows per slice");
+  __shared__ float qs[kSelBT][kSelRows];  // the chunk's query values per row
+  __shared__ __attribute__((aligned(16))) float pp[NS][kSelBT][R];   // slice partial sums
+  const int tid = threadIdx.x, rq = tid % NQ, sl = tid / NQ;
+  const int nh = g < m.H ? (m.H - g + kMlaSelParts - 1) / kMlaSelParts : 0;   // heads of class g
+  for (int b0 = 0; b0 < m.B; b0 += kSelBT) {
+    const int nb = min(kSelBT, m.B - b0);
+    f32x4v acc[kSelBT];
+#pragma unroll
+    for (int bb = 0; bb < kSelBT; ++bb) acc[bb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < nh; i0 += kSelHC) {
+      const int hc = min(kSelHC, nh - i0);              // heads in this chunk
+      auto head = [&](int hi) { return g + kMlaSelParts * (i0 + (hi < hc ? hi : 0)); };   // clamped: valid
+      // query values (loads clamped to valid rows; values past the chunk or
+      // the batch zeroed): q_nope pairs, then rope pairs, one per head
+      constexpr int kNP = kSelBT * kSelHC * 64 / 256;   // q_nope pairs per thread
+      uint32_t qv[kNP];
+#pragma unroll
+      for (int u = 0; u < kNP; ++u) {
+        const int e = tid + 256 * u, bb = e / (kSelHC * 64), x = 2 * (e % (kSelHC * 64)), hi = x / 128;
+        qv[u] = *reinterpret_cast<const uint32_t*>(qn + (int64_t(b0 + (bb < nb ? bb : 0)) * m.H + head(hi)) * 128 +
+                                                   x % 128);
+      }
+      constexpr int kRP = kSelBT * 32 * kSelHC / 256;   // rope pairs per thread
+      uint32_t rv[kRP];
+#pragma unroll
+      for (int u = 0; u < kRP; ++u) {
+        const int e = tid + 256 * u, hi = e % kSelHC, pr = (e / kSelHC) % 32, bb = e / (32 * kSelHC);
+        rv[u] = *reinterpret_cast<const uint32_t*>(qr + (int64_t(b0 + (bb < nb ? bb : 0)) * m.H + head(hi)) * 64 + 2 * pr);
+      }
+      f32x4v uv[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int x = sl + NS * u;
+        const float* row = x < kSelHC * 128 ? U + (int64_t(head(x / 128)) * 128 + x % 128) * R
+                                             : P + int64_t(512 + x - kSelHC * 128) * R;
+        uv[u] = reinterpret_cast<const f32x4v*>(row)[rq];
+      }
+#pragma unroll
+      for (int u = 0; u < kNP; ++u) {
+        const int e = tid + 256 * u, bb = e / (kSelHC * 64), x = 2 * (e % (kSelHC * 64)), hi = x / 128;
+        const bool ok = bb < nb && hi < hc;
+        qs[bb][x] = ok ? bf_lo(qv[u]) : 0.f;
+        qs[bb][x + 1] = ok ? bf_hi(qv[u]) : 0.f;
+      }
+      // rope: the chunk's heads of one (sequence, pair) sit in kSelHC
+      // consecutive lanes and are added in head order
+      static_assert(kSelHC == 2, "rope sum over lane pairs");
+#pragma unroll
+      for (int u = 0; u < kRP; ++u) {
+        const int e = tid + 256 * u, hi = e % kSelHC, pr = (e / kSelHC) % 32, bb = e / (32 * kSelHC);
+        const bool ok = bb < nb && hi < hc;
+        const float lo = ok ? bf_lo(rv[u]) : 0.f, hv = ok ? bf_hi(rv[u]) : 0.f;
+        const float lo1 = __shfl_down(lo, 1, 2), hv1 = __shfl_down(hv, 1, 2);
+        if (hi == 0) {
+          qs[bb][kSelHC * 128 + 2 * pr] = lo + lo1;
+          qs[bb][kSelHC * 128 + 2 * pr + 1] = hv + hv1;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int x = sl + NS * u;
+#pragma unroll
+        for (int bb = 0; bb < kSelBT; ++bb) acc[bb] += qs[bb][x] * uv[u];
+      }
+      __syncthreads();                                  // qs is rewritten by the next chunk
+    }
+#pragma unroll
+    for (int bb = 0; bb < kSelBT; ++bb) *reinterpret_cast<f32x4v*>(&pp[sl][bb][4 * rq]) = acc[bb];
+    __syncthreads();
+    for (int e = tid; e < nb * R; e += 256) {
+      const int bb = e / R, c = e % R;
+      float t = 0.f;
+      for (int x = 0; x < NS; ++x) t += pp[x][bb][c];
+      qsel[(int64_t(b0 + bb) * kMlaSelParts + g) * R + c] = t;
+    }
+    __syncthreads();                                    // pp is rewritten by the next pass
+  }
+}
+
+__device__ __forceinline__ void mla_absorb_block(const MlaDev& m, int h, int cq, const uint16_t* __restrict__ qn,
+                                                 const uint16_t* __restrict__ qr, const uint16_t* __restrict__ Wuk,
+                                                 float* __restrict__ qa) {
+  __shared__ float qs[kAbsBT][128];
+  __shared__ float part[4][kAbsBT][128];
+  const int tid = threadIdx.x;
   const int cp = tid & 63, w = tid >> 6;
   const uint16_t* W = Wuk + (int64_t(h) * 128 + w * 32) * kDl + cq * 128 + 2 * cp;
   uint32_t wr[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) wr[i] = *reinterpret_cast<const uint32_t*>(W + int64_t(i) * kDl);
-  for (int b0 = 0; b0 < m.B; b0 += BT) {
-    const int nb = min(BT, m.B - b0);
+  for (int b0 = 0; b0 < m.B; b0 += kAbsBT) {
+    const int nb = min(kAbsBT, m.B - b0);
     __syncthreads();
-    for (int e = tid; e < BT * 128; e += 256) {
+    for (int e = tid; e < kAbsBT * 128; e += 256) {
       const int bb = e / 128, i = e % 128;
       qs[bb][i] = bb < nb ? bf(qn[(int64_t(b0 + bb) * m.H + h) * 128 + i]) : 0.f;
     }
     __syncthreads();
-    float acc[BT][2];
+    float acc[kAbsBT][2];
 #pragma unroll
-    for (int bb = 0; bb < BT; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
+    for (int bb = 0; bb < kAbsBT; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const float w0 = bf_lo(wr[i]), w1 = bf_hi(wr[i]);
 #pragma unroll
-      for (int bb = 0; bb < BT; ++bb) {
+      for (int bb = 0; bb < kAbsBT; ++bb) {
         const float q = qs[bb][w * 32 + i];
         acc[bb][0] = __builtin_fmaf(q, w0, acc[bb][0]);
         acc[bb][1] = __builtin_fmaf(q, w1, acc[bb][1]);
       }
     }
 #pragma unroll
-    for (int bb = 0; bb < BT; ++bb) {
+    for (int bb = 0; bb < kAbsBT; ++bb) {
       part[w][bb][2 * cp] = acc[bb][0];
       part[w][bb][2 * cp + 1] = acc[bb][1];
     }
@@ -157,68 +280,17 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaDev m, const uint16_
   }
 }
 
-// ---------------------------------------------------------------------------
-// Selection query of a sequence, in parts: q_sel[b,j,:] = P[64j .. 64j+63]^T
-// (sum_h q_abs[b,h,64j .. 64j+63]) for the 9 blocks j of 64 latent + rope
-// dims. The query P^T sum_h q_abs[b,h] is their sum, which the score passes
-// form themselves (parts added in order), so the cross-head sum is spread
-// over B x 9 blocks instead of one block per sequence. Block (b, j), 256
-// threads: thread (c, hq) = (tid % 64, tid / 64) adds heads hq, hq + 4, ...
-// of dim 64j + c (fixed order; the four head classes meet in LDS in order),
-// then thread (rq, sl) projects: columns 4rq .. 4rq+3 of P over the block's
-// rows sl, sl + NS, ... (the slices meet in LDS in order).
-// ---------------------------------------------------------------------------
-static_assert(kMlaSelParts * 64 == kDc, "selection query parts: 64 dims each");
-
 template <int R>
-__global__ __launch_bounds__(256) void mla_selq_kernel(MlaDev m, const float* __restrict__ qa,
-                                                       const float* __restrict__ P,
-                                                       float* __restrict__ qsel) {
-  constexpr int NQ = R / 4;               // 16-byte column groups of P
-  constexpr int NS = 256 / NQ;            // row slices
-  constexpr int NI = (64 + NS - 1) / NS;  // rows per slice
-  __shared__ float part[4][64];
-  __shared__ float qbar[64];
-  __shared__ __attribute__((aligned(16))) float pp[NS][R];
-  const int b = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-  const int c = tid & 63, hq = tid >> 6;
-  const int rq = tid % NQ, sl = tid / NQ;
-  // this slice's P rows (issued first: they do not depend on the sum)
-  f32x4v pv[NI];
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int i = sl + ii * NS;
-    pv[ii] = reinterpret_cast<const f32x4v*>(P + int64_t(64 * j + (i < 64 ? i : 63)) * R)[rq];
-  }
-  const float* qc = qa + int64_t(b) * m.H * kDc + 64 * j + c;
-  float s = 0.f;
-  for (int h0 = hq; h0 < m.H; h0 += 4 * 32) {            // 32 heads of the class in flight at once
-    float a[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int h = h0 + 4 * u;
-      a[u] = qc[int64_t(h < m.H ? h : hq) * kDc];         // clamped: a valid row, not added
-    }
-#pragma unroll
-    for (int u = 0; u < 32; ++u) s += h0 + 4 * u < m.H ? a[u] : 0.f;
-  }
-  part[hq][c] = s;
-  __syncthreads();
-  if (tid < 64) qbar[tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
-  __syncthreads();
-  f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int i = sl + ii * NS;
-    acc += (i < 64 ? qbar[i < 64 ? i : 63] : 0.f) * pv[ii];
-  }
-  *reinterpret_cast<f32x4v*>(&pp[sl][4 * rq]) = acc;
-  __syncthreads();
-  if (tid < R) {
-    float t = 0.f;
-    for (int x = 0; x < NS; ++x) t += pp[x][tid];
-    qsel[(int64_t(b) * kMlaSelParts + j) * R + tid] = t;
-  }
+__global__ __launch_bounds__(256) void mla_queries_kernel(MlaDev m, const uint16_t* __restrict__ qn,
+                                                          const uint16_t* __restrict__ qr,
+                                                          const uint16_t* __restrict__ Wuk,
+                                                          const float* __restrict__ U, const float* __restrict__ P,
+                                                          float* __restrict__ qa, float* __restrict__ qsel) {
+  const int x = blockIdx.x;                             // (block-uniform role)
+  if (x < kMlaSelParts)
+    mla_sel_part<R>(m, x, qn, qr, U, P, qsel);
+  else
+    mla_absorb_block(m, (x - kMlaSelParts) >> 2, (x - kMlaSelParts) & 3, qn, qr, Wuk, qa);
 }
 
 // ---------------------------------------------------------------------------
@@ -677,16 +749,26 @@ hipError_t launch_mla_project(const MlaDev& m, const uint16_t* latent, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
-                             const uint16_t* W_uk, const float* P, float* q_abs, float* q_sel, hipStream_t st) {
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(m.H, kDl / 128), dim3(256), 0, st, m, q_nope, q_rope, W_uk, q_abs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid(m.B, kMlaSelParts);
+hipError_t launch_mla_fold(const MlaDev& m, const uint16_t* W_uk, const float* P, float* U, hipStream_t st) {
+  const dim3 grid(m.H, 128);
   switch (m.r) {
-    case 16: hipLaunchKernelGGL(mla_selq_kernel<16>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
-    case 32: hipLaunchKernelGGL(mla_selq_kernel<32>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
-    case 64: hipLaunchKernelGGL(mla_selq_kernel<64>, grid, dim3(256), 0, st, m, q_abs, P, q_sel); break;
+    case 16: hipLaunchKernelGGL(mla_fold_kernel<16>, grid, dim3(16), 0, st, W_uk, P, U); break;
+    case 32: hipLaunchKernelGGL(mla_fold_kernel<32>, grid, dim3(32), 0, st, W_uk, P, U); break;
+    case 64: hipLaunchKernelGGL(mla_fold_kernel<64>, grid, dim3(64), 0, st, W_uk, P, U); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_absorb(const MlaDev& m, const uint16_t* q_nope, const uint16_t* q_rope,
+                             const uint16_t* W_uk, const float* P, const float* U, float* q_abs, float* q_sel,
+                             hipStream_t st) {
+  // the selection parts first in launch order: the score pass waits on them
+  const dim3 grid(kMlaSelParts + m.H * (kDl / 128));
+  switch (m.r) {
+    case 16: hipLaunchKernelGGL(mla_queries_kernel<16>, grid, dim3(256), 0, st, m, q_nope, q_rope, W_uk, U, P, q_abs, q_sel); break;
+    case 32: hipLaunchKernelGGL(mla_queries_kernel<32>, grid, dim3(256), 0, st, m, q_nope, q_rope, W_uk, U, P, q_abs, q_sel); break;
+    case 64: hipLaunchKernelGGL(mla_queries_kernel<64>, grid, dim3(256), 0, st, m, q_nope, q_rope, W_uk, U, P, q_abs, q_sel); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

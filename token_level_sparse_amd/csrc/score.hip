@@ -8,8 +8,8 @@
 // 2r bytes per token and does r FMAs. For the MLA latent cache the same
 // stream runs with the selection query qp = P^T (sum over all heads of the
 // absorbed query), which the absorb step writes as kMlaSelParts partial
-// sums (one per 64-dim block of the latent + rope dims); every block adds
-// them in the same fixed order in its prologue.
+// sums (one per class of heads); every block adds them in the same fixed
+// order in its prologue.
 //
 // HBM-bound streaming kernel. Each wave reads a tile of 64 tokens' projected
 // keys as 64*r/8 contiguous 16-byte pieces, one coalesced dwordx4 load per

@@ -33,7 +33,7 @@ ENTRY_POINTS = (
     "jssa_score_topk_final",
     "jssa_score_topk_final_attend",
     "jssa_indexed_decode", "jssa_combine", "jssa_dense_decode", "jssa_gather_kv",
-    "jssa_mla_project_latent", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_score_topk_workspace_size",
+    "jssa_mla_project_latent", "jssa_mla_fold_selection", "jssa_mla_absorb_q", "jssa_mla_score", "jssa_mla_score_topk_workspace_size",
     "jssa_mla_score_topk", "jssa_mla_indexed_decode", "jssa_mla_combine_up_v",
     "jssa_mla_up_v", "jssa_score_topdelta_workspace_size", "jssa_score_topdelta", "jssa_score_topdelta_attend",
     "jssa_tile_bounds_size", "jssa_build_tile_bounds", "jssa_update_tile_bounds",
@@ -86,7 +86,8 @@ _SIGS = {
     "jssa_dense_decode": [_P(GqaDesc), _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp],
     "jssa_gather_kv": [_P(GqaDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp],
     "jssa_mla_project_latent": [_P(MlaDesc), _vp, _vp, _vp, _vp],
-    "jssa_mla_absorb_q": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "jssa_mla_fold_selection": [_P(MlaDesc), _vp, _vp, _vp, _vp],
+    "jssa_mla_absorb_q": [_P(MlaDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "jssa_mla_score": [_P(MlaDesc), _vp, _vp, _vp, _vp],
     "jssa_mla_score_topk_workspace_size": [_P(MlaDesc), _i32, _P(_sz)],
     "jssa_mla_score_topk": [_P(MlaDesc), _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
@@ -258,8 +259,13 @@ def jssa_mla_project_latent(desc, latent, P, Kp_lat, stream=None):
            "jssa_mla_project_latent")
 
 
-def jssa_mla_absorb_q(desc, q_nope, q_rope, W_uk, P, q_abs, q_sel, stream=None):
-    _check(_lib.jssa_mla_absorb_q(ctypes.byref(desc), _p(q_nope), _p(q_rope), _p(W_uk), _p(P), _p(q_abs),
+def jssa_mla_fold_selection(desc, W_uk, P, U, stream=None):
+    _check(_lib.jssa_mla_fold_selection(ctypes.byref(desc), _p(W_uk), _p(P), _p(U), _s(stream)),
+           "jssa_mla_fold_selection")
+
+
+def jssa_mla_absorb_q(desc, q_nope, q_rope, W_uk, P, U, q_abs, q_sel, stream=None):
+    _check(_lib.jssa_mla_absorb_q(ctypes.byref(desc), _p(q_nope), _p(q_rope), _p(W_uk), _p(P), _p(U), _p(q_abs),
                                   _p(q_sel), _s(stream)), "jssa_mla_absorb_q")
 
 

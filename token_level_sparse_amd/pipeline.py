@@ -253,7 +253,8 @@ class MlaStep:
         B, H = cfg.B, cfg.H
         self.Kp = torch.zeros((B, cfg.T, cfg.r), dtype=torch.int16, device=device)
         self.q_abs = torch.empty((B, H, cfg.d_c), dtype=torch.float32, device=device)
-        self.q_sel = torch.empty((B, 9, cfg.r), dtype=torch.float32, device=device)   # the query in 9 parts
+        self.U = torch.empty((H, cfg.d_nope, cfg.r), dtype=torch.float32, device=device)   # W_uk[h] . P_lat
+        self.q_sel = torch.empty((B, 64, cfg.r), dtype=torch.float32, device=device)   # the query in 64 parts
         self.scores = torch.empty((B, cfg.T), dtype=torch.float32, device=device)
         nbytes = max(jssa.jssa_topk_workspace_size(B, 1, cfg.T, cfg.k),
                      jssa.jssa_mla_score_topk_workspace_size(self.desc, cfg.k))
@@ -266,12 +267,14 @@ class MlaStep:
         self.out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=device)
 
     def project(self, stream=None):
+        """Set-up: the projected latent cache and the folded selection weights."""
         jssa.jssa_mla_project_latent(self.desc, self.latent, self.P, self.Kp, stream)
+        jssa.jssa_mla_fold_selection(self.desc, self.W_uk, self.P, self.U, stream)
 
     def run(self, stream=None):
         cfg = self.cfg
-        jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.P, self.q_abs, self.q_sel,
-                               stream)
+        jssa.jssa_mla_absorb_q(self.desc, self.q_nope, self.q_rope, self.W_uk, self.P, self.U, self.q_abs,
+                               self.q_sel, stream)
         jssa.jssa_mla_score_topk(self.desc, self.q_sel, self.Kp, self.k, self.scores, self.idx, self.ws, None,
                                  stream)
         jssa.jssa_mla_indexed_decode(self.desc, self.q_abs, self.latent, self.idx, self.k, self.S,
