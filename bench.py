@@ -662,14 +662,21 @@ def bench_mla(args, cfg, torch, pipeline, synth, stream):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping numbers (a virtualised host may give only a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                                   # the first processor's block
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 if __name__ == "__main__":
