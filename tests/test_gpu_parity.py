@@ -1001,12 +1001,14 @@ def test_mla_parity(J, PL, seed, B, T, k, S):
     _mla_parity(PL, replace(synth.MLA_DSV3, B=B, T=T, k=k, seed=seed), S)
 
 
-@pytest.mark.parametrize("H", [48, 192])
-def test_mla_parity_head_counts(J, PL, H):
-    """Head counts other than 128: with 48 heads, 16 of the 64 selection
-    query classes hold no head (their parts are 0); with 192, each class
-    holds 3 heads, so its second chunk of 2 is partial."""
-    _mla_parity(PL, replace(synth.MLA_DSV3, B=3, H=H, T=3000, k=300, seed=29 + H), 4)
+@pytest.mark.parametrize("H,B", [(48, 3), (192, 3), (128, 9)])
+def test_mla_parity_head_counts(J, PL, H, B):
+    """Head and sequence counts beside the workload's: with 48 heads, 16 of
+    the 64 selection query classes hold no head (their parts are 0); with
+    192, each class holds 3 heads, so its second chunk of 2 is partial; 9
+    sequences take the query blocks through a second pass (sequences go 4
+    at a time through a selection block, 8 through an absorb block)."""
+    _mla_parity(PL, replace(synth.MLA_DSV3, B=B, H=H, T=3000 if B < 8 else 1500, k=300, seed=29 + H + B), 4)
 
 
 def _mla_parity(PL, cfg, S):
