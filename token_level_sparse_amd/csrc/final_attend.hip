@@ -41,18 +41,7 @@ constexpr int kBinsPT = kBins / kNT;    // bins per thread in a scan
 constexpr int kSmallBin = 64;           // a bin this small is finished by one wave
 constexpr int kMaxSel = 512;            // selected tokens held in LDS
 
-// Inclusive scan over the 64 lanes of a wave: DPP shifts inside each 16-lane
-// row, then the totals of the rows before (read out of lanes 15, 31, 47).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
-  const int r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
+// (wave_incl_scan, the DPP wave scan, comes from select.hpp)
 
 template <int GT>
 struct FaSmem {

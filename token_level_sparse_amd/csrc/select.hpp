@@ -55,15 +55,25 @@ struct ScanSmem {
   int sc[NT / 64];
 };
 
+// Inclusive scan over the 64 lanes of a wave: DPP shifts inside each 16-lane
+// row (no LDS round trip), then the totals of the rows before, read out of
+// lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // Inclusive scan over the NT threads of the block; total in *tot.
 template <int NT>
 __device__ __forceinline__ int block_scan(int v, ScanSmem<NT>& s, int* tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) s.sc[w] = v;
   __syncthreads();
   int pre = 0, t = 0;
