@@ -122,8 +122,7 @@ __device__ __forceinline__ void attn_batch(const GqaDev& g, int b, int j, int Tb
     float mb = lg[0][h];
 #pragma unroll
     for (int st = 1; st < STEPS; ++st) mb = fmaxf(mb, lg[st][h]);
-    mb = xor_max(mb, 16);
-    mb = xor_max(mb, 32);
+    mb = rows_max(mb);                          // (lg is uniform inside each 16-lane row)
     const float mn = fmaxf(A.m[h], mb);
     if (mn == -__builtin_inff()) continue;      // nothing valid yet (wave-uniform)
     const float alpha = __builtin_amdgcn_exp2f(A.m[h] - mn);
@@ -157,7 +156,7 @@ template <int GT>
 __device__ __forceinline__ void attn_wave_reduce(AttnAcc<GT>& A) {
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
-    A.l[h] = xor_sum(xor_sum(A.l[h], 16), 32);
+    A.l[h] = rows_sum(A.l[h]);                  // (l is uniform inside each 16-lane row)
 #pragma unroll
     for (int e = 0; e < 8; ++e) A.o[h][e] = xor_sum(xor_sum(A.o[h][e], 16), 32);
   }

@@ -103,6 +103,25 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
 }
 
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m, kWave)); }
+
+// Max and sum over the four 16-lane rows of a wave of a value that is
+// uniform inside each row: four read-lanes, no LDS round trip. The sum is
+// added as the xor-16 then xor-32 butterfly adds it, (row0 + row1) + (row2 +
+// row3), so the result is bit-identical to it.
+__device__ __forceinline__ float rows_max(float x) {
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m, kWave); }
 
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 == +0.

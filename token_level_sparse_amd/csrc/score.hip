@@ -510,11 +510,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FUS
           const uint32_t x = score_key(stage[sidx(t - t_begin)]);
           v = x > v ? x : v;
         }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = uint32_t(__shfl_xor(int(v), o, 64));
-          v = y > v ? y : v;
-        }
+        v = wave_max_u32(v);
         if (lane == 0) pred[w] = v;
         __syncthreads();
 #pragma unroll

@@ -185,16 +185,8 @@ __device__ void chunk_select(const uint32_t (&key)[E], int base, int lim, int n,
       if (__popcll(__ballot(m2 >= c)) >= r) bound2 = c;
     }
   }
-  uint32_t mx = m1, mnmx = m1, mn = tmin;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t a = uint32_t(__shfl_xor(int(mx), o, 64));
-    const uint32_t c = uint32_t(__shfl_xor(int(mnmx), o, 64));
-    const uint32_t d = uint32_t(__shfl_xor(int(mn), o, 64));
-    mx = a > mx ? a : mx;
-    mnmx = c < mnmx ? c : mnmx;
-    mn = d < mn ? d : mn;
-  }
+  // (DPP inside rows, read-lanes across them: no LDS round trips)
+  const uint32_t mx = wave_max_u32(m1), mnmx = wave_min_u32(m1), mn = wave_min_u32(tmin);
   nc = wave_sum_u32(nc);
   if (lane == 0) {
     sm.red[0][wv] = mx;
@@ -393,14 +385,7 @@ __device__ bool chunk_select_top2(const uint32_t (&key)[E], int base, int k, Top
     m2 = y > m2 ? y : m2;
     m1 = x > m1 ? x : m1;
   }
-  uint32_t hi = m1, lo = m2;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t a = uint32_t(__shfl_xor(int(hi), o, 64));
-    const uint32_t b = uint32_t(__shfl_xor(int(lo), o, 64));
-    hi = a > hi ? a : hi;
-    lo = b < lo ? b : lo;
-  }
+  uint32_t hi = wave_max_u32(m1), lo = wave_min_u32(m2);   // (DPP: no LDS round trips)
   if (lane == 0) {
     sm.red[0][wv] = hi;
     sm.red[1][wv] = lo;
