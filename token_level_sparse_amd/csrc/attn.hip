@@ -63,13 +63,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(GqaDev g, const uint16_t*
       attn_batch<GT, STEPS, PAGED>(g, b, j, Tb, K, V, qv, qs, base, r1, [&](int rr) { return irow[rr]; }, A);
   }
   attn_wave_reduce(A);
+  auto od = [&](int h) { return part_o + ((int64_t(b) * g.Hq + h0 + h) * S + s) * kAttnD; };
+  auto ld = [&](int h) { return part_lse + (int64_t(b) * g.Hq + h0 + h) * S + s; };
   if constexpr (NW > 1) {
     __shared__ AttnMergeSmem<GT, NW> msm;
-    attn_block_merge(A, msm);
-    if (w != 0) return;
+    attn_block_merge_store(A, msm, nh, od, ld);
+  } else {
+    attn_store(A, nh, od, ld);
   }
-  attn_store(A, nh, [&](int h) { return part_o + ((int64_t(b) * g.Hq + h0 + h) * S + s) * kAttnD; },
-             [&](int h) { return part_lse + (int64_t(b) * g.Hq + h0 + h) * S + s; });
 }
 
 template <int GT, int STEPS, int NW, bool DENSE>

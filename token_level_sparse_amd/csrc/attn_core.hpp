@@ -163,16 +163,24 @@ __device__ __forceinline__ void attn_wave_reduce(AttnAcc<GT>& A) {
 }
 
 template <int GT, int NW>
-struct AttnMergeSmem {
+struct __attribute__((aligned(16))) AttnMergeSmem {
   float m[NW][GT], l[NW][GT];
-  float o[NW][GT][kAttnD];
+  float o[NW][GT][kAttnD];                      // at a 16-byte offset (8 NW GT bytes before it, NW >= 2)
 };
 
-// Merge the NW waves' (reduced) states through LDS into wave 0. Every thread
-// of the block must call it; afterwards wave 0 holds the merged state.
-template <int GT, int NW>
-__device__ __forceinline__ void attn_block_merge(AttnAcc<GT>& A, AttnMergeSmem<GT, NW>& sm) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, sub = lane & 15;
+// Merge the NW waves' (reduced) states through LDS and store the normalised
+// outputs and lse of the block's first nh heads. The merge is spread over
+// the block: thread i < nh * 32 takes head i / 32, dims 4 (i % 32) .. +3,
+// and adds the waves in order 0 .. NW-1, each weighted by exp2(m_w - M)
+// with M the largest m_w; then o / L and lse = (M + log2 L) ln 2. (With one
+// wave walking every head and every wave's state in turn instead, blocks
+// of 8 waves took 1.3 us more for 2 heads and 3.6 us more for 5.) Every
+// thread of the block must call it.
+template <int GT, int NW, class ODst, class LDst>
+__device__ __forceinline__ void attn_block_merge_store(const AttnAcc<GT>& A, AttnMergeSmem<GT, NW>& sm, int nh,
+                                                       ODst o_dst, LDst lse_dst) {
+  static_assert(__builtin_offsetof(AttnMergeSmem<GT, NW>, o) % 16 == 0, "16-byte reads of the merged outputs");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, sub = lane & 15;
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
@@ -188,26 +196,28 @@ __device__ __forceinline__ void attn_block_merge(AttnAcc<GT>& A, AttnMergeSmem<G
     }
   }
   __syncthreads();
-  if (w != 0) return;
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
+  for (int i = tid; i < nh * 32; i += NW * 64) {
+    const int h = i / 32, d = 4 * (i % 32);
     float M = -__builtin_inff();
 #pragma unroll
     for (int x = 0; x < NW; ++x) M = fmaxf(M, sm.m[x][h]);
-    float L = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (M != -__builtin_inff()) {
 #pragma unroll
       for (int x = 0; x < NW; ++x) {
         const float f = __builtin_amdgcn_exp2f(sm.m[x][h] - M);
         L += sm.l[x][h] * f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += sm.o[x][h][sub * 8 + e] * f;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(&sm.o[x][h][d]);
+        acc.x += o.x * f;
+        acc.y += o.y * f;
+        acc.z += o.z * f;
+        acc.w += o.w * f;
       }
     }
-    A.m[h] = M;
-    A.l[h] = L;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) A.o[h][e] = acc[e];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<f32x4*>(o_dst(h) + d) = f32x4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (d == 0) *lse_dst(h) = L > 0.f ? (M + __builtin_log2f(L)) * kAttnLn2 : -__builtin_inff();
   }
 }
 

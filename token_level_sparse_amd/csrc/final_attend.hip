@@ -320,10 +320,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int base = wv * RB; base < cnt_sel; base += kNW * RB)
       attn_batch<GT, STEPS, PAGED>(g, b, j, Tb, a.K, a.V, qv, qs, base, cnt_sel, [&](int rr) { return sm.sel[rr]; }, A);
     attn_wave_reduce(A);
-    attn_block_merge(A, sm.msm);
-    if (wv == 0)
-      attn_store(A, nh, [&](int h) { return a.out + (int64_t(b) * g.Hq + h0 + h) * kAttnD; },
-                 [&](int h) { return a.lse + int64_t(b) * g.Hq + h0 + h; });
+    attn_block_merge_store(A, sm.msm, nh, [&](int h) { return a.out + (int64_t(b) * g.Hq + h0 + h) * kAttnD; },
+                           [&](int h) { return a.lse + int64_t(b) * g.Hq + h0 + h; });
     if (hl + GT < hb1) __syncthreads();                 // msm is reused by the next head group
   }
   // The indices leave last, coalesced from LDS: a store issued before the
