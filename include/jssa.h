@@ -164,7 +164,7 @@ JSSA_API jssa_status jssa_topk(int32_t B, int32_t H, int32_t max_seq, const int3
  * (jssa_score_topk_final); jssa_score_topk issues both.
  * For budgets whose per-chunk candidates would need more than one final
  * pass (chunks x k > 8192), each chunk instead keeps only its own best
- * (about 4x its share of k) and writes its scores below T_b to the
+ * (3x its share of k) and writes its scores below T_b to the
  * workspace; the final pass checks, once the row's k-th key is known, that
  * every chunk that dropped tokens dropped only keys below it, and selects a
  * row that fails that check again from its scores. The indices are the same
@@ -363,7 +363,7 @@ JSSA_API jssa_status jssa_mla_score(const jssa_mla_desc* desc, const float* q_se
  * scores and the same idx [B,k], in fewer and cheaper passes (per sequence
  * one selection over the shared latent cache, digest Perspective; ties and
  * absent tokens as jssa_topk). The score stream also keeps each 1024-token
- * chunk's own best tokens (about 4x its share of k, at least 64), and one
+ * chunk's own best tokens (3x its share of k, at least 48), and one
  * final pass per sequence selects from the union of those lists. The union
  * holds the sequence's top k unless a chunk held more of them than its list
  * (checked on the device once the k-th key is known); such a sequence is

@@ -119,7 +119,7 @@ namespace {
 // token that can be among its row's top k (candidate segments of
 // score_topk_segment_cap(k)), merged level by level when a row's lists are
 // too long for one final pass. Lists (budgets whose candidates would need a
-// merge level): each chunk keeps only its own top kc, kc = 4x the chunk's
+// merge level): each chunk keeps only its own top kc, kc = 3x the chunk's
 // share of k; one final pass selects from their union and checks that the
 // union held the row's top k, selecting the row again from its scores when
 // it did not (so the stream also writes the scores, into the workspace).
@@ -134,7 +134,7 @@ struct TopkWs {
 int gqa_list_k(int max_seq, int k) {
   const int nseg = jssa::score_topk_segments(max_seq);
   if (nseg <= 1 || int64_t(nseg) * k <= 8192) return 0;          // one final pass already
-  int kc = 4 * ((k + nseg - 1) / nseg);
+  int kc = 3 * ((k + nseg - 1) / nseg);
   kc = kc < 64 ? 64 : kc;
   kc = (kc + 3) & ~3;
   return 2 * kc <= k ? kc : 0;
