@@ -125,10 +125,11 @@ __global__ __launch_bounds__(R) void mla_fold_kernel(const uint16_t* __restrict_
 // score passes add the parts in order, which gives P^T sum_h q_abs[b,h].
 // A class's heads go in chunks of 2: 320 reduction rows per chunk (256 rows
 // U[h][n] against q_nope[b,h,n], 64 rows P[512 + e] against the chunk's
-// rope values summed over its heads in head order). Thread (rq, sl) owns columns 4rq .. 4rq+3 and
-// rows sl, sl + NS, ... (all its row loads in flight at once, after the
-// query loads); the NS slices meet in LDS in order. Fixed summation orders
-// throughout: every call gives the same query.
+// rope values summed over its heads in head order). Thread (rq, sl) owns
+// columns 4rq .. 4rq+3 and rows sl, sl + NS, ... (all its row loads in
+// flight at once, after the query loads); the NS slices meet in LDS in
+// order. Fixed summation orders throughout: every call gives the same
+// query.
 //
 // Absorbed query (the other blocks, one per (h, column quarter)):
 // q_abs[b,h,c] = sum_i q_nope[b,h,i] W_uk[h,i,c] for c < 512 (fp32), then
