@@ -252,7 +252,10 @@ def _sparse_and_check(J, PL, inp, k, S, units=None, fused=False):
                                      # load while this one is multiplied), a partial last one
                                      (synth.LLAMA8B_32K, 1024, 1), (synth.TINY, 1000, 2),
                                      # splits past the list's end (k = 3 over 8 splits)
-                                     (synth.TINY, 3, 8)])
+                                     (synth.TINY, 3, 8),
+                                     # 2- and 4-wave attention blocks (33..64 and 65..128 rows
+                                     # per split), one with a partial batch
+                                     (synth.TINY, 64, 1), (synth.TINY, 128, 1), (synth.LLAMA8B_32K, 100, 1)])
 def test_sparse_step_parity(J, PL, cfg, k, S):
     _sparse_and_check(J, PL, synth.make_gqa(cfg), k, S)
 
